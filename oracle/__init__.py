@@ -1,0 +1,126 @@
+"""CPU oracle for the MXFP4 block-scaled cast and GEMM.
+
+TEST INFRASTRUCTURE.  Only the test suite, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  It shares no code
+with the HIP library and never imports it.
+
+What is computed follows the jax-aiter README ("Supported ops" table: the MXFP4
+cast turns BF16 into E2M1 elements plus E8M0 block scales, optionally with a
+transposed copy; the low-level FP4 GEMM consumes fp4x2 operands with e8m0
+block scales) together with the OCP Microscaling conversion rule that fills
+in what the page leaves open (block of 32, shared exponent floor(log2 amax)-2,
+round-to-nearest-even, saturation).
+
+Two implementations live here:
+
+* ``oracle.scalar`` -- pure Python on exact rationals, one block at a time,
+  for hand-sized cases and brute force.
+* the C library ``mx_oracle.c`` wrapped below with numpy, for full-size data.
+
+Canonical layouts (all row-major, no padding except where stated):
+
+* row copy of x [R, C]:   q [R, C/2] uint8 (element 2j in the low nibble of
+  byte j, 2j+1 in the high nibble), s [R, C/32] uint8 (E8M0 = X + 127)
+* column copy of x [R, C]: q [C, Rp/2], s [C, Rp/32], Rp = ceil(R/32)*32; the
+  rows past R are +0
+* GEMM: ref[m, n] = sum_k dq(a)[m, k] * dq(b)[n, k] in fp64, and
+  absref[m, n] = sum_k |dq(a)[m, k] * dq(b)[n, k]|
+"""
+import os
+
+import numpy as np
+
+from . import native
+from . import scalar  # noqa: F401  (re-exported for tests)
+
+
+def _threads(nthreads):
+    if nthreads is None:
+        return len(os.sched_getaffinity(0))
+    return int(nthreads)
+
+
+def _bits(x):
+    x = np.ascontiguousarray(x)
+    if x.dtype != np.uint16:
+        raise TypeError("oracle inputs are bf16 bit patterns as uint16")
+    if x.ndim != 2:
+        raise ValueError("expected a 2-D array")
+    return x
+
+
+def cast_rows(x_bits, nthreads=None):
+    """Row copy: blocks of 32 along the contiguous dim.  Returns (q, s)."""
+    x = _bits(x_bits)
+    R, C = x.shape
+    if C % 32:
+        raise ValueError("the number of columns must be a multiple of 32")
+    q = np.empty((R, C // 2), np.uint8)
+    s = np.empty((R, C // 32), np.uint8)
+    rc = native.lib().mxo_cast_rows(x.ctypes.data, R, C, C, q.ctypes.data, s.ctypes.data, _threads(nthreads))
+    if rc:
+        raise RuntimeError("mxo_cast_rows failed")
+    return q, s
+
+
+def cast_cols(x_bits, nthreads=None):
+    """Column copy: blocks of 32 rows in each column, rows padded with +0.  Returns (q, s)."""
+    x = _bits(x_bits)
+    R, C = x.shape
+    Rp = -(-R // 32) * 32
+    q = np.empty((C, Rp // 2), np.uint8)
+    s = np.empty((C, Rp // 32), np.uint8)
+    rc = native.lib().mxo_cast_cols(x.ctypes.data, R, C, C, q.ctypes.data, s.ctypes.data, _threads(nthreads))
+    if rc:
+        raise RuntimeError("mxo_cast_cols failed")
+    return q, s
+
+
+def dequant(q, s):
+    """Dequantized values (fp64) of a canonical (q, s) pair."""
+    q = np.ascontiguousarray(q, np.uint8)
+    s = np.ascontiguousarray(s, np.uint8)
+    R, K = q.shape[0], q.shape[1] * 2
+    if s.shape != (R, K // 32):
+        raise ValueError("scale shape does not match the codes")
+    out = np.empty((R, K), np.float64)
+    if native.lib().mxo_dequant(q.ctypes.data, s.ctypes.data, R, K, out.ctypes.data):
+        raise RuntimeError("mxo_dequant failed")
+    return out
+
+
+def _gemm_args(qa, sa, qb, sb):
+    qa, sa, qb, sb = (np.ascontiguousarray(t, np.uint8) for t in (qa, sa, qb, sb))
+    M, N, K = qa.shape[0], qb.shape[0], qa.shape[1] * 2
+    if qb.shape[1] * 2 != K or sa.shape != (M, K // 32) or sb.shape != (N, K // 32):
+        raise ValueError("operand shapes do not agree")
+    return qa, sa, qb, sb, M, N, K
+
+
+def gemm(qa, sa, qb, sb, nthreads=None):
+    """Full ref/absref [M, N] for out = A . B^T on canonical operands."""
+    qa, sa, qb, sb, M, N, K = _gemm_args(qa, sa, qb, sb)
+    ref = np.empty((M, N), np.float64)
+    absref = np.empty((M, N), np.float64)
+    rc = native.lib().mxo_gemm(qa.ctypes.data, sa.ctypes.data, qb.ctypes.data, sb.ctypes.data, M, N, K,
+                               ref.ctypes.data, absref.ctypes.data, _threads(nthreads))
+    if rc:
+        raise RuntimeError("mxo_gemm failed")
+    return ref, absref
+
+
+def gemm_pairs(qa, sa, qb, sb, mi, ni, nthreads=None):
+    """ref/absref at the sampled outputs (mi[i], ni[i])."""
+    qa, sa, qb, sb, M, N, K = _gemm_args(qa, sa, qb, sb)
+    mi = np.ascontiguousarray(mi, np.int64)
+    ni = np.ascontiguousarray(ni, np.int64)
+    if mi.shape != ni.shape or mi.ndim != 1:
+        raise ValueError("mi and ni must be 1-D and of equal length")
+    ref = np.empty(mi.shape, np.float64)
+    absref = np.empty(mi.shape, np.float64)
+    rc = native.lib().mxo_gemm_pairs(qa.ctypes.data, sa.ctypes.data, qb.ctypes.data, sb.ctypes.data, M, N, K,
+                                     mi.ctypes.data, ni.ctypes.data, mi.size, ref.ctypes.data, absref.ctypes.data,
+                                     _threads(nthreads))
+    if rc:
+        raise RuntimeError("mxo_gemm_pairs failed")
+    return ref, absref

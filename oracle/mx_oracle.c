@@ -1,0 +1,305 @@
+/*
+ * CPU oracle for the MXFP4 block-scaled cast and the block-scaled GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or calls
+ * this file; only the test suite, the smoke check and the benchmark's CPU
+ * baseline do.  It shares no code, header, table or helper with the HIP
+ * library.
+ *
+ * What it computes (jax-aiter README, "Supported ops" table, rows "MXFP4
+ * Cast" and "FP4 GEMM (low-level)": BF16 is cast to E2M1 elements with one
+ * E8M0 block scale, two E2M1 codes per byte; the GEMM consumes those packed
+ * operands with their e8m0 scales and returns BF16):
+ *
+ *   block   : 32 consecutive elements along the contraction dimension
+ *   scale   : X = floor(log2(max |x| over the block)) - 2, clamped to
+ *             [-127, 127]; an all-zero block gets X = -127; the stored E8M0
+ *             byte is X + 127 (OCP Microscaling v1.0 conversion rule)
+ *   element : x / 2^X rounded to the nearest E2M1 value, ties to the code
+ *             whose mantissa bit is 0, magnitudes past 6 go to 6; the sign
+ *             bit is the sign bit of x (so -0 and small negatives give 0x8)
+ *   packing : byte j of a row holds element 2j in bits 0..3 and element 2j+1
+ *             in bits 4..7
+ *   GEMM    : out[m,n] = sum over blocks b of 2^(Xa+Xb) * sum_{k in b}
+ *             e2m1(a[m,k]) * e2m1(b[n,k]); the inner sums are formed exactly
+ *             as integers (2*e2m1 is an integer) and the blocks are added in
+ *             fp64 in increasing b.
+ *
+ * A block that holds an Inf or NaN gets scale byte 0xFF (the E8M0 NaN) and
+ * element codes 0; a GEMM output that touches a 0xFF scale is NaN.
+ *
+ * Plain C99 + pthreads.  Row-parallel; no blocking or reordering of the sums
+ * beyond the definition above.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define MXO_BLOCK 32
+
+/* ---- bf16 decoding (IEEE-754 binary32 with the low 16 bits dropped) ---- */
+
+static int bf16_is_finite(uint16_t h) { return ((h >> 7) & 0xFF) != 0xFF; }
+
+/* Exact value of a finite bf16 as a double. */
+static double bf16_value(uint16_t h) {
+    int sign = h >> 15;
+    int e = (h >> 7) & 0xFF;
+    int m = h & 0x7F;
+    double mag;
+    if (e == 0) mag = ldexp((double)m, -133);          /* subnormal: m * 2^-126 * 2^-7 */
+    else mag = ldexp((double)(128 + m), e - 127 - 7);  /* normal: (1 + m/128) * 2^(e-127) */
+    return sign ? -mag : mag;
+}
+
+/* ---- E2M1 (1 sign bit, 2 exponent bits with bias 1, 1 mantissa bit) ---- */
+
+/* Magnitude of E2M1 code c (0..7) as a double, from the bit fields. */
+static double e2m1_magnitude(int c) {
+    int e = (c >> 1) & 3;
+    int m = c & 1;
+    if (e == 0) return 0.5 * m;                       /* subnormal: 2^(1-1) * m/2 */
+    return ldexp(1.0 + 0.5 * m, e - 1);
+}
+
+/* Nearest E2M1 magnitude code for a = |v|; ties go to the even code. */
+static int e2m1_round(double a) {
+    if (a > 6.0) return 7;   /* saturation: anything past the largest E2M1 magnitude maps to it */
+    int best = 0;
+    double bestd = fabs(a - e2m1_magnitude(0));
+    for (int c = 1; c < 8; ++c) {
+        double d = fabs(a - e2m1_magnitude(c));
+        if (d < bestd || (d == bestd && (c & 1) == 0 && (best & 1) == 1)) {
+            best = c;
+            bestd = d;
+        }
+    }
+    return best;
+}
+
+/* floor(log2(a)) for a finite a > 0, exactly (frexp returns a = f * 2^e, f in [0.5, 1)). */
+static int floor_log2(double a) {
+    int e;
+    frexp(a, &e);
+    return e - 1;
+}
+
+/* Quantize one block of n (<= 32) bf16 values read with stride `stride`;
+ * positions n..31 are +0 (padding).  Writes 32 codes and returns the scale byte. */
+static uint8_t quantize_block(const uint16_t* x, int64_t stride, int n, uint8_t codes[MXO_BLOCK]) {
+    double amax = 0.0;
+    for (int i = 0; i < n; ++i) {
+        uint16_t h = x[i * stride];
+        if (!bf16_is_finite(h)) {
+            memset(codes, 0, MXO_BLOCK);
+            return 0xFF;
+        }
+        double a = fabs(bf16_value(h));
+        if (a > amax) amax = a;
+    }
+    int X;
+    if (amax == 0.0) {
+        X = -127;
+    } else {
+        X = floor_log2(amax) - 2;
+        if (X < -127) X = -127;
+        if (X > 127) X = 127;
+    }
+    for (int i = 0; i < MXO_BLOCK; ++i) {
+        if (i >= n) { codes[i] = 0; continue; }
+        uint16_t h = x[i * stride];
+        double v = ldexp(fabs(bf16_value(h)), -X);   /* exact: power-of-two scaling */
+        codes[i] = (uint8_t)(e2m1_round(v) | ((h >> 15) << 3));
+    }
+    return (uint8_t)(X + 127);
+}
+
+/* ---- thread fan-out ---- */
+
+typedef void (*mxo_range_fn)(void* ctx, int64_t lo, int64_t hi);
+typedef struct { mxo_range_fn fn; void* ctx; int64_t lo, hi; } mxo_job;
+
+static void* mxo_run(void* p) {
+    mxo_job* j = (mxo_job*)p;
+    j->fn(j->ctx, j->lo, j->hi);
+    return NULL;
+}
+
+static void parallel_for(int64_t n, int nthreads, mxo_range_fn fn, void* ctx) {
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if ((int64_t)nthreads > n) nthreads = (int)(n > 0 ? n : 1);
+    if (nthreads == 1) { fn(ctx, 0, n); return; }
+    pthread_t th[256];
+    mxo_job jobs[256];
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t].fn = fn; jobs[t].ctx = ctx;
+        jobs[t].lo = n * t / nthreads; jobs[t].hi = n * (t + 1) / nthreads;
+        pthread_create(&th[t], NULL, mxo_run, &jobs[t]);
+    }
+    for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
+}
+
+/* ---- row copy: blocks along the contiguous dimension ---- */
+
+typedef struct { const uint16_t* x; int64_t R, C, ldx; uint8_t *q, *s; } cast_ctx;
+
+static void cast_rows_range(void* p, int64_t lo, int64_t hi) {
+    cast_ctx* c = (cast_ctx*)p;
+    uint8_t codes[MXO_BLOCK];
+    int64_t nb = c->C / MXO_BLOCK;
+    for (int64_t r = lo; r < hi; ++r) {
+        for (int64_t b = 0; b < nb; ++b) {
+            c->s[r * nb + b] = quantize_block(c->x + r * c->ldx + b * MXO_BLOCK, 1, MXO_BLOCK, codes);
+            uint8_t* qrow = c->q + r * (c->C / 2) + b * (MXO_BLOCK / 2);
+            for (int i = 0; i < MXO_BLOCK / 2; ++i) qrow[i] = (uint8_t)(codes[2 * i] | (codes[2 * i + 1] << 4));
+        }
+    }
+}
+
+/* x: bf16 bits [R, C] with row stride ldx (elements); C % 32 == 0.
+ * q: [R, C/2] packed codes; s: [R, C/32] scale bytes.  Returns 0 or -1. */
+int mxo_cast_rows(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint8_t* q, uint8_t* s, int nthreads) {
+    if (R < 0 || C < 0 || C % MXO_BLOCK != 0 || ldx < C) return -1;
+    cast_ctx c = {x, R, C, ldx, q, s};
+    parallel_for(R, nthreads, cast_rows_range, &c);
+    return 0;
+}
+
+/* ---- column copy: blocks of 32 rows within each column, rows padded with +0 ---- */
+
+static void cast_cols_range(void* p, int64_t lo, int64_t hi) {
+    cast_ctx* c = (cast_ctx*)p;
+    uint8_t codes[MXO_BLOCK];
+    int64_t nb = (c->R + MXO_BLOCK - 1) / MXO_BLOCK;
+    int64_t Rp = nb * MXO_BLOCK;
+    for (int64_t col = lo; col < hi; ++col) {
+        for (int64_t b = 0; b < nb; ++b) {
+            int64_t r0 = b * MXO_BLOCK;
+            int n = (int)((c->R - r0) < MXO_BLOCK ? (c->R - r0) : MXO_BLOCK);
+            c->s[col * nb + b] = quantize_block(c->x + r0 * c->ldx + col, c->ldx, n, codes);
+            uint8_t* qrow = c->q + col * (Rp / 2) + r0 / 2;
+            for (int i = 0; i < MXO_BLOCK / 2; ++i) qrow[i] = (uint8_t)(codes[2 * i] | (codes[2 * i + 1] << 4));
+        }
+    }
+}
+
+/* Column copy of x [R, C]: q [C, Rp/2], s [C, Rp/32] with Rp = ceil(R/32)*32. */
+int mxo_cast_cols(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint8_t* q, uint8_t* s, int nthreads) {
+    if (R < 0 || C < 0 || ldx < C) return -1;
+    cast_ctx c = {x, R, C, ldx, q, s};
+    parallel_for(C, nthreads, cast_cols_range, &c);
+    return 0;
+}
+
+/* ---- dequantization ---- */
+
+/* out[r, k] = e2m1(q[r,k]) * 2^(s[r, k/32] - 127), NaN for scale 0xFF.  K % 32 == 0. */
+int mxo_dequant(const uint8_t* q, const uint8_t* s, int64_t R, int64_t K, double* out) {
+    if (R < 0 || K < 0 || K % MXO_BLOCK != 0) return -1;
+    for (int64_t r = 0; r < R; ++r) {
+        for (int64_t k = 0; k < K; ++k) {
+            int code = (q[r * (K / 2) + k / 2] >> (4 * (k & 1))) & 0xF;
+            uint8_t sc = s[r * (K / MXO_BLOCK) + k / MXO_BLOCK];
+            double mag = e2m1_magnitude(code & 7);
+            double v = (code & 8) ? -mag : mag;
+            out[r * K + k] = sc == 0xFF ? NAN : ldexp(v, (int)sc - 127);
+        }
+    }
+    return 0;
+}
+
+/* ---- GEMM ---- */
+
+/* 2 * e2m1 value of each code, an integer in {0, +-1, +-2, +-3, +-4, +-6, +-8, +-12}. */
+static int twice_e2m1(int code) {
+    int v = (int)(2.0 * e2m1_magnitude(code & 7));
+    return (code & 8) ? -v : v;
+}
+
+typedef struct {
+    const uint8_t *qa, *sa, *qb, *sb;
+    int64_t M, N, K;
+    const int64_t *mi, *ni;   /* pair mode when non-null */
+    double *ref, *absref;
+} gemm_ctx;
+
+/* One output: sum over blocks of 2^(Xa+Xb-2) * (exact integer dot of 2*a and 2*b). */
+static void gemm_one(const gemm_ctx* g, const int8_t* ua, const int8_t* ub, int64_t m, int64_t n, double* ref, double* absref) {
+    int64_t nb = g->K / MXO_BLOCK;
+    double acc = 0.0, aacc = 0.0;
+    for (int64_t b = 0; b < nb; ++b) {
+        uint8_t xa = g->sa[m * nb + b], xb = g->sb[n * nb + b];
+        if (xa == 0xFF || xb == 0xFF) { acc = NAN; aacc = NAN; continue; }
+        int32_t dot = 0, adot = 0;
+        const int8_t* pa = ua + b * MXO_BLOCK;
+        const int8_t* pb = ub + b * MXO_BLOCK;
+        for (int i = 0; i < MXO_BLOCK; ++i) {
+            int32_t p = (int32_t)pa[i] * (int32_t)pb[i];
+            dot += p;
+            adot += p < 0 ? -p : p;
+        }
+        int e = (int)xa + (int)xb - 254 - 2;
+        acc += ldexp((double)dot, e);
+        aacc += ldexp((double)adot, e);
+    }
+    *ref = acc;
+    *absref = aacc;
+}
+
+static void unpack_row(const uint8_t* q, int64_t K, int8_t* u) {
+    for (int64_t k = 0; k < K; ++k) u[k] = (int8_t)twice_e2m1((q[k / 2] >> (4 * (k & 1))) & 0xF);
+}
+
+static void gemm_rows_range(void* p, int64_t lo, int64_t hi) {
+    gemm_ctx* g = (gemm_ctx*)p;
+    int8_t* ua = (int8_t*)malloc((size_t)(g->K > 0 ? g->K : 1));
+    int8_t* ub = (int8_t*)malloc((size_t)(g->K > 0 ? g->K : 1) * (size_t)(g->N > 0 ? g->N : 1));
+    /* B is unpacked once per worker; each A row once. */
+    for (int64_t n = 0; n < g->N; ++n) unpack_row(g->qb + n * (g->K / 2), g->K, ub + n * g->K);
+    for (int64_t m = lo; m < hi; ++m) {
+        unpack_row(g->qa + m * (g->K / 2), g->K, ua);
+        for (int64_t n = 0; n < g->N; ++n)
+            gemm_one(g, ua, ub + n * g->K, m, n, &g->ref[m * g->N + n], &g->absref[m * g->N + n]);
+    }
+    free(ua);
+    free(ub);
+}
+
+/* ref[m,n], absref[m,n] (= sum_k |a_k b_k| of the dequantized operands) for
+ * a: q [M, K/2], s [M, K/32]; b: q [N, K/2], s [N, K/32].  K % 32 == 0. */
+int mxo_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb, int64_t M, int64_t N,
+             int64_t K, double* ref, double* absref, int nthreads) {
+    if (M < 0 || N < 0 || K < 0 || K % MXO_BLOCK != 0) return -1;
+    gemm_ctx g = {qa, sa, qb, sb, M, N, K, NULL, NULL, ref, absref};
+    parallel_for(M, nthreads, gemm_rows_range, &g);
+    return 0;
+}
+
+static void gemm_pairs_range(void* p, int64_t lo, int64_t hi) {
+    gemm_ctx* g = (gemm_ctx*)p;
+    int8_t* ua = (int8_t*)malloc((size_t)(g->K > 0 ? g->K : 1));
+    int8_t* ub = (int8_t*)malloc((size_t)(g->K > 0 ? g->K : 1));
+    for (int64_t i = lo; i < hi; ++i) {
+        int64_t m = g->mi[i], n = g->ni[i];
+        unpack_row(g->qa + m * (g->K / 2), g->K, ua);
+        unpack_row(g->qb + n * (g->K / 2), g->K, ub);
+        gemm_one(g, ua, ub, m, n, &g->ref[i], &g->absref[i]);
+    }
+    free(ua);
+    free(ub);
+}
+
+/* Sampled outputs: ref[i] = out[mi[i], ni[i]] (indices must be in range). */
+int mxo_gemm_pairs(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb, int64_t M, int64_t N,
+                   int64_t K, const int64_t* mi, const int64_t* ni, int64_t npairs, double* ref, double* absref,
+                   int nthreads) {
+    if (M < 0 || N < 0 || K < 0 || K % MXO_BLOCK != 0 || npairs < 0) return -1;
+    for (int64_t i = 0; i < npairs; ++i)
+        if (mi[i] < 0 || mi[i] >= M || ni[i] < 0 || ni[i] >= N) return -1;
+    gemm_ctx g = {qa, sa, qb, sb, M, N, K, mi, ni, ref, absref};
+    parallel_for(npairs, nthreads, gemm_pairs_range, &g);
+    return 0;
+}

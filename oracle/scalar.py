@@ -1,0 +1,135 @@
+"""Exact, one-block-at-a-time MXFP4 reference on Python rationals.
+
+TEST INFRASTRUCTURE (see the package docstring).  Every quantity is a
+``fractions.Fraction``, so nothing here is subject to floating-point rounding.
+
+Formats (jax-aiter README, "Supported ops": E2M1 elements, E8M0 block scales,
+fp4x2 packing; field layouts from the OCP Microscaling v1.0 specification):
+
+* bf16: 1 sign, 8 exponent (bias 127), 7 mantissa bits
+* E2M1: 1 sign, 2 exponent (bias 1), 1 mantissa bit; exponent field 0 is
+  subnormal (0 or 0.5)
+* E8M0: byte e means 2^(e - 127); 0xFF is NaN
+"""
+from fractions import Fraction
+
+BLOCK = 32
+
+
+def bf16_value(h):
+    """Exact value of bf16 bit pattern h, or None for Inf/NaN."""
+    sign = (h >> 15) & 1
+    e = (h >> 7) & 0xFF
+    m = h & 0x7F
+    if e == 0xFF:
+        return None
+    if e == 0:
+        mag = Fraction(m, 2 ** 133)
+    else:
+        mag = Fraction(128 + m, 128) * Fraction(2) ** (e - 127)
+    return -mag if sign else mag
+
+
+def e2m1_value(code):
+    """Value of the 4-bit E2M1 code, from its bit fields."""
+    sign = (code >> 3) & 1
+    e = (code >> 1) & 3
+    m = code & 1
+    if e == 0:
+        mag = Fraction(m, 2)
+    else:
+        mag = (1 + Fraction(m, 2)) * Fraction(2) ** (e - 1)
+    return -mag if sign else mag
+
+
+def floor_log2(q):
+    """floor(log2(q)) for a rational q > 0, exactly."""
+    q = Fraction(q)
+    if q <= 0:
+        raise ValueError("floor_log2 needs a positive value")
+    e = q.numerator.bit_length() - q.denominator.bit_length()
+    # now 2^(e-1) < q < 2^(e+1); settle which side of 2^e q is on
+    if q >= Fraction(2) ** e:
+        return e
+    return e - 1
+
+
+def shared_exponent(values):
+    """Block exponent X: floor(log2(max |v|)) - 2 clamped to [-127, 127]; -127 for an all-zero block."""
+    amax = max(abs(v) for v in values)
+    if amax == 0:
+        return -127
+    return min(127, max(-127, floor_log2(amax) - 2))
+
+
+def nearest_e2m1_magnitude(a):
+    """Code 0..7 of the E2M1 magnitude nearest to a >= 0; on a tie the even code wins.
+
+    Saturation needs no special case: above 6 the nearest magnitude is 6.
+    """
+    best = None
+    for c in range(8):
+        d = abs(a - e2m1_value(c))
+        if best is None or d < best[0] or (d == best[0] and c % 2 == 0):
+            best = (d, c)
+    return best[1]
+
+
+def quantize_block(bits):
+    """Quantize up to 32 bf16 bit patterns (missing positions are +0).
+
+    Returns (scale_byte, codes[32]).  A block with an Inf or NaN gets scale
+    0xFF and codes 0.
+    """
+    bits = list(bits) + [0] * (BLOCK - len(bits))
+    if len(bits) != BLOCK:
+        raise ValueError("a block has at most 32 elements")
+    vals = [bf16_value(h) for h in bits]
+    if any(v is None for v in vals):
+        return 0xFF, [0] * BLOCK
+    X = shared_exponent(vals)
+    codes = []
+    for h, v in zip(bits, vals):
+        mag = nearest_e2m1_magnitude(abs(v) / Fraction(2) ** X)
+        codes.append(mag | (((h >> 15) & 1) << 3))
+    return X + 127, codes
+
+
+def dequant_block(scale_byte, codes):
+    """Exact values of a quantized block (None for a NaN scale)."""
+    if scale_byte == 0xFF:
+        return None
+    f = Fraction(2) ** (scale_byte - 127)
+    return [e2m1_value(c) * f for c in codes]
+
+
+def pack(codes):
+    """fp4x2 bytes: element 2j in the low nibble of byte j."""
+    return [codes[2 * j] | (codes[2 * j + 1] << 4) for j in range(len(codes) // 2)]
+
+
+def quantize_row(bits):
+    """Row of bf16 bit patterns (length a multiple of 32) -> (scale bytes, packed bytes)."""
+    if len(bits) % BLOCK:
+        raise ValueError("row length must be a multiple of 32")
+    scales, packed = [], []
+    for b in range(0, len(bits), BLOCK):
+        s, c = quantize_block(bits[b:b + BLOCK])
+        scales.append(s)
+        packed.extend(pack(c))
+    return scales, packed
+
+
+def dot_exact(a_bits_row, b_bits_row):
+    """Exact dot product of the dequantized row copies of two bf16 rows, and sum |a_k b_k|."""
+    sa, qa = quantize_row(a_bits_row)
+    sb, qb = quantize_row(b_bits_row)
+    total, atotal = Fraction(0), Fraction(0)
+    for b in range(len(sa)):
+        ca = [(qa[b * 16 + j // 2] >> (4 * (j % 2))) & 0xF for j in range(BLOCK)]
+        cb = [(qb[b * 16 + j // 2] >> (4 * (j % 2))) & 0xF for j in range(BLOCK)]
+        va, vb = dequant_block(sa[b], ca), dequant_block(sb[b], cb)
+        for x, y in zip(va, vb):
+            total += x * y
+            atotal += abs(x * y)
+    return total, atotal
