@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Benchmark: one training step of the MXFP4 GEMM path at Llama-3.1-8B MLP shapes on one MI355X.
+
+A step is the whole hot path for each MLP projection (gate/up 8192x28672x4096
+and down 8192x4096x14336, M = 8192 tokens, one GPU's share):
+    forward : dual cast A, dual cast W, out = A . W^T           (FP4 GEMM)
+    backward: dual cast dOut, dA = dOut . W (NN), dW = dOut^T . A (NT wgrad)
+every kernel launched through the C ABI on torch's current stream, inputs
+resident in HBM before timing starts.
+
+Prints ONE JSON line.  `value` is the whole step's throughput (6*M*N*K
+summed over the projections, divided by the step time including the casts).
+`roofline` describes the dominant kernel (the GEMM): algorithmic FLOPs per
+launch over its average launch time, timed with events on the launch stream
+inside the timed region.  `cpu_baseline` times the CPU oracle on a bounded
+slab of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+FP4_PEAK_TFLOPS = 10100.0   # MI355X dense MXFP4 MFMA
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
+METRIC = "MXFP4 GEMM TFLOP/s + % of MI355X FP4 peak (fwd+dA+dB), cast GB/s"
+
+WORKLOADS = {
+    "llama8b_mlp": ("Llama-3.1-8B MLP projections, one GPU's share (M=8192 tokens): gate/up 8192x28672x4096 "
+                    "and down 8192x4096x14336, fwd + dA + dB with dual casts"),
+    "llama8b_attn": ("Llama-3.1-8B attention projections, one GPU's share (M=8192): QKV 8192x6144x4096 and "
+                     "O 8192x4096x4096, fwd + dA + dB with dual casts"),
+    "llama70b": ("Llama-3-70B per-GPU projections (M=8192): QKV 8192x10240x8192, gate/up 8192x57344x8192, "
+                 "down 8192x8192x28672, fwd + dA + dB with dual casts"),
+}
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="llama8b_mlp", choices=sorted(WORKLOADS))
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="target wall time of the CPU-oracle sample (0 skips the CPU baseline)")
+    p.add_argument("--no-kernel-events", action="store_true",
+                   help="time only the whole step (no per-kernel events)")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        sys.stderr.write("bench.py measures one GPU only: this build has no multi-GPU path "
+                         "(--gpus %d, WORLD_SIZE %d requested)\n" % (args.gpus, world))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mxfp4_block_scaled_cast_amd as mx
+    from mxfp4_block_scaled_cast_amd import _native as N
+    from mxfp4_block_scaled_cast_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L = N.lib()
+    projections = {"llama8b_mlp": W.LLAMA8B_MLP, "llama8b_attn": W.LLAMA8B_ATTN, "llama70b": W.LLAMA70B}[args.workload]
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---- inputs and preallocated operands (resident before timing)
+    t0 = time.time()
+    projs = []
+    host_inputs = {}
+    for idx, (name, M, Nn, K) in enumerate(projections):
+        a, w, g = W.projection_inputs(args.workload, idx, M, Nn, K)
+        if idx == 0:
+            host_inputs = {"a": a, "w": w, "M": M, "N": Nn, "K": K, "name": name}
+        Mp = -(-M // 32) * 32
+        P = dict(name=name, M=M, N=Nn, K=K, Mp=Mp, a=to_dev(a), w=to_dev(w), g=to_dev(g))
+        del a, w, g
+        P["a_row"], P["a_col"] = mx.empty_operand(M, K, dev), mx.empty_operand(K, Mp, dev)
+        P["w_row"], P["w_col"] = mx.empty_operand(Nn, K, dev), mx.empty_operand(K, Nn, dev)
+        P["g_row"], P["g_col"] = mx.empty_operand(M, Nn, dev), mx.empty_operand(Nn, Mp, dev)
+        P["out"] = torch.empty((M, Nn), dtype=torch.bfloat16, device=dev)
+        P["da"] = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        P["dw"] = torch.empty((Nn, K), dtype=torch.bfloat16, device=dev)
+        projs.append(P)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    def cast_dual(x, row, col):
+        R, C = x.shape
+        return lambda: L.mxfp4_cast_dual(x.data_ptr(), R, C, C, row.q.data_ptr(), row.s.data_ptr(),
+                                         col.q.data_ptr(), col.s.data_ptr(), sp)
+
+    def gemm(fn, a, b, out):
+        M, Nn = a.rows, b.rows
+        return lambda: fn(a.q.data_ptr(), a.s.data_ptr(), b.q.data_ptr(), b.s.data_ptr(), M, Nn, a.k,
+                          out.data_ptr(), Nn, sp)
+
+    # ---- the step: (kind, label, launch, algorithmic work)
+    ops = []
+    step_flops = 0.0
+    for P in projs:
+        M, Nn, K = P["M"], P["N"], P["K"]
+        fl = 2.0 * M * Nn * K
+        step_flops += 3 * fl
+        ops.append(("cast", P["name"] + ".cast_dual(A)", cast_dual(P["a"], P["a_row"], P["a_col"]), 3.0625 * M * K))
+        ops.append(("cast", P["name"] + ".cast_dual(W)", cast_dual(P["w"], P["w_row"], P["w_col"]), 3.0625 * Nn * K))
+        ops.append(("gemm", P["name"] + ".fwd", gemm(L.mxfp4_gemm_nt, P["a_row"], P["w_row"], P["out"]), fl))
+        ops.append(("cast", P["name"] + ".cast_dual(dOut)", cast_dual(P["g"], P["g_row"], P["g_col"]),
+                    3.0625 * M * Nn))
+        ops.append(("gemm", P["name"] + ".dA", gemm(L.mxfp4_gemm_nn, P["g_row"], P["w_col"], P["da"]), fl))
+        ops.append(("gemm", P["name"] + ".dB", gemm(L.mxfp4_gemm_nt, P["g_col"], P["a_col"], P["dw"]), fl))
+
+    use_events = not args.no_kernel_events
+
+    def run_step(events):
+        for i, (_, label, launch, _) in enumerate(ops):
+            if events is not None:
+                events[i][0].record(stream)
+            st = launch()
+            if st != 0:
+                raise N.Mxfp4Error(st, label)
+            if events is not None:
+                events[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        run_step(None)
+    torch.cuda.synchronize()
+
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in ops]
+          for _ in range(args.steps)] if use_events else None
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(args.steps):
+        run_step(ev[s] if use_events else None)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+
+    per_op = {}
+    gemm_ms = cast_ms = 0.0
+    gemm_launches = 0
+    gemm_work = cast_bytes = 0.0
+    if use_events:
+        for i, (kind, label, _, work) in enumerate(ops):
+            times = [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
+            avg = sum(times) / len(times)
+            rate = work / (avg * 1e-3)
+            per_op[label] = {"ms": round(avg, 4),
+                             ("tflops" if kind == "gemm" else "gbps"): round(rate / (1e12 if kind == "gemm" else 1e9), 1)}
+            if kind == "gemm":
+                gemm_ms += avg
+                gemm_launches += 1
+                gemm_work += work
+            else:
+                cast_ms += avg
+                cast_bytes += work
+
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.workload],
+                   "projections": [[P["name"], P["M"], P["N"], P["K"]] for P in projs],
+                   "step_tflop": round(step_flops / 1e12, 4)},
+        "frac_of_fp4_peak": round(value / FP4_PEAK_TFLOPS, 4),
+    }
+    if use_events:
+        gemm_tflops = gemm_work / (gemm_ms * 1e-3) / 1e12
+        cast_gbps = cast_bytes / (cast_ms * 1e-3) / 1e9
+        avg_gemm_ms = gemm_ms / gemm_launches
+        result["gemm_tflops"] = round(gemm_tflops, 1)
+        result["gemm_frac_of_fp4_peak"] = round(gemm_tflops / FP4_PEAK_TFLOPS, 4)
+        result["cast_gbps"] = round(cast_gbps, 1)
+        result["cast_frac_of_hbm"] = round(cast_gbps / HBM_PEAK_GBPS, 4)
+        result["per_kernel"] = per_op
+        result["roofline"] = {"kernel": "mxfp4 block-scaled GEMM (fwd, dA, dB launches)",
+                              "bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": FP4_PEAK_TFLOPS,
+                              "unit": "TFLOP/s", "frac": round(gemm_tflops / FP4_PEAK_TFLOPS, 4),
+                              "avg_launch_ms": round(avg_gemm_ms, 4),
+                              "flop_per_launch": gemm_work / gemm_launches, "traffic": None}
+
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(host_inputs, args.cpu_seconds)
+    result["setup_s"] = round(setup_s, 1)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(inp, target_s):
+    """The CPU oracle on a slab of the first projection's forward GEMM: cast the slab's
+    rows of A and all of W, then the exact fp64 GEMM for those rows."""
+    import numpy as np
+    import oracle
+
+    cores = len(os.sched_getaffinity(0))
+    a, w, K, Nn = inp["a"], inp["w"], inp["K"], inp["N"]
+
+    def run(rows):
+        t = time.perf_counter()
+        qa, sa = oracle.cast_rows(np.ascontiguousarray(a[:rows]), nthreads=cores)
+        qw, sw = oracle.cast_rows(w, nthreads=cores)
+        oracle.gemm(qa, sa, qw, sw, nthreads=cores)
+        return time.perf_counter() - t
+
+    rows = 8
+    dt = run(rows)
+    if dt < target_s:
+        rows = int(min(a.shape[0], max(rows, rows * target_s / max(dt, 1e-3))))
+        rows = max(8, rows // 8 * 8)
+        dt = run(rows)
+    flops = 2.0 * rows * Nn * K
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": "%s forward, first %d of %d rows of A (%d x %d x %d): oracle cast of those rows and of W, "
+                      "then the exact fp64 GEMM; %.1f s" % (inp["name"], rows, a.shape[0], rows, Nn, K, dt)}
+
+
+if __name__ == "__main__":
+    main()

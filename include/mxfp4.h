@@ -1,0 +1,170 @@
+/*
+ * mxfp4.h -- C ABI of the MI355X (gfx950) MXFP4 cast + block-scaled GEMM library.
+ *
+ * The operations are the ones the jax-aiter README lists for its MXFP4 path:
+ *   - "MXFP4 Cast" (Supported ops table): BF16 to E2M1 elements with E8M0
+ *     block scales, as a row copy (CastMxfp4JA) or as row plus transposed
+ *     copies (CastMxfp4DualJA);
+ *   - "FP4 GEMM (low-level)" (Supported ops table): a GEMM on pre-quantized
+ *     fp4x2 operands with e8m0 block scales, BF16 out;
+ *   - "FP4 GEMM (training)", gemm_fp4_bf16 (Supported ops table and the
+ *     "MXFP4 training architecture" section): BF16 in/out, forward = cast
+ *     activations, cast weights, GEMM; backward = cast the output gradient,
+ *     then the dA and dB (NT wgrad) GEMMs on the same FP4 kernels.
+ *
+ * Quantization rule (block of 32 along the contraction dimension; the OCP
+ * Microscaling conversion the README relies on):
+ *   X = floor(log2(max |x| over the block)) - 2, clamped to [-127, 127];
+ *   an all-zero block has X = -127; the scale byte is X + 127 (E8M0);
+ *   each element is x / 2^X rounded to the nearest E2M1 value (ties to the
+ *   even code, saturating at +-6), sign bit copied from x (so -0 and small
+ *   negatives give code 0x8).  A block holding Inf/NaN gets scale 0xFF and
+ *   codes 0.
+ *
+ * Conventions for every entry point:
+ *   - All data pointers are DEVICE memory owned by the caller; the library
+ *     never allocates, frees, synchronizes or copies between host and device.
+ *   - Work is enqueued on `stream` (0 = the null stream) of the current device.
+ *   - Return value: MXFP4_OK or a negative mxfp4_status.  Arguments are
+ *     validated before anything is enqueued; on an error nothing is enqueued
+ *     and no output is touched.
+ *   - Calls are thread-safe; calls on different streams may run concurrently
+ *     as long as their output buffers do not overlap.
+ *
+ * Quantized operand format ("MX operand", R rows, contraction length K,
+ * K a multiple of 32):
+ *   q : R * K/2 bytes, row-major, row stride K/2 bytes.  Byte j of a row holds
+ *       element 2j in bits 0..3 and element 2j+1 in bits 4..7.
+ *   s : scale bytes in 256-byte tiles of 32 rows x 8 blocks.  With
+ *       kt = ceil(K/256), the scale of (row r, block b = k/32) is at
+ *         ((r/32) * kt + b/8) * 256 + (r%32) * 8 + (b%2) * 4 + (b%8)/2
+ *       so that one dword holds the scales a 32x32x64 scaled MFMA lane needs
+ *       for four consecutive K steps.  Positions past R rows or K/32 blocks
+ *       are written as 0.  Size: ceil(R/32) * kt * 256 bytes.
+ *   The row copy of x[R, C] is the MX operand (R rows, K = C).  The column
+ *   copy is the MX operand (C rows, K = Rp) with Rp = ceil(R/32)*32: row c of
+ *   it quantizes column c of x in blocks of 32 rows, rows R..Rp-1 taken as +0.
+ */
+#ifndef MXFP4_H
+#define MXFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MXFP4_OK = 0,
+    MXFP4_EINVAL = -1,   /* null pointer, negative size, size not a multiple of 32, ld too small */
+    MXFP4_EALIGN = -2,   /* pointer not 16-byte aligned, or bf16 leading dimension not a multiple of 8 */
+    MXFP4_EDEVICE = -3,  /* no device, or the current device is not gfx950 */
+    MXFP4_ELAUNCH = -4,  /* the HIP runtime reported an error at launch */
+    MXFP4_ERANGE = -5,   /* a size exceeds the supported range (see each entry point) */
+    MXFP4_ESPACE = -6    /* the workspace is smaller than gemm_fp4_bf16_workspace_bytes() */
+} mxfp4_status;
+
+/* Sizes of one MX operand.  Host only; touches no device. */
+typedef struct {
+    int64_t rows;       /* R */
+    int64_t k;          /* contraction length, a multiple of 32 */
+    int64_t q_bytes;    /* R * K/2 */
+    int64_t s_bytes;    /* ceil(R/32) * ceil(K/256) * 256 */
+    int64_t row_tiles;  /* ceil(R/32) */
+    int64_t k_tiles;    /* ceil(K/256) */
+} mxfp4_operand_layout;
+
+/* Fill *out for an operand of `rows` rows and contraction length `k`.
+ * Returns MXFP4_EINVAL for a null `out`, negative sizes or k % 32 != 0. */
+int mxfp4_operand_layout_of(int64_t rows, int64_t k, mxfp4_operand_layout* out);
+
+/* Static description of a status code (never NULL). */
+const char* mxfp4_status_string(int status);
+
+/*
+ * A1 -- row cast (jax-aiter README, Supported ops: "MXFP4 Cast", CastMxfp4JA).
+ * x    : bf16 [rows, cols], row stride ldx elements (ldx >= cols, ldx % 8 == 0,
+ *        x 16-byte aligned); cols % 32 == 0.
+ * q, s : the MX operand (rows, K = cols), sizes from mxfp4_operand_layout_of;
+ *        16-byte aligned.
+ * rows == 0 or cols == 0 is a successful no-op.
+ */
+int mxfp4_cast(const void* x, int64_t rows, int64_t cols, int64_t ldx, void* q, void* s, hipStream_t stream);
+
+/*
+ * A2 -- dual cast (jax-aiter README, Supported ops: "MXFP4 Cast",
+ * CastMxfp4DualJA, BF16 to MXFP4 "with transpose"; the row + col copies of an
+ * Mxfp4Tensor in the Quick start).  One read of x produces
+ *   q_row, s_row : the row copy, MX operand (rows, K = cols)
+ *   q_col, s_col : the column copy, MX operand (cols, K = ceil(rows/32)*32)
+ * Requirements as for mxfp4_cast.
+ */
+int mxfp4_cast_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx, void* q_row, void* s_row, void* q_col,
+                    void* s_col, hipStream_t stream);
+
+/*
+ * A3/A4 -- block-scaled GEMM, NT (jax-aiter README, Supported ops: "FP4 GEMM
+ * (low-level)", gemm_fp4(a, b, a_scale, b_scale), and the A[M,K] @ B[N,K]^T
+ * convention of its GEMM rows):
+ *   out[m, n] = bf16_rne( sum_k dq(a)[m, k] * dq(b)[n, k] ),  fp32 accumulation
+ * a_q, a_s : MX operand (M rows, K);   b_q, b_s : MX operand (N rows, K)
+ * out      : bf16 [M, N], row stride ldo >= N elements (2-byte aligned).
+ * K % 32 == 0.  M or N == 0: no-op.  K == 0: out is filled with +0.
+ * Limits: M, N < 2^31, K < 2^31.
+ */
+int mxfp4_gemm_nt(const void* a_q, const void* a_s, const void* b_q, const void* b_s, int64_t M, int64_t N, int64_t K,
+                  void* out, int64_t ldo, hipStream_t stream);
+
+/*
+ * A5 -- NN form (jax-aiter README, "MXFP4 training architecture": the dA
+ * GEMM, GemmFp4FwdJA(dA), on the same FP4 kernel):
+ *   out[m, n] = sum_k dq(a)[m, k] * dq(b)[k, n]
+ * with b given by its column copy (MX operand: N rows, contraction K), e.g.
+ * dA[M,K] = dOut[M,N] . W[N,K] takes a = row copy of dOut and b = column copy
+ * of W.  Same kernel and requirements as mxfp4_gemm_nt.
+ */
+int mxfp4_gemm_nn(const void* a_q, const void* a_s, const void* bcol_q, const void* bcol_s, int64_t M, int64_t N,
+                  int64_t K, void* out, int64_t ldo, hipStream_t stream);
+
+/*
+ * A7 -- workspace for gemm_fp4_bf16_fwd/bwd with activations [M, K] and
+ * weights [N, K].  training != 0 sizes for fwd + bwd: it holds the row copies
+ * of A and W, the saved column copies of A and W that the backward pass reads,
+ * and the row and column copies of dOut.  training == 0 sizes for an
+ * inference forward (row copies only).  Returns 0 for invalid sizes.
+ */
+size_t gemm_fp4_bf16_workspace_bytes(int64_t M, int64_t N, int64_t K, int training);
+
+/*
+ * A7 -- forward of gemm_fp4_bf16 (jax-aiter README, Supported ops "FP4 GEMM
+ * (training)" and "MXFP4 training architecture"):
+ *   out[M, N] = bf16( cast(a)[M, K] . cast(w)[N, K]^T )
+ * a : bf16 [M, K] contiguous;  w : bf16 [N, K] contiguous;  out : bf16 [M, N]
+ * contiguous.  K % 32 == 0; with training != 0 also N % 32 == 0 (the backward
+ * pass contracts over N).  ws : device workspace of ws_bytes >=
+ * gemm_fp4_bf16_workspace_bytes(M, N, K, training) bytes, 256-byte aligned.
+ * training != 0: a and w are dual-cast and their column copies stay in ws for
+ * gemm_fp4_bf16_bwd; otherwise they are row-cast only.
+ */
+int gemm_fp4_bf16_fwd(const void* a, const void* w, int64_t M, int64_t N, int64_t K, void* out, void* ws,
+                      size_t ws_bytes, int training, hipStream_t stream);
+
+/*
+ * A7 -- backward of gemm_fp4_bf16: dout bf16 [M, N] contiguous ->
+ *   da[M, K] = bf16( cast(dout) . W )      (FP4 dA, NN on W's column copy)
+ *   dw[N, K] = bf16( cast(dout)^T . A )    (FP4 dB, NT wgrad on column copies)
+ * ws must be the workspace a training-mode gemm_fp4_bf16_fwd with the same
+ * M, N, K filled (it reads the saved column copies and overwrites the dOut
+ * copies).  Either of da / dw may be NULL to skip that product.
+ */
+int gemm_fp4_bf16_bwd(const void* dout, int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes, void* da,
+                      void* dw, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP4_H */

@@ -1,0 +1,13 @@
+"""MXFP4 block-scaled cast and GEMM for MI355X (gfx950).
+
+The compute path is the HIP library ``_lib/libmxfp4.so`` (C ABI in
+include/mxfp4.h); this package only marshals arguments.  Importing it does not
+load the library; the first call does, and fails loudly if it is not built.
+"""
+from .api import (Mxfp4Tensor, MxOperand, cast, cast_dual, empty_operand, gemm_fp4_bf16, gemm_fp4_bf16_bwd,
+                  gemm_fp4_bf16_fwd, gemm_nn, gemm_nt, workspace_bytes)
+from ._native import Mxfp4Error, library_path
+
+__all__ = ["Mxfp4Tensor", "MxOperand", "cast", "cast_dual", "empty_operand", "gemm_fp4_bf16",
+           "gemm_fp4_bf16_fwd", "gemm_fp4_bf16_bwd", "gemm_nn", "gemm_nt", "workspace_bytes", "Mxfp4Error",
+           "library_path"]

@@ -1,0 +1,262 @@
+// C ABI of the MXFP4 library: argument validation, device check, dispatch,
+// and the gemm_fp4_bf16 forward/backward composition over the kernels.
+//
+// Composition (jax-aiter README, "MXFP4 training architecture", and the
+// Quick start note that the training recipe runs FP4 forward, FP4 dA and FP4
+// dB NT wgrad):
+//   forward : cast A and W, out = A . W^T
+//   backward: cast dOut, dA = dOut . W (NN on W's column copy),
+//             dB = dOut^T . A (NT on the column copies of dOut and A)
+#include <mutex>
+#include <string.h>
+
+#include "../../include/mxfp4.h"
+
+extern "C" hipError_t mx_launch_cast(const void* x, int64_t R, int64_t C, int64_t ldx, void* q_row, void* s_row,
+                                     void* q_col, void* s_col, bool dual, hipStream_t stream);
+extern "C" hipError_t mx_launch_gemm(const void* aq, const void* as, const void* bq, const void* bs, int64_t M,
+                                     int64_t N, int64_t K, void* out, int64_t ldo, hipStream_t stream);
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_arch_once[kMaxDevices];
+int g_arch_ok[kMaxDevices];
+
+// The current device must be a gfx950; the answer is cached per device.
+int check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MXFP4_EDEVICE;
+    std::call_once(g_arch_once[dev], [dev] {
+        hipDeviceProp_t prop;
+        g_arch_ok[dev] = hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+                         strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    });
+    return g_arch_ok[dev] ? MXFP4_OK : MXFP4_EDEVICE;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+// Largest element count / byte count the kernels index with 64-bit offsets
+// but 32-bit tile counts and row indices.
+constexpr int64_t kMaxDim = 0x7FFFFFFF;
+
+struct OperandSizes {
+    int64_t q, s;
+};
+
+OperandSizes operand_sizes(int64_t rows, int64_t k) {
+    return {rows * (k / 2), ((rows + 31) / 32) * ((k + 255) / 256) * 256};
+}
+
+int validate_cast(const void* x, int64_t rows, int64_t cols, int64_t ldx, const void* q, const void* s) {
+    if (rows < 0 || cols < 0) return MXFP4_EINVAL;
+    if (cols % 32 != 0) return MXFP4_EINVAL;
+    if (rows > kMaxDim || cols > kMaxDim) return MXFP4_ERANGE;
+    if (rows == 0 || cols == 0) return MXFP4_OK;
+    if (!x || !q || !s) return MXFP4_EINVAL;
+    if (ldx < cols) return MXFP4_EINVAL;
+    if (!aligned16(x) || ldx % 8 != 0 || !aligned16(q) || !aligned16(s)) return MXFP4_EALIGN;
+    return MXFP4_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? MXFP4_OK : MXFP4_ELAUNCH; }
+
+int validate_gemm(const void* aq, const void* as, const void* bq, const void* bs, int64_t M, int64_t N, int64_t K,
+                  const void* out, int64_t ldo) {
+    if (M < 0 || N < 0 || K < 0 || K % 32 != 0) return MXFP4_EINVAL;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return MXFP4_ERANGE;
+    if (M == 0 || N == 0) return MXFP4_OK;
+    if (!out || ldo < N) return MXFP4_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(out) & 1u) != 0) return MXFP4_EALIGN;
+    if (K == 0) return MXFP4_OK;
+    if (!aq || !as || !bq || !bs) return MXFP4_EINVAL;
+    if (!aligned16(aq) || !aligned16(bq)) return MXFP4_EALIGN;
+    return MXFP4_OK;
+}
+
+// Workspace carve-up for gemm_fp4_bf16 (each region 256-byte aligned).
+struct Workspace {
+    int64_t a_row_q, a_row_s, w_row_q, w_row_s;  // forward operands
+    int64_t a_col_q, a_col_s, w_col_q, w_col_s;  // saved for the backward pass
+    int64_t g_row_q, g_row_s, g_col_q, g_col_s;  // backward operands
+    int64_t total;
+};
+
+Workspace workspace_layout(int64_t M, int64_t N, int64_t K, bool training) {
+    Workspace w{};
+    int64_t off = 0;
+    auto take = [&off](int64_t bytes) {
+        const int64_t at = off;
+        off += round_up(bytes, 256);
+        return at;
+    };
+    const OperandSizes a_row = operand_sizes(M, K), w_row = operand_sizes(N, K);
+    w.a_row_q = take(a_row.q);
+    w.a_row_s = take(a_row.s);
+    w.w_row_q = take(w_row.q);
+    w.w_row_s = take(w_row.s);
+    if (training) {
+        const int64_t Mp = round_up(M, 32), Np = round_up(N, 32);
+        const OperandSizes a_col = operand_sizes(K, Mp), w_col = operand_sizes(K, Np);
+        const OperandSizes g_row = operand_sizes(M, N), g_col = operand_sizes(N, Mp);
+        w.a_col_q = take(a_col.q);
+        w.a_col_s = take(a_col.s);
+        w.w_col_q = take(w_col.q);
+        w.w_col_s = take(w_col.s);
+        w.g_row_q = take(g_row.q);
+        w.g_row_s = take(g_row.s);
+        w.g_col_q = take(g_col.q);
+        w.g_col_s = take(g_col.s);
+    }
+    w.total = off;
+    return w;
+}
+
+int validate_step_sizes(int64_t M, int64_t N, int64_t K, bool training) {
+    if (M < 0 || N < 0 || K < 0 || K % 32 != 0) return MXFP4_EINVAL;
+    if (training && N % 32 != 0) return MXFP4_EINVAL;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return MXFP4_ERANGE;
+    return MXFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mxfp4_status_string(int status) {
+    switch (status) {
+        case MXFP4_OK: return "ok";
+        case MXFP4_EINVAL: return "invalid argument (null pointer, negative size, size not a multiple of 32, or leading dimension too small)";
+        case MXFP4_EALIGN: return "misaligned pointer or leading dimension";
+        case MXFP4_EDEVICE: return "no usable device: the current device is not a gfx950 (MI355X)";
+        case MXFP4_ELAUNCH: return "kernel launch failed";
+        case MXFP4_ERANGE: return "size exceeds the supported range";
+        case MXFP4_ESPACE: return "workspace too small";
+        default: return "unknown status";
+    }
+}
+
+int mxfp4_operand_layout_of(int64_t rows, int64_t k, mxfp4_operand_layout* out) {
+    if (!out || rows < 0 || k < 0 || k % 32 != 0) return MXFP4_EINVAL;
+    const OperandSizes sz = operand_sizes(rows, k);
+    out->rows = rows;
+    out->k = k;
+    out->q_bytes = sz.q;
+    out->s_bytes = sz.s;
+    out->row_tiles = (rows + 31) / 32;
+    out->k_tiles = (k + 255) / 256;
+    return MXFP4_OK;
+}
+
+int mxfp4_cast(const void* x, int64_t rows, int64_t cols, int64_t ldx, void* q, void* s, hipStream_t stream) {
+    int st = validate_cast(x, rows, cols, ldx, q, s);
+    if (st != MXFP4_OK || rows == 0 || cols == 0) return st;
+    if ((st = check_device()) != MXFP4_OK) return st;
+    return status_of(mx_launch_cast(x, rows, cols, ldx, q, s, nullptr, nullptr, false, stream));
+}
+
+int mxfp4_cast_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx, void* q_row, void* s_row, void* q_col,
+                    void* s_col, hipStream_t stream) {
+    int st = validate_cast(x, rows, cols, ldx, q_row, s_row);
+    if (st != MXFP4_OK || rows == 0 || cols == 0) return st;
+    if (!q_col || !s_col) return MXFP4_EINVAL;
+    if (!aligned16(q_col) || !aligned16(s_col)) return MXFP4_EALIGN;
+    if ((st = check_device()) != MXFP4_OK) return st;
+    return status_of(mx_launch_cast(x, rows, cols, ldx, q_row, s_row, q_col, s_col, true, stream));
+}
+
+int mxfp4_gemm_nt(const void* a_q, const void* a_s, const void* b_q, const void* b_s, int64_t M, int64_t N, int64_t K,
+                  void* out, int64_t ldo, hipStream_t stream) {
+    int st = validate_gemm(a_q, a_s, b_q, b_s, M, N, K, out, ldo);
+    if (st != MXFP4_OK || M == 0 || N == 0) return st;
+    if ((st = check_device()) != MXFP4_OK) return st;
+    return status_of(mx_launch_gemm(a_q, a_s, b_q, b_s, M, N, K, out, ldo, stream));
+}
+
+int mxfp4_gemm_nn(const void* a_q, const void* a_s, const void* bcol_q, const void* bcol_s, int64_t M, int64_t N,
+                  int64_t K, void* out, int64_t ldo, hipStream_t stream) {
+    // B[K, N] enters through its column copy, which is the MX operand (N rows, K):
+    // the NN product is the NT kernel on that operand.
+    return mxfp4_gemm_nt(a_q, a_s, bcol_q, bcol_s, M, N, K, out, ldo, stream);
+}
+
+size_t gemm_fp4_bf16_workspace_bytes(int64_t M, int64_t N, int64_t K, int training) {
+    if (validate_step_sizes(M, N, K, training != 0) != MXFP4_OK) return 0;
+    return (size_t)workspace_layout(M, N, K, training != 0).total;
+}
+
+int gemm_fp4_bf16_fwd(const void* a, const void* w, int64_t M, int64_t N, int64_t K, void* out, void* ws,
+                      size_t ws_bytes, int training, hipStream_t stream) {
+    const bool train = training != 0;
+    int st = validate_step_sizes(M, N, K, train);
+    if (st != MXFP4_OK) return st;
+    if (M == 0 || N == 0) return MXFP4_OK;
+    if (!out) return MXFP4_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(out) & 1u) != 0) return MXFP4_EALIGN;
+    const Workspace L = workspace_layout(M, N, K, train);
+    if (K > 0) {
+        if (!a || !w || !ws) return MXFP4_EINVAL;
+        if (!aligned16(a) || !aligned16(w) || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return MXFP4_EALIGN;
+        if ((int64_t)ws_bytes < L.total) return MXFP4_ESPACE;
+    }
+    if ((st = check_device()) != MXFP4_OK) return st;
+    char* base = static_cast<char*>(ws);
+    hipError_t e = hipSuccess;
+    if (K > 0) {
+        if (train) {
+            e = mx_launch_cast(a, M, K, K, base + L.a_row_q, base + L.a_row_s, base + L.a_col_q, base + L.a_col_s,
+                               true, stream);
+            if (e == hipSuccess)
+                e = mx_launch_cast(w, N, K, K, base + L.w_row_q, base + L.w_row_s, base + L.w_col_q,
+                                   base + L.w_col_s, true, stream);
+        } else {
+            e = mx_launch_cast(a, M, K, K, base + L.a_row_q, base + L.a_row_s, nullptr, nullptr, false, stream);
+            if (e == hipSuccess)
+                e = mx_launch_cast(w, N, K, K, base + L.w_row_q, base + L.w_row_s, nullptr, nullptr, false, stream);
+        }
+    }
+    if (e == hipSuccess)
+        e = mx_launch_gemm(base + L.a_row_q, base + L.a_row_s, base + L.w_row_q, base + L.w_row_s, M, N, K, out, N,
+                           stream);
+    return status_of(e);
+}
+
+int gemm_fp4_bf16_bwd(const void* dout, int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes, void* da,
+                      void* dw, hipStream_t stream) {
+    int st = validate_step_sizes(M, N, K, true);
+    if (st != MXFP4_OK) return st;
+    if (!ws || (!da && !dw)) return ws ? MXFP4_OK : MXFP4_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return MXFP4_EALIGN;
+    if ((da && (reinterpret_cast<uintptr_t>(da) & 1u)) || (dw && (reinterpret_cast<uintptr_t>(dw) & 1u)))
+        return MXFP4_EALIGN;
+    const Workspace L = workspace_layout(M, N, K, true);
+    if ((int64_t)ws_bytes < L.total) return MXFP4_ESPACE;
+    if (K == 0) return MXFP4_OK;  // dA [M, 0] and dW [N, 0] have no elements
+    if (M == 0 || N == 0) {
+        // sums over an empty contraction: the GEMM with contraction length 0 writes +0
+        if ((st = check_device()) != MXFP4_OK) return st;
+        hipError_t e = hipSuccess;
+        if (M == 0 && dw) e = mx_launch_gemm(nullptr, nullptr, nullptr, nullptr, N, K, 0, dw, K, stream);
+        if (e == hipSuccess && N == 0 && da) e = mx_launch_gemm(nullptr, nullptr, nullptr, nullptr, M, K, 0, da, K, stream);
+        return status_of(e);
+    }
+    if (!dout) return MXFP4_EINVAL;
+    if (!aligned16(dout)) return MXFP4_EALIGN;
+    if ((st = check_device()) != MXFP4_OK) return st;
+    char* base = static_cast<char*>(ws);
+    const int64_t Mp = round_up(M, 32);
+    hipError_t e = mx_launch_cast(dout, M, N, N, base + L.g_row_q, base + L.g_row_s, base + L.g_col_q,
+                                  base + L.g_col_s, true, stream);
+    if (e == hipSuccess && da)
+        e = mx_launch_gemm(base + L.g_row_q, base + L.g_row_s, base + L.w_col_q, base + L.w_col_s, M, K, N, da, K,
+                           stream);
+    if (e == hipSuccess && dw)
+        e = mx_launch_gemm(base + L.g_col_q, base + L.g_col_s, base + L.a_col_q, base + L.a_col_s, N, K, Mp, dw, K,
+                           stream);
+    return status_of(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,97 @@
+// Internal device helpers shared by the HIP kernels of this library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kBlock = 32;           // elements per scale block (along the contraction dim)
+constexpr int kScaleTileRows = 32;   // rows per 256-byte scale tile
+constexpr int kScaleTileBlocks = 8;  // blocks per scale tile row (K = 256)
+
+// Byte offset of the scale of (row r, block b) in an MX operand whose
+// contraction length spans k_tiles tiles of 256.  Layout: 256-byte tiles of
+// 32 rows x 8 blocks, tile-row-major; inside a tile, row r%32 owns 8 bytes
+// and block b%8 sits at byte (b%2)*4 + (b%8)/2, so the dword a 32x32x64 MFMA
+// lane reads (half h = b%2) holds blocks h, h+2, h+4, h+6 of the tile.
+__device__ __forceinline__ int64_t scale_offset(int64_t r, int64_t b, int64_t k_tiles) {
+    return ((r >> 5) * k_tiles + (b >> 3)) * 256 + (r & 31) * 8 + (b & 1) * 4 + ((b & 7) >> 1);
+}
+
+// E8M0 scale byte of a block from the bf16 magnitude bits of its amax
+// (amax_bits = max over the block of (bits & 0x7fff); integer order of
+// non-negative bf16 patterns is value order, with Inf/NaN on top).
+// floor(log2 amax) is the unbiased exponent field for normal amax; a
+// subnormal or zero amax is below 2^-126, where X = floor(log2) - 2 is
+// clamped to -127 anyway.  So the byte is max(E - 2, 0), or 0xFF when the
+// block holds Inf/NaN (E = 255).
+__device__ __forceinline__ unsigned scale_byte_from_amax(unsigned amax_bits) {
+    unsigned e = amax_bits >> 7;
+    if (e == 255u) return 255u;
+    return e >= 2u ? e - 2u : 0u;
+}
+
+// 2^X as an fp32 value for the scaled down-conversion (X = byte - 127);
+// byte 0 is 2^-127, an fp32 subnormal.
+__device__ __forceinline__ float scale_value(unsigned sbyte) {
+    return __builtin_bit_cast(float, sbyte ? (sbyte << 23) : 0x00400000u);
+}
+
+// Two bf16 (low half = even element) -> one byte of two E2M1 codes in byte
+// `sel` of `old`: round(x / scale) to nearest-even with saturation, sign
+// kept (hardware conversion, matches the quantization rule bit for bit).
+template <int SEL>
+__device__ __forceinline__ unsigned cvt_pair(unsigned old, unsigned pair, float scale) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(old, __builtin_bit_cast(bf16x2, pair), scale, SEL);
+}
+
+// Eight bf16 (4 dwords) -> 8 codes (one dword).
+__device__ __forceinline__ unsigned cvt8(u32x4 v, float scale) {
+    unsigned r = 0u;
+    r = cvt_pair<0>(r, v.x, scale);
+    r = cvt_pair<1>(r, v.y, scale);
+    r = cvt_pair<2>(r, v.z, scale);
+    r = cvt_pair<3>(r, v.w, scale);
+    return r;
+}
+
+// Per-half max of two packed u16 pairs.
+__device__ __forceinline__ unsigned pk_max_u16(unsigned a, unsigned b) {
+    u16x2 x = __builtin_bit_cast(u16x2, a);
+    u16x2 y = __builtin_bit_cast(u16x2, b);
+    return __builtin_bit_cast(unsigned, __builtin_elementwise_max(x, y));
+}
+
+// Max over the 4 lanes of a quad (DPP quad permutations).
+__device__ __forceinline__ unsigned quad_max_u32(unsigned v) {
+    unsigned o = (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+    v = v > o ? v : o;
+    o = (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
+    return v > o ? v : o;
+}
+
+// Map a hardware workgroup id to a logical tile id so that each of the 8
+// XCDs (which receive workgroups round-robin) works on one contiguous range
+// of logical tiles.
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+    int xcd = bid & 7;
+    int idx = bid >> 3;
+    int per = total >> 3;
+    int rem = total & 7;
+    return xcd * per + (xcd < rem ? xcd : rem) + idx;
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ unsigned short f32_to_bf16_rne(float f) {
+    return __builtin_bit_cast(unsigned short, (__bf16)f);
+}
+
+}  // namespace mx

@@ -1,0 +1,158 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+symbol, reports layouts, and rejects bad arguments before touching a device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from mxfp4_block_scaled_cast_amd import _native as N
+from mxfp4_block_scaled_cast_amd import layout
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxfp4.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for must in ("mxfp4_cast", "mxfp4_cast_dual", "mxfp4_gemm_nt", "mxfp4_gemm_nn", "gemm_fp4_bf16_fwd",
+                 "gemm_fp4_bf16_bwd", "gemm_fp4_bf16_workspace_bytes", "mxfp4_operand_layout_of",
+                 "mxfp4_status_string"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = N.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    bound = {n for n, _, _ in N.SIGNATURES}
+    assert bound == set(declared_functions())
+
+
+def test_library_carries_gfx950_code_for_every_kernel():
+    # the shared object must embed a gfx950 code object holding the cast and GEMM kernels
+    data = open(N.library_path(), "rb").read()
+    assert b"gfx950" in data
+    for k in (b"cast_kernel", b"gemm"):
+        assert k in data
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        s = N.status_string(code)
+        assert isinstance(s, str) and s
+    assert N.status_string(12345) == "unknown status"
+
+
+@pytest.mark.parametrize("rows,k", [(1, 32), (17, 32), (32, 256), (33, 288), (8192, 4096), (128256, 14336)])
+def test_operand_layout(rows, k):
+    L = N.operand_layout(rows, k)
+    assert L.q_bytes == rows * k // 2
+    assert L.row_tiles == -(-rows // 32) and L.k_tiles == -(-k // 256)
+    assert L.s_bytes == L.row_tiles * L.k_tiles * 256 == layout.scale_bytes(rows, k)
+
+
+def test_operand_layout_rejects():
+    out = N.OperandLayout()
+    assert N.lib().mxfp4_operand_layout_of(4, 33, ctypes.byref(out)) == -1
+    assert N.lib().mxfp4_operand_layout_of(-1, 32, ctypes.byref(out)) == -1
+    assert N.lib().mxfp4_operand_layout_of(4, 32, None) == -1
+
+
+FAKE = 1 << 20  # an aligned non-null address; never dereferenced by a rejected call
+
+
+def test_cast_argument_validation():
+    L = N.lib()
+    assert L.mxfp4_cast(FAKE, 4, 33, 40, FAKE, FAKE, None) == -1          # cols % 32
+    assert L.mxfp4_cast(FAKE, -1, 32, 32, FAKE, FAKE, None) == -1         # negative
+    assert L.mxfp4_cast(None, 4, 32, 32, FAKE, FAKE, None) == -1          # null x
+    assert L.mxfp4_cast(FAKE, 4, 64, 32, FAKE, FAKE, None) == -1          # ldx < cols
+    assert L.mxfp4_cast(FAKE + 2, 4, 32, 32, FAKE, FAKE, None) == -2      # misaligned x
+    assert L.mxfp4_cast(FAKE, 4, 32, 36, FAKE, FAKE, None) == -2          # ldx % 8
+    assert L.mxfp4_cast(FAKE, 4, 32, 32, FAKE + 8, FAKE, None) == -2      # misaligned q
+    assert L.mxfp4_cast(FAKE, 0, 32, 32, None, None, None) == 0           # empty: no-op
+    assert L.mxfp4_cast(FAKE, 4, 0, 0, None, None, None) == 0
+    assert L.mxfp4_cast(FAKE, 1 << 31, 32, 32, FAKE, FAKE, None) == -5    # range
+    assert L.mxfp4_cast_dual(FAKE, 4, 32, 32, FAKE, FAKE, None, FAKE, None) == -1
+    assert L.mxfp4_cast_dual(FAKE, 4, 32, 32, FAKE, FAKE, FAKE + 4, FAKE, None) == -2
+
+
+def test_gemm_argument_validation():
+    L = N.lib()
+    for f in (L.mxfp4_gemm_nt, L.mxfp4_gemm_nn):
+        assert f(FAKE, FAKE, FAKE, FAKE, 4, 4, 48, FAKE, 4, None) == -1     # K % 32
+        assert f(FAKE, FAKE, FAKE, FAKE, 4, 8, 32, FAKE, 4, None) == -1     # ldo < N
+        assert f(None, FAKE, FAKE, FAKE, 4, 4, 32, FAKE, 4, None) == -1     # null
+        assert f(FAKE, FAKE, FAKE, FAKE, 4, 4, 32, None, 4, None) == -1
+        assert f(FAKE + 4, FAKE, FAKE, FAKE, 4, 4, 32, FAKE, 4, None) == -2
+        assert f(FAKE, FAKE, FAKE, FAKE, 4, 4, 32, FAKE + 1, 4, None) == -2
+        assert f(FAKE, FAKE, FAKE, FAKE, 0, 4, 32, None, 4, None) == 0      # empty
+        assert f(FAKE, FAKE, FAKE, FAKE, -1, 4, 32, FAKE, 4, None) == -1
+
+
+def test_step_argument_validation():
+    L = N.lib()
+    assert L.gemm_fp4_bf16_workspace_bytes(8, 40, 32, 1) == 0               # N % 32 in training
+    assert L.gemm_fp4_bf16_workspace_bytes(8, 40, 32, 0) > 0                # fine for inference
+    assert L.gemm_fp4_bf16_workspace_bytes(8, 32, 48, 0) == 0
+    need = L.gemm_fp4_bf16_workspace_bytes(64, 64, 64, 1)
+    assert need > L.gemm_fp4_bf16_workspace_bytes(64, 64, 64, 0)
+    assert L.gemm_fp4_bf16_fwd(FAKE, FAKE, 64, 64, 64, FAKE, FAKE, need - 1, 1, None) == -6
+    assert L.gemm_fp4_bf16_fwd(FAKE, FAKE, 64, 64, 64, FAKE, FAKE + 16, need, 1, None) == -2
+    assert L.gemm_fp4_bf16_fwd(FAKE, FAKE, 64, 64, 48, FAKE, FAKE, need, 1, None) == -1
+    assert L.gemm_fp4_bf16_bwd(FAKE, 64, 64, 64, FAKE, need - 1, FAKE, FAKE, None) == -6
+    assert L.gemm_fp4_bf16_bwd(FAKE, 64, 64, 64, None, need, FAKE, FAKE, None) == -1
+
+
+def test_workspace_size_formula():
+    # row copies of A and W, plus (training) column copies of A and W and both copies of dOut
+    def op(rows, k):
+        return -(-rows * k // 2 // 256) * 256 + layout.scale_bytes(rows, k)
+    M, Nn, K = 17, 96, 64
+    Mp = 32
+    inf = op(M, K) + op(Nn, K)
+    train = inf + op(K, Mp) + op(K, Nn) + op(M, Nn) + op(Nn, Mp)
+    assert N.lib().gemm_fp4_bf16_workspace_bytes(M, Nn, K, 0) == inf
+    assert N.lib().gemm_fp4_bf16_workspace_bytes(M, Nn, K, 1) == train
+
+
+def _no_gpu():
+    import torch
+    return torch.cuda.device_count() == 0
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="checks the no-device error path; a device is present")
+def test_no_device_is_an_error_not_a_fallback():
+    L = N.lib()
+    assert L.mxfp4_cast(FAKE, 4, 32, 32, FAKE, FAKE, None) == -3
+    assert L.mxfp4_gemm_nt(FAKE, FAKE, FAKE, FAKE, 4, 4, 32, FAKE, 4, None) == -3
+
+
+def test_layout_offsets_are_a_bijection_into_the_buffer():
+    for rows, k in ((1, 32), (17, 96), (64, 256), (100, 800), (33, 14336 // 16)):
+        if k % 32:
+            continue
+        off = layout.scale_offsets(rows, k).ravel()
+        assert off.min() >= 0 and off.max() < layout.scale_bytes(rows, k)
+        assert np.unique(off).size == off.size
+        s = np.random.default_rng(0).integers(0, 255, (rows, k // 32)).astype(np.uint8)
+        assert np.array_equal(layout.scales_to_rowmajor(layout.scales_from_rowmajor(s, rows, k), rows, k), s)
+
+
+def test_layout_dword_holds_four_consecutive_k_steps():
+    # the dword a 32x32x64 MFMA lane reads (row r, half h) holds blocks h, h+2, h+4, h+6 of a 256-wide K tile
+    off = layout.scale_offsets(32, 256)
+    for r in range(32):
+        for h in range(2):
+            dword = [off[r, h + 2 * t] for t in range(4)]
+            assert dword == [r * 8 + h * 4 + t for t in range(4)]

@@ -1,0 +1,113 @@
+"""GPU cast parity: the HIP row and dual casts must equal the CPU oracle bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import mxfp4_block_scaled_cast_amd as mx
+from mxfp4_block_scaled_cast_amd import workloads as W
+from gpu_util import say, to_device, operand_rowmajor, operand_padding
+
+pytestmark = pytest.mark.gpu
+
+
+def check_row(x_bits, op, what):
+    q_ref, s_ref = oracle.cast_rows(x_bits)
+    q, s = operand_rowmajor(op)
+    assert np.array_equal(s, s_ref), "%s: row scales differ at %s" % (what, np.argwhere(s != s_ref)[:5].tolist())
+    assert np.array_equal(q, q_ref), "%s: row codes differ at %s" % (what, np.argwhere(q != q_ref)[:5].tolist())
+    assert np.all(operand_padding(op) == 0), "%s: row scale padding not zero" % what
+
+
+def check_col(x_bits, op, what):
+    q_ref, s_ref = oracle.cast_cols(x_bits)
+    q, s = operand_rowmajor(op)
+    assert np.array_equal(s, s_ref), "%s: col scales differ at %s" % (what, np.argwhere(s != s_ref)[:5].tolist())
+    assert np.array_equal(q, q_ref), "%s: col codes differ at %s" % (what, np.argwhere(q != q_ref)[:5].tolist())
+    assert np.all(operand_padding(op) == 0), "%s: col scale padding not zero" % what
+
+
+def run_both(x_bits, what):
+    x = to_device(x_bits)
+    say("cast %s %s" % (what, x_bits.shape))
+    op = mx.cast(x)
+    say("cast_dual %s %s" % (what, x_bits.shape))
+    t = mx.cast_dual(x)
+    torch.cuda.synchronize()
+    check_row(x_bits, op, what + " cast")
+    check_row(x_bits, t.row, what + " dual.row")
+    check_col(x_bits, t.col, what + " dual.col")
+
+
+def test_tiny_config():
+    a, w, _ = W.projection_inputs("tiny", 0, 256, 256, 256, with_grad=False)
+    run_both(a, "tiny A")
+    run_both(w, "tiny B")
+
+
+def test_hand_block_matrix():
+    run_both(W.hand_block_matrix(), "hand blocks")
+
+
+@pytest.mark.parametrize("R,C", [(1, 32), (17, 32), (1, 4096), (17, 96), (31, 288), (64, 256), (65, 544),
+                                 (100, 800), (257, 2080), (300, 256)])
+def test_ragged_shapes(R, C):
+    run_both(W.ragged_values((R, C), 7 * R + C), "ragged")
+
+
+def test_every_bf16_pattern_at_every_exponent_band():
+    # each row: an anchor fixing the block exponent, then 31 consecutive bf16 patterns;
+    # anchors sweep 2^-126 .. 2^127 so every pattern meets many scales
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = ((pats >> 7) & 0xFF) != 0xFF
+    pats = pats[finite]
+    nrow = -(-pats.size // 31)
+    pats = np.concatenate([pats, np.zeros(nrow * 31 - pats.size, np.uint16)]).reshape(nrow, 31)
+    rows = []
+    for e in range(1, 255, 9):
+        anchor = np.full((nrow, 1), e << 7, np.uint16)
+        rows.append(np.concatenate([anchor, pats], 1))
+    x = np.concatenate(rows, 0)
+    run_both(x, "bf16 sweep")
+
+
+def test_nonfinite_blocks():
+    rng = np.random.default_rng(3)
+    x = W.normal_bf16((64, 128), 1.0, 5)
+    x[0, 3] = 0x7F80
+    x[5, 100] = 0xFF80
+    x[40, 64] = 0x7FC0
+    x[33, 0:32] = 0x7F81
+    run_both(x, "non-finite")
+
+
+def test_strided_input():
+    base = W.normal_bf16((48, 512), 1.0, 9)
+    xt = to_device(base)[:, :256]      # leading dimension 512, 256 columns
+    say("cast strided")
+    op = mx.cast(xt)
+    t = mx.cast_dual(xt)
+    torch.cuda.synchronize()
+    sub = np.ascontiguousarray(base[:, :256])
+    check_row(sub, op, "strided cast")
+    check_row(sub, t.row, "strided dual.row")
+    check_col(sub, t.col, "strided dual.col")
+
+
+def test_side_stream_ordering():
+    # the cast must run on the caller's stream: queue long work first on a side stream,
+    # cast on that stream, and read the result after synchronizing only that stream
+    x_bits = W.normal_bf16((4096, 4096), 1.0, 77)
+    x = to_device(x_bits)
+    side = torch.cuda.Stream()
+    big = torch.randn(4096, 4096, device="cuda:0")
+    torch.cuda.synchronize()
+    say("cast on a side stream behind ballast work")
+    with torch.cuda.stream(side):
+        for _ in range(8):
+            big = big @ big.T / 4096.0
+        y = x * 1  # produced on the side stream just before the cast
+        t = mx.cast_dual(y)
+    side.synchronize()
+    check_row(x_bits, t.row, "side stream row")
+    check_col(x_bits, t.col, "side stream col")

@@ -1,0 +1,135 @@
+"""GPU GEMM parity: the HIP block-scaled GEMM against the CPU oracle.
+
+Bar: |gpu - ref| <= 2^-7 |ref| + 1e-5 sum_k |a_k b_k| + 2^-126 per element,
+and bit-exact bf16 where fp32 accumulation is exact in any order.
+Operands for the oracle are quantized by the oracle itself from the bf16
+inputs; the GPU GEMM consumes the GPU cast's output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import mxfp4_block_scaled_cast_amd as mx
+from mxfp4_block_scaled_cast_amd import workloads as W
+from gpu_util import say, to_device, bf16_to_f64, assert_gemm_close, bf16_rne_of_exact
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_nt(a_bits, b_bits, what):
+    say("gemm_nt %s M=%d N=%d K=%d" % (what, a_bits.shape[0], b_bits.shape[0], a_bits.shape[1]))
+    a = mx.cast(to_device(a_bits))
+    b = mx.cast(to_device(b_bits))
+    out = mx.gemm_nt(a, b)
+    torch.cuda.synchronize()
+    return bf16_to_f64(out)
+
+
+def oracle_nt(a_bits, b_bits):
+    qa, sa = oracle.cast_rows(a_bits)
+    qb, sb = oracle.cast_rows(b_bits)
+    return oracle.gemm(qa, sa, qb, sb)
+
+
+def test_tiny_config():
+    a, w, _ = W.projection_inputs("tiny", 0, 256, 256, 256, with_grad=False)
+    got = gpu_nt(a, w, "tiny")
+    ref, absref = oracle_nt(a, w)
+    assert_gemm_close(got, ref, absref, "tiny")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 32), (17, 128, 32), (17, 4096 // 16, 4096 // 8), (33, 65, 96),
+                                   (64, 64, 64), (100, 200, 288), (129, 257, 544), (256, 96, 1024),
+                                   (1, 300, 2048), (70, 33, 320)])
+def test_ragged_small(M, N, K):
+    a = W.ragged_values((M, K), M * 31 + K)
+    b = W.ragged_values((N, K), N * 17 + K)
+    got = gpu_nt(a, b, "ragged")
+    ref, absref = oracle_nt(a, b)
+    assert_gemm_close(got, ref, absref, "ragged %dx%dx%d" % (M, N, K))
+
+
+def test_k32_is_bit_exact():
+    # one block: each output is one integer dot times a power of two -> exact in fp32,
+    # so the bf16 result must be the nearest-even rounding of the exact value
+    rng = np.random.default_rng(5)
+    a = W.normal_bf16((96, 32), 1.0, 11)
+    b = W.normal_bf16((160, 32), 3.0, 12)
+    got = gpu_nt(a, b, "K=32")
+    ref, _ = oracle_nt(a, b)
+    assert np.array_equal(got, bf16_rne_of_exact(ref))
+
+
+def test_same_scale_blocks_bit_exact():
+    # every block holds an anchor of magnitude 4 (fixes X = 0) and values in [-4, 4]:
+    # products are multiples of 1/4 below 36 and sums stay far below 2^24 units -> exact
+    rng = np.random.default_rng(6)
+    M, N, K = 80, 72, 512
+    fa = rng.uniform(-4, 4, (M, K)).astype(np.float32)
+    fb = rng.uniform(-4, 4, (N, K)).astype(np.float32)
+    fa[:, ::32] = 4.0
+    fb[:, ::32] = -4.0
+    a, b = W.bf16_bits(fa), W.bf16_bits(fb)
+    got = gpu_nt(a, b, "same-scale")
+    ref, _ = oracle_nt(a, b)
+    assert np.array_equal(got, bf16_rne_of_exact(ref))
+
+
+def test_one_hot_rows_pick_dequantized_entries():
+    # A row m = e_{k_m}: out[m, n] = dequant(B)[n, k_m] exactly (pins the operand lane layout)
+    rng = np.random.default_rng(8)
+    M, N, K = 64, 96, 1024
+    ks = rng.integers(0, K, M)
+    a = np.zeros((M, K), np.uint16)
+    a[np.arange(M), ks] = 0x3F80
+    b = W.normal_bf16((N, K), 1.0, 21)
+    got = gpu_nt(a, b, "one-hot")
+    qb, sb = oracle.cast_rows(b)
+    db = oracle.dequant(qb, sb)
+    expect = bf16_rne_of_exact(db[:, ks].T.copy())
+    assert np.array_equal(got, expect)
+
+
+def test_empty_and_zero_k():
+    a = mx.empty_operand(0, 64, "cuda:0")
+    b = mx.empty_operand(16, 64, "cuda:0")
+    out = mx.gemm_nt(a, b)
+    assert out.shape == (0, 16)
+    say("gemm K=0")
+    a0 = mx.empty_operand(8, 0, "cuda:0")
+    b0 = mx.empty_operand(16, 0, "cuda:0")
+    out = torch.full((8, 16), 7.0, dtype=torch.bfloat16, device="cuda:0")
+    mx.gemm_nt(a0, b0, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0)
+
+
+def test_nn_form_with_column_copy():
+    # out[M, N] = A[M, K] . B[K, N] with B entering through its column copy
+    M, K, N = 96, 320, 160
+    a = W.normal_bf16((M, K), 1.0, 31)
+    bkn = W.normal_bf16((K, N), 1.0, 32)
+    say("gemm_nn")
+    ag = mx.cast(to_device(a))
+    bt = mx.cast_dual(to_device(bkn))
+    out = mx.gemm_nn(ag, bt.col)
+    torch.cuda.synchronize()
+    qa, sa = oracle.cast_rows(a)
+    qc, sc = oracle.cast_cols(bkn)
+    ref, absref = oracle.gemm(qa, sa, qc, sc)
+    assert_gemm_close(bf16_to_f64(out), ref, absref, "nn")
+
+
+def test_output_leading_dimension():
+    M, N, K = 40, 72, 256
+    a = W.normal_bf16((M, K), 1.0, 41)
+    b = W.normal_bf16((N, K), 1.0, 42)
+    big = torch.full((M, 100), -1.0, dtype=torch.bfloat16, device="cuda:0")
+    say("gemm ldo")
+    mx.gemm_nt(mx.cast(to_device(a)), mx.cast(to_device(b)), out=big[:, 10:10 + N])
+    torch.cuda.synchronize()
+    ref, absref = oracle_nt(a, b)
+    got = bf16_to_f64(big)
+    assert_gemm_close(got[:, 10:10 + N], ref, absref, "ldo")
+    assert np.all(got[:, :10] == -1.0) and np.all(got[:, 10 + N:] == -1.0)
