@@ -50,6 +50,30 @@ def test_ragged_small(M, N, K):
     assert_gemm_close(got, ref, absref, "ragged %dx%dx%d" % (M, N, K))
 
 
+@pytest.mark.parametrize("M,N,K", [(128, 128, 256), (256, 256, 512), (300, 520, 288), (513, 260, 800),
+                                   (1000, 2000, 1024), (384, 640, 1312), (257, 129, 32), (2048, 256, 4096)])
+def test_tiled_shapes(M, N, K):
+    # workgroup tiles of 256 x 256 x 256: ragged M / N edges, K tails, odd and even K-tile counts
+    a = W.normal_bf16((M, K), 1.0, M + 7 * K)
+    b = W.normal_bf16((N, K), 0.5, N + 11 * K)
+    got = gpu_nt(a, b, "tiled")
+    ref, absref = oracle_nt(a, b)
+    assert_gemm_close(got, ref, absref, "tiled %dx%dx%d" % (M, N, K))
+
+
+def test_tiled_same_scale_bit_exact():
+    rng = np.random.default_rng(16)
+    M, N, K = 384, 320, 768
+    fa = rng.uniform(-4, 4, (M, K)).astype(np.float32)
+    fb = rng.uniform(-4, 4, (N, K)).astype(np.float32)
+    fa[:, ::32] = 4.0
+    fb[:, ::32] = 4.0
+    a, b = W.bf16_bits(fa), W.bf16_bits(fb)
+    got = gpu_nt(a, b, "tiled same-scale")
+    ref, _ = oracle_nt(a, b)
+    assert np.array_equal(got, bf16_rne_of_exact(ref))
+
+
 def test_k32_is_bit_exact():
     # one block: each output is one integer dot times a power of two -> exact in fp32,
     # so the bf16 result must be the nearest-even rounding of the exact value
