@@ -77,90 +77,166 @@ __global__ __launch_bounds__(256) void gemm_direct_kernel(const uint8_t* __restr
 
 
 // ---------------------------------------------------------------------------
-// Tiled kernel.  Workgroup tile BM x BN = 256 x 256, K tile 256 (128 bytes of
-// FP4 per row), 4 waves in a 2 x 2 grid, each wave 128 x 128 = 4 x 4 MFMA
-// tiles (256 fp32 accumulators per lane).
+// Pipelined kernel.  Workgroup tile 256 x 256, K tile 128 (64 bytes of FP4 per
+// row), 4 waves in a 2 x 2 grid, each wave 128 x 128 = 4 x 4 MFMA tiles
+// (256 fp32 accumulators per lane, in AGPRs).
 //
-// Global -> LDS: direct DMA (buffer_load_dwordx4 ... lds), 16 bytes per lane,
-// eight lanes per 128-byte row, so one wave instruction fills 8 rows (1 KB)
-// of a tile.  Each row's eight 16-byte chunks are stored XOR-swizzled, chunk
-// c of tile row r at position c ^ f(r) with f(r) = (r & 7) ^ ((r >> 3) & 1):
-// the MFMA fragment reads (lanes 0..31 = 32 consecutive rows at one chunk)
-// then hit distinct banks in every group of 8 (and 16) lanes.
-// Buffer resources are rebased per workgroup and bounded by the operand's
-// size, so rows past M / N read as zero without any predicate.
+// LDS holds NST = 4 stages of 36 KB: A codes [256 rows][64 B], B codes
+// [256][64 B], then the A and B scale tiles of the 256-wide K range the tile
+// belongs to (8 x 256 B each, straight copies of the MX scale layout).  All
+// global data arrives by direct DMA (buffer_load_dwordx4 ... lds), 16 bytes
+// per lane: a wave instruction fills 16 rows x 64 B.  Row r keeps its four
+// 16-byte chunks XOR-swizzled (chunk c at position c ^ ((r >> 2) & 3)), so the
+// fragment reads (32 consecutive rows at one chunk) hit 16 distinct 16-byte
+// bank groups per 16 lanes.  Descriptors are rebased per workgroup and
+// bounded by the operand size: rows past M / N, and whole tiles past K (an
+// empty descriptor), read as zero.  A K tail inside a tile needs no special
+// case: codes past K are finite FP4 values and their scale bytes are the
+// layout's zero padding, so those products vanish in fp32.
 //
-// Scales: the dword a lane needs for one K tile (four 64-wide K steps, byte
-// s for step s) is read straight into a VGPR with a bounded buffer load.
-// A K tail (K not a multiple of 256) needs no special case: the codes past K
-// in a row are finite FP4 values (from the next row, or zero past the end)
-// and the scale bytes past K/32 are the zero padding of the MX layout, so
-// their products are at most 6*6*2^-254 per term and vanish in fp32.
-//
-// Pipeline: two LDS stages.  Iteration kt waits for its own DMA (vmcnt 0),
-// meets the other waves at one barrier (tile kt is then complete and
-// everyone has finished reading stage (kt+1)%2), issues the DMA of tile
-// kt+1 into the other stage and runs the MFMAs of tile kt meanwhile.
+// Schedule of iteration kt (register set p = kt % 2 holds tile kt):
+//   MFMAs of K step 0 of tile kt, one DMA instruction of tile kt+3 (into
+//     stage (kt+3)%4, free since the previous barrier) after each of the
+//     first nine
+//   wait for the DMA of tile kt+1 and for this wave's LDS reads, barrier
+//   MFMAs of K step 1 of tile kt, with the LDS reads of tile kt+1 (set 1-p)
+//     spread between them
+// Memory instructions are spread one or two per MFMA: a wave that issues a
+// burst of them stalls on the address unit's queue and lets the MFMA pipe
+// drain.  A tile's DMA has about two tiles of MFMA work to land, and LDS read
+// latency hides behind half a tile.  The loop is unrolled by 4 (static stage
+// and register set) and runs a multiple of 4 tiles; tiles past K are empty
+// (zero codes, zero scales) and add nothing.
 // ---------------------------------------------------------------------------
 
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-typedef __attribute__((address_space(3))) void lds_void;
-
-constexpr int TBM = 256, TBN = 256, TBK = 256;  // tile sizes (elements)
-constexpr int TROWB = TBK / 2;                  // bytes per tile row (128)
-constexpr unsigned kRsrcWord3 = 0x00020000u;    // gfx9 raw buffer: 32-bit dwords, no swizzle
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
-    const int64_t cap = 0xFFFFFFFFll;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(bytes < cap ? bytes : cap),
-                                             (int)kRsrcWord3);
-}
-
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(3))) char* lds_cptr;
 
-// The same descriptor as four dwords (base lo, base hi | stride 0, num_records, word3) for inline asm.
+constexpr int PBM = 256, PBN = 256, PBK = 128;   // tile sizes (elements)
+constexpr int PROWB = PBK / 2;                    // bytes per tile row (64)
+constexpr int NST = 4;                            // LDS stages
+constexpr int ST_A = 0, ST_B = PBM * PROWB;       // code regions in a stage
+constexpr int ST_SA = ST_B + PBN * PROWB;         // 32768: A scale tiles
+constexpr int ST_SB = ST_SA + (PBM / 32) * 256;   // 34816: B scale tiles
+constexpr int STAGE = ST_SB + (PBN / 32) * 256;   // 36864 bytes
+constexpr unsigned kRsrcWord3 = 0x00020000u;      // gfx9 raw buffer: dword format, no swizzle
+constexpr int kDmaPerTile = 9;                    // DMA instructions per wave per tile
+
+// Raw buffer descriptor as four dwords: base, stride 0, num_records (bytes, capped at 4 GiB - 1), word3.
 __device__ __forceinline__ i32x4 make_rsrc_words(const void* base, int64_t bytes) {
     const int64_t cap = 0xFFFFFFFFll;
     const uint64_t a = reinterpret_cast<uint64_t>(base);
     i32x4 r;
     r.x = (int)(uint32_t)a;
-    r.y = (int)(uint32_t)(a >> 32) & 0xFFFF;
-    r.z = (int)(uint32_t)(bytes < cap ? bytes : cap);
+    r.y = (int)((uint32_t)(a >> 32) & 0xFFFFu);
+    r.z = (int)(uint32_t)(bytes <= 0 ? 0 : (bytes < cap ? bytes : cap));
     r.w = (int)kRsrcWord3;
     return r;
 }
 
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-
-// s_waitcnt vmcnt(0), other counters untouched (gfx9 encoding: expcnt 7, lgkmcnt 15).
-__device__ __forceinline__ void wait_vmcnt0() {
-    __builtin_amdgcn_sched_barrier(0);
-    // s_waitcnt vmcnt(0) expcnt(7) lgkmcnt(15) through the builtin, so the
-    // compiler's wait tracking knows every earlier load has completed
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+__device__ __forceinline__ i32x4 uniform(i32x4 v) {
+    i32x4 r;
+    r.x = __builtin_amdgcn_readfirstlane(v.x);
+    r.y = __builtin_amdgcn_readfirstlane(v.y);
+    r.z = __builtin_amdgcn_readfirstlane(v.z);
+    r.w = __builtin_amdgcn_readfirstlane(v.w);
+    return r;
 }
 
-// DMA one K tile of a 256-row operand tile into LDS (8 instructions per wave).
-// Instruction i of wave w fills tile rows (8w + i)*8 .. +7; lane l serves row
-// (8w + i)*8 + l/8 and physical chunk l%8, i.e. logical chunk
-// (l%8) ^ swz(row) = (l%8) ^ (l/8) ^ (i & 1).  voff[p] is the lane's byte
-// offset for instructions of parity p at K tile 0.
-//
-// The DMA is issued as inline assembly: the compiler's own wait insertion
-// treats every LDS read as possibly aliasing every outstanding LDS DMA and
-// would drain the prefetch (vmcnt(0)) before the current tile's fragment
-// reads.  The kernel instead waits for its DMA explicitly (wait_vmcnt0 before
-// the per-tile barrier); M0 (the DMA's LDS base) is written by the same asm
-// statement and nothing else in these kernels uses M0.
-__device__ __forceinline__ void dma_tile(const i32x4& rs, int row_step, int kbyte, const int (&voff)[2],
-                                         unsigned lds_base, int wave) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const unsigned m0v = lds_base + (unsigned)((wave * 8 + i) * 1024);
-        const int vo = voff[i & 1] + i * row_step + kbyte;
-        asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(vo), "s"(rs), "s"(m0v)
-                     : "memory", "m0");
+// One LDS DMA instruction: 64 lanes x 16 bytes from rs + voff into LDS at
+// m0v + 16 * lane.  Issued as inline assembly: the compiler's own wait
+// insertion treats every LDS read as aliasing every outstanding LDS DMA and
+// would drain the prefetch before each fragment read.  The kernel counts its
+// DMA instructions and waits for them explicitly (vmcnt); M0 is written here
+// and used by nothing else in these kernels.
+__device__ __forceinline__ void dma16(const i32x4& rs, int voff, unsigned m0v) {
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "s"(m0v)
+                 : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N) (expcnt/lgkmcnt left alone) through the builtin, so the
+// compiler's own wait tracking sees it.
+// With LDS0, also lgkmcnt(0): every LDS read this wave issued has returned.
+template <int N, bool LDS0 = false>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | ((LDS0 ? 0x0 : 0xF) << 8));
+}
+
+// Keeps LDS reads and MFMAs in program order (IR-level memory fence plus a
+// machine-scheduler barrier).
+__device__ __forceinline__ void order_point() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Component-wise select of two uniform descriptors, kept in SGPRs.
+__device__ __forceinline__ i32x4 pick(bool c, const i32x4& a, const i32x4& b) {
+    i32x4 r;
+    r.x = __builtin_amdgcn_readfirstlane(c ? a.x : b.x);
+    r.y = __builtin_amdgcn_readfirstlane(c ? a.y : b.y);
+    r.z = __builtin_amdgcn_readfirstlane(c ? a.z : b.z);
+    r.w = __builtin_amdgcn_readfirstlane(c ? a.w : b.w);
+    return r;
+}
+
+struct DmaPlan {
+    i32x4 ra, rb, rs;    // code descriptors (A, B) and this wave's scale descriptor (A or B scales)
+    int va, vb;          // lane byte offsets of instruction 0 of the A / B code DMA at tile 0
+    int row16;           // 16 rows of codes, in bytes
+    int vs;              // lane byte offset of this wave's scale DMA at tile-pair 0
+    int scale_region;    // LDS offset of this wave's scale copy inside a stage
+    unsigned lds0;       // LDS address of stage 0
+    int wave;
+};
+
+// Instruction q (0..8) of the DMA of tile kt into stage `st`: 0-3 A codes, 4-7 B codes, 8 scales.
+__device__ __forceinline__ void dma_one(const DmaPlan& P, int kt, bool valid, int st, int q) {
+    // a tile past K goes through a descriptor with num_records 0: every lane reads zero
+    const unsigned sbase = P.lds0 + (unsigned)(st * STAGE);
+    if (q < 4) {
+        i32x4 r = P.ra;
+        r.z = __builtin_amdgcn_readfirstlane(valid ? r.z : 0);
+        dma16(r, P.va + q * P.row16 + kt * PROWB, __builtin_amdgcn_readfirstlane(sbase + ST_A + (P.wave * 4 + q) * 1024));
+    } else if (q < 8) {
+        i32x4 r = P.rb;
+        r.z = __builtin_amdgcn_readfirstlane(valid ? r.z : 0);
+        dma16(r, P.vb + (q - 4) * P.row16 + kt * PROWB,
+              __builtin_amdgcn_readfirstlane(sbase + ST_B + (P.wave * 4 + q - 4) * 1024));
+    } else {
+        i32x4 r = P.rs;
+        r.z = __builtin_amdgcn_readfirstlane(valid ? r.z : 0);
+        dma16(r, P.vs + (kt >> 1) * 256, __builtin_amdgcn_readfirstlane(sbase + (unsigned)P.scale_region));
     }
+}
+
+// Registers holding one tile: fragments of its two 64-wide K steps and the scale dwords.
+struct TileRegs {
+    u32x4 a0[4], b0[4], a1[4], b1[4];
+    int sa[4], sb[4];
+};
+
+struct ReadPlan {
+    int a_off[2], b_off[2];  // per lane: fragment row + swizzled chunk c (c = 2*step + lane/32), A and B
+    int sa_off, sb_off;      // per lane: scale dword of the wave's first 32-row group
+};
+
+__device__ __forceinline__ u32x4 lds128(lds_cptr p) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(p);
+}
+__device__ __forceinline__ int lds32(lds_cptr p) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) int*>(p);
+}
+
+// LDS read q (0..23) of a tile: scales first, then the step-0 fragments, then step 1.
+__device__ __forceinline__ void read_one(TileRegs& T, const ReadPlan& R, lds_cptr stage, int q) {
+    if (q < 4) T.sa[q] = lds32(stage + ST_SA + R.sa_off + q * 256);
+    else if (q < 8) T.sb[q - 4] = lds32(stage + ST_SB + R.sb_off + (q - 4) * 256);
+    else if (q < 12) T.a0[q - 8] = lds128(stage + ST_A + R.a_off[0] + (q - 8) * 32 * PROWB);
+    else if (q < 16) T.b0[q - 12] = lds128(stage + ST_B + R.b_off[0] + (q - 12) * 32 * PROWB);
+    else if (q < 20) T.a1[q - 16] = lds128(stage + ST_A + R.a_off[1] + (q - 16) * 32 * PROWB);
+    else T.b1[q - 20] = lds128(stage + ST_B + R.b_off[1] + (q - 20) * 32 * PROWB);
 }
 
 __device__ __forceinline__ v8i as_operand(u32x4 v) {
@@ -170,71 +246,54 @@ __device__ __forceinline__ v8i as_operand(u32x4 v) {
     return r;
 }
 
-typedef const __attribute__((address_space(3))) char* lds_cptr;
-
-// Fragments of one 64-wide K step: 4 A (rows i*32 + lane%32 of the wave's
-// 128) and 4 B, 16 bytes each.
-struct Frags {
-    u32x4 a[4], b[4];
-};
-
-__device__ __forceinline__ void read_frags(Frags& f, lds_cptr la, lds_cptr lb, int a_base, int b_base, int choff) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        f.a[i] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(la + a_base + i * 32 * TROWB + choff);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        f.b[j] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(lb + b_base + j * 32 * TROWB + choff);
+// MFMA q (0..15) of one K step, (i, j) = (q / 4, q % 4).  B fragments enter the
+// first operand, so the accumulator row is the output column: each lane ends
+// up with 4 consecutive output columns of one output row.  OPSEL picks the
+// scale byte of the step.
+template <int OPSEL>
+__device__ __forceinline__ void mfma_one(f32x16 (&acc)[4][4], const u32x4 (&a)[4], const u32x4 (&b)[4],
+                                         const int (&sa)[4], const int (&sb)[4], int q) {
+    const int i = q >> 2, j = q & 3;
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(as_operand(b[j]), as_operand(a[i]), acc[i][j], 4, 4,
+                                                                OPSEL, sb[j], OPSEL, sa[i]);
 }
 
-template <int S>
-__device__ __forceinline__ void mfma_step(f32x16 (&acc)[4][4], const Frags& f, const int (&sa)[4],
-                                          const int (&sb)[4]) {
+// Iteration kt = 4t + U of the main loop (see the schedule above).
+template <int U>
+__device__ __forceinline__ void pipe_iter(f32x16 (&acc)[4][4], TileRegs& cur, TileRegs& nxt, const DmaPlan& P,
+                                          const ReadPlan& R, lds_cptr lds, int kt, int nkt) {
+    constexpr int OP = (U & 1) * 2;  // tile kt uses bytes 2*(kt%2) and 2*(kt%2)+1 of its scale dwords
+    const bool valid = kt + NST - 1 < nkt;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int q = 0; q < 16; ++q) {
+        mfma_one<OP>(acc, cur.a0, cur.b0, cur.sa, cur.sb, q);
+        if (q < kDmaPerTile) dma_one(P, kt + NST - 1, valid, (U + NST - 1) % NST, q);
+        order_point();
+    }
+    // tile kt+1 has landed (kt+2, kt+3 may be in flight), and this wave's LDS reads are done
+    wait_vmcnt<2 * kDmaPerTile, true>();
+    __syncthreads();
+    lds_cptr next = lds + ((U + 1) % NST) * STAGE;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(as_operand(f.a[i]), as_operand(f.b[j]),
-                                                                        acc[i][j], 4, 4, S, sa[i], S, sb[j]);
+    for (int q = 0; q < 16; ++q) {
+        // the step-0 data of tile kt+1 (reads 0..15) goes first: it is needed first
+        const int r0 = (q * 3) / 2, r1 = ((q + 1) * 3) / 2;
+#pragma unroll
+        for (int r = r0; r < r1; ++r) read_one(nxt, R, next, r);
+        mfma_one<OP + 1>(acc, cur.a1, cur.b1, cur.sa, cur.sb, q);
+        order_point();
+    }
 }
 
-// Keeps each K step's LDS reads and MFMAs in program order: a compiler memory
-// fence (IR level) plus a scheduling barrier (machine scheduler).
-__device__ __forceinline__ void mem_fence_compiler() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-}
-
-// One K tile: the reads of step s+1 are in flight while the MFMAs of step s run.
-__device__ __forceinline__ void compute_tile(f32x16 (&acc)[4][4], lds_cptr la, lds_cptr lb, int a_base, int b_base,
-                                             const int (&choff)[4], const int (&sa)[4], const int (&sb)[4]) {
-    Frags f0, f1;
-    read_frags(f0, la, lb, a_base, b_base, choff[0]);
-    mem_fence_compiler();
-    read_frags(f1, la, lb, a_base, b_base, choff[1]);
-    mem_fence_compiler();
-    mfma_step<0>(acc, f0, sa, sb);
-    read_frags(f0, la, lb, a_base, b_base, choff[2]);
-    mem_fence_compiler();
-    mfma_step<1>(acc, f1, sa, sb);
-    read_frags(f1, la, lb, a_base, b_base, choff[3]);
-    mem_fence_compiler();
-    mfma_step<2>(acc, f0, sa, sb);
-    mem_fence_compiler();
-    mfma_step<3>(acc, f1, sa, sb);
-    mem_fence_compiler();
-}
-
-__global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(const uint8_t* __restrict__ aq,
-                                                            const uint8_t* __restrict__ as,
-                                                            const uint8_t* __restrict__ bq,
-                                                            const uint8_t* __restrict__ bs, int M, int N, int K,
-                                                            uint16_t* __restrict__ out, int64_t ldo, int tiles_m,
-                                                            int tiles_n, int group_m) {
-    __shared__ __attribute__((aligned(1024))) char lds_a0[TBM * TROWB];
-    __shared__ __attribute__((aligned(1024))) char lds_b0[TBN * TROWB];
-    __shared__ __attribute__((aligned(1024))) char lds_a1[TBM * TROWB];
-    __shared__ __attribute__((aligned(1024))) char lds_b1[TBN * TROWB];
+template <bool VEC_STORE>
+__global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __restrict__ aq,
+                                                           const uint8_t* __restrict__ as,
+                                                           const uint8_t* __restrict__ bq,
+                                                           const uint8_t* __restrict__ bs, int M, int N, int K,
+                                                           uint16_t* __restrict__ out, int64_t ldo, int tiles_m,
+                                                           int tiles_n, int group_m) {
+    __shared__ __attribute__((aligned(1024))) char lds_raw[NST * STAGE];
+    lds_cptr lds = (lds_cptr)lds_raw;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -250,36 +309,51 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(const uint8_t* __res
     const int local = t - g * per_group;
     const int tm = first_m + local % gsize;
     const int tn = local / gsize;
-    const int64_t m0 = (int64_t)tm * TBM, n0 = (int64_t)tn * TBN;
+    const int64_t m0 = (int64_t)tm * PBM, n0 = (int64_t)tn * PBN;
 
     const int ldq = K >> 1;
-    const int nkt = (K + TBK - 1) / TBK;
-    const int64_t kt_total = nkt;  // scale tiles per 32-row group
+    const int nkt = (K + PBK - 1) / PBK;
+    const int kt2 = (K + 255) >> 8;  // 256-wide scale tiles per 32-row group
+    const int64_t a_groups = (M + 31) >> 5, b_groups = (N + 31) >> 5;
 
-    const i32x4 ra = make_rsrc_words(aq + m0 * ldq, (M - m0) * (int64_t)ldq);
-    const i32x4 rb = make_rsrc_words(bq + n0 * ldq, (N - n0) * (int64_t)ldq);
-    const unsigned la0 = (unsigned)(uintptr_t)(lds_cptr)lds_a0, lb0 = (unsigned)(uintptr_t)(lds_cptr)lds_b0;
-    const unsigned la1 = (unsigned)(uintptr_t)(lds_cptr)lds_a1, lb1 = (unsigned)(uintptr_t)(lds_cptr)lds_b1;
-    const int64_t a_rows32 = (M + 31) >> 5, b_rows32 = (N + 31) >> 5;
-    const rsrc_t rsa = make_rsrc(as + (m0 >> 5) * kt_total * 256, (a_rows32 - (m0 >> 5)) * kt_total * 256);
-    const rsrc_t rsb = make_rsrc(bs + (n0 >> 5) * kt_total * 256, (b_rows32 - (n0 >> 5)) * kt_total * 256);
-
-    // DMA lane offsets (see dma_tile) and the per-instruction row step (8 rows)
-    int voff[2];
+    DmaPlan P;
+    P.wave = wave;
+    P.ra = uniform(make_rsrc_words(aq + m0 * ldq, (M - m0) * (int64_t)ldq));
+    P.rb = uniform(make_rsrc_words(bq + n0 * ldq, (N - n0) * (int64_t)ldq));
+    {
+        // waves 0, 1 copy the A scale tiles, waves 2, 3 the B scale tiles
+        const i32x4 rsa = make_rsrc_words(as + (m0 >> 5) * kt2 * 256, (a_groups - (m0 >> 5)) * kt2 * 256);
+        const i32x4 rsb = make_rsrc_words(bs + (n0 >> 5) * kt2 * 256, (b_groups - (n0 >> 5)) * kt2 * 256);
+        P.rs = pick(wave >= 2, rsb, rsa);
+        P.scale_region = (wave >= 2 ? ST_SB : ST_SA) + (wave & 1) * 1024;
+    }
+    {
+        // code DMA: instruction i of wave w fills tile rows (4w + i)*16 + lane/4, physical chunk lane%4,
+        // i.e. logical chunk (lane%4) ^ ((row >> 2) & 3) = (lane & 3) ^ ((lane >> 4) & 3)
+        const int row = wave * 64 + (lane >> 2);
+        const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
+        P.va = row * ldq + chunk * 16;
+        P.vb = P.va;
+        P.row16 = 16 * ldq;
+        // scale DMA: 4 scale tiles (32-row groups) of 256 B per instruction
+        const int grp = (wave & 1) * 4 + (lane >> 4);
+        P.vs = grp * kt2 * 256 + (lane & 15) * 16;
+        P.lds0 = (unsigned)(uintptr_t)lds;
+    }
+    ReadPlan R;
+    {
+        const int frow = lane & 31;
+        const int sw = (frow >> 2) & 3;
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
-        voff[p] = (wave * 64 + (lane >> 3)) * ldq + (((lane & 7) ^ (lane >> 3) ^ p) * 16);
-    const int row_step = 8 * ldq;
-
-    // per-lane scale offset inside a 256-byte scale tile
-    const int s_lane = (lane & 31) * 8 + (lane >> 5) * 4;
-    // per-lane LDS fragment offsets: row (lane & 31) of a 32-row group, chunk (2s + lane/32) swizzled
-    const int frow = lane & 31;
-    const int a_base = (wm * 128 + frow) * TROWB;
-    const int b_base = (wn * 128 + frow) * TROWB;
-    int choff[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) choff[s] = ((2 * s + (lane >> 5)) ^ swz(frow)) * 16;
+        for (int st = 0; st < 2; ++st) {
+            const int c = 2 * st + (lane >> 5);
+            R.a_off[st] = (wm * 128 + frow) * PROWB + ((c ^ sw) << 4);
+            R.b_off[st] = (wn * 128 + frow) * PROWB + ((c ^ sw) << 4);
+        }
+        const int s_lane = frow * 8 + (lane >> 5) * 4;
+        R.sa_off = wm * 4 * 256 + s_lane;
+        R.sb_off = wn * 4 * 256 + s_lane;
+    }
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -287,67 +361,63 @@ __global__ __launch_bounds__(256, 1) void gemm_tiled_kernel(const uint8_t* __res
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-    int sa[4], sb[4], sa_n[4], sb_n[4];
-    auto load_scales = [&](int kt, int (&da)[4], int (&db)[4]) {
+    // prologue: tiles 0..2 in flight, then tile 0 into registers
+#pragma unroll
+    for (int st = 0; st < NST - 1; ++st)
+#pragma unroll
+        for (int q = 0; q < kDmaPerTile; ++q) dma_one(P, st, st < nkt, st, q);
+    wait_vmcnt<(NST - 2) * kDmaPerTile, true>();
+    __syncthreads();
+    TileRegs r0, r1;
+#pragma unroll
+    for (int q = 0; q < 24; ++q) read_one(r0, R, lds, q);
+    order_point();
+
+    const int trips = (nkt + NST - 1) / NST;
+    for (int tr = 0; tr < trips; ++tr) {
+        const int kt = tr * NST;
+        pipe_iter<0>(acc, r0, r1, P, R, lds, kt + 0, nkt);
+        pipe_iter<1>(acc, r1, r0, P, R, lds, kt + 1, nkt);
+        pipe_iter<2>(acc, r0, r1, P, R, lds, kt + 2, nkt);
+        pipe_iter<3>(acc, r1, r0, P, R, lds, kt + 3, nkt);
+    }
+    // drain the DMA of the (empty) tiles past the end before the workgroup can exit
+    wait_vmcnt<0>();
+
+    // ---- epilogue: fp32 -> bf16 (nearest even).  acc[i][j][g*4 + e] is output row
+    // m0 + wm*128 + i*32 + lane%32, column n0 + wn*128 + j*32 + g*8 + (lane/32)*4 + e.
+    const int64_t mrow = m0 + wm * 128 + (lane & 31);
+    const int64_t ncol = n0 + wn * 128 + (lane >> 5) * 4;
+    const bool full = (m0 + wm * 128 + 128 <= M) && (n0 + wn * 128 + 128 <= N);
+    if (VEC_STORE && full) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int ga = (wm * 4 + i) * (int)kt_total + kt;   // 32-row group of the fragment, K tile kt
-            const int gb = (wn * 4 + i) * (int)kt_total + kt;
-            da[i] = __builtin_amdgcn_raw_buffer_load_b32(rsa, ga * 256 + s_lane, 0, 0);
-            db[i] = __builtin_amdgcn_raw_buffer_load_b32(rsb, gb * 256 + s_lane, 0, 0);
+            uint16_t* orow = out + (mrow + i * 32) * ldo + ncol;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const f32x16& c = acc[i][j];
+                    uint2 v;
+                    v.x = (uint32_t)f32_to_bf16_rne(c[gq * 4 + 0]) | ((uint32_t)f32_to_bf16_rne(c[gq * 4 + 1]) << 16);
+                    v.y = (uint32_t)f32_to_bf16_rne(c[gq * 4 + 2]) | ((uint32_t)f32_to_bf16_rne(c[gq * 4 + 3]) << 16);
+                    *reinterpret_cast<uint2*>(orow + j * 32 + gq * 8) = v;
+                }
         }
-    };
-
-    dma_tile(ra, row_step, 0, voff, la0, wave);
-    dma_tile(rb, row_step, 0, voff, lb0, wave);
-    load_scales(0, sa, sb);
-
-    // Main loop, two K tiles per iteration and no branches inside (a branch
-    // lets the compiler sink the MFMAs past the next barrier).  The prefetch
-    // of a tile past the end goes through an empty descriptor, so it moves
-    // no data.
-    i32x4 ra_none = ra, rb_none = rb;
-    ra_none.z = 0;
-    rb_none.z = 0;
-    const int iters = nkt >> 1;
-    for (int it = 0; it < iters; ++it) {
-        const int kt = 2 * it;
-        // ---- tile kt from stage 0; prefetch tile kt+1 into stage 1
-        wait_vmcnt0();
-        __syncthreads();
-        dma_tile(ra, row_step, (kt + 1) * TROWB, voff, la1, wave);
-        dma_tile(rb, row_step, (kt + 1) * TROWB, voff, lb1, wave);
-        load_scales(kt + 1, sa_n, sb_n);
-        compute_tile(acc, (lds_cptr)lds_a0, (lds_cptr)lds_b0, a_base, b_base, choff, sa, sb);
-        // ---- tile kt+1 from stage 1; prefetch tile kt+2 (if any) into stage 0
-        wait_vmcnt0();
-        __syncthreads();
-        const bool more = kt + 2 < nkt;
-        dma_tile(more ? ra : ra_none, row_step, (kt + 2) * TROWB, voff, la0, wave);
-        dma_tile(more ? rb : rb_none, row_step, (kt + 2) * TROWB, voff, lb0, wave);
-        load_scales(kt + 2, sa, sb);
-        compute_tile(acc, (lds_cptr)lds_a1, (lds_cptr)lds_b1, a_base, b_base, choff, sa_n, sb_n);
-    }
-    if (nkt & 1) {
-        // ---- odd tail: the last tile sits in stage 0
-        wait_vmcnt0();
-        __syncthreads();
-        compute_tile(acc, (lds_cptr)lds_a0, (lds_cptr)lds_b0, a_base, b_base, choff, sa, sb);
-    }
-
-    // ---- epilogue: fp32 -> bf16 (nearest even), predicated stores
-    const int half = lane >> 5;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int64_t n = n0 + wn * 128 + j * 32 + (lane & 31);
-        if (n >= N) continue;
+    } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+            const int64_t m = mrow + i * 32;
+            if (m >= M) continue;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int64_t m = m0 + wm * 128 + i * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
-                if (m < M) out[m * ldo + n] = f32_to_bf16_rne(acc[i][j][e]);
-            }
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int64_t n = ncol + j * 32 + gq * 8 + e;
+                        if (n < N) out[m * ldo + n] = f32_to_bf16_rne(acc[i][j][gq * 4 + e]);
+                    }
         }
     }
 }
@@ -359,10 +429,13 @@ extern "C" hipError_t mx_launch_gemm(const void* aq, const void* as, const void*
     if (M == 0 || N == 0) return hipSuccess;
     const bool tiled = K > 0 && M >= 128 && N >= 128 && getenv_direct() == 0;
     if (tiled) {
-        const int64_t tiles_m = (M + mx::TBM - 1) / mx::TBM, tiles_n = (N + mx::TBN - 1) / mx::TBN;
+        const int64_t tiles_m = (M + mx::PBM - 1) / mx::PBM, tiles_n = (N + mx::PBN - 1) / mx::PBN;
         if (tiles_m * tiles_n > 0x7FFFFFFF) return hipErrorInvalidValue;
         const int group_m = 8;
-        hipLaunchKernelGGL(mx::gemm_tiled_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, stream,
+        // 8-byte output stores need an 8-byte aligned start for every row
+        const bool vec = (reinterpret_cast<uintptr_t>(out) & 7u) == 0 && (ldo & 3) == 0;
+        auto kern = vec ? mx::gemm_pipe_kernel<true> : mx::gemm_pipe_kernel<false>;
+        hipLaunchKernelGGL(kern, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, stream,
                            static_cast<const uint8_t*>(aq), static_cast<const uint8_t*>(as),
                            static_cast<const uint8_t*>(bq), static_cast<const uint8_t*>(bs), (int)M, (int)N, (int)K,
                            static_cast<uint16_t*>(out), ldo, (int)tiles_m, (int)tiles_n, group_m);
