@@ -32,15 +32,20 @@
  *     as long as their output buffers do not overlap.
  *
  * Quantized operand format ("MX operand", R rows, contraction length K,
- * K a multiple of 32):
- *   q : R * K/2 bytes, row-major, row stride K/2 bytes.  Byte j of a row holds
- *       element 2j in bits 0..3 and element 2j+1 in bits 4..7.
- *   s : scale bytes in 256-byte tiles of 32 rows x 8 blocks.  With
- *       kt = ceil(K/256), the scale of (row r, block b = k/32) is at
- *         ((r/32) * kt + b/8) * 256 + (r%32) * 8 + (b%2) * 4 + (b%8)/2
- *       so that one dword holds the scales a 32x32x64 scaled MFMA lane needs
- *       for four consecutive K steps.  Positions past R rows or K/32 blocks
- *       are written as 0.  Size: ceil(R/32) * kt * 256 bytes.
+ * K a multiple of 32).  Both parts are tiled so that the GEMM moves one
+ * contiguous kilobyte per wave load:
+ *   q : codes in 1 KB tiles of 16 rows x 128 elements.  With KT = ceil(K/128),
+ *       element (r, k) sits in byte
+ *         ((r/16) * KT + k/128) * 1024 + (r%16) * 64 + (k%128)/2
+ *       low nibble for even k, high nibble for odd k.  Rows past R and
+ *       elements past K hold code 0.  Size: ceil(R/16) * KT * 1024 bytes.
+ *   s : E8M0 scales in 1 KB tiles of 128 rows x 256 elements.  With
+ *       KT2 = ceil(K/256), the scale of (row r, block b = k/32) sits in byte
+ *         ((r/128) * KT2 + b/8) * 1024 + ((r/32)%4) * 256 + (r%32) * 8
+ *           + (b%2) * 4 + (b%8)/2
+ *       so that one dword holds the scales a 32x32x64 scaled-MFMA lane needs
+ *       for four consecutive 64-wide K steps.  Positions past R rows or K/32
+ *       blocks hold 0.  Size: ceil(R/128) * KT2 * 1024 bytes.
  *   The row copy of x[R, C] is the MX operand (R rows, K = C).  The column
  *   copy is the MX operand (C rows, K = Rp) with Rp = ceil(R/32)*32: row c of
  *   it quantizes column c of x in blocks of 32 rows, rows R..Rp-1 taken as +0.
@@ -69,12 +74,14 @@ typedef enum {
 
 /* Sizes of one MX operand.  Host only; touches no device. */
 typedef struct {
-    int64_t rows;       /* R */
-    int64_t k;          /* contraction length, a multiple of 32 */
-    int64_t q_bytes;    /* R * K/2 */
-    int64_t s_bytes;    /* ceil(R/32) * ceil(K/256) * 256 */
-    int64_t row_tiles;  /* ceil(R/32) */
-    int64_t k_tiles;    /* ceil(K/256) */
+    int64_t rows;             /* R */
+    int64_t k;                /* contraction length, a multiple of 32 */
+    int64_t q_bytes;          /* ceil(R/16) * ceil(K/128) * 1024 */
+    int64_t s_bytes;          /* ceil(R/128) * ceil(K/256) * 1024 */
+    int64_t code_row_tiles;   /* ceil(R/16) */
+    int64_t code_k_tiles;     /* ceil(K/128) */
+    int64_t scale_row_tiles;  /* ceil(R/128) */
+    int64_t scale_k_tiles;    /* ceil(K/256) */
 } mxfp4_operand_layout;
 
 /* Fill *out for an operand of `rows` rows and contraction length `k`.

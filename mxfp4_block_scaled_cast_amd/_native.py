@@ -15,7 +15,8 @@ _i64, _p, _i32, _sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_si
 
 class OperandLayout(ctypes.Structure):
     _fields_ = [("rows", _i64), ("k", _i64), ("q_bytes", _i64), ("s_bytes", _i64),
-                ("row_tiles", _i64), ("k_tiles", _i64)]
+                ("code_row_tiles", _i64), ("code_k_tiles", _i64), ("scale_row_tiles", _i64),
+                ("scale_k_tiles", _i64)]
 
 
 SIGNATURES = [

@@ -17,7 +17,7 @@ from . import _native as N
 
 @dataclass
 class MxOperand:
-    """One quantized copy: packed E2M1 codes q [rows, k/2] and E8M0 scales s (device layout)."""
+    """One quantized copy in the tiled MX layout: E2M1 codes q and E8M0 scales s (flat uint8 buffers)."""
     q: torch.Tensor
     s: torch.Tensor
     rows: int
@@ -47,7 +47,7 @@ def _check_bf16_matrix(x, name):
 
 def empty_operand(rows, k, device):
     L = N.operand_layout(rows, k)
-    q = torch.empty((rows, k // 2), dtype=torch.uint8, device=device)
+    q = torch.empty((L.q_bytes,), dtype=torch.uint8, device=device)
     s = torch.empty((L.s_bytes,), dtype=torch.uint8, device=device)
     return MxOperand(q, s, rows, k)
 

@@ -47,8 +47,10 @@ struct OperandSizes {
     int64_t q, s;
 };
 
+// Tiled MX operand layout: codes in 1 KB tiles of 16 rows x 128 elements,
+// scales in 1 KB tiles of 128 rows x 256 elements (include/mxfp4.h).
 OperandSizes operand_sizes(int64_t rows, int64_t k) {
-    return {rows * (k / 2), ((rows + 31) / 32) * ((k + 255) / 256) * 256};
+    return {((rows + 15) / 16) * ((k + 127) / 128) * 1024, ((rows + 127) / 128) * ((k + 255) / 256) * 1024};
 }
 
 int validate_cast(const void* x, int64_t rows, int64_t cols, int64_t ldx, const void* q, const void* s) {
@@ -146,8 +148,10 @@ int mxfp4_operand_layout_of(int64_t rows, int64_t k, mxfp4_operand_layout* out) 
     out->k = k;
     out->q_bytes = sz.q;
     out->s_bytes = sz.s;
-    out->row_tiles = (rows + 31) / 32;
-    out->k_tiles = (k + 255) / 256;
+    out->code_row_tiles = (rows + 15) / 16;
+    out->code_k_tiles = (k + 127) / 128;
+    out->scale_row_tiles = (rows + 127) / 128;
+    out->scale_k_tiles = (k + 255) / 256;
     return MXFP4_OK;
 }
 

@@ -20,8 +20,10 @@
 // bytes per row); v_perm pairs rows 2j and 2j+1 of one column, the pair is
 // converted to a byte, and each column's 32 codes leave as one 16-byte store.
 //
-// The grid is extended to cover the padded scale region of both copies, so
-// every padding scale byte is written (as 0: padded positions load as +0).
+// Both copies are written in the tiled MX operand layout (16 x 128 code
+// tiles, 128 x 256 scale tiles).  The grid is extended to cover the padded
+// regions of both copies, so every padding byte is written (codes and scales
+// 0: padded positions load as +0).
 #include "mx_device.h"
 
 namespace mx {
@@ -39,8 +41,10 @@ __global__ __launch_bounds__(256) void cast_kernel(const uint16_t* __restrict__ 
     const int64_t r0 = (int64_t)rt * TILE_R;
     const int64_t c0 = (int64_t)ct * 256;
 
-    const int64_t row_pad = (R + 31) & ~(int64_t)31;  // rows of the row copy's scale region
-    const int64_t k_tiles_row = (C + 255) >> 8;        // contraction tiles of the row copy
+    const int64_t row16 = (R + 15) & ~(int64_t)15;     // code rows of the row copy (padded)
+    const int64_t row128 = (R + 127) & ~(int64_t)127;  // scale rows of the row copy (padded)
+    const int64_t kt128_row = (C + 127) >> 7;          // 128-wide code tiles of the row copy
+    const int64_t kt256_row = (C + 255) >> 8;          // 256-wide scale tiles of the row copy
     const int cl = t & 31;                              // 16-byte column chunk within the tile
     const int64_t col = c0 + cl * 8;
     const bool col_ok = col < C;
@@ -68,11 +72,11 @@ __global__ __launch_bounds__(256) void cast_kernel(const uint16_t* __restrict__ 
         const unsigned sb = scale_byte_from_amax(amax);
         unsigned codes = cvt8(v[i], scale_value(sb));
         if (sb == 255u) codes = 0u;
-        if (col_ok && row < R) {
-            *reinterpret_cast<unsigned*>(q_row + row * (C >> 1) + (col >> 1)) = codes;
+        if (row < row16 && col < kt128_row * 128) {
+            *reinterpret_cast<unsigned*>(q_row + code_offset(row, col, kt128_row)) = codes;
         }
-        if ((cl & 3) == 0 && row < row_pad) {
-            s_row[scale_offset(row, col >> 5, k_tiles_row)] = (uint8_t)sb;
+        if ((cl & 3) == 0 && row < row128) {
+            s_row[scale_offset(row, col >> 5, kt256_row)] = (uint8_t)sb;
         }
     }
 
@@ -85,9 +89,11 @@ __global__ __launch_bounds__(256) void cast_kernel(const uint16_t* __restrict__ 
         }
         __syncthreads();
 
-        const int64_t Rp = row_pad;                 // contraction length of the column copy
-        const int64_t k_tiles_col = (Rp + 255) >> 8;
-        const int64_t col_pad = (C + 31) & ~(int64_t)31;
+        const int64_t Rp = (R + 31) & ~(int64_t)31;  // contraction length of the column copy
+        const int64_t kt128_col = (Rp + 127) >> 7;
+        const int64_t kt256_col = (Rp + 255) >> 8;
+        const int64_t col16 = (C + 15) & ~(int64_t)15;
+        const int64_t col128 = (C + 127) & ~(int64_t)127;
         constexpr int ITEMS = TILE_R / 64;          // 32x2 strips per thread
 #pragma unroll
         for (int it = 0; it < ITEMS; ++it) {
@@ -96,7 +102,7 @@ __global__ __launch_bounds__(256) void cast_kernel(const uint16_t* __restrict__ 
             const int rb = item >> 7;               // 32-row block within the tile
             const int64_t c = c0 + cp * 2;
             const int64_t rblk = r0 + rb * 32;      // first row of the block
-            if (rblk >= ((k_tiles_col * 256))) continue;  // beyond the padded scale region
+            if (rblk >= kt256_col * 256) continue;  // beyond the padded scale region
             unsigned d[32];
 #pragma unroll
             for (int r = 0; r < 32; ++r) d[r] = lds[(rb * 32 + r) * 128 + cp];
@@ -121,13 +127,13 @@ __global__ __launch_bounds__(256) void cast_kernel(const uint16_t* __restrict__ 
                 o0[w] = sb0 == 255u ? 0u : a0;
                 o1[w] = sb1 == 255u ? 0u : a1;
             }
-            if (c < C && rblk < Rp) {
-                *reinterpret_cast<u32x4*>(q_col + c * (Rp >> 1) + (rblk >> 1)) = o0;
-                *reinterpret_cast<u32x4*>(q_col + (c + 1) * (Rp >> 1) + (rblk >> 1)) = o1;
+            if (c < col16 && rblk < kt128_col * 128) {
+                *reinterpret_cast<u32x4*>(q_col + code_offset(c, rblk, kt128_col)) = o0;
+                *reinterpret_cast<u32x4*>(q_col + code_offset(c + 1, rblk, kt128_col)) = o1;
             }
-            if (c < col_pad) {
-                s_col[scale_offset(c, rblk >> 5, k_tiles_col)] = (uint8_t)sb0;
-                s_col[scale_offset(c + 1, rblk >> 5, k_tiles_col)] = (uint8_t)sb1;
+            if (c < col128) {
+                s_col[scale_offset(c, rblk >> 5, kt256_col)] = (uint8_t)sb0;
+                s_col[scale_offset(c + 1, rblk >> 5, kt256_col)] = (uint8_t)sb1;
             }
         }
     }
@@ -139,10 +145,9 @@ __global__ __launch_bounds__(256) void cast_kernel(const uint16_t* __restrict__ 
 extern "C" hipError_t mx_launch_cast(const void* x, int64_t R, int64_t C, int64_t ldx, void* q_row, void* s_row,
                                      void* q_col, void* s_col, bool dual, hipStream_t stream) {
     constexpr int TILE_R = 64;
-    const int64_t row_pad = (R + 31) & ~(int64_t)31;
-    // rows covered: the row copy's padded scale rows, and for the dual cast the
-    // column copy's padded contraction (a multiple of 256)
-    const int64_t rows_cover = dual ? ((row_pad + 255) & ~(int64_t)255) : row_pad;
+    // rows covered: the row copy's padded scale rows (a multiple of 128), and for
+    // the dual cast the column copy's padded contraction (a multiple of 256)
+    const int64_t rows_cover = dual ? ((R + 255) & ~(int64_t)255) : ((R + 127) & ~(int64_t)127);
     const int64_t n_rtiles = (rows_cover + TILE_R - 1) / TILE_R;
     const int64_t n_ctiles = (C + 255) / 256;
     const int64_t total = n_rtiles * n_ctiles;

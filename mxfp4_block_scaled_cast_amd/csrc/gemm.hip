@@ -43,8 +43,7 @@ __global__ __launch_bounds__(256) void gemm_direct_kernel(const uint8_t* __restr
     const int ra = m0 + (lane & 31);
     const int rb = n0 + (lane & 31);
     const int half = lane >> 5;
-    const int64_t kt = (K + 255) >> 8;
-    const int64_t ldq = K >> 1;
+    const int64_t kt128 = (K + 127) >> 7, kt256 = (K + 255) >> 8;
 
     f32x16 acc = {};
     for (int k0 = 0; k0 < K; k0 += 64) {
@@ -53,14 +52,14 @@ __global__ __launch_bounds__(256) void gemm_direct_kernel(const uint8_t* __restr
         int sa = 0, sb = 0;
         if (kk < K) {
             if (ra < M) {
-                const u32x4 v = *reinterpret_cast<const u32x4*>(aq + (int64_t)ra * ldq + (kk >> 1));
+                const u32x4 v = *reinterpret_cast<const u32x4*>(aq + code_offset(ra, kk, kt128));
                 a[0] = (int)v.x; a[1] = (int)v.y; a[2] = (int)v.z; a[3] = (int)v.w;
-                sa = as[scale_offset(ra, kk >> 5, kt)];
+                sa = as[scale_offset(ra, kk >> 5, kt256)];
             }
             if (rb < N) {
-                const u32x4 v = *reinterpret_cast<const u32x4*>(bq + (int64_t)rb * ldq + (kk >> 1));
+                const u32x4 v = *reinterpret_cast<const u32x4*>(bq + code_offset(rb, kk, kt128));
                 b[0] = (int)v.x; b[1] = (int)v.y; b[2] = (int)v.z; b[3] = (int)v.w;
-                sb = bs[scale_offset(rb, kk >> 5, kt)];
+                sb = bs[scale_offset(rb, kk >> 5, kt256)];
             }
         }
         acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 4, 4, 0, sa, 0, sb);
@@ -83,24 +82,28 @@ __global__ __launch_bounds__(256) void gemm_direct_kernel(const uint8_t* __restr
 //
 // LDS holds NST = 4 stages of 36 KB: A codes [256 rows][64 B], B codes
 // [256][64 B], then the A and B scale tiles of the 256-wide K range the tile
-// belongs to (8 x 256 B each, straight copies of the MX scale layout).  All
+// belongs to (2 x 1 KB each, straight copies of the MX scale layout).  All
 // global data arrives by direct DMA (buffer_load_dwordx4 ... lds), 16 bytes
-// per lane: a wave instruction fills 16 rows x 64 B.  Row r keeps its four
-// 16-byte chunks XOR-swizzled (chunk c at position c ^ ((r >> 2) & 3)), so the
-// fragment reads (32 consecutive rows at one chunk) hit 16 distinct 16-byte
-// bank groups per 16 lanes.  Descriptors are rebased per workgroup and
-// bounded by the operand size: rows past M / N, and whole tiles past K (an
-// empty descriptor), read as zero.  A K tail inside a tile needs no special
-// case: codes past K are finite FP4 values and their scale bytes are the
-// layout's zero padding, so those products vanish in fp32.
+// per lane: a wave instruction moves one 1 KB code tile of the MX layout
+// (16 rows x 64 B, contiguous in memory, so one instruction touches one page;
+// row-major codes made every instruction span 16 rows and stalled the L1
+// address translation) or one 1 KB scale tile.  Row r keeps its four
+// 16-byte chunks XOR-swizzled, chunk c at position c ^ swz(r) with
+// swz(r) = ((r >> 1) & 3) ^ (3 * ((r >> 3) & 1)): for the fragment reads (32
+// consecutive rows at one chunk) every aligned group of 8 rows then covers 8
+// distinct 16-byte slots of a 128-byte bank window and every aligned group of
+// 16 rows 16 distinct slots of a 256-byte window.  Descriptors are rebased per workgroup and
+// bounded by the operand size: rows past the padded M / N, and whole tiles
+// past K (an empty descriptor), read as zero.  A K tail inside a tile needs
+// no special case: the layout pads codes to a multiple of 128 elements with
+// zero codes and the scales with zero bytes.
 //
 // Schedule of iteration kt (register set p = kt % 2 holds tile kt):
-//   MFMAs of K step 0 of tile kt, one DMA instruction of tile kt+3 (into
-//     stage (kt+3)%4, free since the previous barrier) after each of the
-//     first nine
+//   MFMAs of K step 0 of tile kt, with 4 of the 9 DMA instructions of tile
+//     kt+3 (into stage (kt+3)%4, free since the previous barrier)
 //   wait for the DMA of tile kt+1 and for this wave's LDS reads, barrier
 //   MFMAs of K step 1 of tile kt, with the LDS reads of tile kt+1 (set 1-p)
-//     spread between them
+//     and the other 5 DMA instructions of tile kt+3 spread between them
 // Memory instructions are spread one or two per MFMA: a wave that issues a
 // burst of them stalls on the address unit's queue and lets the MFMA pipe
 // drain.  A tile's DMA has about two tiles of MFMA work to land, and LDS read
@@ -121,6 +124,10 @@ constexpr int ST_SB = ST_SA + (PBM / 32) * 256;   // 34816: B scale tiles
 constexpr int STAGE = ST_SB + (PBN / 32) * 256;   // 36864 bytes
 constexpr unsigned kRsrcWord3 = 0x00020000u;      // gfx9 raw buffer: dword format, no swizzle
 constexpr int kDmaPerTile = 9;                    // DMA instructions per wave per tile
+constexpr int kDmaStep0 = 4;                      // of which issued during K step 0
+
+// Chunk swizzle of a 64-byte tile row (depends on the row's low 4 bits only).
+__device__ __forceinline__ int swz64(int r) { return ((r >> 1) & 3) ^ (3 * ((r >> 3) & 1)); }
 
 // Raw buffer descriptor as four dwords: base, stride 0, num_records (bytes, capped at 4 GiB - 1), word3.
 __device__ __forceinline__ i32x4 make_rsrc_words(const void* base, int64_t bytes) {
@@ -183,9 +190,9 @@ __device__ __forceinline__ i32x4 pick(bool c, const i32x4& a, const i32x4& b) {
 
 struct DmaPlan {
     i32x4 ra, rb, rs;    // code descriptors (A, B) and this wave's scale descriptor (A or B scales)
-    int va, vb;          // lane byte offsets of instruction 0 of the A / B code DMA at tile 0
-    int row16;           // 16 rows of codes, in bytes
-    int vs;              // lane byte offset of this wave's scale DMA at tile-pair 0
+    int va, vb;          // lane byte offsets of instruction 0 of the A / B code DMA at K tile 0
+    int tstep;           // bytes between consecutive 16-row code tiles (KT * 1 KB)
+    int vs;              // lane byte offset of this wave's scale DMA at K-tile pair 0
     int scale_region;    // LDS offset of this wave's scale copy inside a stage
     unsigned lds0;       // LDS address of stage 0
     int wave;
@@ -198,16 +205,16 @@ __device__ __forceinline__ void dma_one(const DmaPlan& P, int kt, bool valid, in
     if (q < 4) {
         i32x4 r = P.ra;
         r.z = __builtin_amdgcn_readfirstlane(valid ? r.z : 0);
-        dma16(r, P.va + q * P.row16 + kt * PROWB, __builtin_amdgcn_readfirstlane(sbase + ST_A + (P.wave * 4 + q) * 1024));
+        dma16(r, P.va + q * P.tstep + kt * 1024, __builtin_amdgcn_readfirstlane(sbase + ST_A + (P.wave * 4 + q) * 1024));
     } else if (q < 8) {
         i32x4 r = P.rb;
         r.z = __builtin_amdgcn_readfirstlane(valid ? r.z : 0);
-        dma16(r, P.vb + (q - 4) * P.row16 + kt * PROWB,
+        dma16(r, P.vb + (q - 4) * P.tstep + kt * 1024,
               __builtin_amdgcn_readfirstlane(sbase + ST_B + (P.wave * 4 + q - 4) * 1024));
     } else {
         i32x4 r = P.rs;
         r.z = __builtin_amdgcn_readfirstlane(valid ? r.z : 0);
-        dma16(r, P.vs + (kt >> 1) * 256, __builtin_amdgcn_readfirstlane(sbase + (unsigned)P.scale_region));
+        dma16(r, P.vs + (kt >> 1) * 1024, __builtin_amdgcn_readfirstlane(sbase + (unsigned)P.scale_region));
     }
 }
 
@@ -263,15 +270,17 @@ template <int U>
 __device__ __forceinline__ void pipe_iter(f32x16 (&acc)[4][4], TileRegs& cur, TileRegs& nxt, const DmaPlan& P,
                                           const ReadPlan& R, lds_cptr lds, int kt, int nkt) {
     constexpr int OP = (U & 1) * 2;  // tile kt uses bytes 2*(kt%2) and 2*(kt%2)+1 of its scale dwords
+    constexpr int DST = (U + NST - 1) % NST;
     const bool valid = kt + NST - 1 < nkt;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
         mfma_one<OP>(acc, cur.a0, cur.b0, cur.sa, cur.sb, q);
-        if (q < kDmaPerTile) dma_one(P, kt + NST - 1, valid, (U + NST - 1) % NST, q);
+        if ((q & 3) == 1) dma_one(P, kt + NST - 1, valid, DST, q >> 2);  // DMA instructions 0..3
         order_point();
     }
-    // tile kt+1 has landed (kt+2, kt+3 may be in flight), and this wave's LDS reads are done
-    wait_vmcnt<2 * kDmaPerTile, true>();
+    // tile kt+1 has landed (tile kt+2 and the first part of kt+3 may be in flight),
+    // and this wave's LDS reads are done
+    wait_vmcnt<kDmaPerTile + kDmaStep0, true>();
     __syncthreads();
     lds_cptr next = lds + ((U + 1) % NST) * STAGE;
 #pragma unroll
@@ -280,6 +289,7 @@ __device__ __forceinline__ void pipe_iter(f32x16 (&acc)[4][4], TileRegs& cur, Ti
         const int r0 = (q * 3) / 2, r1 = ((q + 1) * 3) / 2;
 #pragma unroll
         for (int r = r0; r < r1; ++r) read_one(nxt, R, next, r);
+        if (q % 3 == 2) dma_one(P, kt + NST - 1, valid, DST, kDmaStep0 + q / 3);  // DMA instructions 4..8
         mfma_one<OP + 1>(acc, cur.a1, cur.b1, cur.sa, cur.sb, q);
         order_point();
     }
@@ -311,39 +321,36 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
     const int tn = local / gsize;
     const int64_t m0 = (int64_t)tm * PBM, n0 = (int64_t)tn * PBN;
 
-    const int ldq = K >> 1;
-    const int nkt = (K + PBK - 1) / PBK;
-    const int kt2 = (K + 255) >> 8;  // 256-wide scale tiles per 32-row group
-    const int64_t a_groups = (M + 31) >> 5, b_groups = (N + 31) >> 5;
+    const int nkt = (K + PBK - 1) / PBK;   // 128-wide K tiles (= code tiles per 16-row group)
+    const int kt2 = (K + 255) >> 8;         // 256-wide scale tiles per 128-row group
+    const int64_t a_t16 = (M + 15) >> 4, b_t16 = (N + 15) >> 4;
+    const int64_t a_t128 = (M + 127) >> 7, b_t128 = (N + 127) >> 7;
 
     DmaPlan P;
     P.wave = wave;
-    P.ra = uniform(make_rsrc_words(aq + m0 * ldq, (M - m0) * (int64_t)ldq));
-    P.rb = uniform(make_rsrc_words(bq + n0 * ldq, (N - n0) * (int64_t)ldq));
+    P.ra = uniform(make_rsrc_words(aq + (m0 >> 4) * nkt * 1024, (a_t16 - (m0 >> 4)) * nkt * 1024));
+    P.rb = uniform(make_rsrc_words(bq + (n0 >> 4) * nkt * 1024, (b_t16 - (n0 >> 4)) * nkt * 1024));
     {
-        // waves 0, 1 copy the A scale tiles, waves 2, 3 the B scale tiles
-        const i32x4 rsa = make_rsrc_words(as + (m0 >> 5) * kt2 * 256, (a_groups - (m0 >> 5)) * kt2 * 256);
-        const i32x4 rsb = make_rsrc_words(bs + (n0 >> 5) * kt2 * 256, (b_groups - (n0 >> 5)) * kt2 * 256);
+        // waves 0, 1 copy the A scale tiles (rows 0-127, 128-255 of the tile), waves 2, 3 the B ones
+        const i32x4 rsa = make_rsrc_words(as + (m0 >> 7) * kt2 * 1024, (a_t128 - (m0 >> 7)) * kt2 * 1024);
+        const i32x4 rsb = make_rsrc_words(bs + (n0 >> 7) * kt2 * 1024, (b_t128 - (n0 >> 7)) * kt2 * 1024);
         P.rs = pick(wave >= 2, rsb, rsa);
         P.scale_region = (wave >= 2 ? ST_SB : ST_SA) + (wave & 1) * 1024;
     }
     {
-        // code DMA: instruction i of wave w fills tile rows (4w + i)*16 + lane/4, physical chunk lane%4,
-        // i.e. logical chunk (lane%4) ^ ((row >> 2) & 3) = (lane & 3) ^ ((lane >> 4) & 3)
-        const int row = wave * 64 + (lane >> 2);
-        const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
-        P.va = row * ldq + chunk * 16;
+        // code DMA: instruction q of wave w moves 16-row tile 4w + q; lane l takes row l/4 of it,
+        // physical chunk l%4, i.e. logical chunk (l%4) ^ swz64(l/4)
+        const int chunk = (lane & 3) ^ swz64(lane >> 2);
+        P.tstep = nkt * 1024;
+        P.va = wave * 4 * P.tstep + (lane >> 2) * 64 + chunk * 16;
         P.vb = P.va;
-        P.row16 = 16 * ldq;
-        // scale DMA: 4 scale tiles (32-row groups) of 256 B per instruction
-        const int grp = (wave & 1) * 4 + (lane >> 4);
-        P.vs = grp * kt2 * 256 + (lane & 15) * 16;
+        P.vs = (wave & 1) * kt2 * 1024 + lane * 16;
         P.lds0 = (unsigned)(uintptr_t)lds;
     }
     ReadPlan R;
     {
         const int frow = lane & 31;
-        const int sw = (frow >> 2) & 3;
+        const int sw = swz64(frow);
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
             const int c = 2 * st + (lane >> 5);
@@ -421,6 +428,7 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
         }
     }
 }
+
 
 }  // namespace mx
 

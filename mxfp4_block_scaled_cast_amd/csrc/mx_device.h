@@ -13,17 +13,28 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBlock = 32;           // elements per scale block (along the contraction dim)
-constexpr int kScaleTileRows = 32;   // rows per 256-byte scale tile
-constexpr int kScaleTileBlocks = 8;  // blocks per scale tile row (K = 256)
+constexpr int kBlock = 32;  // elements per scale block (along the contraction dim)
 
-// Byte offset of the scale of (row r, block b) in an MX operand whose
-// contraction length spans k_tiles tiles of 256.  Layout: 256-byte tiles of
-// 32 rows x 8 blocks, tile-row-major; inside a tile, row r%32 owns 8 bytes
-// and block b%8 sits at byte (b%2)*4 + (b%8)/2, so the dword a 32x32x64 MFMA
-// lane reads (half h = b%2) holds blocks h, h+2, h+4, h+6 of the tile.
-__device__ __forceinline__ int64_t scale_offset(int64_t r, int64_t b, int64_t k_tiles) {
-    return ((r >> 5) * k_tiles + (b >> 3)) * 256 + (r & 31) * 8 + (b & 1) * 4 + ((b & 7) >> 1);
+// MX operand layout (rows R, contraction length K; see include/mxfp4.h).
+//
+// Codes: 1 KB tiles of 16 rows x 128 elements (64 bytes per row), stored
+// tile-row-major: tile (r/16, k/128) at ((r/16) * KT + k/128) * 1024 with
+// KT = ceil(K/128); inside a tile, row r%16 owns 64 bytes, element k%128 sits
+// in byte (k%128)/2, even elements in the low nibble.  One tile is exactly
+// what one 16-byte-per-lane wave load moves, so a GEMM load touches one
+// contiguous kilobyte (one page) instead of 16 rows of a row-major matrix.
+__device__ __forceinline__ int64_t code_offset(int64_t r, int64_t k, int64_t kt128) {
+    return ((r >> 4) * kt128 + (k >> 7)) * 1024 + (r & 15) * 64 + ((k & 127) >> 1);
+}
+
+// Scales: 1 KB tiles of 128 rows x 256 elements (8 blocks of 32), tile
+// (r/128, b/8) at ((r/128) * KT2 + b/8) * 1024 with KT2 = ceil(K/256); inside
+// a tile, 32-row group (r/32)%4 owns 256 bytes, row r%32 owns 8 of them, and
+// block b%8 sits at byte (b%2)*4 + (b%8)/2 -- so the dword a 32x32x64 MFMA
+// lane reads (row r, half h = b%2) holds blocks h, h+2, h+4, h+6, the scales
+// of four consecutive 64-wide K steps.
+__device__ __forceinline__ int64_t scale_offset(int64_t r, int64_t b, int64_t kt256) {
+    return ((r >> 7) * kt256 + (b >> 3)) * 1024 + ((r >> 5) & 3) * 256 + (r & 31) * 8 + (b & 1) * 4 + ((b & 7) >> 1);
 }
 
 // E8M0 scale byte of a block from the bf16 magnitude bits of its amax

@@ -1,44 +1,86 @@
-"""Index maps between the device scale layout and a plain [rows, K/32] array.
+"""Index maps between the tiled MX operand layout and plain row-major arrays.
 
-The device layout (see include/mxfp4.h) stores the E8M0 scale of
-(row r, block b) of an MX operand at
-    ((r // 32) * kt + b // 8) * 256 + (r % 32) * 8 + (b % 2) * 4 + (b % 8) // 2
-with kt = ceil(K / 256).  The packed codes are already row-major [rows, K/2].
+The layout (include/mxfp4.h) for an operand of `rows` rows and contraction
+length `k`:
+
+* codes: 1 KB tiles of 16 rows x 128 elements; byte j of row r (elements 2j,
+  2j+1) sits at ((r//16) * KT + j//64) * 1024 + (r%16) * 64 + j%64 with
+  KT = ceil(k/128);
+* scales: 1 KB tiles of 128 rows x 256 elements; the scale of (r, block b)
+  sits at ((r//128) * KT2 + b//8) * 1024 + ((r//32)%4) * 256 + (r%32) * 8
+  + (b%2) * 4 + (b%8)//2 with KT2 = ceil(k/256).
 """
 import numpy as np
 
 
-def scale_offsets(rows, k):
-    """int64 [rows, k/32] array of byte offsets of each scale in the device layout."""
+def _check(k):
     if k % 32:
         raise ValueError("k must be a multiple of 32")
-    kt = -(-k // 256)
-    r = np.arange(rows, dtype=np.int64)[:, None]
-    b = np.arange(k // 32, dtype=np.int64)[None, :]
-    return ((r // 32) * kt + b // 8) * 256 + (r % 32) * 8 + (b % 2) * 4 + (b % 8) // 2
+
+
+def code_bytes(rows, k):
+    return -(-rows // 16) * (-(-k // 128)) * 1024
 
 
 def scale_bytes(rows, k):
-    return -(-rows // 32) * (-(-k // 256)) * 256
+    return -(-rows // 128) * (-(-k // 256)) * 1024
+
+
+def code_offsets(rows, k):
+    """int64 [rows, k/2]: device byte offset of each packed code byte."""
+    _check(k)
+    kt = -(-k // 128)
+    r = np.arange(rows, dtype=np.int64)[:, None]
+    j = np.arange(k // 2, dtype=np.int64)[None, :]
+    return ((r // 16) * kt + j // 64) * 1024 + (r % 16) * 64 + j % 64
+
+
+def scale_offsets(rows, k):
+    """int64 [rows, k/32]: device byte offset of each scale."""
+    _check(k)
+    kt2 = -(-k // 256)
+    r = np.arange(rows, dtype=np.int64)[:, None]
+    b = np.arange(k // 32, dtype=np.int64)[None, :]
+    return ((r // 128) * kt2 + b // 8) * 1024 + ((r // 32) % 4) * 256 + (r % 32) * 8 + (b % 2) * 4 + (b % 8) // 2
+
+
+def codes_to_rowmajor(q_dev, rows, k):
+    """Device code bytes -> uint8 [rows, k/2] (element 2j in the low nibble of byte j)."""
+    q_dev = np.asarray(q_dev, np.uint8).reshape(-1)
+    if q_dev.size < code_bytes(rows, k):
+        raise ValueError("code buffer too small")
+    return q_dev[code_offsets(rows, k)]
 
 
 def scales_to_rowmajor(s_dev, rows, k):
-    """Device-layout scale bytes -> uint8 [rows, k/32]."""
+    """Device scale bytes -> uint8 [rows, k/32]."""
     s_dev = np.asarray(s_dev, np.uint8).reshape(-1)
     if s_dev.size < scale_bytes(rows, k):
         raise ValueError("scale buffer too small")
     return s_dev[scale_offsets(rows, k)]
 
 
+def codes_from_rowmajor(q, rows, k):
+    out = np.zeros(code_bytes(rows, k), np.uint8)
+    out[code_offsets(rows, k)] = np.asarray(q, np.uint8)
+    return out
+
+
 def scales_from_rowmajor(s, rows, k):
-    """uint8 [rows, k/32] -> device-layout bytes (padding positions 0)."""
     out = np.zeros(scale_bytes(rows, k), np.uint8)
     out[scale_offsets(rows, k)] = np.asarray(s, np.uint8)
     return out
 
 
-def padding_mask(rows, k):
-    """Boolean mask over the device scale buffer: True where no (row, block) maps."""
+def code_padding_mask(rows, k):
+    """True at device code bytes that no (row, element) maps to."""
+    m = np.ones(code_bytes(rows, k), bool)
+    m[code_offsets(rows, k)] = False
+    return m
+
+
+def scale_padding_mask(rows, k):
+    """True at device scale bytes that no (row, block) maps to."""
     m = np.ones(scale_bytes(rows, k), bool)
     m[scale_offsets(rows, k)] = False
     return m

@@ -26,15 +26,16 @@ def bf16_to_f64(t):
 
 def operand_rowmajor(op):
     """(q [rows, k/2], s [rows, k/32]) of an MX operand, as the oracle lays them out."""
-    q = op.q.cpu().numpy()
+    q = layout.codes_to_rowmajor(op.q.cpu().numpy(), op.rows, op.k)
     s = layout.scales_to_rowmajor(op.s.cpu().numpy(), op.rows, op.k)
     return q, s
 
 
 def operand_padding(op):
-    """Scale bytes at padding positions of the device layout."""
+    """Code and scale bytes at padding positions of the device layout (all must be 0)."""
+    q = op.q.cpu().numpy()
     s = op.s.cpu().numpy()
-    return s[layout.padding_mask(op.rows, op.k)]
+    return np.concatenate([q[layout.code_padding_mask(op.rows, op.k)], s[layout.scale_padding_mask(op.rows, op.k)]])
 
 
 def gemm_bound(ref, absref):

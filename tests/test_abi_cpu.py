@@ -56,9 +56,10 @@ def test_status_strings():
 @pytest.mark.parametrize("rows,k", [(1, 32), (17, 32), (32, 256), (33, 288), (8192, 4096), (128256, 14336)])
 def test_operand_layout(rows, k):
     L = N.operand_layout(rows, k)
-    assert L.q_bytes == rows * k // 2
-    assert L.row_tiles == -(-rows // 32) and L.k_tiles == -(-k // 256)
-    assert L.s_bytes == L.row_tiles * L.k_tiles * 256 == layout.scale_bytes(rows, k)
+    assert L.code_row_tiles == -(-rows // 16) and L.code_k_tiles == -(-k // 128)
+    assert L.scale_row_tiles == -(-rows // 128) and L.scale_k_tiles == -(-k // 256)
+    assert L.q_bytes == L.code_row_tiles * L.code_k_tiles * 1024 == layout.code_bytes(rows, k)
+    assert L.s_bytes == L.scale_row_tiles * L.scale_k_tiles * 1024 == layout.scale_bytes(rows, k)
 
 
 def test_operand_layout_rejects():
@@ -117,7 +118,7 @@ def test_step_argument_validation():
 def test_workspace_size_formula():
     # row copies of A and W, plus (training) column copies of A and W and both copies of dOut
     def op(rows, k):
-        return -(-rows * k // 2 // 256) * 256 + layout.scale_bytes(rows, k)
+        return layout.code_bytes(rows, k) + layout.scale_bytes(rows, k)
     M, Nn, K = 17, 96, 64
     Mp = 32
     inf = op(M, K) + op(Nn, K)
@@ -139,20 +140,33 @@ def test_no_device_is_an_error_not_a_fallback():
 
 
 def test_layout_offsets_are_a_bijection_into_the_buffer():
-    for rows, k in ((1, 32), (17, 96), (64, 256), (100, 800), (33, 14336 // 16)):
-        if k % 32:
-            continue
-        off = layout.scale_offsets(rows, k).ravel()
-        assert off.min() >= 0 and off.max() < layout.scale_bytes(rows, k)
-        assert np.unique(off).size == off.size
-        s = np.random.default_rng(0).integers(0, 255, (rows, k // 32)).astype(np.uint8)
+    rng = np.random.default_rng(0)
+    for rows, k in ((1, 32), (17, 96), (64, 256), (100, 800), (33, 896), (257, 4096)):
+        for offs, size in ((layout.code_offsets(rows, k), layout.code_bytes(rows, k)),
+                           (layout.scale_offsets(rows, k), layout.scale_bytes(rows, k))):
+            off = offs.ravel()
+            assert off.min() >= 0 and off.max() < size
+            assert np.unique(off).size == off.size
+        s = rng.integers(0, 255, (rows, k // 32)).astype(np.uint8)
         assert np.array_equal(layout.scales_to_rowmajor(layout.scales_from_rowmajor(s, rows, k), rows, k), s)
+        q = rng.integers(0, 255, (rows, k // 2)).astype(np.uint8)
+        assert np.array_equal(layout.codes_to_rowmajor(layout.codes_from_rowmajor(q, rows, k), rows, k), q)
+
+
+def test_code_tile_is_one_contiguous_kilobyte():
+    # a 16-row x 128-element code tile occupies exactly one aligned kilobyte
+    off = layout.code_offsets(48, 512)
+    for r0 in (0, 16, 32):
+        for j0 in (0, 64, 128, 192):
+            blk = off[r0:r0 + 16, j0:j0 + 64].ravel()
+            assert blk.min() % 1024 == 0 and np.array_equal(np.sort(blk), blk.min() + np.arange(1024))
 
 
 def test_layout_dword_holds_four_consecutive_k_steps():
-    # the dword a 32x32x64 MFMA lane reads (row r, half h) holds blocks h, h+2, h+4, h+6 of a 256-wide K tile
-    off = layout.scale_offsets(32, 256)
-    for r in range(32):
+    # the dword a 32x32x64 MFMA lane reads (row r, half h) holds blocks h, h+2, h+4, h+6 of a 256-wide K tile,
+    # and the four 32-row groups of a 128-row tile are consecutive 256-byte pieces of one kilobyte
+    off = layout.scale_offsets(128, 256)
+    for r in range(128):
         for h in range(2):
             dword = [off[r, h + 2 * t] for t in range(4)]
-            assert dword == [r * 8 + h * 4 + t for t in range(4)]
+            assert dword == [(r // 32) * 256 + (r % 32) * 8 + h * 4 + t for t in range(4)]

@@ -16,7 +16,7 @@ def check_row(x_bits, op, what):
     q, s = operand_rowmajor(op)
     assert np.array_equal(s, s_ref), "%s: row scales differ at %s" % (what, np.argwhere(s != s_ref)[:5].tolist())
     assert np.array_equal(q, q_ref), "%s: row codes differ at %s" % (what, np.argwhere(q != q_ref)[:5].tolist())
-    assert np.all(operand_padding(op) == 0), "%s: row scale padding not zero" % what
+    assert np.all(operand_padding(op) == 0), "%s: row padding not zero" % what
 
 
 def check_col(x_bits, op, what):
@@ -24,7 +24,7 @@ def check_col(x_bits, op, what):
     q, s = operand_rowmajor(op)
     assert np.array_equal(s, s_ref), "%s: col scales differ at %s" % (what, np.argwhere(s != s_ref)[:5].tolist())
     assert np.array_equal(q, q_ref), "%s: col codes differ at %s" % (what, np.argwhere(q != q_ref)[:5].tolist())
-    assert np.all(operand_padding(op) == 0), "%s: col scale padding not zero" % what
+    assert np.all(operand_padding(op) == 0), "%s: col padding not zero" % what
 
 
 def run_both(x_bits, what):
