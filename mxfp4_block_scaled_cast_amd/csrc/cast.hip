@@ -29,7 +29,7 @@
 namespace mx {
 
 template <int TILE_R, bool DUAL>
-__global__ __launch_bounds__(256) void cast_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C, int64_t ldx,
+__global__ __launch_bounds__(256, 4) void cast_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C, int64_t ldx,
                                                    uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
                                                    uint8_t* __restrict__ q_col, uint8_t* __restrict__ s_col,
                                                    int n_rtiles, int n_ctiles) {
