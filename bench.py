@@ -49,11 +49,46 @@ def parse():
                    help="target wall time of the CPU-oracle sample (0 skips the CPU baseline)")
     p.add_argument("--no-kernel-events", action="store_true",
                    help="time only the whole step (no per-kernel events)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain device copy of COPY_BYTES (for scaling HBM counters), then exit")
     return p.parse_args()
+
+
+COPY_BYTES = 1 << 30  # plain copy used to calibrate FETCH_SIZE / WRITE_SIZE
+
+
+def copy_calibration():
+    import torch
+    a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "calls": 3}), flush=True)
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_pipe_llama8b_mlp_traffic.json")
+
+
+def measured_traffic():
+    """Per-launch HBM bytes of the GEMM kernel from the committed counter summary, if the kernel is unchanged."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        from mxfp4_block_scaled_cast_amd import rocprof_summary as rs
+        if t.get("source_hash") != rs.source_hash(rs.GEMM_SOURCES):
+            return None
+        return round(t["traffic_bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        return None
 
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         sys.stderr.write("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -203,7 +238,7 @@ def main():
                               "bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": FP4_PEAK_TFLOPS,
                               "unit": "TFLOP/s", "frac": round(gemm_tflops / FP4_PEAK_TFLOPS, 4),
                               "avg_launch_ms": round(avg_gemm_ms, 4),
-                              "flop_per_launch": gemm_work / gemm_launches, "traffic": None}
+                              "flop_per_launch": gemm_work / gemm_launches, "traffic": measured_traffic()}
 
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(host_inputs, args.cpu_seconds)
@@ -227,12 +262,15 @@ def cpu_baseline(inp, target_s):
         oracle.gemm(qa, sa, qw, sw, nthreads=cores)
         return time.perf_counter() - t
 
-    rows = 8
+    # calibrate: a fixed part (W's cast, B's unpacking) plus a part linear in the rows
+    r1, r2 = 8, 8 * cores
+    t1, t2 = run(r1), run(r2)
+    per_row = max((t2 - t1) / (r2 - r1), 1e-6)
+    fixed = max(t1 - per_row * r1, 0.0)
+    rows = int(max(target_s - fixed, per_row * r2) / per_row)
+    rows = max(r2, min(a.shape[0], rows // 8 * 8))
+
     dt = run(rows)
-    if dt < target_s:
-        rows = int(min(a.shape[0], max(rows, rows * target_s / max(dt, 1e-3))))
-        rows = max(8, rows // 8 * 8)
-        dt = run(rows)
     flops = 2.0 * rows * Nn * K
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": "%s forward, first %d of %d rows of A (%d x %d x %d): oracle cast of those rows and of W, "

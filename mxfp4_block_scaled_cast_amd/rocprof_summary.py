@@ -1,0 +1,112 @@
+"""Summaries of rocprofv3 output for the committed profiles.
+
+Two uses:
+
+* ``kernel-stats``: turn a ``--kernel-trace --stats`` kernel_stats CSV into a
+  short markdown table (calls, total / average / min / max duration).
+* ``traffic``: from two ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs over
+  the benchmark (and the same two counters over a plain copy of known size),
+  write the per-launch HBM traffic of one kernel as JSON.  The counters are
+  in KiB per dispatch; each is scaled by (bytes the copy really moves) /
+  (bytes the counter reports for the copy).  The JSON carries a hash of the
+  kernel's sources so ``bench.py`` reports the figure only while the kernel
+  is unchanged.
+
+Usage:
+  python -m mxfp4_block_scaled_cast_amd.rocprof_summary kernel-stats STATS_CSV OUT_MD --command "..."
+  python -m mxfp4_block_scaled_cast_amd.rocprof_summary traffic --kernel REGEX --fetch CSV --write CSV \
+      --copy-fetch CSV --copy-write CSV --copy-bytes N --out OUT_JSON --command "..."
+"""
+import argparse
+import csv
+import hashlib
+import json
+import os
+import re
+import statistics
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+GEMM_SOURCES = [os.path.join(PKG, "csrc", "gemm.hip"), os.path.join(PKG, "csrc", "mx_device.h")]
+CAST_SOURCES = [os.path.join(PKG, "csrc", "cast.hip"), os.path.join(PKG, "csrc", "mx_device.h")]
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_stats(csv_path, out_md, command):
+    rows = list(csv.DictReader(open(csv_path)))
+    lines = ["# rocprofv3 kernel statistics", "", "Command:", "", "```", command, "```", "",
+             "| kernel | calls | total ms | average us | min us | max us | % |", "|---|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"]
+        name = re.sub(r"\(.*", "", name)
+        lines.append("| %s | %s | %.3f | %.1f | %.1f | %.1f | %.1f |" % (
+            name, r["Calls"], float(r["TotalDurationNs"]) / 1e6, float(r["AverageNs"]) / 1e3,
+            float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def _per_dispatch(csv_path, counter, kernel_regex):
+    vals = []
+    for r in csv.DictReader(open(csv_path)):
+        if r["Counter_Name"] == counter and re.search(kernel_regex, r["Kernel_Name"]):
+            vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit("no %s values for kernels matching %r in %s" % (counter, kernel_regex, csv_path))
+    return vals
+
+
+def traffic(a):
+    fetch = _per_dispatch(a.fetch, "FETCH_SIZE", a.kernel)
+    write = _per_dispatch(a.write, "WRITE_SIZE", a.kernel)
+    cf = statistics.mean(_per_dispatch(a.copy_fetch, "FETCH_SIZE", a.copy_kernel))
+    cw = statistics.mean(_per_dispatch(a.copy_write, "WRITE_SIZE", a.copy_kernel))
+    f_scale = a.copy_bytes / (cf * 1024.0)
+    w_scale = a.copy_bytes / (cw * 1024.0)
+    fetch_b = statistics.mean(fetch) * 1024.0 * f_scale
+    write_b = statistics.mean(write) * 1024.0 * w_scale
+    out = {"kernel_regex": a.kernel, "dispatches": len(fetch),
+           "fetch_kib_per_dispatch": statistics.mean(fetch), "write_kib_per_dispatch": statistics.mean(write),
+           "copy_bytes": a.copy_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "traffic_bytes_per_launch": fetch_b + write_b,
+           "source_hash": source_hash(GEMM_SOURCES if a.sources == "gemm" else CAST_SOURCES),
+           "command": a.command}
+    with open(a.out, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def main():
+    p = argparse.ArgumentParser()
+    sub = p.add_subparsers(dest="cmd", required=True)
+    k = sub.add_parser("kernel-stats")
+    k.add_argument("csv")
+    k.add_argument("out")
+    k.add_argument("--command", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--copy-kernel", default="elementwise|copy|Copy")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--copy-fetch", required=True)
+    t.add_argument("--copy-write", required=True)
+    t.add_argument("--copy-bytes", type=float, required=True)
+    t.add_argument("--sources", choices=["gemm", "cast"], default="gemm")
+    t.add_argument("--out", required=True)
+    t.add_argument("--command", required=True)
+    a = p.parse_args()
+    if a.cmd == "kernel-stats":
+        kernel_stats(a.csv, a.out, a.command)
+    else:
+        traffic(a)
+
+
+if __name__ == "__main__":
+    main()

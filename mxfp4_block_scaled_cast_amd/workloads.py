@@ -172,3 +172,30 @@ def ragged_inputs(combo_index, with_grad=True):
     w = ragged_values((N, K), seed_of(cid, W, combo_index))
     dout = ragged_values((M, N), seed_of(cid, DOUT, combo_index)) if with_grad else None
     return a, w, dout
+
+
+def ragged_values_torch(shape, seed, device, lo=-1e3, hi=1e3, zero_frac=0.05, subnormal_frac=0.05):
+    """The ragged recipe drawn on a device with torch's seeded generator (for sizes the host draws too slowly).
+
+    Same distribution as ``ragged_values`` (U(lo, hi), 5% all-zero and 5%
+    subnormal aligned 32x32 tiles), different random stream.  Returns an
+    int16 tensor of bf16 bit patterns on `device`.
+    """
+    import torch
+
+    R, C = shape
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    vals = torch.empty((R, C), dtype=torch.float32, device=device).uniform_(lo, hi, generator=g)
+    bits = vals.to(torch.bfloat16).view(torch.int16)
+    del vals
+    tr, tc = -(-R // 32), -(-C // 32)
+    kind = torch.rand((tr, tc), generator=g, device=device)
+    tile_kind = kind.repeat_interleave(32, 0)[:R].repeat_interleave(32, 1)[:, :C]
+    zero = tile_kind < zero_frac
+    sub = (tile_kind >= zero_frac) & (tile_kind < zero_frac + subnormal_frac)
+    mant = torch.randint(1, 128, (R, C), generator=g, device=device, dtype=torch.int16)
+    sign = torch.randint(0, 2, (R, C), generator=g, device=device, dtype=torch.int16) * -32768
+    bits = torch.where(zero, torch.zeros_like(bits), bits)
+    bits = torch.where(sub, (mant | sign).to(torch.int16), bits)
+    return bits

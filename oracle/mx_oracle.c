@@ -224,6 +224,7 @@ typedef struct {
     int64_t M, N, K;
     const int64_t *mi, *ni;   /* pair mode when non-null */
     double *ref, *absref;
+    int8_t* ub;               /* B unpacked to 2*e2m1 values, [N, K] (full mode) */
 } gemm_ctx;
 
 /* One output: sum over blocks of 2^(Xa+Xb-2) * (exact integer dot of 2*a and 2*b). */
@@ -253,19 +254,20 @@ static void unpack_row(const uint8_t* q, int64_t K, int8_t* u) {
     for (int64_t k = 0; k < K; ++k) u[k] = (int8_t)twice_e2m1((q[k / 2] >> (4 * (k & 1))) & 0xF);
 }
 
+static void unpack_b_range(void* p, int64_t lo, int64_t hi) {
+    gemm_ctx* g = (gemm_ctx*)p;
+    for (int64_t n = lo; n < hi; ++n) unpack_row(g->qb + n * (g->K / 2), g->K, g->ub + n * g->K);
+}
+
 static void gemm_rows_range(void* p, int64_t lo, int64_t hi) {
     gemm_ctx* g = (gemm_ctx*)p;
     int8_t* ua = (int8_t*)malloc((size_t)(g->K > 0 ? g->K : 1));
-    int8_t* ub = (int8_t*)malloc((size_t)(g->K > 0 ? g->K : 1) * (size_t)(g->N > 0 ? g->N : 1));
-    /* B is unpacked once per worker; each A row once. */
-    for (int64_t n = 0; n < g->N; ++n) unpack_row(g->qb + n * (g->K / 2), g->K, ub + n * g->K);
     for (int64_t m = lo; m < hi; ++m) {
         unpack_row(g->qa + m * (g->K / 2), g->K, ua);
         for (int64_t n = 0; n < g->N; ++n)
-            gemm_one(g, ua, ub + n * g->K, m, n, &g->ref[m * g->N + n], &g->absref[m * g->N + n]);
+            gemm_one(g, ua, g->ub + n * g->K, m, n, &g->ref[m * g->N + n], &g->absref[m * g->N + n]);
     }
     free(ua);
-    free(ub);
 }
 
 /* ref[m,n], absref[m,n] (= sum_k |a_k b_k| of the dequantized operands) for
@@ -273,8 +275,13 @@ static void gemm_rows_range(void* p, int64_t lo, int64_t hi) {
 int mxo_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb, int64_t M, int64_t N,
              int64_t K, double* ref, double* absref, int nthreads) {
     if (M < 0 || N < 0 || K < 0 || K % MXO_BLOCK != 0) return -1;
-    gemm_ctx g = {qa, sa, qb, sb, M, N, K, NULL, NULL, ref, absref};
+    gemm_ctx g = {qa, sa, qb, sb, M, N, K, NULL, NULL, ref, absref, NULL};
+    /* B is unpacked once, shared by all workers; each worker unpacks its A rows */
+    g.ub = (int8_t*)malloc((size_t)(N > 0 ? N : 1) * (size_t)(K > 0 ? K : 1));
+    if (!g.ub) return -1;
+    parallel_for(N, nthreads, unpack_b_range, &g);
     parallel_for(M, nthreads, gemm_rows_range, &g);
+    free(g.ub);
     return 0;
 }
 
@@ -299,7 +306,7 @@ int mxo_gemm_pairs(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, cons
     if (M < 0 || N < 0 || K < 0 || K % MXO_BLOCK != 0 || npairs < 0) return -1;
     for (int64_t i = 0; i < npairs; ++i)
         if (mi[i] < 0 || mi[i] >= M || ni[i] < 0 || ni[i] >= N) return -1;
-    gemm_ctx g = {qa, sa, qb, sb, M, N, K, mi, ni, ref, absref};
+    gemm_ctx g = {qa, sa, qb, sb, M, N, K, mi, ni, ref, absref, NULL};
     parallel_for(npairs, nthreads, gemm_pairs_range, &g);
     return 0;
 }
