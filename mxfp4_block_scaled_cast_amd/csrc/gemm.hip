@@ -15,7 +15,31 @@
 // the epilogue rounds to bf16 (nearest even).
 #include <stdlib.h>
 
+#include <algorithm>
+
 #include "mx_device.h"
+
+// MXFP4_GEMM_PERSIST=0 disables the persistent kernel (comparison aid).
+static int getenv_persist() {
+    static const int v = [] {
+        const char* e = getenv("MXFP4_GEMM_PERSIST");
+        return e && e[0] == '0' ? 0 : 1;
+    }();
+    return v;
+}
+
+// Compute units of the current device (cached per device).
+static int num_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
 
 // MXFP4_GEMM_DIRECT=1 forces the untiled kernel (testing aid).
 static int getenv_direct() {
@@ -161,6 +185,19 @@ __device__ __forceinline__ void dma16(const i32x4& rs, int voff, unsigned m0v) {
                  : "memory", "m0");
 }
 
+// Same, with the LDS address given as a wave-uniform base plus a compile-time
+// offset (keeps one SGPR live instead of one per destination), and the
+// K-tile part of the source offset in the scalar offset `soff`.  `soff` must
+// stay below the size of one 16-row tile, so that the in-bounds test on the
+// lane offset alone decides whether the whole address is in bounds.
+template <int IMM>
+__device__ __forceinline__ void dma16_at(const i32x4& rs, int voff, int soff, unsigned base) {
+    // s_add_u32 writes SCC: declared, so no compare result is kept in SCC across this
+    asm volatile("s_add_u32 m0, %3, %4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rs), "s"(soff),
+                 "s"(base), "i"(IMM)
+                 : "memory", "m0", "scc");
+}
+
 // s_waitcnt vmcnt(N) (expcnt/lgkmcnt left alone) through the builtin, so the
 // compiler's own wait tracking sees it.
 // With LDS0, also lgkmcnt(0): every LDS read this wave issued has returned.
@@ -188,34 +225,82 @@ __device__ __forceinline__ i32x4 pick(bool c, const i32x4& a, const i32x4& b) {
     return r;
 }
 
+// Descriptors of one output tile's operands: A codes, B codes, and this
+// wave's scale source (A scales for waves 0, 1, B scales for waves 2, 3).
+struct TileSrc {
+    i32x4 ra, rb, rs;
+};
+
 struct DmaPlan {
-    i32x4 ra, rb, rs;    // code descriptors (A, B) and this wave's scale descriptor (A or B scales)
     int va, vb;          // lane byte offsets of instruction 0 of the A / B code DMA at K tile 0
     int tstep;           // bytes between consecutive 16-row code tiles (KT * 1 KB)
     int vs;              // lane byte offset of this wave's scale DMA at K-tile pair 0
     int scale_region;    // LDS offset of this wave's scale copy inside a stage
     unsigned lds0;       // LDS address of stage 0
+    unsigned code_base;  // lds0 + 4 KB * wave: this wave's code rows in stage 0 (uniform)
+    unsigned scale_base; // lds0 + scale_region (uniform)
     int wave;
 };
 
-// Instruction q (0..8) of the DMA of tile kt into stage `st`: 0-3 A codes, 4-7 B codes, 8 scales.
-__device__ __forceinline__ void dma_one(const DmaPlan& P, int kt, bool valid, int st, int q) {
+// Instruction Q (0..8) of the DMA of K tile kt of source S into stage ST:
+// 0-3 A codes, 4-7 B codes, 8 scales.  P.code_base / P.scale_base are this
+// wave's LDS bases (wave-uniform SGPRs); the rest of the address is constant.
+template <int ST, int Q>
+__device__ __forceinline__ void dma_one(const DmaPlan& P, const TileSrc& S, int kt, bool valid) {
     // a tile past K goes through a descriptor with num_records 0: every lane reads zero
-    const unsigned sbase = P.lds0 + (unsigned)(st * STAGE);
-    if (q < 4) {
-        i32x4 r = P.ra;
+    if constexpr (Q < 4) {
+        i32x4 r = S.ra;
         r.z = __builtin_amdgcn_readfirstlane(valid ? r.z : 0);
-        dma16(r, P.va + q * P.tstep + kt * 1024, __builtin_amdgcn_readfirstlane(sbase + ST_A + (P.wave * 4 + q) * 1024));
-    } else if (q < 8) {
-        i32x4 r = P.rb;
+        dma16_at<ST * STAGE + ST_A + Q * 1024>(r, P.va + Q * P.tstep, kt * 1024, P.code_base);
+    } else if constexpr (Q < 8) {
+        i32x4 r = S.rb;
         r.z = __builtin_amdgcn_readfirstlane(valid ? r.z : 0);
-        dma16(r, P.vb + (q - 4) * P.tstep + kt * 1024,
-              __builtin_amdgcn_readfirstlane(sbase + ST_B + (P.wave * 4 + q - 4) * 1024));
+        dma16_at<ST * STAGE + ST_B + (Q - 4) * 1024>(r, P.vb + (Q - 4) * P.tstep, kt * 1024, P.code_base);
     } else {
-        i32x4 r = P.rs;
+        i32x4 r = S.rs;
         r.z = __builtin_amdgcn_readfirstlane(valid ? r.z : 0);
-        dma16(r, P.vs + (kt >> 1) * 1024, __builtin_amdgcn_readfirstlane(sbase + (unsigned)P.scale_region));
+        dma16_at<ST * STAGE>(r, P.vs, (kt >> 1) * 1024, P.scale_base);
     }
+}
+
+template <int ST>
+__device__ __forceinline__ void dma_tile_all(const DmaPlan& P, const TileSrc& S, int kt, bool valid) {
+    dma_one<ST, 0>(P, S, kt, valid);
+    dma_one<ST, 1>(P, S, kt, valid);
+    dma_one<ST, 2>(P, S, kt, valid);
+    dma_one<ST, 3>(P, S, kt, valid);
+    dma_one<ST, 4>(P, S, kt, valid);
+    dma_one<ST, 5>(P, S, kt, valid);
+    dma_one<ST, 6>(P, S, kt, valid);
+    dma_one<ST, 7>(P, S, kt, valid);
+    dma_one<ST, 8>(P, S, kt, valid);
+}
+
+// Operand descriptors of the output tile at (m0, n0), rebased at the tile and
+// bounded by the operand sizes (tiles past M / N read zero).
+__device__ __forceinline__ TileSrc tile_src(const uint8_t* aq, const uint8_t* as, const uint8_t* bq,
+                                            const uint8_t* bs, int M, int N, int nkt, int kt2, int64_t m0, int64_t n0,
+                                            int wave) {
+    const int64_t a_t16 = (M + 15) >> 4, b_t16 = (N + 15) >> 4;
+    const int64_t a_t128 = (M + 127) >> 7, b_t128 = (N + 127) >> 7;
+    TileSrc S;
+    S.ra = uniform(make_rsrc_words(aq + (m0 >> 4) * nkt * 1024, (a_t16 - (m0 >> 4)) * nkt * 1024));
+    S.rb = uniform(make_rsrc_words(bq + (n0 >> 4) * nkt * 1024, (b_t16 - (n0 >> 4)) * nkt * 1024));
+    const i32x4 rsa = make_rsrc_words(as + (m0 >> 7) * kt2 * 1024, (a_t128 - (m0 >> 7)) * kt2 * 1024);
+    const i32x4 rsb = make_rsrc_words(bs + (n0 >> 7) * kt2 * 1024, (b_t128 - (n0 >> 7)) * kt2 * 1024);
+    S.rs = pick(wave >= 2, rsb, rsa);
+    return S;
+}
+
+// Grouped tile order: `group_m` tile rows at a time, tile rows fastest.
+__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int group_m, int& tm, int& tn) {
+    const int per_group = group_m * tiles_n;
+    const int g = t / per_group;
+    const int first_m = g * group_m;
+    const int gsize = min(tiles_m - first_m, group_m);
+    const int local = t - g * per_group;
+    tm = first_m + local % gsize;
+    tn = local / gsize;
 }
 
 // Registers holding one tile: fragments of its two 64-wide K steps and the scale dwords.
@@ -265,22 +350,37 @@ __device__ __forceinline__ void mfma_one(f32x16 (&acc)[4][4], const u32x4 (&a)[4
                                                                 OPSEL, sb[j], OPSEL, sa[i]);
 }
 
-// Iteration kt = 4t + U of the main loop (see the schedule above).
-template <int U>
+constexpr int kEpiStores = 32;  // 16-byte output stores per wave per tile (persistent kernel)
+
+// Iteration kt = 4t + U of the main loop (see the schedule above).  The DMA
+// it issues is for K tile kt+3 of the current output tile, or with LAST (the
+// final trip of a tile) and U >= 1 for K tile U-1 of the next output tile.
+// With POST (first trip after an epilogue) the waits of the first two
+// iterations also let the epilogue's stores be outstanding.
+template <int U, bool POST = false, bool LAST = false>
 __device__ __forceinline__ void pipe_iter(f32x16 (&acc)[4][4], TileRegs& cur, TileRegs& nxt, const DmaPlan& P,
+                                          const TileSrc& Scur, const TileSrc& Snext, bool next_ok,
                                           const ReadPlan& R, lds_cptr lds, int kt, int nkt) {
     constexpr int OP = (U & 1) * 2;  // tile kt uses bytes 2*(kt%2) and 2*(kt%2)+1 of its scale dwords
     constexpr int DST = (U + NST - 1) % NST;
-    const bool valid = kt + NST - 1 < nkt;
+    constexpr bool TO_NEXT = LAST && U >= 1;
+    constexpr int WAIT = kDmaPerTile + kDmaStep0 + ((POST && U < 2) ? kEpiStores : 0);
+    const TileSrc& S = TO_NEXT ? Snext : Scur;
+    const int dkt = TO_NEXT ? U - 1 : kt + NST - 1;
+    const bool valid = TO_NEXT ? (next_ok && U - 1 < nkt) : (kt + NST - 1 < nkt);
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
         mfma_one<OP>(acc, cur.a0, cur.b0, cur.sa, cur.sb, q);
-        if ((q & 3) == 1) dma_one(P, kt + NST - 1, valid, DST, q >> 2);  // DMA instructions 0..3
+        // DMA instructions 0..3 after MFMAs 1, 5, 9, 13
+        if (q == 1) dma_one<DST, 0>(P, S, dkt, valid);
+        if (q == 5) dma_one<DST, 1>(P, S, dkt, valid);
+        if (q == 9) dma_one<DST, 2>(P, S, dkt, valid);
+        if (q == 13) dma_one<DST, 3>(P, S, dkt, valid);
         order_point();
     }
     // tile kt+1 has landed (tile kt+2 and the first part of kt+3 may be in flight),
     // and this wave's LDS reads are done
-    wait_vmcnt<kDmaPerTile + kDmaStep0, true>();
+    wait_vmcnt<WAIT, true>();
     __syncthreads();
     lds_cptr next = lds + ((U + 1) % NST) * STAGE;
 #pragma unroll
@@ -289,10 +389,26 @@ __device__ __forceinline__ void pipe_iter(f32x16 (&acc)[4][4], TileRegs& cur, Ti
         const int r0 = (q * 3) / 2, r1 = ((q + 1) * 3) / 2;
 #pragma unroll
         for (int r = r0; r < r1; ++r) read_one(nxt, R, next, r);
-        if (q % 3 == 2) dma_one(P, kt + NST - 1, valid, DST, kDmaStep0 + q / 3);  // DMA instructions 4..8
+        // DMA instructions 4..8 before MFMAs 2, 5, 8, 11, 14
+        if (q == 2) dma_one<DST, 4>(P, S, dkt, valid);
+        if (q == 5) dma_one<DST, 5>(P, S, dkt, valid);
+        if (q == 8) dma_one<DST, 6>(P, S, dkt, valid);
+        if (q == 11) dma_one<DST, 7>(P, S, dkt, valid);
+        if (q == 14) dma_one<DST, 8>(P, S, dkt, valid);
         mfma_one<OP + 1>(acc, cur.a1, cur.b1, cur.sa, cur.sb, q);
         order_point();
     }
+}
+
+// Four iterations kt0 .. kt0+3 (kt0 a multiple of 4).
+template <bool POST, bool LAST>
+__device__ __forceinline__ void pipe_trip(f32x16 (&acc)[4][4], TileRegs& r0, TileRegs& r1, const DmaPlan& P,
+                                          const TileSrc& Scur, const TileSrc& Snext, bool next_ok,
+                                          const ReadPlan& R, lds_cptr lds, int kt0, int nkt) {
+    pipe_iter<0, POST, LAST>(acc, r0, r1, P, Scur, Snext, next_ok, R, lds, kt0 + 0, nkt);
+    pipe_iter<1, POST, LAST>(acc, r1, r0, P, Scur, Snext, next_ok, R, lds, kt0 + 1, nkt);
+    pipe_iter<2, POST, LAST>(acc, r0, r1, P, Scur, Snext, next_ok, R, lds, kt0 + 2, nkt);
+    pipe_iter<3, POST, LAST>(acc, r1, r0, P, Scur, Snext, next_ok, R, lds, kt0 + 3, nkt);
 }
 
 template <bool VEC_STORE>
@@ -323,20 +439,11 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
 
     const int nkt = (K + PBK - 1) / PBK;   // 128-wide K tiles (= code tiles per 16-row group)
     const int kt2 = (K + 255) >> 8;         // 256-wide scale tiles per 128-row group
-    const int64_t a_t16 = (M + 15) >> 4, b_t16 = (N + 15) >> 4;
-    const int64_t a_t128 = (M + 127) >> 7, b_t128 = (N + 127) >> 7;
-
     DmaPlan P;
     P.wave = wave;
-    P.ra = uniform(make_rsrc_words(aq + (m0 >> 4) * nkt * 1024, (a_t16 - (m0 >> 4)) * nkt * 1024));
-    P.rb = uniform(make_rsrc_words(bq + (n0 >> 4) * nkt * 1024, (b_t16 - (n0 >> 4)) * nkt * 1024));
-    {
-        // waves 0, 1 copy the A scale tiles (rows 0-127, 128-255 of the tile), waves 2, 3 the B ones
-        const i32x4 rsa = make_rsrc_words(as + (m0 >> 7) * kt2 * 1024, (a_t128 - (m0 >> 7)) * kt2 * 1024);
-        const i32x4 rsb = make_rsrc_words(bs + (n0 >> 7) * kt2 * 1024, (b_t128 - (n0 >> 7)) * kt2 * 1024);
-        P.rs = pick(wave >= 2, rsb, rsa);
-        P.scale_region = (wave >= 2 ? ST_SB : ST_SA) + (wave & 1) * 1024;
-    }
+    // waves 0, 1 copy the A scale tiles (rows 0-127, 128-255 of the tile), waves 2, 3 the B ones
+    P.scale_region = (wave >= 2 ? ST_SB : ST_SA) + (wave & 1) * 1024;
+    const TileSrc S = tile_src(aq, as, bq, bs, M, N, nkt, kt2, m0, n0, wave);
     {
         // code DMA: instruction q of wave w moves 16-row tile 4w + q; lane l takes row l/4 of it,
         // physical chunk l%4, i.e. logical chunk (l%4) ^ swz64(l/4)
@@ -346,6 +453,8 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
         P.vb = P.va;
         P.vs = (wave & 1) * kt2 * 1024 + lane * 16;
         P.lds0 = (unsigned)(uintptr_t)lds;
+        P.code_base = __builtin_amdgcn_readfirstlane(P.lds0 + (unsigned)(wave * 4 * 1024));
+        P.scale_base = __builtin_amdgcn_readfirstlane(P.lds0 + (unsigned)P.scale_region);
     }
     ReadPlan R;
     {
@@ -369,10 +478,9 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
     // prologue: tiles 0..2 in flight, then tile 0 into registers
-#pragma unroll
-    for (int st = 0; st < NST - 1; ++st)
-#pragma unroll
-        for (int q = 0; q < kDmaPerTile; ++q) dma_one(P, st, st < nkt, st, q);
+    dma_tile_all<0>(P, S, 0, 0 < nkt);
+    dma_tile_all<1>(P, S, 1, 1 < nkt);
+    dma_tile_all<2>(P, S, 2, 2 < nkt);
     wait_vmcnt<(NST - 2) * kDmaPerTile, true>();
     __syncthreads();
     TileRegs r0, r1;
@@ -381,13 +489,7 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
     order_point();
 
     const int trips = (nkt + NST - 1) / NST;
-    for (int tr = 0; tr < trips; ++tr) {
-        const int kt = tr * NST;
-        pipe_iter<0>(acc, r0, r1, P, R, lds, kt + 0, nkt);
-        pipe_iter<1>(acc, r1, r0, P, R, lds, kt + 1, nkt);
-        pipe_iter<2>(acc, r0, r1, P, R, lds, kt + 2, nkt);
-        pipe_iter<3>(acc, r1, r0, P, R, lds, kt + 3, nkt);
-    }
+    for (int tr = 0; tr < trips; ++tr) pipe_trip<false, false>(acc, r0, r1, P, S, S, false, R, lds, tr * NST, nkt);
     // drain the DMA of the (empty) tiles past the end before the workgroup can exit
     wait_vmcnt<0>();
 
@@ -430,6 +532,179 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
 }
 
 
+
+// ---------------------------------------------------------------------------
+// Persistent kernel: one workgroup per CU walks its output tiles (logical tile
+// slot, slot + G, ... with G the grid size).  At a tile boundary it first
+// issues the DMA of K tiles 0..2 of the next tile, then the previous tile's
+// epilogue (exactly 32 16-byte buffer stores per wave, bounded by a per-tile
+// descriptor so rows and columns outside the output are dropped), so the DMA
+// latency of the new tile overlaps the epilogue and the stores drain while
+// the new tile's MFMAs run.  The first two waits of every tile allow for the
+// 32 stores; before the first tile 32 empty loads stand in for them.  K is
+// padded to a multiple of 4 K tiles (at least 8); tiles past K are empty.
+// ---------------------------------------------------------------------------
+
+constexpr int ST_DUMMY = NST * STAGE;  // 1 KB landing area of the empty priming loads
+
+// fp32 x4 -> 4 bf16 (nearest even) in two dwords.
+__device__ __forceinline__ void pack4(const f32x16& c, int g, unsigned& lo, unsigned& hi) {
+    lo = (uint32_t)f32_to_bf16_rne(c[g * 4 + 0]) | ((uint32_t)f32_to_bf16_rne(c[g * 4 + 1]) << 16);
+    hi = (uint32_t)f32_to_bf16_rne(c[g * 4 + 2]) | ((uint32_t)f32_to_bf16_rne(c[g * 4 + 3]) << 16);
+}
+
+// Epilogue of one tile: lanes l and l+32 hold columns 0-3 and 4-7 of each
+// 8-column group; a permlane32 swap gives each lane 8 consecutive columns, so
+// a wave writes 32 x 16-byte stores.  Out-of-range chunks go to an offset past
+// the descriptor's end (dropped).  Needs N % 8 == 0 (no chunk straddles N).
+__device__ __forceinline__ void persist_epilogue(const f32x16 (&acc)[4][4], uint16_t* out, int64_t ldo, int M, int N,
+                                                 int64_t m0, int64_t n0, int wm, int wn) {
+    // 32-bit tile-local arithmetic: the launcher guarantees 256 * ldo * 2 < 2^31
+    const int rows_left = (int)min((int64_t)M - m0, (int64_t)PBM);  // >= 1
+    const int cols_left = (int)min((int64_t)N - n0, (int64_t)PBN);
+    const int row_bytes = (int)(ldo * 2);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        out + m0 * ldo + n0, (short)0, rows_left * row_bytes, (int)kRsrcWord3);
+    // the lane id is recomputed here (volatile, so it is neither hoisted nor
+    // merged with an earlier copy): the per-lane offsets below are then formed
+    // once per tile instead of living in registers across the main loop
+    int lane_v;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_v));
+    const int h = lane_v >> 5;
+    const int lrow = wm * 128 + (lane_v & 31);  // tile-local row for i = 0
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = lrow + i * 32;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                unsigned x0, x1, y0, y1;
+                pack4(acc[i][j], 2 * p, x0, x1);      // columns 16p + 4h .. +3
+                pack4(acc[i][j], 2 * p + 1, y0, y1);  // columns 16p + 8 + 4h .. +3
+                const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+                // lower lanes: own x then partner's x; upper lanes: partner's y then own y
+                const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
+                const int c = wn * 128 + j * 32 + p * 16 + h * 8;  // tile-local column
+                const int off = (r < rows_left && c < cols_left) ? r * row_bytes + c * 2 : (int)0x80000000;
+                __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, 0);
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(256, 1) void gemm_persist_kernel(const uint8_t* __restrict__ aq,
+                                                              const uint8_t* __restrict__ as,
+                                                              const uint8_t* __restrict__ bq,
+                                                              const uint8_t* __restrict__ bs, int M, int N, int K,
+                                                              uint16_t* __restrict__ out, int64_t ldo, int tiles_m,
+                                                              int tiles_n, int group_m) {
+    __shared__ __attribute__((aligned(1024))) char lds_raw[NST * STAGE + 1024];
+    lds_cptr lds = (lds_cptr)lds_raw;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+
+    const int total = tiles_m * tiles_n;
+    const int G = gridDim.x;
+    const int slot = xcd_remap(blockIdx.x, G);  // each XCD takes a contiguous range of slots per round
+
+    const int nkt = (K + PBK - 1) / PBK;
+    const int trips = (nkt + NST - 1) / NST;  // >= 2 (the launcher guarantees it)
+    const int kt2 = (K + 255) >> 8;
+
+    DmaPlan P;
+    P.wave = wave;
+    P.scale_region = (wave >= 2 ? ST_SB : ST_SA) + (wave & 1) * 1024;
+    {
+        const int chunk = (lane & 3) ^ swz64(lane >> 2);
+        P.tstep = nkt * 1024;
+        P.va = wave * 4 * P.tstep + (lane >> 2) * 64 + chunk * 16;
+        P.vb = P.va;
+        P.vs = (wave & 1) * kt2 * 1024 + lane * 16;
+        P.lds0 = (unsigned)(uintptr_t)lds;
+        P.code_base = __builtin_amdgcn_readfirstlane(P.lds0 + (unsigned)(wave * 4 * 1024));
+        P.scale_base = __builtin_amdgcn_readfirstlane(P.lds0 + (unsigned)P.scale_region);
+    }
+    ReadPlan R;
+    {
+        const int frow = lane & 31;
+        const int sw = swz64(frow);
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            const int c = 2 * st + (lane >> 5);
+            R.a_off[st] = (wm * 128 + frow) * PROWB + ((c ^ sw) << 4);
+            R.b_off[st] = (wn * 128 + frow) * PROWB + ((c ^ sw) << 4);
+        }
+        const int s_lane = frow * 8 + (lane >> 5) * 4;
+        R.sa_off = wm * 4 * 256 + s_lane;
+        R.sb_off = wn * 4 * 256 + s_lane;
+    }
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+    int tm = 0, tn = 0;
+    tile_coords(slot, tiles_m, tiles_n, group_m, tm, tn);
+    int64_t m0 = (int64_t)tm * PBM, n0 = (int64_t)tn * PBN;
+    TileSrc S = tile_src(aq, as, bq, bs, M, N, nkt, kt2, m0, n0, wave);
+
+    // first tile: K tiles 0..2, then 32 empty loads standing in for an epilogue's stores
+    dma_tile_all<0>(P, S, 0, 0 < nkt);
+    dma_tile_all<1>(P, S, 1, 1 < nkt);
+    dma_tile_all<2>(P, S, 2, 2 < nkt);
+    {
+        i32x4 none = S.ra;
+        none.z = 0;
+        none = uniform(none);
+        const unsigned dummy = __builtin_amdgcn_readfirstlane(P.lds0 + (unsigned)ST_DUMMY);
+#pragma unroll
+        for (int q = 0; q < kEpiStores; ++q) dma16(none, lane * 16, dummy);
+    }
+
+    TileRegs r0, r1;
+    for (int t = slot; t < total; t += G) {
+        // K tile 0 of this tile has landed (tiles 1, 2 and the 32 stores may be outstanding)
+        wait_vmcnt<(NST - 2) * kDmaPerTile + kEpiStores, true>();
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 24; ++q) read_one(r0, R, lds, q);
+        order_point();
+
+        pipe_trip<true, false>(acc, r0, r1, P, S, S, false, R, lds, 0, nkt);
+        for (int tr = 1; tr < trips; ++tr) pipe_trip<false, false>(acc, r0, r1, P, S, S, false, R, lds, tr * NST, nkt);
+
+        // tile boundary: drain this tile's (empty) trailing DMA and everyone's LDS reads,
+        // start the next tile's DMA, then write this tile out
+        wait_vmcnt<0, true>();
+        __syncthreads();
+        const int64_t em0 = m0, en0 = n0;
+        const int tnext = t + G;
+        if (tnext < total) tile_coords(tnext, tiles_m, tiles_n, group_m, tm, tn);
+        m0 = (int64_t)tm * PBM;
+        n0 = (int64_t)tn * PBN;
+        S = tile_src(aq, as, bq, bs, M, N, nkt, kt2, m0, n0, wave);
+        const bool more = tnext < total;
+        dma_tile_all<0>(P, S, 0, more && 0 < nkt);
+        dma_tile_all<1>(P, S, 1, more && 1 < nkt);
+        dma_tile_all<2>(P, S, 2, more && 2 < nkt);
+        order_point();
+        persist_epilogue(acc, out, ldo, M, N, em0, en0, wm, wn);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+        order_point();
+    }
+    // drain the last (empty) prefetch and the last stores
+    wait_vmcnt<0>();
+}
+
 }  // namespace mx
 
 extern "C" hipError_t mx_launch_gemm(const void* aq, const void* as, const void* bq, const void* bs, int64_t M,
@@ -440,6 +715,20 @@ extern "C" hipError_t mx_launch_gemm(const void* aq, const void* as, const void*
         const int64_t tiles_m = (M + mx::PBM - 1) / mx::PBM, tiles_n = (N + mx::PBN - 1) / mx::PBN;
         if (tiles_m * tiles_n > 0x7FFFFFFF) return hipErrorInvalidValue;
         const int group_m = 8;
+        const int64_t nkt = (K + mx::PBK - 1) / mx::PBK;
+        // persistent kernel: needs >= 5 K tiles (two trips per output tile), 16-byte aligned output
+        // rows, N % 8 == 0, and a tile's output bytes (256 rows) addressable by a 31-bit buffer offset
+        const bool persist = nkt > 4 && (reinterpret_cast<uintptr_t>(out) & 15u) == 0 && (ldo & 7) == 0 &&
+                             (N & 7) == 0 &&
+                             (int64_t)mx::PBM * ldo * 2 < 0x7FFFFFF0ll && getenv_persist() != 0;
+        if (persist) {
+            const int64_t grid = std::min<int64_t>(tiles_m * tiles_n, num_cus());
+            hipLaunchKernelGGL(mx::gemm_persist_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                               static_cast<const uint8_t*>(aq), static_cast<const uint8_t*>(as),
+                               static_cast<const uint8_t*>(bq), static_cast<const uint8_t*>(bs), (int)M, (int)N,
+                               (int)K, static_cast<uint16_t*>(out), ldo, (int)tiles_m, (int)tiles_n, group_m);
+            return hipGetLastError();
+        }
         // 8-byte output stores need an 8-byte aligned start for every row
         const bool vec = (reinterpret_cast<uintptr_t>(out) & 7u) == 0 && (ldo & 3) == 0;
         auto kern = vec ? mx::gemm_pipe_kernel<true> : mx::gemm_pipe_kernel<false>;
