@@ -68,7 +68,7 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": COPY_BYTES, "calls": 3}), flush=True)
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_pipe_llama8b_mlp_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_llama8b_mlp_traffic.json")
 
 
 def measured_traffic():

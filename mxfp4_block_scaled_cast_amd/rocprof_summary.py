@@ -92,7 +92,8 @@ def main():
     k.add_argument("--command", required=True)
     t = sub.add_parser("traffic")
     t.add_argument("--kernel", required=True)
-    t.add_argument("--copy-kernel", default="elementwise|copy|Copy")
+    # the runtime's copy kernel only: the fill that initialises the source reads nothing
+    t.add_argument("--copy-kernel", default="copyBuffer")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
     t.add_argument("--copy-fetch", required=True)
