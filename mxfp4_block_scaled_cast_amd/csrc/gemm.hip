@@ -508,8 +508,8 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
                 for (int gq = 0; gq < 4; ++gq) {
                     const f32x16& c = acc[i][j];
                     uint2 v;
-                    v.x = (uint32_t)f32_to_bf16_rne(c[gq * 4 + 0]) | ((uint32_t)f32_to_bf16_rne(c[gq * 4 + 1]) << 16);
-                    v.y = (uint32_t)f32_to_bf16_rne(c[gq * 4 + 2]) | ((uint32_t)f32_to_bf16_rne(c[gq * 4 + 3]) << 16);
+                    v.x = f32x2_to_bf16x2_rne(c[gq * 4 + 0], c[gq * 4 + 1]);
+                    v.y = f32x2_to_bf16x2_rne(c[gq * 4 + 2], c[gq * 4 + 3]);
                     *reinterpret_cast<uint2*>(orow + j * 32 + gq * 8) = v;
                 }
         }
@@ -535,22 +535,23 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
 
 // ---------------------------------------------------------------------------
 // Persistent kernel: one workgroup per CU walks its output tiles (logical tile
-// slot, slot + G, ... with G the grid size).  At a tile boundary it first
-// issues the DMA of K tiles 0..2 of the next tile, then the previous tile's
-// epilogue (exactly 32 16-byte buffer stores per wave, bounded by a per-tile
-// descriptor so rows and columns outside the output are dropped), so the DMA
-// latency of the new tile overlaps the epilogue and the stores drain while
-// the new tile's MFMAs run.  The first two waits of every tile allow for the
-// 32 stores; before the first tile 32 empty loads stand in for them.  K is
-// padded to a multiple of 4 K tiles (at least 8); tiles past K are empty.
+// slot, slot + G, ... with G the grid size).  The K loop runs on across tiles:
+// the last trip of a tile issues the DMA of K tiles 0..2 of the next tile
+// (nkt is a multiple of 4, so K tile k of every tile lives in stage k % 4) and
+// its last iteration reads the next tile's K tile 0 into registers.  Between
+// the two the finished tile is written: exactly 32 16-byte buffer stores per
+// wave, bounded by a per-tile descriptor so rows and columns outside the
+// output are dropped; they drain while the next tile's MFMAs run.  The first
+// two waits of every tile allow for the 32 stores; before the first tile 32
+// empty loads stand in for them.  Needs nkt % 4 == 0 and nkt >= 8.
 // ---------------------------------------------------------------------------
 
 constexpr int ST_DUMMY = NST * STAGE;  // 1 KB landing area of the empty priming loads
 
 // fp32 x4 -> 4 bf16 (nearest even) in two dwords.
 __device__ __forceinline__ void pack4(const f32x16& c, int g, unsigned& lo, unsigned& hi) {
-    lo = (uint32_t)f32_to_bf16_rne(c[g * 4 + 0]) | ((uint32_t)f32_to_bf16_rne(c[g * 4 + 1]) << 16);
-    hi = (uint32_t)f32_to_bf16_rne(c[g * 4 + 2]) | ((uint32_t)f32_to_bf16_rne(c[g * 4 + 3]) << 16);
+    lo = f32x2_to_bf16x2_rne(c[g * 4 + 0], c[g * 4 + 1]);
+    hi = f32x2_to_bf16x2_rne(c[g * 4 + 2], c[g * 4 + 3]);
 }
 
 // Epilogue of one tile: lanes l and l+32 hold columns 0-3 and 4-7 of each
@@ -667,33 +668,33 @@ __global__ __launch_bounds__(256, 1) void gemm_persist_kernel(const uint8_t* __r
         for (int q = 0; q < kEpiStores; ++q) dma16(none, lane * 16, dummy);
     }
 
+    // K tile 0 of the first tile has landed (tiles 1, 2 and the 32 empty loads may be outstanding)
+    wait_vmcnt<(NST - 2) * kDmaPerTile + kEpiStores, true>();
+    __syncthreads();
     TileRegs r0, r1;
-    for (int t = slot; t < total; t += G) {
-        // K tile 0 of this tile has landed (tiles 1, 2 and the 32 stores may be outstanding)
-        wait_vmcnt<(NST - 2) * kDmaPerTile + kEpiStores, true>();
-        __syncthreads();
 #pragma unroll
-        for (int q = 0; q < 24; ++q) read_one(r0, R, lds, q);
-        order_point();
+    for (int q = 0; q < 24; ++q) read_one(r0, R, lds, q);
+    order_point();
 
+    for (int t = slot; t < total; t += G) {
+        // r0 holds K tile 0 of tile t; K tiles 1, 2 are in flight or landed
         pipe_trip<true, false>(acc, r0, r1, P, S, S, false, R, lds, 0, nkt);
-        for (int tr = 1; tr < trips; ++tr) pipe_trip<false, false>(acc, r0, r1, P, S, S, false, R, lds, tr * NST, nkt);
+        for (int tr = 1; tr < trips - 1; ++tr)
+            pipe_trip<false, false>(acc, r0, r1, P, S, S, false, R, lds, tr * NST, nkt);
 
-        // tile boundary: drain this tile's (empty) trailing DMA and everyone's LDS reads,
-        // start the next tile's DMA, then write this tile out
-        wait_vmcnt<0, true>();
-        __syncthreads();
+        // the last trip streams K tiles 0..2 of the next tile into stages 0..2
+        // (nkt % 4 == 0, so they are the stages those K tiles use) and ends with
+        // the next tile's K tile 0 in r0
         const int64_t em0 = m0, en0 = n0;
         const int tnext = t + G;
-        if (tnext < total) tile_coords(tnext, tiles_m, tiles_n, group_m, tm, tn);
+        const bool more = tnext < total;
+        if (more) tile_coords(tnext, tiles_m, tiles_n, group_m, tm, tn);
         m0 = (int64_t)tm * PBM;
         n0 = (int64_t)tn * PBN;
-        S = tile_src(aq, as, bq, bs, M, N, nkt, kt2, m0, n0, wave);
-        const bool more = tnext < total;
-        dma_tile_all<0>(P, S, 0, more && 0 < nkt);
-        dma_tile_all<1>(P, S, 1, more && 1 < nkt);
-        dma_tile_all<2>(P, S, 2, more && 2 < nkt);
-        order_point();
+        const TileSrc Sn = tile_src(aq, as, bq, bs, M, N, nkt, kt2, m0, n0, wave);
+        pipe_trip<false, true>(acc, r0, r1, P, S, Sn, more, R, lds, (trips - 1) * NST, nkt);
+        S = Sn;
+
         persist_epilogue(acc, out, ldo, M, N, em0, en0, wm, wn);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -716,9 +717,11 @@ extern "C" hipError_t mx_launch_gemm(const void* aq, const void* as, const void*
         if (tiles_m * tiles_n > 0x7FFFFFFF) return hipErrorInvalidValue;
         const int group_m = 8;
         const int64_t nkt = (K + mx::PBK - 1) / mx::PBK;
-        // persistent kernel: needs >= 5 K tiles (two trips per output tile), 16-byte aligned output
-        // rows, N % 8 == 0, and a tile's output bytes (256 rows) addressable by a 31-bit buffer offset
-        const bool persist = nkt > 4 && (reinterpret_cast<uintptr_t>(out) & 15u) == 0 && (ldo & 7) == 0 &&
+        // persistent kernel: needs K a multiple of 512 with at least two trips of 4 K tiles,
+        // 16-byte aligned output rows, N % 8 == 0, and a tile's output bytes (256 rows)
+        // addressable by a 31-bit buffer offset
+        const bool persist = nkt % 4 == 0 && nkt >= 8 && (reinterpret_cast<uintptr_t>(out) & 15u) == 0 &&
+                             (ldo & 7) == 0 &&
                              (N & 7) == 0 &&
                              (int64_t)mx::PBM * ldo * 2 < 0x7FFFFFF0ll && getenv_persist() != 0;
         if (persist) {

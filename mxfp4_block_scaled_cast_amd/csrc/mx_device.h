@@ -105,4 +105,11 @@ __device__ __forceinline__ unsigned short f32_to_bf16_rne(float f) {
     return __builtin_bit_cast(unsigned short, (__bf16)f);
 }
 
+// Two fp32 -> two bf16 in one dword (lo in the low half), same rounding, one
+// v_cvt_pk_bf16_f32.
+__device__ __forceinline__ unsigned f32x2_to_bf16x2_rne(float lo, float hi) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+
 }  // namespace mx
