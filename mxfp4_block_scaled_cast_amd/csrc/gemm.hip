@@ -122,18 +122,21 @@ __global__ __launch_bounds__(256) void gemm_direct_kernel(const uint8_t* __restr
 // no special case: the layout pads codes to a multiple of 128 elements with
 // zero codes and the scales with zero bytes.
 //
-// Schedule of iteration kt (register set p = kt % 2 holds tile kt):
-//   MFMAs of K step 0 of tile kt, with 4 of the 9 DMA instructions of tile
-//     kt+3 (into stage (kt+3)%4, free since the previous barrier)
+// Schedule of iteration kt (register set p = kt % 2 holds tile kt, read
+// from stage kt%4 during the previous iteration):
+//   MFMAs of K step 0 of tile kt
 //   wait for the DMA of tile kt+1 and for this wave's LDS reads, barrier
+//     (after it no wave reads stage kt%4 any more)
 //   MFMAs of K step 1 of tile kt, with the LDS reads of tile kt+1 (set 1-p)
-//     and the other 5 DMA instructions of tile kt+3 spread between them
+//     and the 9 DMA instructions of tile kt+4 into stage kt%4 spread
+//     between them
 // Memory instructions are spread one or two per MFMA: a wave that issues a
 // burst of them stalls on the address unit's queue and lets the MFMA pipe
-// drain.  A tile's DMA has about two tiles of MFMA work to land, and LDS read
-// latency hides behind half a tile.  The loop is unrolled by 4 (static stage
-// and register set) and runs a multiple of 4 tiles; tiles past K are empty
-// (zero codes, zero scales) and add nothing.
+// drain.  With the register double buffer, 4 stages give a tile's DMA about
+// three tiles of MFMA work to land; LDS read latency hides behind half a
+// tile.  The loop is unrolled by 4 (static stage and register set) and runs
+// a multiple of 4 tiles; tiles past K are empty (zero codes, zero scales)
+// and add nothing.
 // ---------------------------------------------------------------------------
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -148,7 +151,6 @@ constexpr int ST_SB = ST_SA + (PBM / 32) * 256;   // 34816: B scale tiles
 constexpr int STAGE = ST_SB + (PBN / 32) * 256;   // 36864 bytes
 constexpr unsigned kRsrcWord3 = 0x00020000u;      // gfx9 raw buffer: dword format, no swizzle
 constexpr int kDmaPerTile = 9;                    // DMA instructions per wave per tile
-constexpr int kDmaStep0 = 4;                      // of which issued during K step 0
 
 // Chunk swizzle of a 64-byte tile row (depends on the row's low 4 bits only).
 __device__ __forceinline__ int swz64(int r) { return ((r >> 1) & 3) ^ (3 * ((r >> 3) & 1)); }
@@ -353,33 +355,28 @@ __device__ __forceinline__ void mfma_one(f32x16 (&acc)[4][4], const u32x4 (&a)[4
 constexpr int kEpiStores = 32;  // 16-byte output stores per wave per tile (persistent kernel)
 
 // Iteration kt = 4t + U of the main loop (see the schedule above).  The DMA
-// it issues is for K tile kt+3 of the current output tile, or with LAST (the
-// final trip of a tile) and U >= 1 for K tile U-1 of the next output tile.
-// With POST (first trip after an epilogue) the waits of the first two
-// iterations also let the epilogue's stores be outstanding.
+// it issues is for K tile kt+4 of the current output tile, or with LAST (the
+// final trip of a tile) for K tile U of the next output tile; both land in
+// stage U.  With POST (first trip after an epilogue) the waits of the first
+// three iterations also let the epilogue's stores, issued after the DMA of K
+// tile 3, be outstanding.
 template <int U, bool POST = false, bool LAST = false>
 __device__ __forceinline__ void pipe_iter(f32x16 (&acc)[4][4], TileRegs& cur, TileRegs& nxt, const DmaPlan& P,
                                           const TileSrc& Scur, const TileSrc& Snext, bool next_ok,
                                           const ReadPlan& R, lds_cptr lds, int kt, int nkt) {
     constexpr int OP = (U & 1) * 2;  // tile kt uses bytes 2*(kt%2) and 2*(kt%2)+1 of its scale dwords
-    constexpr int DST = (U + NST - 1) % NST;
-    constexpr bool TO_NEXT = LAST && U >= 1;
-    constexpr int WAIT = kDmaPerTile + kDmaStep0 + ((POST && U < 2) ? kEpiStores : 0);
-    const TileSrc& S = TO_NEXT ? Snext : Scur;
-    const int dkt = TO_NEXT ? U - 1 : kt + NST - 1;
-    const bool valid = TO_NEXT ? (next_ok && U - 1 < nkt) : (kt + NST - 1 < nkt);
+    constexpr int DST = U;
+    constexpr int WAIT = 2 * kDmaPerTile + ((POST && U < 3) ? kEpiStores : 0);
+    const TileSrc& S = LAST ? Snext : Scur;
+    const int dkt = LAST ? U : kt + NST;
+    const bool valid = LAST ? (next_ok && U < nkt) : (kt + NST < nkt);
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
         mfma_one<OP>(acc, cur.a0, cur.b0, cur.sa, cur.sb, q);
-        // DMA instructions 0..3 after MFMAs 1, 5, 9, 13
-        if (q == 1) dma_one<DST, 0>(P, S, dkt, valid);
-        if (q == 5) dma_one<DST, 1>(P, S, dkt, valid);
-        if (q == 9) dma_one<DST, 2>(P, S, dkt, valid);
-        if (q == 13) dma_one<DST, 3>(P, S, dkt, valid);
         order_point();
     }
-    // tile kt+1 has landed (tile kt+2 and the first part of kt+3 may be in flight),
-    // and this wave's LDS reads are done
+    // tile kt+1 has landed (tiles kt+2 and kt+3 may be in flight), this wave's
+    // LDS reads are done, and after the barrier nobody reads stage U any more
     wait_vmcnt<WAIT, true>();
     __syncthreads();
     lds_cptr next = lds + ((U + 1) % NST) * STAGE;
@@ -389,12 +386,16 @@ __device__ __forceinline__ void pipe_iter(f32x16 (&acc)[4][4], TileRegs& cur, Ti
         const int r0 = (q * 3) / 2, r1 = ((q + 1) * 3) / 2;
 #pragma unroll
         for (int r = r0; r < r1; ++r) read_one(nxt, R, next, r);
-        // DMA instructions 4..8 before MFMAs 2, 5, 8, 11, 14
-        if (q == 2) dma_one<DST, 4>(P, S, dkt, valid);
-        if (q == 5) dma_one<DST, 5>(P, S, dkt, valid);
-        if (q == 8) dma_one<DST, 6>(P, S, dkt, valid);
-        if (q == 11) dma_one<DST, 7>(P, S, dkt, valid);
+        // DMA instructions 0..7 before the odd MFMAs, 8 (scales) before MFMA 14
+        if (q == 1) dma_one<DST, 0>(P, S, dkt, valid);
+        if (q == 3) dma_one<DST, 1>(P, S, dkt, valid);
+        if (q == 5) dma_one<DST, 2>(P, S, dkt, valid);
+        if (q == 7) dma_one<DST, 3>(P, S, dkt, valid);
+        if (q == 9) dma_one<DST, 4>(P, S, dkt, valid);
+        if (q == 11) dma_one<DST, 5>(P, S, dkt, valid);
+        if (q == 13) dma_one<DST, 6>(P, S, dkt, valid);
         if (q == 14) dma_one<DST, 8>(P, S, dkt, valid);
+        if (q == 15) dma_one<DST, 7>(P, S, dkt, valid);
         mfma_one<OP + 1>(acc, cur.a1, cur.b1, cur.sa, cur.sb, q);
         order_point();
     }
@@ -477,11 +478,12 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-    // prologue: tiles 0..2 in flight, then tile 0 into registers
+    // prologue: tiles 0..3 in flight, then tile 0 into registers
     dma_tile_all<0>(P, S, 0, 0 < nkt);
     dma_tile_all<1>(P, S, 1, 1 < nkt);
     dma_tile_all<2>(P, S, 2, 2 < nkt);
-    wait_vmcnt<(NST - 2) * kDmaPerTile, true>();
+    dma_tile_all<3>(P, S, 3, 3 < nkt);
+    wait_vmcnt<(NST - 1) * kDmaPerTile, true>();
     __syncthreads();
     TileRegs r0, r1;
 #pragma unroll
@@ -536,17 +538,15 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
 // ---------------------------------------------------------------------------
 // Persistent kernel: one workgroup per CU walks its output tiles (logical tile
 // slot, slot + G, ... with G the grid size).  The K loop runs on across tiles:
-// the last trip of a tile issues the DMA of K tiles 0..2 of the next tile
+// the last trip of a tile issues the DMA of K tiles 0..3 of the next tile
 // (nkt is a multiple of 4, so K tile k of every tile lives in stage k % 4) and
 // its last iteration reads the next tile's K tile 0 into registers.  Between
 // the two the finished tile is written: exactly 32 16-byte buffer stores per
 // wave, bounded by a per-tile descriptor so rows and columns outside the
-// output are dropped; they drain while the next tile's MFMAs run.  The first
-// two waits of every tile allow for the 32 stores; before the first tile 32
-// empty loads stand in for them.  Needs nkt % 4 == 0 and nkt >= 8.
+// output are dropped; they drain while the next tile's MFMAs run, and the
+// first three waits of the next tile allow for them.  Needs nkt % 4 == 0 and
+// nkt >= 8.
 // ---------------------------------------------------------------------------
-
-constexpr int ST_DUMMY = NST * STAGE;  // 1 KB landing area of the empty priming loads
 
 // fp32 x4 -> 4 bf16 (nearest even) in two dwords.
 __device__ __forceinline__ void pack4(const f32x16& c, int g, unsigned& lo, unsigned& hi) {
@@ -601,7 +601,7 @@ __global__ __launch_bounds__(256, 1) void gemm_persist_kernel(const uint8_t* __r
                                                               const uint8_t* __restrict__ bs, int M, int N, int K,
                                                               uint16_t* __restrict__ out, int64_t ldo, int tiles_m,
                                                               int tiles_n, int group_m) {
-    __shared__ __attribute__((aligned(1024))) char lds_raw[NST * STAGE + 1024];
+    __shared__ __attribute__((aligned(1024))) char lds_raw[NST * STAGE];
     lds_cptr lds = (lds_cptr)lds_raw;
 
     const int lane = threadIdx.x & 63;
@@ -655,34 +655,25 @@ __global__ __launch_bounds__(256, 1) void gemm_persist_kernel(const uint8_t* __r
     int64_t m0 = (int64_t)tm * PBM, n0 = (int64_t)tn * PBN;
     TileSrc S = tile_src(aq, as, bq, bs, M, N, nkt, kt2, m0, n0, wave);
 
-    // first tile: K tiles 0..2, then 32 empty loads standing in for an epilogue's stores
+    // first tile: K tiles 0..3 in flight, K tile 0 into registers, then its first trip
     dma_tile_all<0>(P, S, 0, 0 < nkt);
     dma_tile_all<1>(P, S, 1, 1 < nkt);
     dma_tile_all<2>(P, S, 2, 2 < nkt);
-    {
-        i32x4 none = S.ra;
-        none.z = 0;
-        none = uniform(none);
-        const unsigned dummy = __builtin_amdgcn_readfirstlane(P.lds0 + (unsigned)ST_DUMMY);
-#pragma unroll
-        for (int q = 0; q < kEpiStores; ++q) dma16(none, lane * 16, dummy);
-    }
-
-    // K tile 0 of the first tile has landed (tiles 1, 2 and the 32 empty loads may be outstanding)
-    wait_vmcnt<(NST - 2) * kDmaPerTile + kEpiStores, true>();
+    dma_tile_all<3>(P, S, 3, 3 < nkt);
+    wait_vmcnt<(NST - 1) * kDmaPerTile, true>();
     __syncthreads();
     TileRegs r0, r1;
 #pragma unroll
     for (int q = 0; q < 24; ++q) read_one(r0, R, lds, q);
     order_point();
+    pipe_trip<false, false>(acc, r0, r1, P, S, S, false, R, lds, 0, nkt);
 
-    for (int t = slot; t < total; t += G) {
-        // r0 holds K tile 0 of tile t; K tiles 1, 2 are in flight or landed
-        pipe_trip<true, false>(acc, r0, r1, P, S, S, false, R, lds, 0, nkt);
+    for (int t = slot;;) {
+        // trip 0 of tile t is done; K tiles 4..7 are in flight or landed
         for (int tr = 1; tr < trips - 1; ++tr)
             pipe_trip<false, false>(acc, r0, r1, P, S, S, false, R, lds, tr * NST, nkt);
 
-        // the last trip streams K tiles 0..2 of the next tile into stages 0..2
+        // the last trip streams K tiles 0..3 of the next tile into stages 0..3
         // (nkt % 4 == 0, so they are the stages those K tiles use) and ends with
         // the next tile's K tile 0 in r0
         const int64_t em0 = m0, en0 = n0;
@@ -701,6 +692,10 @@ __global__ __launch_bounds__(256, 1) void gemm_persist_kernel(const uint8_t* __r
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
         order_point();
+        if (!more) break;
+        t = tnext;
+        // trip 0 of the next tile; its first three waits allow for the 32 stores
+        pipe_trip<true, false>(acc, r0, r1, P, S, S, false, R, lds, 0, nkt);
     }
     // drain the last (empty) prefetch and the last stores
     wait_vmcnt<0>();
