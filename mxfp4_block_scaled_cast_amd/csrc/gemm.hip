@@ -210,6 +210,12 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | ((LDS0 ? 0x0 : 0xF) << 8));
 }
 
+// s_waitcnt lgkmcnt(0): every LDS access this wave issued has completed.
+__device__ __forceinline__ void wait_lgkm0() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63 and expcnt 7 (no wait), lgkmcnt 0
+}
+
 // Keeps LDS reads and MFMAs in program order (IR-level memory fence plus a
 // machine-scheduler barrier).
 __device__ __forceinline__ void order_point() {
@@ -541,11 +547,11 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
 // the last trip of a tile issues the DMA of K tiles 0..3 of the next tile
 // (nkt is a multiple of 4, so K tile k of every tile lives in stage k % 4) and
 // its last iteration reads the next tile's K tile 0 into registers.  Between
-// the two the finished tile is written: exactly 32 16-byte buffer stores per
-// wave, bounded by a per-tile descriptor so rows and columns outside the
-// output are dropped; they drain while the next tile's MFMAs run, and the
-// first three waits of the next tile allow for them.  Needs nkt % 4 == 0 and
-// nkt >= 8.
+// the two the finished tile is written through LDS stage 0 (free at that
+// point): exactly 32 16-byte buffer stores per wave, bounded by a per-tile
+// descriptor so rows and columns outside the output are dropped; they drain
+// while the next tile's MFMAs run, and the first three waits of the next tile
+// allow for them.  Needs nkt % 4 == 0 and nkt >= 8.
 // ---------------------------------------------------------------------------
 
 // fp32 x4 -> 4 bf16 (nearest even) in two dwords.
@@ -554,12 +560,26 @@ __device__ __forceinline__ void pack4(const f32x16& c, int g, unsigned& lo, unsi
     hi = f32x2_to_bf16x2_rne(c[g * 4 + 2], c[g * 4 + 3]);
 }
 
-// Epilogue of one tile: lanes l and l+32 hold columns 0-3 and 4-7 of each
-// 8-column group; a permlane32 swap gives each lane 8 consecutive columns, so
-// a wave writes 32 x 16-byte stores.  Out-of-range chunks go to an offset past
-// the descriptor's end (dropped).  Needs N % 8 == 0 (no chunk straddles N).
+// Epilogue of one tile, staged through LDS so that every store writes whole
+// 128-byte lines.  Each wave owns a 9 KB slice of the stage that is free at a
+// tile boundary and goes through its 128 x 128 outputs in four passes of 32
+// rows: lanes l and l+32 hold columns 0-3 and 4-7 of each 8-column group of
+// row l % 32; a permlane32 swap gives each lane 8 consecutive columns (16
+// bytes), written to the slice row-major; read back, 16 lanes cover one
+// 256-byte row of the wave's block, so a store moves 4 rows x 256 contiguous
+// bytes.  Stores carry the non-temporal hint (the output is not read again
+// here; operand panels keep the L2).  Chunks outside the output get an offset
+// past the descriptor's end and are dropped.  Needs N % 8 == 0.
+constexpr int kEpiPitch = 272;          // bytes per staged row: 256 + 16 (conflict-free 16-byte writes)
+constexpr int kEpiSlice = STAGE / 4;    // per-wave slice, 32 * 272 <= 9216
+constexpr int kStoreNT = 2;             // buffer store cache policy: non-temporal
+static_assert(32 * kEpiPitch <= kEpiSlice, "a pass of 32 staged rows fits the wave's slice");
+
 __device__ __forceinline__ void persist_epilogue(const f32x16 (&acc)[4][4], uint16_t* out, int64_t ldo, int M, int N,
-                                                 int64_t m0, int64_t n0, int wm, int wn) {
+                                                 int64_t m0, int64_t n0, int wm, int wn, lds_cptr slice_c) {
+    typedef __attribute__((address_space(3))) char* lds_ptr;
+    typedef __attribute__((address_space(3))) u32x4* lds_v4;
+    lds_ptr slice = (lds_ptr)slice_c;
     // 32-bit tile-local arithmetic: the launcher guarantees 256 * ldo * 2 < 2^31
     const int rows_left = (int)min((int64_t)M - m0, (int64_t)PBM);  // >= 1
     const int cols_left = (int)min((int64_t)N - n0, (int64_t)PBN);
@@ -572,10 +592,9 @@ __device__ __forceinline__ void persist_epilogue(const f32x16 (&acc)[4][4], uint
     int lane_v;
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_v));
     const int h = lane_v >> 5;
-    const int lrow = wm * 128 + (lane_v & 31);  // tile-local row for i = 0
+    const int lr = lane_v & 31;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int r = lrow + i * 32;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
 #pragma unroll
@@ -587,11 +606,23 @@ __device__ __forceinline__ void persist_epilogue(const f32x16 (&acc)[4][4], uint
                 const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
                 // lower lanes: own x then partner's x; upper lanes: partner's y then own y
                 const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
-                const int c = wn * 128 + j * 32 + p * 16 + h * 8;  // tile-local column
-                const int off = (r < rows_left && c < cols_left) ? r * row_bytes + c * 2 : (int)0x80000000;
-                __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, 0);
+                const int c = j * 32 + p * 16 + h * 8;  // column within the wave's block
+                *reinterpret_cast<lds_v4>(slice + lr * kEpiPitch + c * 2) = v;
             }
         }
+        wait_lgkm0();  // this wave's slice is written (the slice is private: no barrier)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int rr = k * 4 + (lane_v >> 4);  // row within the pass
+            const int ch = lane_v & 15;            // 16-byte chunk of the wave's 256-byte row
+            const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+                slice + rr * kEpiPitch + ch * 16);
+            const int r = wm * 128 + i * 32 + rr;  // tile-local row and column
+            const int c = wn * 128 + ch * 8;
+            const int off = (r < rows_left && c < cols_left) ? r * row_bytes + c * 2 : (int)0x80000000;
+            __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, kStoreNT);
+        }
+        wait_lgkm0();  // read back before the next pass overwrites the slice
     }
 }
 
@@ -686,7 +717,12 @@ __global__ __launch_bounds__(256, 1) void gemm_persist_kernel(const uint8_t* __r
         pipe_trip<false, true>(acc, r0, r1, P, S, Sn, more, R, lds, (trips - 1) * NST, nkt);
         S = Sn;
 
-        persist_epilogue(acc, out, ldo, M, N, em0, en0, wm, wn);
+        // stage 0 (the next tile's K tile 0, now in r0) is free until the next
+        // DMA into it, after the first barrier of the next trip; every wave's
+        // reads of it must be done before the epilogue writes its slice
+        wait_lgkm0();
+        __syncthreads();
+        persist_epilogue(acc, out, ldo, M, N, em0, en0, wm, wn, lds + wave * kEpiSlice);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
