@@ -36,6 +36,9 @@ WORKLOADS = {
                      "O 8192x4096x4096, fwd + dA + dB with dual casts"),
     "llama70b": ("Llama-3-70B per-GPU projections (M=8192): QKV 8192x10240x8192, gate/up 8192x57344x8192, "
                  "down 8192x8192x28672, fwd + dA + dB with dual casts"),
+    "ragged": ("edge / ragged sweep: all 36 (M, N, K) with M in {1, 17, 4096, 16384}, N in {128, 4096, 128256}, "
+               "K in {32, 4096, 14336}, U(-1e3, 1e3) with 5% zero and 5% subnormal 32x32 tiles; "
+               "fwd + dA + dB with dual casts per combination"),
 }
 
 
@@ -84,6 +87,128 @@ def measured_traffic():
         return None
 
 
+def gemm_roofline(m, n, k):
+    """Algorithmic FLOPs and minimum HBM bytes of out[m, n] = sum over k, and the bound they imply."""
+    flops = 2.0 * m * n * k
+    nbytes = m * k / 2 + n * k / 2 + (m + n) * k / 32 + 2.0 * m * n
+    t_mfma = flops / (FP4_PEAK_TFLOPS * 1e12)
+    t_hbm = nbytes / (HBM_PEAK_GBPS * 1e9)
+    return flops, nbytes, ("mfma" if t_mfma >= t_hbm else "hbm"), max(t_mfma, t_hbm)
+
+
+def step_ops(P, L, sp, N):
+    """The training step of one projection: (kind, label, launch, work, roofline-ideal seconds)."""
+
+    def cast_dual(x, row, col):
+        R, C = x.shape
+        return lambda: L.mxfp4_cast_dual(x.data_ptr(), R, C, C, row.q.data_ptr(), row.s.data_ptr(),
+                                         col.q.data_ptr(), col.s.data_ptr(), sp)
+
+    def gemm(fn, a, b, out):
+        M, Nn = a.rows, b.rows
+        return lambda: fn(a.q.data_ptr(), a.s.data_ptr(), b.q.data_ptr(), b.s.data_ptr(), M, Nn, a.k,
+                          out.data_ptr(), Nn, sp)
+
+    M, Nn, K, name = P["M"], P["N"], P["K"], P["name"]
+    ops = []
+    for label, x, row, col in (("cast_dual(A)", P["a"], P["a_row"], P["a_col"]),
+                               ("cast_dual(W)", P["w"], P["w_row"], P["w_col"])):
+        nb = 3.0625 * x.shape[0] * x.shape[1]
+        ops.append(("cast", name + "." + label, cast_dual(x, row, col), nb, nb / (HBM_PEAK_GBPS * 1e9)))
+    fl, _, _, t = gemm_roofline(M, Nn, K)
+    ops.append(("gemm", name + ".fwd", gemm(L.mxfp4_gemm_nt, P["a_row"], P["w_row"], P["out"]), fl, t))
+    nb = 3.0625 * M * Nn
+    ops.append(("cast", name + ".cast_dual(dOut)", cast_dual(P["g"], P["g_row"], P["g_col"]), nb,
+                nb / (HBM_PEAK_GBPS * 1e9)))
+    fl, _, _, t = gemm_roofline(M, K, Nn)
+    ops.append(("gemm", name + ".dA", gemm(L.mxfp4_gemm_nn, P["g_row"], P["w_col"], P["da"]), fl, t))
+    fl, _, _, t = gemm_roofline(Nn, K, M)
+    ops.append(("gemm", name + ".dB", gemm(L.mxfp4_gemm_nt, P["g_col"], P["a_col"], P["dw"]), fl, t))
+    return ops
+
+
+def alloc_projection(name, M, Nn, K, a, w, g, mx, torch, dev):
+    """Device operands of one projection's step (a, w, g: bf16 device tensors)."""
+    Mp = -(-M // 32) * 32
+    P = dict(name=name, M=M, N=Nn, K=K, Mp=Mp, a=a, w=w, g=g)
+    P["a_row"], P["a_col"] = mx.empty_operand(M, K, dev), mx.empty_operand(K, Mp, dev)
+    P["w_row"], P["w_col"] = mx.empty_operand(Nn, K, dev), mx.empty_operand(K, Nn, dev)
+    P["g_row"], P["g_col"] = mx.empty_operand(M, Nn, dev), mx.empty_operand(Nn, Mp, dev)
+    P["out"] = torch.empty((M, Nn), dtype=torch.bfloat16, device=dev)
+    P["da"] = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    P["dw"] = torch.empty((Nn, K), dtype=torch.bfloat16, device=dev)
+    return P
+
+
+def time_ops(ops, steps, warmup, stream, torch, N, per_kernel=True):
+    """Warm up, then time `steps` passes over `ops` (events per kernel if asked).
+    Returns (ms per pass, [average ms per op] or None)."""
+
+    def run(events):
+        for i, (_, label, launch, _, _) in enumerate(ops):
+            if events is not None:
+                events[i][0].record(stream)
+            st = launch()
+            if st != 0:
+                raise N.Mxfp4Error(st, label)
+            if events is not None:
+                events[i][1].record(stream)
+
+    for _ in range(warmup):
+        run(None)
+    torch.cuda.synchronize()
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in ops]
+          for _ in range(steps)] if per_kernel else None
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s_ in range(steps):
+        run(ev[s_] if per_kernel else None)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    if not per_kernel:
+        return ms, None
+    return ms, [sum(ev[s_][i][0].elapsed_time(ev[s_][i][1]) for s_ in range(steps)) / steps for i in range(len(ops))]
+
+
+def ragged_sweep(args, torch, mx, N, W, L, dev):
+    """Every (M, N, K) of the edge sweep: one step each, per-kernel times against each kernel's roofline."""
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    cid = W.CONFIG_IDS["ragged"]
+    combos = []
+    tot_flops = tot_ms = 0.0
+    for ci, (M, Nn, K) in enumerate(W.ragged_combos()):
+        seed = W.seed_of(cid, 0, ci)
+        a = W.ragged_values_torch((M, K), seed + W.A, dev).view(torch.bfloat16)
+        w = W.ragged_values_torch((Nn, K), seed + W.W, dev).view(torch.bfloat16)
+        g = W.ragged_values_torch((M, Nn), seed + W.DOUT, dev).view(torch.bfloat16)
+        P = alloc_projection("M%d-N%d-K%d" % (M, Nn, K), M, Nn, K, a, w, g, mx, torch, dev)
+        ops = step_ops(P, L, sp, N)
+        ms, per = time_ops(ops, args.steps, args.warmup, stream, torch, N)
+        fl = 6.0 * M * Nn * K
+        tot_flops += fl
+        tot_ms += ms
+        kernels = {}
+        for (kind, label, _, work, ideal), t in zip(ops, per):
+            rate = work / (t * 1e-3)
+            kernels[label.split(".", 1)[1]] = {
+                "ms": round(t, 4), ("tflops" if kind == "gemm" else "gbps"): round(rate / (1e12 if kind == "gemm" else 1e9), 1),
+                "roofline_frac": round(ideal / (t * 1e-3), 3)}
+        combos.append({"M": M, "N": Nn, "K": K, "ms_step": round(ms, 4), "kernels": kernels})
+        print("[ragged %2d/36] M=%d N=%d K=%d step %.3f ms" % (ci + 1, M, Nn, K, ms), file=sys.stderr, flush=True)
+        del P, ops, a, w, g
+        torch.cuda.empty_cache()
+    value = tot_flops / (tot_ms * 1e-3) / 1e12
+    return {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(tot_ms, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "mxfp4", "data": "synthetic",
+            "config": {"workload": WORKLOADS["ragged"], "combos": len(combos),
+                       "step_tflop": round(tot_flops / 1e12, 4)},
+            "per_combo": combos}
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -105,6 +230,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     L = N.lib()
+
+    if args.workload == "ragged":
+        print(json.dumps(ragged_sweep(args, torch, mx, N, W, L, dev)), flush=True)
+        return
     projections = {"llama8b_mlp": W.LLAMA8B_MLP, "llama8b_attn": W.LLAMA8B_ATTN, "llama70b": W.LLAMA70B}[args.workload]
 
     def to_dev(bits):
@@ -118,83 +247,28 @@ def main():
         a, w, g = W.projection_inputs(args.workload, idx, M, Nn, K)
         if idx == 0:
             host_inputs = {"a": a, "w": w, "M": M, "N": Nn, "K": K, "name": name}
-        Mp = -(-M // 32) * 32
-        P = dict(name=name, M=M, N=Nn, K=K, Mp=Mp, a=to_dev(a), w=to_dev(w), g=to_dev(g))
+        projs.append(alloc_projection(name, M, Nn, K, to_dev(a), to_dev(w), to_dev(g), mx, torch, dev))
         del a, w, g
-        P["a_row"], P["a_col"] = mx.empty_operand(M, K, dev), mx.empty_operand(K, Mp, dev)
-        P["w_row"], P["w_col"] = mx.empty_operand(Nn, K, dev), mx.empty_operand(K, Nn, dev)
-        P["g_row"], P["g_col"] = mx.empty_operand(M, Nn, dev), mx.empty_operand(Nn, Mp, dev)
-        P["out"] = torch.empty((M, Nn), dtype=torch.bfloat16, device=dev)
-        P["da"] = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
-        P["dw"] = torch.empty((Nn, K), dtype=torch.bfloat16, device=dev)
-        projs.append(P)
     torch.cuda.synchronize()
     setup_s = time.time() - t0
 
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
-
-    def cast_dual(x, row, col):
-        R, C = x.shape
-        return lambda: L.mxfp4_cast_dual(x.data_ptr(), R, C, C, row.q.data_ptr(), row.s.data_ptr(),
-                                         col.q.data_ptr(), col.s.data_ptr(), sp)
-
-    def gemm(fn, a, b, out):
-        M, Nn = a.rows, b.rows
-        return lambda: fn(a.q.data_ptr(), a.s.data_ptr(), b.q.data_ptr(), b.s.data_ptr(), M, Nn, a.k,
-                          out.data_ptr(), Nn, sp)
-
-    # ---- the step: (kind, label, launch, algorithmic work)
     ops = []
     step_flops = 0.0
     for P in projs:
-        M, Nn, K = P["M"], P["N"], P["K"]
-        fl = 2.0 * M * Nn * K
-        step_flops += 3 * fl
-        ops.append(("cast", P["name"] + ".cast_dual(A)", cast_dual(P["a"], P["a_row"], P["a_col"]), 3.0625 * M * K))
-        ops.append(("cast", P["name"] + ".cast_dual(W)", cast_dual(P["w"], P["w_row"], P["w_col"]), 3.0625 * Nn * K))
-        ops.append(("gemm", P["name"] + ".fwd", gemm(L.mxfp4_gemm_nt, P["a_row"], P["w_row"], P["out"]), fl))
-        ops.append(("cast", P["name"] + ".cast_dual(dOut)", cast_dual(P["g"], P["g_row"], P["g_col"]),
-                    3.0625 * M * Nn))
-        ops.append(("gemm", P["name"] + ".dA", gemm(L.mxfp4_gemm_nn, P["g_row"], P["w_col"], P["da"]), fl))
-        ops.append(("gemm", P["name"] + ".dB", gemm(L.mxfp4_gemm_nt, P["g_col"], P["a_col"], P["dw"]), fl))
+        step_flops += 6.0 * P["M"] * P["N"] * P["K"]
+        ops += step_ops(P, L, sp, N)
 
     use_events = not args.no_kernel_events
-
-    def run_step(events):
-        for i, (_, label, launch, _) in enumerate(ops):
-            if events is not None:
-                events[i][0].record(stream)
-            st = launch()
-            if st != 0:
-                raise N.Mxfp4Error(st, label)
-            if events is not None:
-                events[i][1].record(stream)
-
-    for _ in range(args.warmup):
-        run_step(None)
-    torch.cuda.synchronize()
-
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in ops]
-          for _ in range(args.steps)] if use_events else None
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for s in range(args.steps):
-        run_step(ev[s] if use_events else None)
-    end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / args.steps
+    ms_per_step, per = time_ops(ops, args.steps, args.warmup, stream, torch, N, per_kernel=use_events)
 
     per_op = {}
     gemm_ms = cast_ms = 0.0
     gemm_launches = 0
     gemm_work = cast_bytes = 0.0
     if use_events:
-        for i, (kind, label, _, work) in enumerate(ops):
-            times = [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
-            avg = sum(times) / len(times)
+        for (kind, label, _, work, _), avg in zip(ops, per):
             rate = work / (avg * 1e-3)
             per_op[label] = {"ms": round(avg, 4),
                              ("tflops" if kind == "gemm" else "gbps"): round(rate / (1e12 if kind == "gemm" else 1e9), 1)}

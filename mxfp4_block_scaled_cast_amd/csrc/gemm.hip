@@ -18,6 +18,7 @@
 #include <algorithm>
 
 #include "mx_device.h"
+#include "mx_host.h"
 
 // MXFP4_GEMM_PERSIST=0 disables the persistent kernel (comparison aid).
 static int getenv_persist() {
@@ -26,19 +27,6 @@ static int getenv_persist() {
         return e && e[0] == '0' ? 0 : 1;
     }();
     return v;
-}
-
-// Compute units of the current device (cached per device).
-static int num_cus() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
 }
 
 // MXFP4_GEMM_DIRECT=1 forces the untiled kernel (testing aid).
@@ -53,8 +41,8 @@ static int getenv_direct() {
 namespace mx {
 
 // Reference-shaped kernel: each wave computes a 32x32 output tile reading its
-// operands straight from global memory (no LDS).  Used for small problems and
-// as the correctness baseline for the tiled kernel.
+// operands straight from global memory (no LDS), one 64-wide K step at a
+// time.  Only used when MXFP4_GEMM_DIRECT=1 (a cross-check of the others).
 __global__ __launch_bounds__(256) void gemm_direct_kernel(const uint8_t* __restrict__ aq,
                                                           const uint8_t* __restrict__ as,
                                                           const uint8_t* __restrict__ bq,
@@ -98,6 +86,160 @@ __global__ __launch_bounds__(256) void gemm_direct_kernel(const uint8_t* __restr
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Skinny kernel, for outputs too small to fill the chip with 256 x 256 tiles
+// (one side below 128, or few tiles) and for long contractions behind a small
+// output (e.g. dA of an LM head: 1 x 4096 outputs, contraction 128256).
+//
+// C[i, j] = sum_k A[i, k] B[j, k], written to out[i * ld_i + j * ld_j]; the
+// launcher passes the smaller operand as A (and swaps the output strides when
+// that is the GEMM's B).  A wave owns 32 rows of A x 32*NB rows of B (NB
+// scaled MFMAs per 64-wide K step, sharing the A fragment) over one slice of
+// the contraction; the W waves of a workgroup take consecutive slices of the
+// same output block and add their partial sums through LDS.  Operands come
+// straight from global memory in 256-wide K chunks: per lane four 16-byte
+// code loads per row group (one per K step; 32 rows x 256 K = four whole 1 KB
+// code tiles per row group) and one scale dword, whose four bytes are the
+// lane's scales for the four steps (the MFMA picks one with opsel).  All of a
+// chunk's loads are issued before its MFMAs; the other waves of the CU cover
+// the latency.  Rows past the operands and K steps past the padded code tiles
+// are not loaded (zero).
+// ---------------------------------------------------------------------------
+
+// NB = 1 runs up to 16 waves per workgroup (92 VGPRs), NB = 2, 4 up to 8.
+template <int NB>
+constexpr int skinny_max_waves() { return NB == 1 ? 16 : 8; }
+
+template <int NB>
+__global__ __launch_bounds__(64 * skinny_max_waves<NB>()) void gemm_skinny_kernel(
+    const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as, const uint8_t* __restrict__ bq,
+    const uint8_t* __restrict__ bs, int Ma, int Nb, int K, uint16_t* __restrict__ out, int64_t ld_i, int64_t ld_j,
+    int tiles_b) {
+    extern __shared__ float red[];  // [W][NB][16][64] partial sums (W > 1)
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int W = blockDim.x >> 6;
+    const int half = lane >> 5;
+    const int i0 = (blockIdx.x / tiles_b) * 32;
+    const int j0 = (blockIdx.x % tiles_b) * (32 * NB);
+    const int64_t kt128 = (K + 127) >> 7, kt256 = (K + 255) >> 8;
+
+    const int ia = i0 + (lane & 31);
+    const bool a_ok = ia < Ma;
+    int jb[NB];
+    bool b_ok[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        jb[nb] = j0 + nb * 32 + (lane & 31);
+        b_ok[nb] = jb[nb] < Nb;
+    }
+
+    // this wave's slice of the 256-wide chunks
+    const int chunks = (int)kt256;
+    const int c_begin = (int)((int64_t)chunks * w / W), c_end = (int)((int64_t)chunks * (w + 1) / W);
+
+    f32x16 acc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16{};
+
+    for (int c = c_begin; c < c_end; ++c) {
+        u32x4 av[4], bv[NB][4];
+        unsigned sa = 0u, sb[NB];
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const int64_t kk = (int64_t)c * 256 + st * 64 + half * 32;
+            const bool k_ok = (int64_t)c * 256 + st * 64 < kt128 * 128;
+            av[st] = (a_ok && k_ok) ? *reinterpret_cast<const u32x4*>(aq + code_offset(ia, kk, kt128))
+                                    : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                bv[nb][st] = (b_ok[nb] && k_ok) ? *reinterpret_cast<const u32x4*>(bq + code_offset(jb[nb], kk, kt128))
+                                                : u32x4{0u, 0u, 0u, 0u};
+        }
+        // scale dword of (row, half): blocks c*8 + half + 2*st, st = 0..3
+        if (a_ok) sa = *reinterpret_cast<const unsigned*>(as + scale_offset(ia, (int64_t)c * 8 + half, kt256));
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+            sb[nb] = b_ok[nb] ? *reinterpret_cast<const unsigned*>(bs + scale_offset(jb[nb], (int64_t)c * 8 + half, kt256))
+                              : 0u;
+#define MX_SKINNY_STEP(ST)                                                                                         \
+    _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) acc[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4( \
+        as_operand(av[ST]), as_operand(bv[nb][ST]), acc[nb], 4, 4, ST, (int)sa, ST, (int)sb[nb]);
+        MX_SKINNY_STEP(0) MX_SKINNY_STEP(1) MX_SKINNY_STEP(2) MX_SKINNY_STEP(3)
+#undef MX_SKINNY_STEP
+    }
+
+    // acc[nb][r] is C[i0 + (r/4)*8 + half*4 + r%4, j0 + nb*32 + lane%32]
+    if (W == 1) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            if (!b_ok[nb]) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = i0 + (r >> 2) * 8 + half * 4 + (r & 3);
+                if (i < Ma) out[(int64_t)i * ld_i + (int64_t)jb[nb] * ld_j] = f32_to_bf16_rne(acc[nb][r]);
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[((w * NB + nb) * 16 + r) * 64 + lane] = acc[nb][r];
+    __syncthreads();
+    constexpr int ELEMS = NB * 16 * 64;
+    for (int e = threadIdx.x; e < ELEMS; e += blockDim.x) {
+        float v = 0.f;
+        for (int ww = 0; ww < W; ++ww) v += red[ww * ELEMS + e];
+        const int l = e & 63, r = (e >> 6) & 15, nb = e >> 10;
+        const int i = i0 + (r >> 2) * 8 + (l >> 5) * 4 + (r & 3);
+        const int j = j0 + nb * 32 + (l & 31);
+        if (i < Ma && j < Nb) out[(int64_t)i * ld_i + (int64_t)j * ld_j] = f32_to_bf16_rne(v);
+    }
+}
+
+// Launch the skinny kernel for out[M, N] = a . b^T.
+static hipError_t launch_skinny(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t M,
+                                int64_t N, int64_t K, uint16_t* out, int64_t ldo, hipStream_t stream) {
+    // the smaller side is A (32-row groups), the larger one B (32*NB-row groups)
+    const bool swap = M > N;
+    const int64_t Ma = swap ? N : M, Nb = swap ? M : N;
+    const int64_t ld_i = swap ? 1 : ldo, ld_j = swap ? ldo : 1;
+    // split the contraction over W waves (LDS: W * NB * 4 KB <= 64 KB) until ~16 waves per CU; take the
+    // widest B block (most reuse of the A fragment) that still reaches that, else NB = 1 (most waves)
+    const int64_t chunks = (K + 255) / 256;
+    const int64_t target = (int64_t)mx::num_cus() * 16;
+    const int64_t tiles_a = (Ma + 31) / 32;
+    int nb = 1, W = 1;
+    int64_t tiles_b = 0;
+    for (int cand = 4; cand >= 1; cand /= 2) {
+        if (cand > 1 && Nb < 32 * cand) continue;
+        const int wmax = cand == 1 ? 16 : 8;
+        int w = 1;
+        const int64_t tb = (Nb + 32 * cand - 1) / (32 * cand);
+        while (w * 2 <= wmax && w * 2 * cand <= 16 && w * 2 <= chunks && tiles_a * tb * w < target) w *= 2;
+        nb = cand;
+        W = w;
+        tiles_b = tb;
+        if (tiles_a * tb * w >= target) break;
+    }
+    const int64_t tiles = tiles_a * tiles_b;
+    if (tiles > 0x7FFFFFFF || Ma > 0x7FFFFFFF || Nb > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const size_t lds = W > 1 ? (size_t)W * nb * 16 * 64 * sizeof(float) : 0;
+    const dim3 grid((unsigned)tiles), block((unsigned)(64 * W));
+    const uint8_t *pa = swap ? bq : aq, *psa = swap ? bs : as, *pb = swap ? aq : bq, *psb = swap ? as : bs;
+    if (nb == 4)
+        hipLaunchKernelGGL(mx::gemm_skinny_kernel<4>, grid, block, lds, stream, pa, psa, pb, psb, (int)Ma, (int)Nb,
+                           (int)K, out, ld_i, ld_j, (int)tiles_b);
+    else if (nb == 2)
+        hipLaunchKernelGGL(mx::gemm_skinny_kernel<2>, grid, block, lds, stream, pa, psa, pb, psb, (int)Ma, (int)Nb,
+                           (int)K, out, ld_i, ld_j, (int)tiles_b);
+    else
+        hipLaunchKernelGGL(mx::gemm_skinny_kernel<1>, grid, block, lds, stream, pa, psa, pb, psb, (int)Ma, (int)Nb,
+                           (int)K, out, ld_i, ld_j, (int)tiles_b);
+    return hipGetLastError();
+}
 
 // ---------------------------------------------------------------------------
 // Pipelined kernel.  Workgroup tile 256 x 256, K tile 128 (64 bytes of FP4 per
@@ -337,13 +479,6 @@ __device__ __forceinline__ void read_one(TileRegs& T, const ReadPlan& R, lds_cpt
     else if (q < 16) T.b0[q - 12] = lds128(stage + ST_B + R.b_off[0] + (q - 12) * 32 * PROWB);
     else if (q < 20) T.a1[q - 16] = lds128(stage + ST_A + R.a_off[1] + (q - 16) * 32 * PROWB);
     else T.b1[q - 20] = lds128(stage + ST_B + R.b_off[1] + (q - 20) * 32 * PROWB);
-}
-
-__device__ __forceinline__ v8i as_operand(u32x4 v) {
-    v8i r;
-    r[0] = (int)v.x; r[1] = (int)v.y; r[2] = (int)v.z; r[3] = (int)v.w;
-    r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;  // FP4 operands occupy four registers; the rest is ignored
-    return r;
 }
 
 // MFMA q (0..15) of one K step, (i, j) = (q / 4, q % 4).  B fragments enter the
@@ -742,9 +877,21 @@ __global__ __launch_bounds__(256, 1) void gemm_persist_kernel(const uint8_t* __r
 extern "C" hipError_t mx_launch_gemm(const void* aq, const void* as, const void* bq, const void* bs, int64_t M,
                                      int64_t N, int64_t K, void* out, int64_t ldo, hipStream_t stream) {
     if (M == 0 || N == 0) return hipSuccess;
-    const bool tiled = K > 0 && M >= 128 && N >= 128 && getenv_direct() == 0;
-    if (tiled) {
-        const int64_t tiles_m = (M + mx::PBM - 1) / mx::PBM, tiles_n = (N + mx::PBN - 1) / mx::PBN;
+    const uint8_t *a8 = static_cast<const uint8_t*>(aq), *as8 = static_cast<const uint8_t*>(as);
+    const uint8_t *b8 = static_cast<const uint8_t*>(bq), *bs8 = static_cast<const uint8_t*>(bs);
+    uint16_t* o16 = static_cast<uint16_t*>(out);
+    if (getenv_direct() != 0) {
+        if ((M + 63) / 64 > 65535 || (N + 63) / 64 > 0x7FFFFFFF) return hipErrorInvalidValue;
+        const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64)), block(256);
+        hipLaunchKernelGGL(mx::gemm_direct_kernel, grid, block, 0, stream, a8, as8, b8, bs8, (int)M, (int)N, (int)K,
+                           o16, ldo);
+        return hipGetLastError();
+    }
+    const int64_t tiles_m = (M + mx::PBM - 1) / mx::PBM, tiles_n = (N + mx::PBN - 1) / mx::PBN;
+    // 256 x 256 tiles need both sides >= 128 and enough tiles to fill half the CUs
+    const bool tiled = K > 0 && M >= 128 && N >= 128 && tiles_m * tiles_n * 2 >= mx::num_cus();
+    if (!tiled) return mx::launch_skinny(a8, as8, b8, bs8, M, N, K, o16, ldo, stream);
+    {
         if (tiles_m * tiles_n > 0x7FFFFFFF) return hipErrorInvalidValue;
         const int group_m = 8;
         const int64_t nkt = (K + mx::PBK - 1) / mx::PBK;
@@ -756,7 +903,7 @@ extern "C" hipError_t mx_launch_gemm(const void* aq, const void* as, const void*
                              (N & 7) == 0 &&
                              (int64_t)mx::PBM * ldo * 2 < 0x7FFFFFF0ll && getenv_persist() != 0;
         if (persist) {
-            const int64_t grid = std::min<int64_t>(tiles_m * tiles_n, num_cus());
+            const int64_t grid = std::min<int64_t>(tiles_m * tiles_n, mx::num_cus());
             hipLaunchKernelGGL(mx::gemm_persist_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
                                static_cast<const uint8_t*>(aq), static_cast<const uint8_t*>(as),
                                static_cast<const uint8_t*>(bq), static_cast<const uint8_t*>(bs), (int)M, (int)N,
@@ -772,10 +919,4 @@ extern "C" hipError_t mx_launch_gemm(const void* aq, const void* as, const void*
                            static_cast<uint16_t*>(out), ldo, (int)tiles_m, (int)tiles_n, group_m);
         return hipGetLastError();
     }
-    if ((M + 63) / 64 > 65535 || (N + 63) / 64 > 0x7FFFFFFF) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64)), block(256);
-    hipLaunchKernelGGL(mx::gemm_direct_kernel, grid, block, 0, stream, static_cast<const uint8_t*>(aq),
-                       static_cast<const uint8_t*>(as), static_cast<const uint8_t*>(bq),
-                       static_cast<const uint8_t*>(bs), (int)M, (int)N, (int)K, static_cast<uint16_t*>(out), ldo);
-    return hipGetLastError();
 }

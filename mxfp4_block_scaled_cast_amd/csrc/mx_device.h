@@ -74,6 +74,16 @@ __device__ __forceinline__ unsigned cvt8(u32x4 v, float scale) {
     return r;
 }
 
+// A 32x32x64 FP4 MFMA operand from the lane's 16 bytes (32 codes): FP4
+// operands occupy the low four registers of the 8-register operand; the rest
+// is ignored.
+__device__ __forceinline__ v8i as_operand(u32x4 v) {
+    v8i r;
+    r[0] = (int)v.x; r[1] = (int)v.y; r[2] = (int)v.z; r[3] = (int)v.w;
+    r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
+    return r;
+}
+
 // Per-half max of two packed u16 pairs.
 __device__ __forceinline__ unsigned pk_max_u16(unsigned a, unsigned b) {
     u16x2 x = __builtin_bit_cast(u16x2, a);

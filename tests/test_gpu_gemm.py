@@ -50,10 +50,12 @@ def test_ragged_small(M, N, K):
     assert_gemm_close(got, ref, absref, "ragged %dx%dx%d" % (M, N, K))
 
 
-@pytest.mark.parametrize("M,N,K", [(128, 128, 256), (256, 256, 512), (300, 520, 288), (513, 260, 800),
-                                   (1000, 2000, 1024), (384, 640, 1312), (257, 129, 32), (2048, 256, 4096)])
+# Shapes with at least 128 output tiles of 256 x 256 (the launcher gives fewer to the skinny kernel):
+# pipelined kernel for K <= 512 / K not a multiple of 512 / N % 8 != 0, persistent kernel otherwise;
+# ragged M / N edges and K tails.
+@pytest.mark.parametrize("M,N,K", [(2048, 4096, 256), (2100, 4000, 288), (4096, 2056, 800), (2048, 4100, 1024),
+                                   (2304, 3840, 1024), (3000, 2568, 1536)])
 def test_tiled_shapes(M, N, K):
-    # workgroup tiles of 256 x 256 x 256: ragged M / N edges, K tails, odd and even K-tile counts
     a = W.normal_bf16((M, K), 1.0, M + 7 * K)
     b = W.normal_bf16((N, K), 0.5, N + 11 * K)
     got = gpu_nt(a, b, "tiled")
@@ -61,9 +63,23 @@ def test_tiled_shapes(M, N, K):
     assert_gemm_close(got, ref, absref, "tiled %dx%dx%d" % (M, N, K))
 
 
-def test_tiled_same_scale_bit_exact():
+# Skinny kernel (one side below 128 or few tiles): split of the contraction over the waves of a
+# workgroup, 32 x 32*NB blocks with NB = 1, 2, 4, the smaller side taken as A (output written
+# transposed when that is the GEMM's B), K chunks past the padded code tiles.
+@pytest.mark.parametrize("M,N,K", [(1, 4096, 14336), (4096, 32, 8192), (32, 65536, 1024), (128, 65536, 512),
+                                   (65536, 100, 544), (17, 300, 2080), (1, 128256, 32), (1000, 2000, 1024)])
+def test_skinny_shapes(M, N, K):
+    a = W.ragged_values((M, K), 3 * M + K)
+    b = W.ragged_values((N, K), 5 * N + K)
+    got = gpu_nt(a, b, "skinny")
+    ref, absref = oracle_nt(a, b)
+    assert_gemm_close(got, ref, absref, "skinny %dx%dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M,N,K", [(384, 320, 768), (2048, 4096, 1024)])
+def test_same_scale_bit_exact(M, N, K):
+    # skinny (few tiles) and persistent tiled kernels
     rng = np.random.default_rng(16)
-    M, N, K = 384, 320, 768
     fa = rng.uniform(-4, 4, (M, K)).astype(np.float32)
     fb = rng.uniform(-4, 4, (N, K)).astype(np.float32)
     fa[:, ::32] = 4.0
