@@ -16,6 +16,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "mx_device.h"
 #include "mx_host.h"
@@ -680,13 +681,14 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
 // Persistent kernel: one workgroup per CU walks its output tiles (logical tile
 // slot, slot + G, ... with G the grid size).  The K loop runs on across tiles:
 // the last trip of a tile issues the DMA of K tiles 0..3 of the next tile
-// (nkt is a multiple of 4, so K tile k of every tile lives in stage k % 4) and
+// (every tile runs a multiple of 4 K tiles, those past K reading as zero, so
+// K tile k of every tile lives in stage k % 4) and
 // its last iteration reads the next tile's K tile 0 into registers.  Between
 // the two the finished tile is written through LDS stage 0 (free at that
 // point): exactly 32 16-byte buffer stores per wave, bounded by a per-tile
 // descriptor so rows and columns outside the output are dropped; they drain
 // while the next tile's MFMAs run, and the first three waits of the next tile
-// allow for them.  Needs nkt % 4 == 0 and nkt >= 8.
+// allow for them.  Needs N % 8 == 0 (16-byte output chunks).
 // ---------------------------------------------------------------------------
 
 // fp32 x4 -> 4 bf16 (nearest even) in two dwords.
@@ -761,6 +763,7 @@ __device__ __forceinline__ void persist_epilogue(const f32x16 (&acc)[4][4], uint
     }
 }
 
+template <bool SINGLE>
 __global__ __launch_bounds__(256, 1) void gemm_persist_kernel(const uint8_t* __restrict__ aq,
                                                               const uint8_t* __restrict__ as,
                                                               const uint8_t* __restrict__ bq,
@@ -779,7 +782,7 @@ __global__ __launch_bounds__(256, 1) void gemm_persist_kernel(const uint8_t* __r
     const int slot = xcd_remap(blockIdx.x, G);  // each XCD takes a contiguous range of slots per round
 
     const int nkt = (K + PBK - 1) / PBK;
-    const int trips = (nkt + NST - 1) / NST;  // >= 2 (the launcher guarantees it)
+    const int trips = (nkt + NST - 1) / NST;  // 1 with SINGLE, else >= 2; K tiles past nkt read as zero
     const int kt2 = (K + 255) >> 8;
 
     DmaPlan P;
@@ -832,16 +835,13 @@ __global__ __launch_bounds__(256, 1) void gemm_persist_kernel(const uint8_t* __r
 #pragma unroll
     for (int q = 0; q < 24; ++q) read_one(r0, R, lds, q);
     order_point();
-    pipe_trip<false, false>(acc, r0, r1, P, S, S, false, R, lds, 0, nkt);
 
-    for (int t = slot;;) {
-        // trip 0 of tile t is done; K tiles 4..7 are in flight or landed
-        for (int tr = 1; tr < trips - 1; ++tr)
-            pipe_trip<false, false>(acc, r0, r1, P, S, S, false, R, lds, tr * NST, nkt);
-
+    // one tile's last trip, then its epilogue; returns false after the last tile
+    auto finish_tile = [&](int t, auto post_tag, int kt0) {
+        constexpr bool POST = decltype(post_tag)::value;
         // the last trip streams K tiles 0..3 of the next tile into stages 0..3
-        // (nkt % 4 == 0, so they are the stages those K tiles use) and ends with
-        // the next tile's K tile 0 in r0
+        // (every tile runs a multiple of 4 K tiles, so K tile k of every tile
+        // lives in stage k % 4) and ends with the next tile's K tile 0 in r0
         const int64_t em0 = m0, en0 = n0;
         const int tnext = t + G;
         const bool more = tnext < total;
@@ -849,7 +849,7 @@ __global__ __launch_bounds__(256, 1) void gemm_persist_kernel(const uint8_t* __r
         m0 = (int64_t)tm * PBM;
         n0 = (int64_t)tn * PBN;
         const TileSrc Sn = tile_src(aq, as, bq, bs, M, N, nkt, kt2, m0, n0, wave);
-        pipe_trip<false, true>(acc, r0, r1, P, S, Sn, more, R, lds, (trips - 1) * NST, nkt);
+        pipe_trip<POST, true>(acc, r0, r1, P, S, Sn, more, R, lds, kt0, nkt);
         S = Sn;
 
         // stage 0 (the next tile's K tile 0, now in r0) is free until the next
@@ -863,10 +863,26 @@ __global__ __launch_bounds__(256, 1) void gemm_persist_kernel(const uint8_t* __r
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
         order_point();
-        if (!more) break;
-        t = tnext;
-        // trip 0 of the next tile; its first three waits allow for the 32 stores
-        pipe_trip<true, false>(acc, r0, r1, P, S, S, false, R, lds, 0, nkt);
+        return more;
+    };
+
+    if constexpr (SINGLE) {
+        // one trip per tile (K <= 512): the first tile's trip is not POST, the others are
+        if (finish_tile(slot, std::false_type{}, 0)) {
+            for (int t = slot + G;; t += G)
+                if (!finish_tile(t, std::true_type{}, 0)) break;
+        }
+    } else {
+        pipe_trip<false, false>(acc, r0, r1, P, S, S, false, R, lds, 0, nkt);
+        for (int t = slot;;) {
+            // trip 0 of tile t is done; K tiles 4..7 are in flight or landed
+            for (int tr = 1; tr < trips - 1; ++tr)
+                pipe_trip<false, false>(acc, r0, r1, P, S, S, false, R, lds, tr * NST, nkt);
+            if (!finish_tile(t, std::false_type{}, (trips - 1) * NST)) break;
+            t += G;
+            // trip 0 of the next tile; its first three waits allow for the 32 stores
+            pipe_trip<true, false>(acc, r0, r1, P, S, S, false, R, lds, 0, nkt);
+        }
     }
     // drain the last (empty) prefetch and the last stores
     wait_vmcnt<0>();
@@ -895,16 +911,14 @@ extern "C" hipError_t mx_launch_gemm(const void* aq, const void* as, const void*
         if (tiles_m * tiles_n > 0x7FFFFFFF) return hipErrorInvalidValue;
         const int group_m = 8;
         const int64_t nkt = (K + mx::PBK - 1) / mx::PBK;
-        // persistent kernel: needs K a multiple of 512 with at least two trips of 4 K tiles,
-        // 16-byte aligned output rows, N % 8 == 0, and a tile's output bytes (256 rows)
-        // addressable by a 31-bit buffer offset
-        const bool persist = nkt % 4 == 0 && nkt >= 8 && (reinterpret_cast<uintptr_t>(out) & 15u) == 0 &&
-                             (ldo & 7) == 0 &&
-                             (N & 7) == 0 &&
+        // persistent kernel: needs 16-byte aligned output rows, N % 8 == 0, and a tile's output
+        // bytes (256 rows) addressable by a 31-bit buffer offset
+        const bool persist = (reinterpret_cast<uintptr_t>(out) & 15u) == 0 && (ldo & 7) == 0 && (N & 7) == 0 &&
                              (int64_t)mx::PBM * ldo * 2 < 0x7FFFFFF0ll && getenv_persist() != 0;
         if (persist) {
             const int64_t grid = std::min<int64_t>(tiles_m * tiles_n, mx::num_cus());
-            hipLaunchKernelGGL(mx::gemm_persist_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+            auto kern = nkt <= mx::NST ? mx::gemm_persist_kernel<true> : mx::gemm_persist_kernel<false>;
+            hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, stream,
                                static_cast<const uint8_t*>(aq), static_cast<const uint8_t*>(as),
                                static_cast<const uint8_t*>(bq), static_cast<const uint8_t*>(bs), (int)M, (int)N,
                                (int)K, static_cast<uint16_t*>(out), ldo, (int)tiles_m, (int)tiles_n, group_m);
