@@ -141,24 +141,26 @@ def alloc_projection(name, M, Nn, K, a, w, g, mx, torch, dev):
 
 
 def time_ops(ops, steps, warmup, stream, torch, N, per_kernel=True):
-    """Warm up, then time `steps` passes over `ops` (events per kernel if asked).
+    """Warm up, then time `steps` passes over `ops` on `stream`.  With per_kernel, one event
+    goes before the first launch and after every launch, so kernel i is timed between
+    events i and i+1 (no extra gaps between launches).
     Returns (ms per pass, [average ms per op] or None)."""
 
     def run(events):
+        if events is not None:
+            events[0].record(stream)
         for i, (_, label, launch, _, _) in enumerate(ops):
-            if events is not None:
-                events[i][0].record(stream)
             st = launch()
             if st != 0:
                 raise N.Mxfp4Error(st, label)
             if events is not None:
-                events[i][1].record(stream)
+                events[i + 1].record(stream)
 
     for _ in range(warmup):
         run(None)
     torch.cuda.synchronize()
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in ops]
-          for _ in range(steps)] if per_kernel else None
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(steps)] \
+        if per_kernel else None
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
@@ -169,7 +171,7 @@ def time_ops(ops, steps, warmup, stream, torch, N, per_kernel=True):
     ms = start.elapsed_time(end) / steps
     if not per_kernel:
         return ms, None
-    return ms, [sum(ev[s_][i][0].elapsed_time(ev[s_][i][1]) for s_ in range(steps)) / steps for i in range(len(ops))]
+    return ms, [sum(ev[s_][i].elapsed_time(ev[s_][i + 1]) for s_ in range(steps)) / steps for i in range(len(ops))]
 
 
 def ragged_sweep(args, torch, mx, N, W, L, dev):

@@ -4,6 +4,9 @@ Two uses:
 
 * ``kernel-stats``: turn a ``--kernel-trace --stats`` kernel_stats CSV into a
   short markdown table (calls, total / average / min / max duration).
+* ``sweep-table``: turn the JSON line of ``bench.py --workload ragged`` into a
+  markdown table (per combination: step time, each kernel's time and rate,
+  and its fraction of the roofline that bounds it).
 * ``traffic``: from two ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs over
   the benchmark (and the same two counters over a plain copy of known size),
   write the per-launch HBM traffic of one kernel as JSON.  The counters are
@@ -13,7 +16,8 @@ Two uses:
   is unchanged.
 
 Usage:
-  python -m mxfp4_block_scaled_cast_amd.rocprof_summary kernel-stats STATS_CSV OUT_MD --command "..."
+  python -m mxfp4_block_scaled_cast_amd.rocprof_summary kernel-stats STATS_CSV OUT_MD --command "..." [--include REGEX]
+  python -m mxfp4_block_scaled_cast_amd.rocprof_summary sweep-table BENCH_JSON OUT_MD --command "..."
   python -m mxfp4_block_scaled_cast_amd.rocprof_summary traffic --kernel REGEX --fetch CSV --write CSV \
       --copy-fetch CSV --copy-write CSV --copy-bytes N --out OUT_JSON --command "..."
 """
@@ -26,8 +30,8 @@ import re
 import statistics
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-GEMM_SOURCES = [os.path.join(PKG, "csrc", "gemm.hip"), os.path.join(PKG, "csrc", "mx_device.h")]
-CAST_SOURCES = [os.path.join(PKG, "csrc", "cast.hip"), os.path.join(PKG, "csrc", "mx_device.h")]
+GEMM_SOURCES = [os.path.join(PKG, "csrc", f) for f in ("gemm.hip", "mx_device.h", "mx_host.h")]
+CAST_SOURCES = [os.path.join(PKG, "csrc", f) for f in ("cast.hip", "mx_device.h", "mx_host.h")]
 
 
 def source_hash(paths):
@@ -38,8 +42,8 @@ def source_hash(paths):
     return h.hexdigest()[:16]
 
 
-def kernel_stats(csv_path, out_md, command):
-    rows = list(csv.DictReader(open(csv_path)))
+def kernel_stats(csv_path, out_md, command, include=None):
+    rows = [r for r in csv.DictReader(open(csv_path)) if include is None or re.search(include, r["Name"])]
     lines = ["# rocprofv3 kernel statistics", "", "Command:", "", "```", command, "```", "",
              "| kernel | calls | total ms | average us | min us | max us | % |", "|---|---|---|---|---|---|---|"]
     for r in rows:
@@ -48,6 +52,27 @@ def kernel_stats(csv_path, out_md, command):
         lines.append("| %s | %s | %.3f | %.1f | %.1f | %.1f | %.1f |" % (
             name, r["Calls"], float(r["TotalDurationNs"]) / 1e6, float(r["AverageNs"]) / 1e3,
             float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def sweep_table(json_path, out_md, command):
+    d = json.load(open(json_path))
+    kinds = ["cast_dual(A)", "cast_dual(W)", "fwd", "cast_dual(dOut)", "dA", "dB"]
+    lines = ["# Edge / ragged sweep: one training step per (M, N, K)", "", "Command:", "", "```", command, "```", "",
+             "Each cell: kernel time in us, its rate (TFLOP/s for GEMMs, GB/s for casts) and, in brackets, the "
+             "fraction of the roofline that bounds it (ideal time at 10.1 PFLOP/s or 8 TB/s, whichever is "
+             "longer, over the measured time).", "",
+             "Whole sweep: %.2f ms for %.1f TFLOP, %.1f TFLOP/s." % (d["ms_per_step"], d["config"]["step_tflop"],
+                                                                    d["value"]), "",
+             "| M | N | K | step us | " + " | ".join(kinds) + " |", "|---|---|---|---|" + "---|" * len(kinds)]
+    for c in d["per_combo"]:
+        cells = []
+        for k in kinds:
+            x = c["kernels"][k]
+            rate = ("%.0f T" % x["tflops"]) if "tflops" in x else ("%.0f GB/s" % x["gbps"])
+            cells.append("%.1f, %s (%.2f)" % (x["ms"] * 1e3, rate, x["roofline_frac"]))
+        lines.append("| %d | %d | %d | %.1f | %s |" % (c["M"], c["N"], c["K"], c["ms_step"] * 1e3, " | ".join(cells)))
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -90,6 +115,11 @@ def main():
     k.add_argument("csv")
     k.add_argument("out")
     k.add_argument("--command", required=True)
+    k.add_argument("--include", default=None, help="only kernels whose name matches this regex")
+    w = sub.add_parser("sweep-table")
+    w.add_argument("json")
+    w.add_argument("out")
+    w.add_argument("--command", required=True)
     t = sub.add_parser("traffic")
     t.add_argument("--kernel", required=True)
     # the runtime's copy kernel only: the fill that initialises the source reads nothing
@@ -104,7 +134,9 @@ def main():
     t.add_argument("--command", required=True)
     a = p.parse_args()
     if a.cmd == "kernel-stats":
-        kernel_stats(a.csv, a.out, a.command)
+        kernel_stats(a.csv, a.out, a.command, a.include)
+    elif a.cmd == "sweep-table":
+        sweep_table(a.json, a.out, a.command)
     else:
         traffic(a)
 
