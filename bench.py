@@ -50,6 +50,8 @@ def parse():
     p.add_argument("--workload", default="llama8b_mlp", choices=sorted(WORKLOADS))
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target wall time of the CPU-oracle sample (0 skips the CPU baseline)")
+    p.add_argument("--cached-weights", action="store_true",
+                   help="weights quantized once before timing (WeightWorkspace reuse): the step skips W's dual cast")
     p.add_argument("--no-kernel-events", action="store_true",
                    help="time only the whole step (no per-kernel events)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -96,8 +98,9 @@ def gemm_roofline(m, n, k):
     return flops, nbytes, ("mfma" if t_mfma >= t_hbm else "hbm"), max(t_mfma, t_hbm)
 
 
-def step_ops(P, L, sp, N):
-    """The training step of one projection: (kind, label, launch, work, roofline-ideal seconds)."""
+def step_ops(P, L, sp, N, cached_weights=False):
+    """The training step of one projection: (kind, label, launch, work, roofline-ideal seconds).
+    With cached_weights, W's copies are made once beforehand and the step has no W cast."""
 
     def cast_dual(x, row, col):
         R, C = x.shape
@@ -111,8 +114,10 @@ def step_ops(P, L, sp, N):
 
     M, Nn, K, name = P["M"], P["N"], P["K"], P["name"]
     ops = []
-    for label, x, row, col in (("cast_dual(A)", P["a"], P["a_row"], P["a_col"]),
-                               ("cast_dual(W)", P["w"], P["w_row"], P["w_col"])):
+    casts = [("cast_dual(A)", P["a"], P["a_row"], P["a_col"])]
+    if not cached_weights:
+        casts.append(("cast_dual(W)", P["w"], P["w_row"], P["w_col"]))
+    for label, x, row, col in casts:
         nb = 3.0625 * x.shape[0] * x.shape[1]
         ops.append(("cast", name + "." + label, cast_dual(x, row, col), nb, nb / (HBM_PEAK_GBPS * 1e9)))
     fl, _, _, t = gemm_roofline(M, Nn, K)
@@ -140,11 +145,13 @@ def alloc_projection(name, M, Nn, K, a, w, g, mx, torch, dev):
     return P
 
 
-def time_ops(ops, steps, warmup, stream, torch, N, per_kernel=True):
+def time_ops(ops, steps, warmup, stream, torch, N, per_kernel=True, before_step=None):
     """Warm up, then time `steps` passes over `ops` on `stream`.  With per_kernel, one event
     goes before the first launch and after every launch, so kernel i is timed between
-    events i and i+1 (no extra gaps between launches).
-    Returns (ms per pass, [average ms per op] or None)."""
+    events i and i+1 (no extra gaps between launches).  `before_step` (e.g. a cache flush)
+    runs before every timed pass, outside the events; the pass time is then the sum of the
+    per-pass event spans instead of one bracket around all passes.
+    Returns (ms per pass, per-op lists of per-pass ms, or None)."""
 
     def run(events):
         if events is not None:
@@ -157,21 +164,91 @@ def time_ops(ops, steps, warmup, stream, torch, N, per_kernel=True):
                 events[i + 1].record(stream)
 
     for _ in range(warmup):
+        if before_step is not None:
+            before_step()
         run(None)
     torch.cuda.synchronize()
+    use_events = per_kernel or before_step is not None
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(steps)] \
-        if per_kernel else None
+        if use_events else None
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for s_ in range(steps):
-        run(ev[s_] if per_kernel else None)
+        if before_step is not None:
+            before_step()
+        run(ev[s_] if use_events else None)
     end.record(stream)
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
+    if before_step is not None:
+        ms = sum(ev[s_][0].elapsed_time(ev[s_][-1]) for s_ in range(steps)) / steps
+    else:
+        ms = start.elapsed_time(end) / steps
     if not per_kernel:
         return ms, None
-    return ms, [sum(ev[s_][i].elapsed_time(ev[s_][i + 1]) for s_ in range(steps)) / steps for i in range(len(ops))]
+    return ms, [[ev[s_][i].elapsed_time(ev[s_][i + 1]) for s_ in range(steps)] for i in range(len(ops))]
+
+
+def percentiles(xs):
+    import numpy as np
+    p10, p50, p90 = np.percentile(np.asarray(xs, dtype=np.float64), [10, 50, 90])
+    return {"p10": round(float(p10), 4), "p50": round(float(p50), 4), "p90": round(float(p90), 4)}
+
+
+class ClockSampler:
+    """Samples the GPU's shader clock (MHz) and board power (W) from sysfs in a thread.
+    Reads the first card exposing pp_dpm_sclk; `summary()` is None where sysfs has neither."""
+
+    def __init__(self, period_s=0.002):
+        import glob
+        import threading
+        cards = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.sclk = cards[0] if cards else None
+        base = os.path.dirname(self.sclk) if self.sclk else None
+        powers = sorted(glob.glob(os.path.join(base, "hwmon", "hwmon*", "power1_input"))) if base else []
+        self.power = powers[0] if powers else None
+        self.period = period_s
+        self.mhz, self.watts = [], []
+        self._stop = threading.Event()
+        self._t = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        if self.sclk:
+            try:
+                for line in open(self.sclk):
+                    if line.rstrip().endswith("*"):
+                        self.mhz.append(float(line.split(":")[1].strip().split("M")[0]))
+            except (OSError, ValueError, IndexError):
+                pass
+        if self.power:
+            try:
+                self.watts.append(float(open(self.power).read()) / 1e6)
+            except (OSError, ValueError):
+                pass
+
+    def _run(self):
+        while not self._stop.is_set():
+            self._read()
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._t.join()
+
+    def summary(self):
+        import numpy as np
+        if not self.mhz and not self.watts:
+            return None
+        out = {"samples": len(self.mhz)}
+        if self.mhz:
+            out["sclk_mhz"] = {"p50": float(np.median(self.mhz)), "min": min(self.mhz), "max": max(self.mhz)}
+        if self.watts:
+            out["power_w"] = {"p50": round(float(np.median(self.watts)), 1), "max": round(max(self.watts), 1)}
+        return out
 
 
 def ragged_sweep(args, torch, mx, N, W, L, dev):
@@ -179,6 +256,7 @@ def ragged_sweep(args, torch, mx, N, W, L, dev):
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
     cid = W.CONFIG_IDS["ragged"]
+    flush = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
     combos = []
     tot_flops = tot_ms = 0.0
     for ci, (M, Nn, K) in enumerate(W.ragged_combos()):
@@ -188,12 +266,15 @@ def ragged_sweep(args, torch, mx, N, W, L, dev):
         g = W.ragged_values_torch((M, Nn), seed + W.DOUT, dev).view(torch.bfloat16)
         P = alloc_projection("M%d-N%d-K%d" % (M, Nn, K), M, Nn, K, a, w, g, mx, torch, dev)
         ops = step_ops(P, L, sp, N)
-        ms, per = time_ops(ops, args.steps, args.warmup, stream, torch, N)
+        # a 1 GiB read before every timed step: small operands would otherwise stay in the 256 MB MALL
+        # (a read leaves clean lines, so the step pays no write-back of the flush)
+        ms, per = time_ops(ops, args.steps, args.warmup, stream, torch, N, before_step=lambda: torch.sum(flush))
         fl = 6.0 * M * Nn * K
         tot_flops += fl
         tot_ms += ms
         kernels = {}
-        for (kind, label, _, work, ideal), t in zip(ops, per):
+        for (kind, label, _, work, ideal), ts in zip(ops, per):
+            t = sum(ts) / len(ts)
             rate = work / (t * 1e-3)
             kernels[label.split(".", 1)[1]] = {
                 "ms": round(t, 4), ("tflops" if kind == "gemm" else "gbps"): round(rate / (1e12 if kind == "gemm" else 1e9), 1),
@@ -207,7 +288,7 @@ def ragged_sweep(args, torch, mx, N, W, L, dev):
             "warmup": args.warmup, "ms_per_step": round(tot_ms, 4), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "mxfp4", "data": "synthetic",
             "config": {"workload": WORKLOADS["ragged"], "combos": len(combos),
-                       "step_tflop": round(tot_flops / 1e12, 4)},
+                       "step_tflop": round(tot_flops / 1e12, 4), "cache": "1 GiB read before every timed step"},
             "per_combo": combos}
 
 
@@ -260,7 +341,12 @@ def main():
     step_flops = 0.0
     for P in projs:
         step_flops += 6.0 * P["M"] * P["N"] * P["K"]
-        ops += step_ops(P, L, sp, N)
+        ops += step_ops(P, L, sp, N, cached_weights=args.cached_weights)
+        if args.cached_weights:
+            # the WeightWorkspace fill: W's dual cast once, outside the timed region
+            R, C = P["w"].shape
+            N.check(L.mxfp4_cast_dual(P["w"].data_ptr(), R, C, C, P["w_row"].q.data_ptr(), P["w_row"].s.data_ptr(),
+                                      P["w_col"].q.data_ptr(), P["w_col"].s.data_ptr(), sp), "mxfp4_cast_dual")
 
     use_events = not args.no_kernel_events
     ms_per_step, per = time_ops(ops, args.steps, args.warmup, stream, torch, N, per_kernel=use_events)
@@ -270,10 +356,12 @@ def main():
     gemm_launches = 0
     gemm_work = cast_bytes = 0.0
     if use_events:
-        for (kind, label, _, work, _), avg in zip(ops, per):
+        for (kind, label, _, work, _), ts in zip(ops, per):
+            avg = sum(ts) / len(ts)
             rate = work / (avg * 1e-3)
             per_op[label] = {"ms": round(avg, 4),
-                             ("tflops" if kind == "gemm" else "gbps"): round(rate / (1e12 if kind == "gemm" else 1e9), 1)}
+                             ("tflops" if kind == "gemm" else "gbps"): round(rate / (1e12 if kind == "gemm" else 1e9), 1),
+                             **percentiles(ts)}
             if kind == "gemm":
                 gemm_ms += avg
                 gemm_launches += 1
@@ -296,7 +384,8 @@ def main():
         "vs_baseline": None,
         "dtype": "mxfp4",
         "data": "synthetic",
-        "config": {"workload": WORKLOADS[args.workload],
+        "config": {"workload": WORKLOADS[args.workload] + (
+                       "; weights quantized once (cached), no W cast in the step" if args.cached_weights else ""),
                    "projections": [[P["name"], P["M"], P["N"], P["K"]] for P in projs],
                    "step_tflop": round(step_flops / 1e12, 4)},
         "frac_of_fp4_peak": round(value / FP4_PEAK_TFLOPS, 4),
@@ -315,6 +404,17 @@ def main():
                               "unit": "TFLOP/s", "frac": round(gemm_tflops / FP4_PEAK_TFLOPS, 4),
                               "avg_launch_ms": round(avg_gemm_ms, 4),
                               "flop_per_launch": gemm_work / gemm_launches, "traffic": measured_traffic()}
+        # sustained clock and power over ~0.5 s of further steps (not part of the timed region)
+        with ClockSampler() as cs:
+            t_end = time.time() + 0.5
+            while time.time() < t_end:
+                time_ops(ops, 5, 0, stream, torch, N, per_kernel=False)
+        clk = cs.summary()
+        result["clock"] = clk
+        if clk and "sclk_mhz" in clk:
+            peak_clk = FP4_PEAK_TFLOPS * clk["sclk_mhz"]["p50"] / 2400.0
+            result["roofline"]["peak_at_clock"] = round(peak_clk, 1)
+            result["roofline"]["frac_at_clock"] = round(gemm_tflops / peak_clk, 4)
 
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(host_inputs, args.cpu_seconds)

@@ -170,6 +170,43 @@ int gemm_fp4_bf16_fwd(const void* a, const void* w, int64_t M, int64_t N, int64_
 int gemm_fp4_bf16_bwd(const void* dout, int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes, void* da,
                       void* dw, hipStream_t stream);
 
+/*
+ * Cached weight quantization (jax-aiter README, Quick start: a weight
+ * quantizer, MXFP4Quantizer.for_weight(), turns W into an Mxfp4Tensor with
+ * row and column copies, and WeightWorkspace.get_or_quantize(...) keeps it
+ * for later GEMMs).  These are gemm_fp4_bf16_fwd / _bwd with W's cast
+ * skipped: the caller passes W's copies, made once by mxfp4_cast_dual(w, N,
+ * K, ...) and reused while W is unchanged (inference, gradient-accumulation
+ * micro-batches).
+ *
+ * Workspace without W's slots: A's row (and, training, column) copy and
+ * dOut's copies.  Returns 0 for invalid sizes.
+ */
+size_t gemm_fp4_bf16_workspace_bytes_qw(int64_t M, int64_t N, int64_t K, int training);
+
+/*
+ * Forward with a pre-quantized weight:
+ *   out[M, N] = bf16( cast(a)[M, K] . W_row^T )
+ * w_row_q, w_row_s : W's row copy, MX operand (N rows, K), 16-byte aligned,
+ *                    read only.  Other arguments, requirements and errors as
+ *                    gemm_fp4_bf16_fwd, with ws_bytes >=
+ *                    gemm_fp4_bf16_workspace_bytes_qw(M, N, K, training).
+ */
+int gemm_fp4_bf16_fwd_qw(const void* a, const void* w_row_q, const void* w_row_s, int64_t M, int64_t N, int64_t K,
+                         void* out, void* ws, size_t ws_bytes, int training, hipStream_t stream);
+
+/*
+ * Backward with a pre-quantized weight (ws from a training
+ * gemm_fp4_bf16_fwd_qw with the same M, N, K):
+ *   da[M, K] = bf16( cast(dout) . W )  on W's column copy
+ *   dw[N, K] = bf16( cast(dout)^T . A )
+ * w_col_q, w_col_s : W's column copy, MX operand (K rows, ceil(N/32)*32),
+ *                    needed only when da != NULL.  Otherwise as
+ *                    gemm_fp4_bf16_bwd.
+ */
+int gemm_fp4_bf16_bwd_qw(const void* dout, const void* w_col_q, const void* w_col_s, int64_t M, int64_t N, int64_t K,
+                         void* ws, size_t ws_bytes, void* da, void* dw, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -5,9 +5,12 @@ include/mxfp4.h); this package only marshals arguments.  Importing it does not
 load the library; the first call does, and fails loudly if it is not built.
 """
 from .api import (Mxfp4Tensor, MxOperand, cast, cast_dual, empty_operand, gemm_fp4_bf16, gemm_fp4_bf16_bwd,
-                  gemm_fp4_bf16_fwd, gemm_nn, gemm_nt, workspace_bytes)
+                  gemm_fp4_bf16_bwd_qw, gemm_fp4_bf16_fwd, gemm_fp4_bf16_fwd_qw, gemm_nn, gemm_nt, workspace_bytes,
+                  workspace_bytes_qw)
+from .quant import MXFP4Quantizer, WeightWorkspace
 from ._native import Mxfp4Error, library_path
 
 __all__ = ["Mxfp4Tensor", "MxOperand", "cast", "cast_dual", "empty_operand", "gemm_fp4_bf16",
-           "gemm_fp4_bf16_fwd", "gemm_fp4_bf16_bwd", "gemm_nn", "gemm_nt", "workspace_bytes", "Mxfp4Error",
+           "gemm_fp4_bf16_fwd", "gemm_fp4_bf16_bwd", "gemm_fp4_bf16_fwd_qw", "gemm_fp4_bf16_bwd_qw", "gemm_nn",
+           "gemm_nt", "workspace_bytes", "workspace_bytes_qw", "MXFP4Quantizer", "WeightWorkspace", "Mxfp4Error",
            "library_path"]

@@ -29,6 +29,9 @@ SIGNATURES = [
     ("gemm_fp4_bf16_workspace_bytes", _sz, [_i64, _i64, _i64, _i32]),
     ("gemm_fp4_bf16_fwd", _i32, [_p, _p, _i64, _i64, _i64, _p, _p, _sz, _i32, _p]),
     ("gemm_fp4_bf16_bwd", _i32, [_p, _i64, _i64, _i64, _p, _sz, _p, _p, _p]),
+    ("gemm_fp4_bf16_workspace_bytes_qw", _sz, [_i64, _i64, _i64, _i32]),
+    ("gemm_fp4_bf16_fwd_qw", _i32, [_p, _p, _p, _i64, _i64, _i64, _p, _p, _sz, _i32, _p]),
+    ("gemm_fp4_bf16_bwd_qw", _i32, [_p, _p, _p, _i64, _i64, _i64, _p, _sz, _p, _p, _p]),
 ]
 
 STATUS = {0: "MXFP4_OK", -1: "MXFP4_EINVAL", -2: "MXFP4_EALIGN", -3: "MXFP4_EDEVICE",

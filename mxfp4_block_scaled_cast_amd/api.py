@@ -140,29 +140,89 @@ def gemm_fp4_bf16_bwd(dout, M, Nn, K, ws, need_da=True, need_dw=True, da=None, d
     return (da if need_da else None), (dw if need_dw else None)
 
 
+def workspace_bytes_qw(M, Nn, K, training=True):
+    return int(N.lib().gemm_fp4_bf16_workspace_bytes_qw(M, Nn, K, 1 if training else 0))
+
+
+def _check_weight_fp4(w_fp4, Nn, K, training):
+    if w_fp4.shape != (Nn, K):
+        raise ValueError("w_fp4 holds a [%d, %d] weight, expected [%d, %d]" % (w_fp4.shape + (Nn, K)))
+    if training and w_fp4.col is None:
+        raise ValueError("training needs the weight's column copy: quantize with columnwise=True")
+
+
+def gemm_fp4_bf16_fwd_qw(a, w_fp4, training=True, ws=None, out=None):
+    """Forward with a pre-quantized weight (Mxfp4Tensor of W [N, K]) -> (out [M, N], ws)."""
+    _check_bf16_matrix(a, "a")
+    if not a.is_contiguous():
+        raise ValueError("a must be contiguous")
+    M, K = a.shape
+    Nn = w_fp4.shape[0]
+    _check_weight_fp4(w_fp4, Nn, K, training)
+    nbytes = workspace_bytes_qw(M, Nn, K, training)
+    if ws is None:
+        ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=a.device)
+    if out is None:
+        out = torch.empty((M, Nn), dtype=torch.bfloat16, device=a.device)
+    r = w_fp4.row
+    st = N.lib().gemm_fp4_bf16_fwd_qw(a.data_ptr(), r.q.data_ptr(), r.s.data_ptr(), M, Nn, K, out.data_ptr(),
+                                      ws.data_ptr(), ws.numel(), 1 if training else 0, _stream(a.device))
+    N.check(st, "gemm_fp4_bf16_fwd_qw")
+    return out, ws
+
+
+def gemm_fp4_bf16_bwd_qw(dout, w_fp4, M, Nn, K, ws, need_da=True, need_dw=True, da=None, dw=None):
+    """Backward of gemm_fp4_bf16_fwd_qw (W's column copy from w_fp4) -> (da, dw)."""
+    _check_bf16_matrix(dout, "dout")
+    if not dout.is_contiguous():
+        dout = dout.contiguous()
+    if need_da and da is None:
+        da = torch.empty((M, K), dtype=torch.bfloat16, device=dout.device)
+    if need_dw and dw is None:
+        dw = torch.empty((Nn, K), dtype=torch.bfloat16, device=dout.device)
+    c = w_fp4.col
+    st = N.lib().gemm_fp4_bf16_bwd_qw(dout.data_ptr(), c.q.data_ptr() if c is not None else None,
+                                      c.s.data_ptr() if c is not None else None, M, Nn, K, ws.data_ptr(), ws.numel(),
+                                      da.data_ptr() if need_da else None, dw.data_ptr() if need_dw else None,
+                                      _stream(dout.device))
+    N.check(st, "gemm_fp4_bf16_bwd_qw")
+    return (da if need_da else None), (dw if need_dw else None)
+
+
 class _GemmFp4Bf16(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, a, w):
+    def forward(ctx, a, w, w_fp4):
         training = bool(ctx.needs_input_grad[0] or ctx.needs_input_grad[1])
-        out, ws = gemm_fp4_bf16_fwd(a, w, training=training)
+        if w_fp4 is None:
+            out, ws = gemm_fp4_bf16_fwd(a, w, training=training)
+        else:
+            out, ws = gemm_fp4_bf16_fwd_qw(a, w_fp4, training=training)
         ctx.dims = (a.shape[0], w.shape[0], a.shape[1])
         ctx.ws = ws if training else None
+        ctx.w_fp4 = w_fp4
         return out
 
     @staticmethod
     def backward(ctx, dout):
         M, Nn, K = ctx.dims
-        da, dw = gemm_fp4_bf16_bwd(dout, M, Nn, K, ctx.ws, ctx.needs_input_grad[0], ctx.needs_input_grad[1])
+        if ctx.w_fp4 is None:
+            da, dw = gemm_fp4_bf16_bwd(dout, M, Nn, K, ctx.ws, ctx.needs_input_grad[0], ctx.needs_input_grad[1])
+        else:
+            da, dw = gemm_fp4_bf16_bwd_qw(dout, ctx.w_fp4, M, Nn, K, ctx.ws, ctx.needs_input_grad[0],
+                                          ctx.needs_input_grad[1])
         ctx.ws = None
-        return da, dw
+        ctx.w_fp4 = None
+        return da, dw, None
 
 
-def gemm_fp4_bf16(a, w):
+def gemm_fp4_bf16(a, w, w_fp4: Optional[Mxfp4Tensor] = None):
     """BF16 in/out MXFP4 GEMM, out = a . w^T, differentiable (FP4 forward, FP4 dA, FP4 dB).
 
     a: [..., K] bfloat16, w: [N, K] bfloat16 -> [..., N] bfloat16.
+    w_fp4: w already quantized (e.g. from WeightWorkspace.get_or_quantize with a weight
+    quantizer); its copies replace w's cast in the forward and in dA.  w still receives dW.
     """
     lead = a.shape[:-1]
     a2 = a.reshape(-1, a.shape[-1]).contiguous()
-    out = _GemmFp4Bf16.apply(a2, w.contiguous())
+    out = _GemmFp4Bf16.apply(a2, w.contiguous(), w_fp4)
     return out.reshape(*lead, w.shape[0])

@@ -87,7 +87,8 @@ struct Workspace {
     int64_t total;
 };
 
-Workspace workspace_layout(int64_t M, int64_t N, int64_t K, bool training) {
+// with_w == false: W's copies come from the caller (pre-quantized weight), no W slots.
+Workspace workspace_layout(int64_t M, int64_t N, int64_t K, bool training, bool with_w = true) {
     Workspace w{};
     int64_t off = 0;
     auto take = [&off](int64_t bytes) {
@@ -98,16 +99,16 @@ Workspace workspace_layout(int64_t M, int64_t N, int64_t K, bool training) {
     const OperandSizes a_row = operand_sizes(M, K), w_row = operand_sizes(N, K);
     w.a_row_q = take(a_row.q);
     w.a_row_s = take(a_row.s);
-    w.w_row_q = take(w_row.q);
-    w.w_row_s = take(w_row.s);
+    w.w_row_q = take(with_w ? w_row.q : 0);
+    w.w_row_s = take(with_w ? w_row.s : 0);
     if (training) {
         const int64_t Mp = round_up(M, 32), Np = round_up(N, 32);
         const OperandSizes a_col = operand_sizes(K, Mp), w_col = operand_sizes(K, Np);
         const OperandSizes g_row = operand_sizes(M, N), g_col = operand_sizes(N, Mp);
         w.a_col_q = take(a_col.q);
         w.a_col_s = take(a_col.s);
-        w.w_col_q = take(w_col.q);
-        w.w_col_s = take(w_col.s);
+        w.w_col_q = take(with_w ? w_col.q : 0);
+        w.w_col_s = take(with_w ? w_col.s : 0);
         w.g_row_q = take(g_row.q);
         w.g_row_s = take(g_row.s);
         w.g_col_q = take(g_col.q);
@@ -192,51 +193,58 @@ size_t gemm_fp4_bf16_workspace_bytes(int64_t M, int64_t N, int64_t K, int traini
     return (size_t)workspace_layout(M, N, K, training != 0).total;
 }
 
-int gemm_fp4_bf16_fwd(const void* a, const void* w, int64_t M, int64_t N, int64_t K, void* out, void* ws,
-                      size_t ws_bytes, int training, hipStream_t stream) {
-    const bool train = training != 0;
+size_t gemm_fp4_bf16_workspace_bytes_qw(int64_t M, int64_t N, int64_t K, int training) {
+    if (validate_step_sizes(M, N, K, training != 0) != MXFP4_OK) return 0;
+    return (size_t)workspace_layout(M, N, K, training != 0, false).total;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Forward: cast A (dual when training, its column copy kept in ws), then the
+// GEMM with W's row copy -- cast here from bf16 w (own_w), or given.
+int step_fwd(const void* a, bool own_w, const void* w, const void* w_row_q, const void* w_row_s, int64_t M, int64_t N,
+             int64_t K, void* out, void* ws, size_t ws_bytes, bool train, hipStream_t stream) {
     int st = validate_step_sizes(M, N, K, train);
     if (st != MXFP4_OK) return st;
     if (M == 0 || N == 0) return MXFP4_OK;
     if (!out) return MXFP4_EINVAL;
     if ((reinterpret_cast<uintptr_t>(out) & 1u) != 0) return MXFP4_EALIGN;
-    const Workspace L = workspace_layout(M, N, K, train);
+    const Workspace L = workspace_layout(M, N, K, train, own_w);
+    char* base = static_cast<char*>(ws);
+    const void* wq = own_w ? base + L.w_row_q : w_row_q;
+    const void* wsc = own_w ? base + L.w_row_s : w_row_s;
     if (K > 0) {
-        if (!a || !w || !ws) return MXFP4_EINVAL;
-        if (!aligned16(a) || !aligned16(w) || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return MXFP4_EALIGN;
+        if (!a || !ws || (own_w ? !w : (!w_row_q || !w_row_s))) return MXFP4_EINVAL;
+        if (!aligned16(a) || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return MXFP4_EALIGN;
+        if (own_w ? !aligned16(w) : (!aligned16(w_row_q) || !aligned16(w_row_s))) return MXFP4_EALIGN;
         if ((int64_t)ws_bytes < L.total) return MXFP4_ESPACE;
     }
     if ((st = check_device()) != MXFP4_OK) return st;
-    char* base = static_cast<char*>(ws);
     hipError_t e = hipSuccess;
     if (K > 0) {
-        if (train) {
-            e = mx_launch_cast(a, M, K, K, base + L.a_row_q, base + L.a_row_s, base + L.a_col_q, base + L.a_col_s,
-                               true, stream);
-            if (e == hipSuccess)
-                e = mx_launch_cast(w, N, K, K, base + L.w_row_q, base + L.w_row_s, base + L.w_col_q,
-                                   base + L.w_col_s, true, stream);
-        } else {
-            e = mx_launch_cast(a, M, K, K, base + L.a_row_q, base + L.a_row_s, nullptr, nullptr, false, stream);
-            if (e == hipSuccess)
-                e = mx_launch_cast(w, N, K, K, base + L.w_row_q, base + L.w_row_s, nullptr, nullptr, false, stream);
-        }
+        e = mx_launch_cast(a, M, K, K, base + L.a_row_q, base + L.a_row_s, train ? base + L.a_col_q : nullptr,
+                           train ? base + L.a_col_s : nullptr, train, stream);
+        if (e == hipSuccess && own_w)
+            e = mx_launch_cast(w, N, K, K, base + L.w_row_q, base + L.w_row_s, train ? base + L.w_col_q : nullptr,
+                               train ? base + L.w_col_s : nullptr, train, stream);
     }
-    if (e == hipSuccess)
-        e = mx_launch_gemm(base + L.a_row_q, base + L.a_row_s, base + L.w_row_q, base + L.w_row_s, M, N, K, out, N,
-                           stream);
+    if (e == hipSuccess) e = mx_launch_gemm(base + L.a_row_q, base + L.a_row_s, wq, wsc, M, N, K, out, N, stream);
     return status_of(e);
 }
 
-int gemm_fp4_bf16_bwd(const void* dout, int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes, void* da,
-                      void* dw, hipStream_t stream) {
+// Backward: cast dOut (dual), dA = dOut . W on W's column copy (from ws, or
+// given), dW = dOut^T . A on the column copies of dOut and A.
+int step_bwd(const void* dout, bool own_w, const void* w_col_q, const void* w_col_s, int64_t M, int64_t N, int64_t K,
+             void* ws, size_t ws_bytes, void* da, void* dw, hipStream_t stream) {
     int st = validate_step_sizes(M, N, K, true);
     if (st != MXFP4_OK) return st;
     if (!ws || (!da && !dw)) return ws ? MXFP4_OK : MXFP4_EINVAL;
     if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return MXFP4_EALIGN;
     if ((da && (reinterpret_cast<uintptr_t>(da) & 1u)) || (dw && (reinterpret_cast<uintptr_t>(dw) & 1u)))
         return MXFP4_EALIGN;
-    const Workspace L = workspace_layout(M, N, K, true);
+    const Workspace L = workspace_layout(M, N, K, true, own_w);
     if ((int64_t)ws_bytes < L.total) return MXFP4_ESPACE;
     if (K == 0) return MXFP4_OK;  // dA [M, 0] and dW [N, 0] have no elements
     if (M == 0 || N == 0) {
@@ -249,18 +257,46 @@ int gemm_fp4_bf16_bwd(const void* dout, int64_t M, int64_t N, int64_t K, void* w
     }
     if (!dout) return MXFP4_EINVAL;
     if (!aligned16(dout)) return MXFP4_EALIGN;
+    if (!own_w && da) {
+        if (!w_col_q || !w_col_s) return MXFP4_EINVAL;
+        if (!aligned16(w_col_q) || !aligned16(w_col_s)) return MXFP4_EALIGN;
+    }
     if ((st = check_device()) != MXFP4_OK) return st;
     char* base = static_cast<char*>(ws);
     const int64_t Mp = round_up(M, 32);
+    const void* wq = own_w ? base + L.w_col_q : w_col_q;
+    const void* wsc = own_w ? base + L.w_col_s : w_col_s;
     hipError_t e = mx_launch_cast(dout, M, N, N, base + L.g_row_q, base + L.g_row_s, base + L.g_col_q,
                                   base + L.g_col_s, true, stream);
-    if (e == hipSuccess && da)
-        e = mx_launch_gemm(base + L.g_row_q, base + L.g_row_s, base + L.w_col_q, base + L.w_col_s, M, K, N, da, K,
-                           stream);
+    if (e == hipSuccess && da) e = mx_launch_gemm(base + L.g_row_q, base + L.g_row_s, wq, wsc, M, K, N, da, K, stream);
     if (e == hipSuccess && dw)
         e = mx_launch_gemm(base + L.g_col_q, base + L.g_col_s, base + L.a_col_q, base + L.a_col_s, N, K, Mp, dw, K,
                            stream);
     return status_of(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_fp4_bf16_fwd(const void* a, const void* w, int64_t M, int64_t N, int64_t K, void* out, void* ws,
+                      size_t ws_bytes, int training, hipStream_t stream) {
+    return step_fwd(a, true, w, nullptr, nullptr, M, N, K, out, ws, ws_bytes, training != 0, stream);
+}
+
+int gemm_fp4_bf16_bwd(const void* dout, int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes, void* da,
+                      void* dw, hipStream_t stream) {
+    return step_bwd(dout, true, nullptr, nullptr, M, N, K, ws, ws_bytes, da, dw, stream);
+}
+
+int gemm_fp4_bf16_fwd_qw(const void* a, const void* w_row_q, const void* w_row_s, int64_t M, int64_t N, int64_t K,
+                         void* out, void* ws, size_t ws_bytes, int training, hipStream_t stream) {
+    return step_fwd(a, false, nullptr, w_row_q, w_row_s, M, N, K, out, ws, ws_bytes, training != 0, stream);
+}
+
+int gemm_fp4_bf16_bwd_qw(const void* dout, const void* w_col_q, const void* w_col_s, int64_t M, int64_t N, int64_t K,
+                         void* ws, size_t ws_bytes, void* da, void* dw, hipStream_t stream) {
+    return step_bwd(dout, false, w_col_q, w_col_s, M, N, K, ws, ws_bytes, da, dw, stream);
 }
 
 }  // extern "C"

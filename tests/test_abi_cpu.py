@@ -26,7 +26,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for must in ("mxfp4_cast", "mxfp4_cast_dual", "mxfp4_gemm_nt", "mxfp4_gemm_nn", "gemm_fp4_bf16_fwd",
                  "gemm_fp4_bf16_bwd", "gemm_fp4_bf16_workspace_bytes", "mxfp4_operand_layout_of",
-                 "mxfp4_status_string"):
+                 "mxfp4_status_string", "gemm_fp4_bf16_workspace_bytes_qw", "gemm_fp4_bf16_fwd_qw",
+                 "gemm_fp4_bf16_bwd_qw"):
         assert must in names
 
 
@@ -115,6 +116,23 @@ def test_step_argument_validation():
     assert L.gemm_fp4_bf16_bwd(FAKE, 64, 64, 64, None, need, FAKE, FAKE, None) == -1
 
 
+def test_step_with_quantized_weight_argument_validation():
+    L = N.lib()
+    need = L.gemm_fp4_bf16_workspace_bytes_qw(64, 64, 64, 1)
+    assert 0 < need < L.gemm_fp4_bf16_workspace_bytes(64, 64, 64, 1)
+    assert L.gemm_fp4_bf16_workspace_bytes_qw(8, 40, 32, 1) == 0            # N % 32 in training
+    f = L.gemm_fp4_bf16_fwd_qw
+    assert f(FAKE, None, FAKE, 64, 64, 64, FAKE, FAKE, need, 1, None) == -1   # null W codes
+    assert f(FAKE, FAKE, None, 64, 64, 64, FAKE, FAKE, need, 1, None) == -1   # null W scales
+    assert f(FAKE, FAKE + 4, FAKE, 64, 64, 64, FAKE, FAKE, need, 1, None) == -2
+    assert f(FAKE, FAKE, FAKE, 64, 64, 64, FAKE, FAKE, need - 1, 1, None) == -6
+    assert f(FAKE, FAKE, FAKE, 0, 64, 64, FAKE, FAKE, 0, 1, None) == 0         # empty
+    b = L.gemm_fp4_bf16_bwd_qw
+    assert b(FAKE, None, FAKE, 64, 64, 64, FAKE, need, FAKE, None, None) == -1  # dA needs W's column copy
+    assert b(FAKE, FAKE, FAKE + 8, 64, 64, 64, FAKE, need, FAKE, None, None) == -2
+    assert b(FAKE, FAKE, FAKE, 64, 64, 64, FAKE, need - 1, FAKE, FAKE, None) == -6
+
+
 def test_workspace_size_formula():
     # row copies of A and W, plus (training) column copies of A and W and both copies of dOut
     def op(rows, k):
@@ -125,6 +143,9 @@ def test_workspace_size_formula():
     train = inf + op(K, Mp) + op(K, Nn) + op(M, Nn) + op(Nn, Mp)
     assert N.lib().gemm_fp4_bf16_workspace_bytes(M, Nn, K, 0) == inf
     assert N.lib().gemm_fp4_bf16_workspace_bytes(M, Nn, K, 1) == train
+    # with a pre-quantized weight the W copies are the caller's
+    assert N.lib().gemm_fp4_bf16_workspace_bytes_qw(M, Nn, K, 0) == inf - op(Nn, K)
+    assert N.lib().gemm_fp4_bf16_workspace_bytes_qw(M, Nn, K, 1) == train - op(Nn, K) - op(K, Nn)
 
 
 def _no_gpu():

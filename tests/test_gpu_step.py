@@ -75,3 +75,54 @@ def test_only_one_gradient():
     _, _, (g, ga) = oracle_step(a, w, dout)
     assert at.grad is None
     assert_gemm_close(bf16_to_f64(wt.grad), g, ga, "dB only")
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 512, 1024), (17, 128, 544), (1000, 2048, 4096)])
+def test_cached_weight_matches_uncached(M, N, K):
+    # the cached copies are the same casts of the same W, so every output is bit-identical,
+    # and the uncached path is the one checked against the oracle above
+    a = W.ragged_values((M, K), 11 * M + K)
+    w = W.ragged_values((N, K), 13 * N + K)
+    dout = W.ragged_values((M, N), 17 * M + N)
+    say("gemm_fp4_bf16 cached weight M=%d N=%d K=%d" % (M, N, K))
+    ws = mx.WeightWorkspace()
+    w_dev = to_device(w)
+    outs = []
+    for cached in (False, True, True):
+        at = to_device(a).requires_grad_(True)
+        wt = w_dev.clone().requires_grad_(True)
+        w_fp4 = ws.get_or_quantize(w_dev, mx.MXFP4Quantizer.for_weight(), cache_name="w") if cached else None
+        out = mx.gemm_fp4_bf16(at, wt, w_fp4=w_fp4)
+        out.backward(to_device(dout))
+        torch.cuda.synchronize()
+        outs.append((out.detach().cpu(), at.grad.cpu(), wt.grad.cpu()))
+    assert ws.misses == 1 and ws.hits == 1
+    for got in outs[1:]:
+        for x, y in zip(outs[0], got):
+            assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+def test_cached_weight_inference_and_role_checks():
+    M, N, K = 64, 96, 128
+    a = to_device(W.normal_bf16((M, K), 1.0, 61))
+    w = to_device(W.normal_bf16((N, K), 0.02, 62))
+    say("gemm_fp4_bf16 cached weight, inference")
+    w_row = mx.MXFP4Quantizer.for_weight(columnwise=False).quantize(w)
+    assert w_row.col is None
+    with torch.no_grad():
+        got = mx.gemm_fp4_bf16(a, w, w_fp4=w_row)
+        ref = mx.gemm_fp4_bf16(a, w)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    # training needs W's column copy
+    with pytest.raises(ValueError):
+        mx.gemm_fp4_bf16(a.clone().requires_grad_(True), w, w_fp4=w_row)
+    # a stale cache entry is refreshed after an in-place update of W
+    ws = mx.WeightWorkspace()
+    q1 = ws.get_or_quantize(w, mx.MXFP4Quantizer.for_weight(), cache_name="w")
+    w.mul_(2)
+    q2 = ws.get_or_quantize(w, mx.MXFP4Quantizer.for_weight(), cache_name="w")
+    torch.cuda.synchronize()
+    assert q1 is not q2 and ws.misses == 2
+    # doubling W moves every nonzero block's scale up by one (codes unchanged)
+    assert torch.equal(q1.row.q, q2.row.q)
