@@ -25,6 +25,13 @@ Canonical layouts (all row-major, no padding except where stated):
   rows past R are +0
 * GEMM: ref[m, n] = sum_k dq(a)[m, k] * dq(b)[n, k] in fp64, and
   absref[m, n] = sum_k |dq(a)[m, k] * dq(b)[n, k]|
+
+Hadamard-transformed casts (README "Quick start": grad_out is cast with a
+Hadamard transform): ``cast_rows_hadamard`` / ``cast_cols_hadamard`` apply
+the 32-point Sylvester Walsh-Hadamard matrix to every block in binary32
+(butterflies of half-width 1, 2, 4, 8, 16, each (u, w) -> (u + w, u - w)),
+divide by 2^shift and quantize by the same rule.  Used on both operands of a
+contraction, with shift 5 on one of them (H H = 32 I).
 """
 import os
 
@@ -74,6 +81,47 @@ def cast_cols(x_bits, nthreads=None):
     if rc:
         raise RuntimeError("mxo_cast_cols failed")
     return q, s
+
+
+def cast_rows_hadamard(x_bits, shift=0, nthreads=None):
+    """Row copy with each 32-block Walsh-Hadamard transformed (binary32 butterflies) and
+    divided by 2^shift before quantization.  Returns (q, s) shaped as cast_rows."""
+    x = _bits(x_bits)
+    R, C = x.shape
+    if C % 32:
+        raise ValueError("the number of columns must be a multiple of 32")
+    q = np.empty((R, C // 2), np.uint8)
+    s = np.empty((R, C // 32), np.uint8)
+    rc = native.lib().mxo_cast_rows_hadamard(x.ctypes.data, R, C, C, int(shift), q.ctypes.data, s.ctypes.data,
+                                             _threads(nthreads))
+    if rc:
+        raise RuntimeError("mxo_cast_rows_hadamard failed")
+    return q, s
+
+
+def cast_cols_hadamard(x_bits, shift=0, nthreads=None):
+    """Column copy (blocks of 32 rows, padded with +0) with the block transform.  Returns (q, s)."""
+    x = _bits(x_bits)
+    R, C = x.shape
+    Rp = -(-R // 32) * 32
+    q = np.empty((C, Rp // 2), np.uint8)
+    s = np.empty((C, Rp // 32), np.uint8)
+    rc = native.lib().mxo_cast_cols_hadamard(x.ctypes.data, R, C, C, int(shift), q.ctypes.data, s.ctypes.data,
+                                             _threads(nthreads))
+    if rc:
+        raise RuntimeError("mxo_cast_cols_hadamard failed")
+    return q, s
+
+
+def fwht32(x_f32):
+    """The binary32 32-point Walsh-Hadamard transform of each row of a [n, 32] float32 array."""
+    x = np.ascontiguousarray(x_f32, dtype=np.float32)
+    if x.ndim != 2 or x.shape[1] != 32:
+        raise ValueError("expected [n, 32] float32")
+    out = np.empty_like(x)
+    if native.lib().mxo_fwht32(x.ctypes.data, out.ctypes.data, x.shape[0]):
+        raise RuntimeError("mxo_fwht32 failed")
+    return out
 
 
 def dequant(q, s):

@@ -194,6 +194,142 @@ int mxo_cast_cols(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint8_t*
     return 0;
 }
 
+/* ---- Hadamard-transformed casts ----
+ *
+ * jax-aiter README, "Quick start" comment on gemm_fp4_bf16: in the training
+ * recipe grad_out is cast with a Hadamard transform.  Nothing else is stated;
+ * the reading implemented here:
+ *   - the transform is the 32-point Sylvester Walsh-Hadamard matrix H
+ *     (H[i][j] = (-1)^popcount(i & j), entries +-1, H H = 32 I), applied to
+ *     each 32-element block along the contraction dimension (a column copy's
+ *     padding rows enter as +0);
+ *   - it is evaluated in IEEE binary32 from the exact binary32 values of the
+ *     bf16 inputs, by the butterfly with half-widths 1, 2, 4, 8, 16 in that
+ *     order, each butterfly replacing (u, w) by (u + w, u - w);
+ *   - the transformed block divided by 2^shift (exactly, in double) is
+ *     quantized by the rule above, the sign bit of each value giving the
+ *     code's sign; a non-finite value (bf16 Inf/NaN, or binary32 overflow)
+ *     makes the block scale 0xFF with codes 0.
+ * Both operands of a contraction carry the transform; with shift 5 on one of
+ * them (H^T H = 32 I) their product is that of the untransformed operands up
+ * to quantization.
+ */
+
+/* In-place 32-point Walsh-Hadamard transform of v in binary32. */
+static void fwht32_f32(float v[MXO_BLOCK]) {
+    for (int h = 1; h < MXO_BLOCK; h <<= 1)
+        for (int i = 0; i < MXO_BLOCK; i += 2 * h)
+            for (int j = i; j < i + h; ++j) {
+                const float u = v[j], w = v[j + h];
+                v[j] = u + w;
+                v[j + h] = u - w;
+            }
+}
+
+/* bf16 bits -> binary32 (exact: bf16 is binary32 with the low 16 bits dropped). */
+static float bf16_to_f32(uint16_t h) {
+    uint32_t b = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &b, sizeof f);
+    return f;
+}
+
+/* Quantize 32 real values (doubles) by the block rule; returns the scale byte. */
+static uint8_t quantize_values(const double v[MXO_BLOCK], uint8_t codes[MXO_BLOCK]) {
+    double amax = 0.0;
+    for (int i = 0; i < MXO_BLOCK; ++i) {
+        if (!isfinite(v[i])) {
+            memset(codes, 0, MXO_BLOCK);
+            return 0xFF;
+        }
+        if (fabs(v[i]) > amax) amax = fabs(v[i]);
+    }
+    int X;
+    if (amax == 0.0) {
+        X = -127;
+    } else {
+        X = floor_log2(amax) - 2;
+        if (X < -127) X = -127;
+        if (X > 127) X = 127;
+    }
+    for (int i = 0; i < MXO_BLOCK; ++i)
+        codes[i] = (uint8_t)(e2m1_round(ldexp(fabs(v[i]), -X)) | (signbit(v[i]) ? 8 : 0));
+    return (uint8_t)(X + 127);
+}
+
+/* Transform and quantize one block of n (<= 32) bf16 values read with `stride`. */
+static uint8_t quantize_block_hadamard(const uint16_t* x, int64_t stride, int n, int shift,
+                                       uint8_t codes[MXO_BLOCK]) {
+    float y[MXO_BLOCK];
+    for (int i = 0; i < MXO_BLOCK; ++i) y[i] = i < n ? bf16_to_f32(x[i * stride]) : 0.0f;
+    fwht32_f32(y);
+    double v[MXO_BLOCK];
+    for (int i = 0; i < MXO_BLOCK; ++i) v[i] = ldexp((double)y[i], -shift);
+    return quantize_values(v, codes);
+}
+
+typedef struct { const uint16_t* x; int64_t R, C, ldx; int shift; uint8_t *q, *s; } hcast_ctx;
+
+static void hcast_rows_range(void* p, int64_t lo, int64_t hi) {
+    hcast_ctx* c = (hcast_ctx*)p;
+    uint8_t codes[MXO_BLOCK];
+    int64_t nb = c->C / MXO_BLOCK;
+    for (int64_t r = lo; r < hi; ++r) {
+        for (int64_t b = 0; b < nb; ++b) {
+            c->s[r * nb + b] = quantize_block_hadamard(c->x + r * c->ldx + b * MXO_BLOCK, 1, MXO_BLOCK, c->shift, codes);
+            uint8_t* qrow = c->q + r * (c->C / 2) + b * (MXO_BLOCK / 2);
+            for (int i = 0; i < MXO_BLOCK / 2; ++i) qrow[i] = (uint8_t)(codes[2 * i] | (codes[2 * i + 1] << 4));
+        }
+    }
+}
+
+static void hcast_cols_range(void* p, int64_t lo, int64_t hi) {
+    hcast_ctx* c = (hcast_ctx*)p;
+    uint8_t codes[MXO_BLOCK];
+    int64_t nb = (c->R + MXO_BLOCK - 1) / MXO_BLOCK;
+    int64_t Rp = nb * MXO_BLOCK;
+    for (int64_t col = lo; col < hi; ++col) {
+        for (int64_t b = 0; b < nb; ++b) {
+            int64_t r0 = b * MXO_BLOCK;
+            int n = (int)((c->R - r0) < MXO_BLOCK ? (c->R - r0) : MXO_BLOCK);
+            c->s[col * nb + b] = quantize_block_hadamard(c->x + r0 * c->ldx + col, c->ldx, n, c->shift, codes);
+            uint8_t* qrow = c->q + col * (Rp / 2) + r0 / 2;
+            for (int i = 0; i < MXO_BLOCK / 2; ++i) qrow[i] = (uint8_t)(codes[2 * i] | (codes[2 * i + 1] << 4));
+        }
+    }
+}
+
+/* Row copy of x [R, C] with every 32-block transformed, divided by 2^shift, quantized.
+ * Same output shapes as mxo_cast_rows.  0 <= shift <= 64. */
+int mxo_cast_rows_hadamard(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int shift, uint8_t* q, uint8_t* s,
+                           int nthreads) {
+    if (R < 0 || C < 0 || C % MXO_BLOCK != 0 || ldx < C || shift < 0 || shift > 64) return -1;
+    hcast_ctx c = {x, R, C, ldx, shift, q, s};
+    parallel_for(R, nthreads, hcast_rows_range, &c);
+    return 0;
+}
+
+/* Column copy of x [R, C] (blocks of 32 rows, rows padded with +0) with the transform. */
+int mxo_cast_cols_hadamard(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int shift, uint8_t* q, uint8_t* s,
+                           int nthreads) {
+    if (R < 0 || C < 0 || ldx < C || shift < 0 || shift > 64) return -1;
+    hcast_ctx c = {x, R, C, ldx, shift, q, s};
+    parallel_for(C, nthreads, hcast_cols_range, &c);
+    return 0;
+}
+
+/* The binary32 transform alone, on n blocks of 32 floats (for the tests). */
+int mxo_fwht32(const float* in, float* out, int64_t nblocks) {
+    if (nblocks < 0) return -1;
+    for (int64_t b = 0; b < nblocks; ++b) {
+        float v[MXO_BLOCK];
+        memcpy(v, in + b * MXO_BLOCK, sizeof v);
+        fwht32_f32(v);
+        memcpy(out + b * MXO_BLOCK, v, sizeof v);
+    }
+    return 0;
+}
+
 /* ---- dequantization ---- */
 
 /* out[r, k] = e2m1(q[r,k]) * 2^(s[r, k/32] - 127), NaN for scale 0xFF.  K % 32 == 0. */

@@ -38,7 +38,11 @@ def lib():
         L.mxo_dequant.argtypes = [p, p, i64, i64, p]
         L.mxo_gemm.argtypes = [p, p, p, p, i64, i64, i64, p, p, i32]
         L.mxo_gemm_pairs.argtypes = [p, p, p, p, i64, i64, i64, p, p, i64, p, p, i32]
-        for f in (L.mxo_cast_rows, L.mxo_cast_cols, L.mxo_dequant, L.mxo_gemm, L.mxo_gemm_pairs):
+        L.mxo_cast_rows_hadamard.argtypes = [p, i64, i64, i64, i32, p, p, i32]
+        L.mxo_cast_cols_hadamard.argtypes = [p, i64, i64, i64, i32, p, p, i32]
+        L.mxo_fwht32.argtypes = [p, p, i64]
+        for f in (L.mxo_cast_rows, L.mxo_cast_cols, L.mxo_dequant, L.mxo_gemm, L.mxo_gemm_pairs,
+                  L.mxo_cast_rows_hadamard, L.mxo_cast_cols_hadamard, L.mxo_fwht32):
             f.restype = i32
         _lib = L
     return _lib

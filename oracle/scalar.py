@@ -133,3 +133,30 @@ def dot_exact(a_bits_row, b_bits_row):
             total += x * y
             atotal += abs(x * y)
     return total, atotal
+
+
+# ---- Hadamard-transformed blocks (jax-aiter README, "Quick start": grad_out is cast with a
+# Hadamard transform; the transform is read as the 32-point Sylvester Walsh-Hadamard matrix
+# on each block along the contraction dimension) ----
+
+def hadamard_entry(i, j):
+    """Entry (i, j) of the 32-point Sylvester Walsh-Hadamard matrix: (-1)^popcount(i & j)."""
+    return -1 if bin(i & j).count("1") % 2 else 1
+
+
+def hadamard_block(values):
+    """Exact H . values for a block of 32 rationals (the matrix product, no butterflies)."""
+    if len(values) != BLOCK:
+        raise ValueError("a block has 32 elements")
+    return [sum(hadamard_entry(i, j) * Fraction(values[j]) for j in range(BLOCK)) for i in range(BLOCK)]
+
+
+def quantize_rationals(values, negative=None):
+    """(scale byte, codes) of 32 rationals by the block rule.  negative[i] is the code's sign
+    bit (default: value < 0; a zero has no sign of its own as a rational)."""
+    vals = [Fraction(v) for v in values]
+    if negative is None:
+        negative = [v < 0 for v in vals]
+    X = shared_exponent(vals)
+    codes = [nearest_e2m1_magnitude(abs(v) / Fraction(2) ** X) | (8 if neg else 0) for v, neg in zip(vals, negative)]
+    return X + 127, codes
