@@ -52,6 +52,8 @@ def parse():
                    help="target wall time of the CPU-oracle sample (0 skips the CPU baseline)")
     p.add_argument("--cached-weights", action="store_true",
                    help="weights quantized once before timing (WeightWorkspace reuse): the step skips W's dual cast")
+    p.add_argument("--hadamard-grad", action="store_true",
+                   help="the Hadamard gradient recipe: column copies of A and W and both copies of dOut transformed")
     p.add_argument("--no-kernel-events", action="store_true",
                    help="time only the whole step (no per-kernel events)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -98,12 +100,17 @@ def gemm_roofline(m, n, k):
     return flops, nbytes, ("mfma" if t_mfma >= t_hbm else "hbm"), max(t_mfma, t_hbm)
 
 
-def step_ops(P, L, sp, N, cached_weights=False):
+def step_ops(P, L, sp, N, cached_weights=False, hadamard=False):
     """The training step of one projection: (kind, label, launch, work, roofline-ideal seconds).
-    With cached_weights, W's copies are made once beforehand and the step has no W cast."""
+    With cached_weights, W's copies are made once beforehand and the step has no W cast.
+    With hadamard, the casts apply the gradient recipe's block transform (A and W: column copy;
+    dOut: both copies, divided by 32)."""
 
-    def cast_dual(x, row, col):
+    def cast_dual(x, row, col, t_row=False, t_col=False, shift=0):
         R, C = x.shape
+        if hadamard:
+            return lambda: L.mxfp4_cast_hadamard(x.data_ptr(), R, C, C, row.q.data_ptr(), row.s.data_ptr(),
+                                                 col.q.data_ptr(), col.s.data_ptr(), int(t_row), int(t_col), shift, sp)
         return lambda: L.mxfp4_cast_dual(x.data_ptr(), R, C, C, row.q.data_ptr(), row.s.data_ptr(),
                                          col.q.data_ptr(), col.s.data_ptr(), sp)
 
@@ -119,11 +126,11 @@ def step_ops(P, L, sp, N, cached_weights=False):
         casts.append(("cast_dual(W)", P["w"], P["w_row"], P["w_col"]))
     for label, x, row, col in casts:
         nb = 3.0625 * x.shape[0] * x.shape[1]
-        ops.append(("cast", name + "." + label, cast_dual(x, row, col), nb, nb / (HBM_PEAK_GBPS * 1e9)))
+        ops.append(("cast", name + "." + label, cast_dual(x, row, col, False, True, 0), nb, nb / (HBM_PEAK_GBPS * 1e9)))
     fl, _, _, t = gemm_roofline(M, Nn, K)
     ops.append(("gemm", name + ".fwd", gemm(L.mxfp4_gemm_nt, P["a_row"], P["w_row"], P["out"]), fl, t))
     nb = 3.0625 * M * Nn
-    ops.append(("cast", name + ".cast_dual(dOut)", cast_dual(P["g"], P["g_row"], P["g_col"]), nb,
+    ops.append(("cast", name + ".cast_dual(dOut)", cast_dual(P["g"], P["g_row"], P["g_col"], True, True, 5), nb,
                 nb / (HBM_PEAK_GBPS * 1e9)))
     fl, _, _, t = gemm_roofline(M, K, Nn)
     ops.append(("gemm", name + ".dA", gemm(L.mxfp4_gemm_nn, P["g_row"], P["w_col"], P["da"]), fl, t))
@@ -341,12 +348,13 @@ def main():
     step_flops = 0.0
     for P in projs:
         step_flops += 6.0 * P["M"] * P["N"] * P["K"]
-        ops += step_ops(P, L, sp, N, cached_weights=args.cached_weights)
+        ops += step_ops(P, L, sp, N, cached_weights=args.cached_weights, hadamard=args.hadamard_grad)
         if args.cached_weights:
             # the WeightWorkspace fill: W's dual cast once, outside the timed region
             R, C = P["w"].shape
-            N.check(L.mxfp4_cast_dual(P["w"].data_ptr(), R, C, C, P["w_row"].q.data_ptr(), P["w_row"].s.data_ptr(),
-                                      P["w_col"].q.data_ptr(), P["w_col"].s.data_ptr(), sp), "mxfp4_cast_dual")
+            N.check(L.mxfp4_cast_hadamard(P["w"].data_ptr(), R, C, C, P["w_row"].q.data_ptr(),
+                                          P["w_row"].s.data_ptr(), P["w_col"].q.data_ptr(), P["w_col"].s.data_ptr(),
+                                          0, int(args.hadamard_grad), 0, sp), "mxfp4_cast_hadamard")
 
     use_events = not args.no_kernel_events
     ms_per_step, per = time_ops(ops, args.steps, args.warmup, stream, torch, N, per_kernel=use_events)
@@ -385,7 +393,8 @@ def main():
         "dtype": "mxfp4",
         "data": "synthetic",
         "config": {"workload": WORKLOADS[args.workload] + (
-                       "; weights quantized once (cached), no W cast in the step" if args.cached_weights else ""),
+                       "; weights quantized once (cached), no W cast in the step" if args.cached_weights else "") + (
+                       "; Hadamard gradient recipe" if args.hadamard_grad else ""),
                    "projections": [[P["name"], P["M"], P["N"], P["K"]] for P in projs],
                    "step_tflop": round(step_flops / 1e12, 4)},
         "frac_of_fp4_peak": round(value / FP4_PEAK_TFLOPS, 4),

@@ -113,6 +113,28 @@ int mxfp4_cast_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx, void
                     void* s_col, hipStream_t stream);
 
 /*
+ * F2 -- Hadamard-transformed cast (jax-aiter README, "Quick start": in the
+ * training recipe grad_out is cast with a Hadamard transform).  As
+ * mxfp4_cast_dual when q_col / s_col are given, as mxfp4_cast when both are
+ * NULL, except that every 32-element block of the row copy (transform_row !=
+ * 0) and / or of the column copy (transform_col != 0, needs q_col, s_col) is
+ * first multiplied by the 32-point Sylvester Walsh-Hadamard matrix H
+ * (H[i][j] = (-1)^popcount(i & j), H H = 32 I) and divided by 2^shift:
+ *   - the transform is evaluated in IEEE binary32 from the bf16 values by
+ *     butterflies of half-width 1, 2, 4, 8, 16 in that order, each (u, w) ->
+ *     (u + w, u - w); a column copy's padding rows enter as +0;
+ *   - the result / 2^shift is quantized by the rule above (shared exponent
+ *     from its amax, E2M1 nearest-even, sign kept); a block that becomes
+ *     non-finite (bf16 Inf/NaN, binary32 overflow) gets scale 0xFF, codes 0.
+ * Both operands of a GEMM contraction must carry the transform; shift = 5 on
+ * one of them keeps their product.  0 <= shift <= 64; other requirements and
+ * errors as mxfp4_cast_dual.
+ */
+int mxfp4_cast_hadamard(const void* x, int64_t rows, int64_t cols, int64_t ldx, void* q_row, void* s_row,
+                        void* q_col, void* s_col, int transform_row, int transform_col, int shift,
+                        hipStream_t stream);
+
+/*
  * A3/A4 -- block-scaled GEMM, NT (jax-aiter README, Supported ops: "FP4 GEMM
  * (low-level)", gemm_fp4(a, b, a_scale, b_scale), and the A[M,K] @ B[N,K]^T
  * convention of its GEMM rows):
@@ -206,6 +228,33 @@ int gemm_fp4_bf16_fwd_qw(const void* a, const void* w_row_q, const void* w_row_s
  */
 int gemm_fp4_bf16_bwd_qw(const void* dout, const void* w_col_q, const void* w_col_s, int64_t M, int64_t N, int64_t K,
                          void* ws, size_t ws_bytes, void* da, void* dw, hipStream_t stream);
+
+/*
+ * The gemm_fp4_bf16 step with options, as flags:
+ *   MXFP4_STEP_TRAINING      : forward keeps the column copies for the backward pass;
+ *   MXFP4_STEP_HADAMARD_GRAD : F2 recipe (needs TRAINING in the forward): the
+ *     column copies of A and W carry the transform of mxfp4_cast_hadamard
+ *     (shift 0) and both copies of dOut carry it with shift 5, so dA and dB
+ *     contract transformed operands (same products, smaller quantization error
+ *     for blocks with outliers);
+ *   MXFP4_STEP_QUANTIZED_W   : W is given quantized (w == NULL, w_row_q /
+ *     w_row_s in the forward, w_col_q / w_col_s in the backward, made by
+ *     mxfp4_cast_dual, or by mxfp4_cast_hadamard with transform_col = 1,
+ *     shift 0 under HADAMARD_GRAD); the workspace is
+ *     gemm_fp4_bf16_workspace_bytes_qw's, else gemm_fp4_bf16_workspace_bytes'.
+ * The backward pass takes the forward's flags.  Unknown flags: MXFP4_EINVAL.
+ * gemm_fp4_bf16_fwd / _bwd / _fwd_qw / _bwd_qw are these with HADAMARD_GRAD
+ * clear.
+ */
+#define MXFP4_STEP_TRAINING 1u
+#define MXFP4_STEP_HADAMARD_GRAD 2u
+#define MXFP4_STEP_QUANTIZED_W 4u
+
+int gemm_fp4_bf16_fwd_ex(const void* a, const void* w, const void* w_row_q, const void* w_row_s, int64_t M, int64_t N,
+                         int64_t K, void* out, void* ws, size_t ws_bytes, unsigned flags, hipStream_t stream);
+
+int gemm_fp4_bf16_bwd_ex(const void* dout, const void* w_col_q, const void* w_col_s, int64_t M, int64_t N, int64_t K,
+                         void* ws, size_t ws_bytes, void* da, void* dw, unsigned flags, hipStream_t stream);
 
 #ifdef __cplusplus
 }

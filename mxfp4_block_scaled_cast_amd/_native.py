@@ -32,7 +32,12 @@ SIGNATURES = [
     ("gemm_fp4_bf16_workspace_bytes_qw", _sz, [_i64, _i64, _i64, _i32]),
     ("gemm_fp4_bf16_fwd_qw", _i32, [_p, _p, _p, _i64, _i64, _i64, _p, _p, _sz, _i32, _p]),
     ("gemm_fp4_bf16_bwd_qw", _i32, [_p, _p, _p, _i64, _i64, _i64, _p, _sz, _p, _p, _p]),
+    ("mxfp4_cast_hadamard", _i32, [_p, _i64, _i64, _i64, _p, _p, _p, _p, _i32, _i32, _i32, _p]),
+    ("gemm_fp4_bf16_fwd_ex", _i32, [_p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _sz, ctypes.c_uint, _p]),
+    ("gemm_fp4_bf16_bwd_ex", _i32, [_p, _p, _p, _i64, _i64, _i64, _p, _sz, _p, _p, ctypes.c_uint, _p]),
 ]
+
+STEP_TRAINING, STEP_HADAMARD_GRAD, STEP_QUANTIZED_W = 1, 2, 4
 
 STATUS = {0: "MXFP4_OK", -1: "MXFP4_EINVAL", -2: "MXFP4_EALIGN", -3: "MXFP4_EDEVICE",
           -4: "MXFP4_ELAUNCH", -5: "MXFP4_ERANGE", -6: "MXFP4_ESPACE"}

@@ -26,10 +26,13 @@ class MxOperand:
 
 @dataclass
 class Mxfp4Tensor:
-    """Row copy (blocks along the last dim) and optional column copy of a bf16 [R, C] matrix."""
+    """Row copy (blocks along the last dim) and optional column copy of a bf16 [R, C] matrix.
+    hadamard_row / hadamard_col mark copies quantized after the block Walsh-Hadamard transform."""
     row: MxOperand
     col: Optional[MxOperand]
     shape: Tuple[int, int]
+    hadamard_row: bool = False
+    hadamard_col: bool = False
 
 
 def _stream(device):
@@ -75,6 +78,26 @@ def cast_dual(x, row: Optional[MxOperand] = None, col: Optional[MxOperand] = Non
     return Mxfp4Tensor(row, col, (R, C))
 
 
+def cast_hadamard(x, transform_row=True, transform_col=True, shift=0, columnwise=True) -> Mxfp4Tensor:
+    """Row (and, if columnwise, column) copy of bf16 x [R, C] with each 32-block of the chosen
+    copies Walsh-Hadamard transformed and divided by 2^shift before quantization (the gradient
+    recipe of the README's Quick start; see mxfp4_cast_hadamard)."""
+    _check_bf16_matrix(x, "x")
+    if transform_col and not columnwise:
+        raise ValueError("transform_col needs the column copy")
+    R, C = x.shape
+    Rp = -(-R // 32) * 32
+    row = empty_operand(R, C, x.device)
+    col = empty_operand(C, Rp, x.device) if columnwise else None
+    st = N.lib().mxfp4_cast_hadamard(x.data_ptr(), R, C, x.stride(0), row.q.data_ptr(), row.s.data_ptr(),
+                                     col.q.data_ptr() if col is not None else None,
+                                     col.s.data_ptr() if col is not None else None,
+                                     1 if transform_row else 0, 1 if transform_col else 0, int(shift),
+                                     _stream(x.device))
+    N.check(st, "mxfp4_cast_hadamard")
+    return Mxfp4Tensor(row, col, (R, C), bool(transform_row), bool(transform_col and columnwise))
+
+
 def _gemm(fn, name, a: MxOperand, b: MxOperand, out):
     if a.k != b.k:
         raise ValueError("contraction lengths differ: %d vs %d" % (a.k, b.k))
@@ -103,76 +126,59 @@ def workspace_bytes(M, Nn, K, training=True):
     return int(N.lib().gemm_fp4_bf16_workspace_bytes(M, Nn, K, 1 if training else 0))
 
 
-def gemm_fp4_bf16_fwd(a, w, training=True, ws=None, out=None):
-    """Forward of gemm_fp4_bf16 on 2-D contiguous bf16 a [M, K], w [N, K] -> (out [M, N], ws)."""
-    _check_bf16_matrix(a, "a")
-    _check_bf16_matrix(w, "w")
-    if not (a.is_contiguous() and w.is_contiguous()):
-        raise ValueError("a and w must be contiguous")
-    M, K = a.shape
-    Nn = w.shape[0]
-    if w.shape[1] != K:
-        raise ValueError("a and w disagree on K")
-    nbytes = workspace_bytes(M, Nn, K, training)
-    if ws is None:
-        ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=a.device)
-    if out is None:
-        out = torch.empty((M, Nn), dtype=torch.bfloat16, device=a.device)
-    st = N.lib().gemm_fp4_bf16_fwd(a.data_ptr(), w.data_ptr(), M, Nn, K, out.data_ptr(), ws.data_ptr(),
-                                   ws.numel(), 1 if training else 0, _stream(a.device))
-    N.check(st, "gemm_fp4_bf16_fwd")
-    return out, ws
-
-
-def gemm_fp4_bf16_bwd(dout, M, Nn, K, ws, need_da=True, need_dw=True, da=None, dw=None):
-    """Backward of gemm_fp4_bf16 from the workspace of a training forward -> (da, dw)."""
-    _check_bf16_matrix(dout, "dout")
-    if not dout.is_contiguous():
-        dout = dout.contiguous()
-    if need_da and da is None:
-        da = torch.empty((M, K), dtype=torch.bfloat16, device=dout.device)
-    if need_dw and dw is None:
-        dw = torch.empty((Nn, K), dtype=torch.bfloat16, device=dout.device)
-    st = N.lib().gemm_fp4_bf16_bwd(dout.data_ptr(), M, Nn, K, ws.data_ptr(), ws.numel(),
-                                   da.data_ptr() if need_da else None, dw.data_ptr() if need_dw else None,
-                                   _stream(dout.device))
-    N.check(st, "gemm_fp4_bf16_bwd")
-    return (da if need_da else None), (dw if need_dw else None)
-
-
 def workspace_bytes_qw(M, Nn, K, training=True):
     return int(N.lib().gemm_fp4_bf16_workspace_bytes_qw(M, Nn, K, 1 if training else 0))
 
 
-def _check_weight_fp4(w_fp4, Nn, K, training):
+def _flags(training, hadamard_grad, quantized_w):
+    if hadamard_grad and not training:
+        raise ValueError("the Hadamard gradient recipe only applies to training")
+    return ((N.STEP_TRAINING if training else 0) | (N.STEP_HADAMARD_GRAD if hadamard_grad else 0) |
+            (N.STEP_QUANTIZED_W if quantized_w else 0))
+
+
+def _check_weight_fp4(w_fp4, Nn, K, training, hadamard_grad):
     if w_fp4.shape != (Nn, K):
         raise ValueError("w_fp4 holds a [%d, %d] weight, expected [%d, %d]" % (w_fp4.shape + (Nn, K)))
     if training and w_fp4.col is None:
         raise ValueError("training needs the weight's column copy: quantize with columnwise=True")
+    if training and w_fp4.hadamard_col != bool(hadamard_grad):
+        raise ValueError("the weight's column copy %s the Hadamard transform but hadamard_grad is %s" %
+                         ("carries" if w_fp4.hadamard_col else "lacks", bool(hadamard_grad)))
 
 
-def gemm_fp4_bf16_fwd_qw(a, w_fp4, training=True, ws=None, out=None):
-    """Forward with a pre-quantized weight (Mxfp4Tensor of W [N, K]) -> (out [M, N], ws)."""
+def _fwd(a, w, w_fp4, training, ws, out, hadamard_grad):
     _check_bf16_matrix(a, "a")
     if not a.is_contiguous():
         raise ValueError("a must be contiguous")
     M, K = a.shape
-    Nn = w_fp4.shape[0]
-    _check_weight_fp4(w_fp4, Nn, K, training)
-    nbytes = workspace_bytes_qw(M, Nn, K, training)
+    if w_fp4 is None:
+        _check_bf16_matrix(w, "w")
+        if not w.is_contiguous():
+            raise ValueError("w must be contiguous")
+        if w.shape[1] != K:
+            raise ValueError("a and w disagree on K")
+        Nn = w.shape[0]
+        nbytes = workspace_bytes(M, Nn, K, training)
+    else:
+        Nn = w_fp4.shape[0]
+        _check_weight_fp4(w_fp4, Nn, K, training, hadamard_grad)
+        nbytes = workspace_bytes_qw(M, Nn, K, training)
+    flags = _flags(training, hadamard_grad, w_fp4 is not None)
     if ws is None:
         ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=a.device)
     if out is None:
         out = torch.empty((M, Nn), dtype=torch.bfloat16, device=a.device)
-    r = w_fp4.row
-    st = N.lib().gemm_fp4_bf16_fwd_qw(a.data_ptr(), r.q.data_ptr(), r.s.data_ptr(), M, Nn, K, out.data_ptr(),
-                                      ws.data_ptr(), ws.numel(), 1 if training else 0, _stream(a.device))
-    N.check(st, "gemm_fp4_bf16_fwd_qw")
+    r = w_fp4.row if w_fp4 is not None else None
+    st = N.lib().gemm_fp4_bf16_fwd_ex(a.data_ptr(), w.data_ptr() if w_fp4 is None else None,
+                                      r.q.data_ptr() if r is not None else None,
+                                      r.s.data_ptr() if r is not None else None, M, Nn, K, out.data_ptr(),
+                                      ws.data_ptr(), ws.numel(), flags, _stream(a.device))
+    N.check(st, "gemm_fp4_bf16_fwd")
     return out, ws
 
 
-def gemm_fp4_bf16_bwd_qw(dout, w_fp4, M, Nn, K, ws, need_da=True, need_dw=True, da=None, dw=None):
-    """Backward of gemm_fp4_bf16_fwd_qw (W's column copy from w_fp4) -> (da, dw)."""
+def _bwd(dout, w_fp4, M, Nn, K, ws, need_da, need_dw, da, dw, hadamard_grad):
     _check_bf16_matrix(dout, "dout")
     if not dout.is_contiguous():
         dout = dout.contiguous()
@@ -180,49 +186,69 @@ def gemm_fp4_bf16_bwd_qw(dout, w_fp4, M, Nn, K, ws, need_da=True, need_dw=True, 
         da = torch.empty((M, K), dtype=torch.bfloat16, device=dout.device)
     if need_dw and dw is None:
         dw = torch.empty((Nn, K), dtype=torch.bfloat16, device=dout.device)
-    c = w_fp4.col
-    st = N.lib().gemm_fp4_bf16_bwd_qw(dout.data_ptr(), c.q.data_ptr() if c is not None else None,
+    c = w_fp4.col if w_fp4 is not None else None
+    st = N.lib().gemm_fp4_bf16_bwd_ex(dout.data_ptr(), c.q.data_ptr() if c is not None else None,
                                       c.s.data_ptr() if c is not None else None, M, Nn, K, ws.data_ptr(), ws.numel(),
                                       da.data_ptr() if need_da else None, dw.data_ptr() if need_dw else None,
-                                      _stream(dout.device))
-    N.check(st, "gemm_fp4_bf16_bwd_qw")
+                                      _flags(True, hadamard_grad, w_fp4 is not None), _stream(dout.device))
+    N.check(st, "gemm_fp4_bf16_bwd")
     return (da if need_da else None), (dw if need_dw else None)
+
+
+def gemm_fp4_bf16_fwd(a, w, training=True, ws=None, out=None, hadamard_grad=False):
+    """Forward of gemm_fp4_bf16 on 2-D contiguous bf16 a [M, K], w [N, K] -> (out [M, N], ws)."""
+    return _fwd(a, w, None, training, ws, out, hadamard_grad)
+
+
+def gemm_fp4_bf16_bwd(dout, M, Nn, K, ws, need_da=True, need_dw=True, da=None, dw=None, hadamard_grad=False):
+    """Backward of gemm_fp4_bf16 from the workspace of a training forward -> (da, dw)."""
+    return _bwd(dout, None, M, Nn, K, ws, need_da, need_dw, da, dw, hadamard_grad)
+
+
+def gemm_fp4_bf16_fwd_qw(a, w_fp4, training=True, ws=None, out=None, hadamard_grad=False):
+    """Forward with a pre-quantized weight (Mxfp4Tensor of W [N, K]) -> (out [M, N], ws)."""
+    return _fwd(a, None, w_fp4, training, ws, out, hadamard_grad)
+
+
+def gemm_fp4_bf16_bwd_qw(dout, w_fp4, M, Nn, K, ws, need_da=True, need_dw=True, da=None, dw=None,
+                         hadamard_grad=False):
+    """Backward of gemm_fp4_bf16_fwd_qw (W's column copy from w_fp4) -> (da, dw)."""
+    return _bwd(dout, w_fp4, M, Nn, K, ws, need_da, need_dw, da, dw, hadamard_grad)
 
 
 class _GemmFp4Bf16(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, a, w, w_fp4):
+    def forward(ctx, a, w, w_fp4, hadamard_grad):
         training = bool(ctx.needs_input_grad[0] or ctx.needs_input_grad[1])
-        if w_fp4 is None:
-            out, ws = gemm_fp4_bf16_fwd(a, w, training=training)
-        else:
-            out, ws = gemm_fp4_bf16_fwd_qw(a, w_fp4, training=training)
+        had = bool(hadamard_grad) and training
+        out, ws = _fwd(a, w if w_fp4 is None else None, w_fp4, training, None, None, had)
         ctx.dims = (a.shape[0], w.shape[0], a.shape[1])
         ctx.ws = ws if training else None
         ctx.w_fp4 = w_fp4
+        ctx.hadamard = had
         return out
 
     @staticmethod
     def backward(ctx, dout):
         M, Nn, K = ctx.dims
-        if ctx.w_fp4 is None:
-            da, dw = gemm_fp4_bf16_bwd(dout, M, Nn, K, ctx.ws, ctx.needs_input_grad[0], ctx.needs_input_grad[1])
-        else:
-            da, dw = gemm_fp4_bf16_bwd_qw(dout, ctx.w_fp4, M, Nn, K, ctx.ws, ctx.needs_input_grad[0],
-                                          ctx.needs_input_grad[1])
+        da, dw = _bwd(dout, ctx.w_fp4, M, Nn, K, ctx.ws, ctx.needs_input_grad[0], ctx.needs_input_grad[1], None,
+                      None, ctx.hadamard)
         ctx.ws = None
         ctx.w_fp4 = None
-        return da, dw, None
+        return da, dw, None, None
 
 
-def gemm_fp4_bf16(a, w, w_fp4: Optional[Mxfp4Tensor] = None):
+def gemm_fp4_bf16(a, w, w_fp4: Optional[Mxfp4Tensor] = None, hadamard_grad: bool = False):
     """BF16 in/out MXFP4 GEMM, out = a . w^T, differentiable (FP4 forward, FP4 dA, FP4 dB).
 
     a: [..., K] bfloat16, w: [N, K] bfloat16 -> [..., N] bfloat16.
     w_fp4: w already quantized (e.g. from WeightWorkspace.get_or_quantize with a weight
     quantizer); its copies replace w's cast in the forward and in dA.  w still receives dW.
+    hadamard_grad: the README's gradient recipe -- dA and dB contract Walsh-Hadamard
+    transformed operands (dOut's copies and the column copies of a and w); a w_fp4 then
+    has to come from a weight quantizer with hadamard=True.
     """
     lead = a.shape[:-1]
     a2 = a.reshape(-1, a.shape[-1]).contiguous()
-    out = _GemmFp4Bf16.apply(a2, w.contiguous(), w_fp4)
+    out = _GemmFp4Bf16.apply(a2, w.contiguous(), w_fp4, hadamard_grad)
     return out.reshape(*lead, w.shape[0])

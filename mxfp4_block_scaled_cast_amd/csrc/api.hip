@@ -7,6 +7,11 @@
 //   forward : cast A and W, out = A . W^T
 //   backward: cast dOut, dA = dOut . W (NN on W's column copy),
 //             dB = dOut^T . A (NT on the column copies of dOut and A)
+// With the Hadamard-gradient recipe (README "Quick start": grad_out is cast
+// with a Hadamard transform) every operand of dA and dB carries the block
+// transform along its contraction dimension: the column copies of A and W
+// (forward casts, divisor 1) and both copies of dOut (divisor 32 = 2^5, so
+// the products are unchanged: H H = 32 I).
 #include <mutex>
 #include <string.h>
 
@@ -14,6 +19,9 @@
 
 extern "C" hipError_t mx_launch_cast(const void* x, int64_t R, int64_t C, int64_t ldx, void* q_row, void* s_row,
                                      void* q_col, void* s_col, bool dual, hipStream_t stream);
+extern "C" hipError_t mx_launch_cast_h(const void* x, int64_t R, int64_t C, int64_t ldx, void* q_row, void* s_row,
+                                       void* q_col, void* s_col, bool dual, bool transform_row, bool transform_col,
+                                       int hshift, hipStream_t stream);
 extern "C" hipError_t mx_launch_gemm(const void* aq, const void* as, const void* bq, const void* bs, int64_t M,
                                      int64_t N, int64_t K, void* out, int64_t ldo, hipStream_t stream);
 
@@ -118,6 +126,11 @@ Workspace workspace_layout(int64_t M, int64_t N, int64_t K, bool training, bool 
     return w;
 }
 
+// 2^5 = 32: H H = 32 I for the 32-point Walsh-Hadamard matrix.
+constexpr int kHadamardShift = 5;
+
+constexpr unsigned kStepFlags = MXFP4_STEP_TRAINING | MXFP4_STEP_HADAMARD_GRAD | MXFP4_STEP_QUANTIZED_W;
+
 int validate_step_sizes(int64_t M, int64_t N, int64_t K, bool training) {
     if (M < 0 || N < 0 || K < 0 || K % 32 != 0) return MXFP4_EINVAL;
     if (training && N % 32 != 0) return MXFP4_EINVAL;
@@ -173,6 +186,23 @@ int mxfp4_cast_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx, void
     return status_of(mx_launch_cast(x, rows, cols, ldx, q_row, s_row, q_col, s_col, true, stream));
 }
 
+int mxfp4_cast_hadamard(const void* x, int64_t rows, int64_t cols, int64_t ldx, void* q_row, void* s_row,
+                        void* q_col, void* s_col, int transform_row, int transform_col, int shift,
+                        hipStream_t stream) {
+    if (shift < 0 || shift > 64) return MXFP4_EINVAL;
+    const bool dual = q_col != nullptr || s_col != nullptr;
+    if (transform_col && !dual) return MXFP4_EINVAL;
+    int st = validate_cast(x, rows, cols, ldx, q_row, s_row);
+    if (st != MXFP4_OK || rows == 0 || cols == 0) return st;
+    if (dual) {
+        if (!q_col || !s_col) return MXFP4_EINVAL;
+        if (!aligned16(q_col) || !aligned16(s_col)) return MXFP4_EALIGN;
+    }
+    if ((st = check_device()) != MXFP4_OK) return st;
+    return status_of(mx_launch_cast_h(x, rows, cols, ldx, q_row, s_row, q_col, s_col, dual, transform_row != 0,
+                                      transform_col != 0, shift, stream));
+}
+
 int mxfp4_gemm_nt(const void* a_q, const void* a_s, const void* b_q, const void* b_s, int64_t M, int64_t N, int64_t K,
                   void* out, int64_t ldo, hipStream_t stream) {
     int st = validate_gemm(a_q, a_s, b_q, b_s, M, N, K, out, ldo);
@@ -205,7 +235,8 @@ namespace {
 // Forward: cast A (dual when training, its column copy kept in ws), then the
 // GEMM with W's row copy -- cast here from bf16 w (own_w), or given.
 int step_fwd(const void* a, bool own_w, const void* w, const void* w_row_q, const void* w_row_s, int64_t M, int64_t N,
-             int64_t K, void* out, void* ws, size_t ws_bytes, bool train, hipStream_t stream) {
+             int64_t K, void* out, void* ws, size_t ws_bytes, bool train, bool hadamard, hipStream_t stream) {
+    if (hadamard && !train) return MXFP4_EINVAL;  // the transform only concerns the backward operands
     int st = validate_step_sizes(M, N, K, train);
     if (st != MXFP4_OK) return st;
     if (M == 0 || N == 0) return MXFP4_OK;
@@ -224,11 +255,12 @@ int step_fwd(const void* a, bool own_w, const void* w, const void* w_row_q, cons
     if ((st = check_device()) != MXFP4_OK) return st;
     hipError_t e = hipSuccess;
     if (K > 0) {
-        e = mx_launch_cast(a, M, K, K, base + L.a_row_q, base + L.a_row_s, train ? base + L.a_col_q : nullptr,
-                           train ? base + L.a_col_s : nullptr, train, stream);
+        // with the Hadamard recipe the column copies (dB's and dA's B operands) carry the transform
+        e = mx_launch_cast_h(a, M, K, K, base + L.a_row_q, base + L.a_row_s, train ? base + L.a_col_q : nullptr,
+                             train ? base + L.a_col_s : nullptr, train, false, hadamard, 0, stream);
         if (e == hipSuccess && own_w)
-            e = mx_launch_cast(w, N, K, K, base + L.w_row_q, base + L.w_row_s, train ? base + L.w_col_q : nullptr,
-                               train ? base + L.w_col_s : nullptr, train, stream);
+            e = mx_launch_cast_h(w, N, K, K, base + L.w_row_q, base + L.w_row_s, train ? base + L.w_col_q : nullptr,
+                                 train ? base + L.w_col_s : nullptr, train, false, hadamard, 0, stream);
     }
     if (e == hipSuccess) e = mx_launch_gemm(base + L.a_row_q, base + L.a_row_s, wq, wsc, M, N, K, out, N, stream);
     return status_of(e);
@@ -237,7 +269,7 @@ int step_fwd(const void* a, bool own_w, const void* w, const void* w_row_q, cons
 // Backward: cast dOut (dual), dA = dOut . W on W's column copy (from ws, or
 // given), dW = dOut^T . A on the column copies of dOut and A.
 int step_bwd(const void* dout, bool own_w, const void* w_col_q, const void* w_col_s, int64_t M, int64_t N, int64_t K,
-             void* ws, size_t ws_bytes, void* da, void* dw, hipStream_t stream) {
+             void* ws, size_t ws_bytes, void* da, void* dw, bool hadamard, hipStream_t stream) {
     int st = validate_step_sizes(M, N, K, true);
     if (st != MXFP4_OK) return st;
     if (!ws || (!da && !dw)) return ws ? MXFP4_OK : MXFP4_EINVAL;
@@ -266,8 +298,9 @@ int step_bwd(const void* dout, bool own_w, const void* w_col_q, const void* w_co
     const int64_t Mp = round_up(M, 32);
     const void* wq = own_w ? base + L.w_col_q : w_col_q;
     const void* wsc = own_w ? base + L.w_col_s : w_col_s;
-    hipError_t e = mx_launch_cast(dout, M, N, N, base + L.g_row_q, base + L.g_row_s, base + L.g_col_q,
-                                  base + L.g_col_s, true, stream);
+    // Hadamard recipe: both copies of dOut transformed and divided by 32 (kHadamardShift)
+    hipError_t e = mx_launch_cast_h(dout, M, N, N, base + L.g_row_q, base + L.g_row_s, base + L.g_col_q,
+                                    base + L.g_col_s, true, hadamard, hadamard, hadamard ? kHadamardShift : 0, stream);
     if (e == hipSuccess && da) e = mx_launch_gemm(base + L.g_row_q, base + L.g_row_s, wq, wsc, M, K, N, da, K, stream);
     if (e == hipSuccess && dw)
         e = mx_launch_gemm(base + L.g_col_q, base + L.g_col_s, base + L.a_col_q, base + L.a_col_s, N, K, Mp, dw, K,
@@ -281,22 +314,40 @@ extern "C" {
 
 int gemm_fp4_bf16_fwd(const void* a, const void* w, int64_t M, int64_t N, int64_t K, void* out, void* ws,
                       size_t ws_bytes, int training, hipStream_t stream) {
-    return step_fwd(a, true, w, nullptr, nullptr, M, N, K, out, ws, ws_bytes, training != 0, stream);
+    return step_fwd(a, true, w, nullptr, nullptr, M, N, K, out, ws, ws_bytes, training != 0, false, stream);
 }
 
 int gemm_fp4_bf16_bwd(const void* dout, int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes, void* da,
                       void* dw, hipStream_t stream) {
-    return step_bwd(dout, true, nullptr, nullptr, M, N, K, ws, ws_bytes, da, dw, stream);
+    return step_bwd(dout, true, nullptr, nullptr, M, N, K, ws, ws_bytes, da, dw, false, stream);
 }
 
 int gemm_fp4_bf16_fwd_qw(const void* a, const void* w_row_q, const void* w_row_s, int64_t M, int64_t N, int64_t K,
                          void* out, void* ws, size_t ws_bytes, int training, hipStream_t stream) {
-    return step_fwd(a, false, nullptr, w_row_q, w_row_s, M, N, K, out, ws, ws_bytes, training != 0, stream);
+    return step_fwd(a, false, nullptr, w_row_q, w_row_s, M, N, K, out, ws, ws_bytes, training != 0, false, stream);
 }
 
 int gemm_fp4_bf16_bwd_qw(const void* dout, const void* w_col_q, const void* w_col_s, int64_t M, int64_t N, int64_t K,
                          void* ws, size_t ws_bytes, void* da, void* dw, hipStream_t stream) {
-    return step_bwd(dout, false, w_col_q, w_col_s, M, N, K, ws, ws_bytes, da, dw, stream);
+    return step_bwd(dout, false, w_col_q, w_col_s, M, N, K, ws, ws_bytes, da, dw, false, stream);
+}
+
+int gemm_fp4_bf16_fwd_ex(const void* a, const void* w, const void* w_row_q, const void* w_row_s, int64_t M, int64_t N,
+                         int64_t K, void* out, void* ws, size_t ws_bytes, unsigned flags, hipStream_t stream) {
+    if (flags & ~kStepFlags) return MXFP4_EINVAL;
+    const bool qw = (flags & MXFP4_STEP_QUANTIZED_W) != 0;
+    if (qw ? w != nullptr : (w_row_q != nullptr || w_row_s != nullptr)) return MXFP4_EINVAL;
+    return step_fwd(a, !qw, w, w_row_q, w_row_s, M, N, K, out, ws, ws_bytes, (flags & MXFP4_STEP_TRAINING) != 0,
+                    (flags & MXFP4_STEP_HADAMARD_GRAD) != 0, stream);
+}
+
+int gemm_fp4_bf16_bwd_ex(const void* dout, const void* w_col_q, const void* w_col_s, int64_t M, int64_t N, int64_t K,
+                         void* ws, size_t ws_bytes, void* da, void* dw, unsigned flags, hipStream_t stream) {
+    if (flags & ~kStepFlags) return MXFP4_EINVAL;
+    const bool qw = (flags & MXFP4_STEP_QUANTIZED_W) != 0;
+    if (!qw && (w_col_q || w_col_s)) return MXFP4_EINVAL;
+    return step_bwd(dout, !qw, w_col_q, w_col_s, M, N, K, ws, ws_bytes, da, dw,
+                    (flags & MXFP4_STEP_HADAMARD_GRAD) != 0, stream);
 }
 
 }  // extern "C"

@@ -28,11 +28,65 @@
 
 namespace mx {
 
-template <int TILE_R, bool DUAL>
+// Walsh-Hadamard variant (HROW / HCOL: transform the row / column copy).
+// jax-aiter README, "Quick start": grad_out is cast with a Hadamard
+// transform.  Each 32-element block along the contraction dimension is
+// multiplied by the 32-point Sylvester Walsh-Hadamard matrix in binary32,
+// by butterflies of half-width 1, 2, 4, 8, 16 in that order, (u, w) ->
+// (u + w, u - w); the result divided by 2^hshift is quantized by the usual
+// rule (shared exponent from its amax, E2M1 RNE via the fp32 scaled
+// conversion).  Row copy: a lane's 8 elements take half-widths 1, 2, 4 in
+// registers and 8, 16 across the quad (DPP); column copy: each thread holds
+// its two 32-row columns in registers.
+
+// E8M0 byte of a transformed block from the binary32 bits of its amax, with
+// the block divided by 2^shift: max(floor(log2 amax) - 2 - shift, -127) + 127;
+// 0xFF for Inf/NaN (the byte also covers amax = 0 and binary32 subnormals,
+// whose exponent is clamped).
+__device__ __forceinline__ unsigned scale_byte_from_f32_amax(unsigned amax_bits, int shift) {
+    const int e = (int)(amax_bits >> 23);
+    if (e == 255) return 255u;
+    if (e == 0) return 0u;
+    const int b = e - 2 - shift;
+    return b > 0 ? (unsigned)b : 0u;
+}
+
+// Two binary32 values -> byte SEL of `old`: RNE(x / scale) to E2M1, saturating, sign kept.
+template <int SEL>
+__device__ __forceinline__ unsigned cvt_pair_f32(unsigned old, float lo, float hi, float scale) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, lo, hi, scale, SEL);
+}
+
+__device__ __forceinline__ float bf16_lo(unsigned pair) { return __builtin_bit_cast(float, pair << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned pair) { return __builtin_bit_cast(float, pair & 0xFFFF0000u); }
+
+// Half-width H butterflies inside an array of N values (N a multiple of 2H).
+template <int H, int N>
+__device__ __forceinline__ void butterflies(float (&f)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; i += 2 * H)
+#pragma unroll
+        for (int j = i; j < i + H; ++j) {
+            const float u = f[j], w = f[j + H];
+            f[j] = u + w;
+            f[j + H] = u - w;
+        }
+}
+
+// Half-width butterfly across lanes: this lane holds element j (lower) or
+// j + H (upper) of every pair; DPP mask MASK reads the partner lane.
+template <int MASK>
+__device__ __forceinline__ float butterfly_lanes(float own, bool upper) {
+    const float other = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, own), MASK,
+                                                                               0xF, 0xF, false));
+    return upper ? other - own : own + other;
+}
+
+template <int TILE_R, bool DUAL, bool HROW, bool HCOL>
 __global__ __launch_bounds__(256, 4) void cast_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C, int64_t ldx,
                                                    uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
                                                    uint8_t* __restrict__ q_col, uint8_t* __restrict__ s_col,
-                                                   int n_rtiles, int n_ctiles) {
+                                                   int n_rtiles, int n_ctiles, int hshift) {
     constexpr int NI = TILE_R / 8;  // 16-byte loads per thread
     const int t = threadIdx.x;
     const int tile = xcd_remap(blockIdx.x, n_rtiles * n_ctiles);
@@ -64,13 +118,40 @@ __global__ __launch_bounds__(256, 4) void cast_kernel(const uint16_t* __restrict
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const int64_t row = r0 + i * 8 + (t >> 5);
-        unsigned m = pk_max_u16(v[i].x & 0x7FFF7FFFu, v[i].y & 0x7FFF7FFFu);
-        m = pk_max_u16(m, v[i].z & 0x7FFF7FFFu);
-        m = pk_max_u16(m, v[i].w & 0x7FFF7FFFu);
-        unsigned amax = (m & 0xFFFFu) > (m >> 16) ? (m & 0xFFFFu) : (m >> 16);
-        amax = quad_max_u32(amax);
-        const unsigned sb = scale_byte_from_amax(amax);
-        unsigned codes = cvt8(v[i], scale_value(sb));
+        unsigned sb, codes;
+        if constexpr (HROW) {
+            // this lane holds elements 8q .. 8q+7 of its block, q = lane % 4
+            float f[8] = {bf16_lo(v[i].x), bf16_hi(v[i].x), bf16_lo(v[i].y), bf16_hi(v[i].y),
+                          bf16_lo(v[i].z), bf16_hi(v[i].z), bf16_lo(v[i].w), bf16_hi(v[i].w)};
+            butterflies<1>(f);
+            butterflies<2>(f);
+            butterflies<4>(f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = butterfly_lanes<0xB1>(f[e], (t & 1) != 0);  // half-width 8
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = butterfly_lanes<0x4E>(f[e], (t & 2) != 0);  // half-width 16
+            unsigned am = 0u;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const unsigned a = __builtin_bit_cast(unsigned, f[e]) & 0x7FFFFFFFu;
+                am = a > am ? a : am;
+            }
+            sb = scale_byte_from_f32_amax(quad_max_u32(am), hshift);
+            const float sc = scale_value(sb + (unsigned)hshift);
+            codes = 0u;
+            codes = cvt_pair_f32<0>(codes, f[0], f[1], sc);
+            codes = cvt_pair_f32<1>(codes, f[2], f[3], sc);
+            codes = cvt_pair_f32<2>(codes, f[4], f[5], sc);
+            codes = cvt_pair_f32<3>(codes, f[6], f[7], sc);
+        } else {
+            unsigned m = pk_max_u16(v[i].x & 0x7FFF7FFFu, v[i].y & 0x7FFF7FFFu);
+            m = pk_max_u16(m, v[i].z & 0x7FFF7FFFu);
+            m = pk_max_u16(m, v[i].w & 0x7FFF7FFFu);
+            unsigned amax = (m & 0xFFFFu) > (m >> 16) ? (m & 0xFFFFu) : (m >> 16);
+            amax = quad_max_u32(amax);
+            sb = scale_byte_from_amax(amax);
+            codes = cvt8(v[i], scale_value(sb));
+        }
         if (sb == 255u) codes = 0u;
         if (row < row16 && col < kt128_row * 128) {
             *reinterpret_cast<unsigned*>(q_row + code_offset(row, col, kt128_row)) = codes;
@@ -103,16 +184,57 @@ __global__ __launch_bounds__(256, 4) void cast_kernel(const uint16_t* __restrict
             const int64_t c = c0 + cp * 2;
             const int64_t rblk = r0 + rb * 32;      // first row of the block
             if (rblk >= kt256_col * 256) continue;  // beyond the padded scale region
+            u32x4 o0, o1;
+            unsigned sb0, sb1;
+            if constexpr (HCOL) {
+                // both columns of the strip as 32 binary32 values each, transformed in registers
+                float y0[32], y1[32];
+#pragma unroll
+                for (int r = 0; r < 32; ++r) {
+                    const unsigned d = lds[(rb * 32 + r) * 128 + cp];
+                    y0[r] = bf16_lo(d);
+                    y1[r] = bf16_hi(d);
+                }
+                butterflies<1>(y0), butterflies<1>(y1);
+                butterflies<2>(y0), butterflies<2>(y1);
+                butterflies<4>(y0), butterflies<4>(y1);
+                butterflies<8>(y0), butterflies<8>(y1);
+                butterflies<16>(y0), butterflies<16>(y1);
+                unsigned m0 = 0u, m1 = 0u;
+#pragma unroll
+                for (int r = 0; r < 32; ++r) {
+                    const unsigned a0 = __builtin_bit_cast(unsigned, y0[r]) & 0x7FFFFFFFu;
+                    const unsigned a1 = __builtin_bit_cast(unsigned, y1[r]) & 0x7FFFFFFFu;
+                    m0 = a0 > m0 ? a0 : m0;
+                    m1 = a1 > m1 ? a1 : m1;
+                }
+                sb0 = scale_byte_from_f32_amax(m0, hshift);
+                sb1 = scale_byte_from_f32_amax(m1, hshift);
+                const float f0 = scale_value(sb0 + (unsigned)hshift), f1 = scale_value(sb1 + (unsigned)hshift);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    unsigned a0 = 0u, a1 = 0u;
+                    a0 = cvt_pair_f32<0>(a0, y0[w * 8 + 0], y0[w * 8 + 1], f0);
+                    a0 = cvt_pair_f32<1>(a0, y0[w * 8 + 2], y0[w * 8 + 3], f0);
+                    a0 = cvt_pair_f32<2>(a0, y0[w * 8 + 4], y0[w * 8 + 5], f0);
+                    a0 = cvt_pair_f32<3>(a0, y0[w * 8 + 6], y0[w * 8 + 7], f0);
+                    a1 = cvt_pair_f32<0>(a1, y1[w * 8 + 0], y1[w * 8 + 1], f1);
+                    a1 = cvt_pair_f32<1>(a1, y1[w * 8 + 2], y1[w * 8 + 3], f1);
+                    a1 = cvt_pair_f32<2>(a1, y1[w * 8 + 4], y1[w * 8 + 5], f1);
+                    a1 = cvt_pair_f32<3>(a1, y1[w * 8 + 6], y1[w * 8 + 7], f1);
+                    o0[w] = sb0 == 255u ? 0u : a0;
+                    o1[w] = sb1 == 255u ? 0u : a1;
+                }
+            } else {
             unsigned d[32];
 #pragma unroll
             for (int r = 0; r < 32; ++r) d[r] = lds[(rb * 32 + r) * 128 + cp];
             unsigned m = d[0] & 0x7FFF7FFFu;
 #pragma unroll
             for (int r = 1; r < 32; ++r) m = pk_max_u16(m, d[r] & 0x7FFF7FFFu);
-            const unsigned sb0 = scale_byte_from_amax(m & 0xFFFFu);
-            const unsigned sb1 = scale_byte_from_amax(m >> 16);
+            sb0 = scale_byte_from_amax(m & 0xFFFFu);
+            sb1 = scale_byte_from_amax(m >> 16);
             const float f0 = scale_value(sb0), f1 = scale_value(sb1);
-            u32x4 o0, o1;
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
                 unsigned a0 = 0u, a1 = 0u;
@@ -126,6 +248,7 @@ __global__ __launch_bounds__(256, 4) void cast_kernel(const uint16_t* __restrict
 #undef MX_COLPAIR
                 o0[w] = sb0 == 255u ? 0u : a0;
                 o1[w] = sb1 == 255u ? 0u : a1;
+            }
             }
             if (c < col16 && rblk < kt128_col * 128) {
                 *reinterpret_cast<u32x4*>(q_col + code_offset(c, rblk, kt128_col)) = o0;
@@ -142,8 +265,11 @@ __global__ __launch_bounds__(256, 4) void cast_kernel(const uint16_t* __restrict
 }  // namespace mx
 
 // Launchers (internal, called by the C ABI layer after validation).
-extern "C" hipError_t mx_launch_cast(const void* x, int64_t R, int64_t C, int64_t ldx, void* q_row, void* s_row,
-                                     void* q_col, void* s_col, bool dual, hipStream_t stream) {
+// transform_row / transform_col: Walsh-Hadamard on the row / column copy, the
+// transformed copies divided by 2^hshift.
+extern "C" hipError_t mx_launch_cast_h(const void* x, int64_t R, int64_t C, int64_t ldx, void* q_row, void* s_row,
+                                       void* q_col, void* s_col, bool dual, bool transform_row, bool transform_col,
+                                       int hshift, hipStream_t stream) {
     constexpr int TILE_R = 64;
     // rows covered: the row copy's padded scale rows (a multiple of 128), and for
     // the dual cast the column copy's padded contraction (a multiple of 256)
@@ -155,14 +281,27 @@ extern "C" hipError_t mx_launch_cast(const void* x, int64_t R, int64_t C, int64_
     if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
     const dim3 grid((unsigned)total), block(256);
     const uint16_t* xb = static_cast<const uint16_t*>(x);
-    if (dual) {
-        hipLaunchKernelGGL((mx::cast_kernel<TILE_R, true>), grid, block, 0, stream, xb, R, C, ldx,
-                           static_cast<uint8_t*>(q_row), static_cast<uint8_t*>(s_row), static_cast<uint8_t*>(q_col),
-                           static_cast<uint8_t*>(s_col), (int)n_rtiles, (int)n_ctiles);
+    uint8_t *qr = static_cast<uint8_t*>(q_row), *sr = static_cast<uint8_t*>(s_row);
+    uint8_t *qc = static_cast<uint8_t*>(q_col), *scl = static_cast<uint8_t*>(s_col);
+    const int nr = (int)n_rtiles, nc = (int)n_ctiles;
+#define MX_CAST(D, HR, HC)                                                                                  \
+    hipLaunchKernelGGL((mx::cast_kernel<TILE_R, D, HR, HC>), grid, block, 0, stream, xb, R, C, ldx, qr, sr, \
+                       D ? qc : nullptr, D ? scl : nullptr, nr, nc, hshift)
+    if (!dual) {
+        if (transform_row) MX_CAST(false, true, false);
+        else MX_CAST(false, false, false);
+    } else if (transform_row) {
+        if (transform_col) MX_CAST(true, true, true);
+        else MX_CAST(true, true, false);
     } else {
-        hipLaunchKernelGGL((mx::cast_kernel<TILE_R, false>), grid, block, 0, stream, xb, R, C, ldx,
-                           static_cast<uint8_t*>(q_row), static_cast<uint8_t*>(s_row), nullptr, nullptr,
-                           (int)n_rtiles, (int)n_ctiles);
+        if (transform_col) MX_CAST(true, false, true);
+        else MX_CAST(true, false, false);
     }
+#undef MX_CAST
     return hipGetLastError();
+}
+
+extern "C" hipError_t mx_launch_cast(const void* x, int64_t R, int64_t C, int64_t ldx, void* q_row, void* s_row,
+                                     void* q_col, void* s_col, bool dual, hipStream_t stream) {
+    return mx_launch_cast_h(x, R, C, ldx, q_row, s_row, q_col, s_col, dual, false, false, 0, stream);
 }

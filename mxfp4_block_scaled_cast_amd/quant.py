@@ -13,14 +13,17 @@ Roles (which copies a GEMM operand needs in training):
   weight     : row copy (forward B) and column copy (dA's B);
   activation : row copy (forward A) and column copy (dB's B);
   grad       : row copy (dA's A) and column copy (dB's A).
-With ``columnwise=False`` only the row copy is made (inference).
+With ``columnwise=False`` only the row copy is made (inference).  With
+``hadamard=True`` (the README's gradient recipe) the copies that enter the
+backward contractions carry the block Walsh-Hadamard transform
+(``cast_hadamard``).
 """
 from dataclasses import dataclass
 from typing import Dict, Optional, Tuple
 
 import torch
 
-from .api import Mxfp4Tensor, cast, cast_dual
+from .api import Mxfp4Tensor, cast, cast_dual, cast_hadamard
 
 
 @dataclass(frozen=True)
@@ -28,23 +31,33 @@ class MXFP4Quantizer:
     role: str
     rowwise: bool = True
     columnwise: bool = True
+    hadamard: bool = False
 
     @classmethod
-    def for_weight(cls, columnwise=True):
-        return cls("weight", True, columnwise)
+    def for_weight(cls, columnwise=True, hadamard=False):
+        return cls("weight", True, columnwise, hadamard)
 
     @classmethod
-    def for_activation(cls, columnwise=True):
-        return cls("activation", True, columnwise)
+    def for_activation(cls, columnwise=True, hadamard=False):
+        return cls("activation", True, columnwise, hadamard)
 
     @classmethod
-    def for_grad(cls, columnwise=True):
-        return cls("grad", True, columnwise)
+    def for_grad(cls, columnwise=True, hadamard=False):
+        return cls("grad", True, columnwise, hadamard)
 
     def quantize(self, x: torch.Tensor) -> Mxfp4Tensor:
-        """bf16 [R, C] (C % 32 == 0) -> Mxfp4Tensor with the row copy and, if columnwise, the column copy."""
+        """bf16 [R, C] (C % 32 == 0) -> Mxfp4Tensor with the row copy and, if columnwise, the column copy.
+
+        With hadamard (the gradient recipe): a weight or an activation gets its column copy
+        Walsh-Hadamard transformed (it is a B operand of dA or dB), a grad both copies, divided
+        by 32, so the backward products stay unchanged.
+        """
         if not self.rowwise:
             raise ValueError("an MXFP4 operand always carries its row copy")
+        if self.hadamard and self.role == "grad":
+            return cast_hadamard(x, True, self.columnwise, 5, self.columnwise)
+        if self.hadamard and self.columnwise:
+            return cast_hadamard(x, False, True, 0, True)
         if self.columnwise:
             return cast_dual(x)
         return Mxfp4Tensor(cast(x), None, tuple(x.shape))
