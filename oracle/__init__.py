@@ -26,6 +26,11 @@ Canonical layouts (all row-major, no padding except where stated):
 * GEMM: ref[m, n] = sum_k dq(a)[m, k] * dq(b)[n, k] in fp64, and
   absref[m, n] = sum_k |dq(a)[m, k] * dq(b)[n, k]|
 
+MXFP8 (E4M3 elements, E8M0 block scales; the FP8 dB variant): ``cast_rows_fp8``
+/ ``cast_cols_fp8`` with X = floor(log2 amax) - 8 and nearest-even E4M3
+saturating at 448, one code per byte; ``gemm_fp8`` forms exact integer block
+sums.
+
 Hadamard-transformed casts (README "Quick start": grad_out is cast with a
 Hadamard transform): ``cast_rows_hadamard`` / ``cast_cols_hadamard`` apply
 the 32-point Sylvester Walsh-Hadamard matrix to every block in binary32
@@ -122,6 +127,58 @@ def fwht32(x_f32):
     if native.lib().mxo_fwht32(x.ctypes.data, out.ctypes.data, x.shape[0]):
         raise RuntimeError("mxo_fwht32 failed")
     return out
+
+
+def cast_rows_fp8(x_bits, nthreads=None):
+    """MXFP8 (E4M3, E8M0 block scales) row copy: q [R, C] codes, s [R, C/32]."""
+    x = _bits(x_bits)
+    R, C = x.shape
+    if C % 32:
+        raise ValueError("the number of columns must be a multiple of 32")
+    q = np.empty((R, C), np.uint8)
+    s = np.empty((R, C // 32), np.uint8)
+    if native.lib().mxo_cast_rows_fp8(x.ctypes.data, R, C, C, q.ctypes.data, s.ctypes.data, _threads(nthreads)):
+        raise RuntimeError("mxo_cast_rows_fp8 failed")
+    return q, s
+
+
+def cast_cols_fp8(x_bits, nthreads=None):
+    """MXFP8 column copy (blocks of 32 rows, padded with +0): q [C, Rp], s [C, Rp/32]."""
+    x = _bits(x_bits)
+    R, C = x.shape
+    Rp = -(-R // 32) * 32
+    q = np.empty((C, Rp), np.uint8)
+    s = np.empty((C, Rp // 32), np.uint8)
+    if native.lib().mxo_cast_cols_fp8(x.ctypes.data, R, C, C, q.ctypes.data, s.ctypes.data, _threads(nthreads)):
+        raise RuntimeError("mxo_cast_cols_fp8 failed")
+    return q, s
+
+
+def dequant_fp8(q, s):
+    """Dequantized values (fp64) of an MXFP8 (q [R, K], s [R, K/32]) pair."""
+    q = np.ascontiguousarray(q, np.uint8)
+    s = np.ascontiguousarray(s, np.uint8)
+    R, K = q.shape
+    if s.shape != (R, K // 32):
+        raise ValueError("scale shape does not match the codes")
+    out = np.empty((R, K), np.float64)
+    if native.lib().mxo_dequant_fp8(q.ctypes.data, s.ctypes.data, R, K, out.ctypes.data):
+        raise RuntimeError("mxo_dequant_fp8 failed")
+    return out
+
+
+def gemm_fp8(qa, sa, qb, sb, nthreads=None):
+    """ref / absref [M, N] for out = A . B^T on MXFP8 operands."""
+    qa, sa, qb, sb = (np.ascontiguousarray(t, np.uint8) for t in (qa, sa, qb, sb))
+    M, N, K = qa.shape[0], qb.shape[0], qa.shape[1]
+    if qb.shape[1] != K or sa.shape != (M, K // 32) or sb.shape != (N, K // 32):
+        raise ValueError("operand shapes do not agree")
+    ref = np.empty((M, N), np.float64)
+    absref = np.empty((M, N), np.float64)
+    if native.lib().mxo_gemm_fp8(qa.ctypes.data, sa.ctypes.data, qb.ctypes.data, sb.ctypes.data, M, N, K,
+                                 ref.ctypes.data, absref.ctypes.data, _threads(nthreads)):
+        raise RuntimeError("mxo_gemm_fp8 failed")
+    return ref, absref
 
 
 def dequant(q, s):

@@ -330,6 +330,192 @@ int mxo_fwht32(const float* in, float* out, int64_t nblocks) {
     return 0;
 }
 
+/* ---- MXFP8: E4M3 elements with E8M0 block scales ----
+ *
+ * The pages run dB in FP8 (README "MXFP4 training architecture": hipBLASLt
+ * FP8 dB; the 8B recipe note: FP8 current scaling).  This oracle implements
+ * the block-scaled FP8 form (OCP Microscaling v1.0, MXFP8 with E4M3), the FP8
+ * format the MI355X scaled MFMA takes; a per-tensor scale is the case of
+ * equal block scales:
+ *   E4M3    : 1 sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent
+ *             field 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN; no
+ *             infinities; largest magnitude 448 (code 0x7E)
+ *   scale   : X = floor(log2 amax) - 8 (8 = exponent of 448), clamped to
+ *             [-127, 127], -127 for an all-zero block; byte X + 127
+ *   element : x / 2^X rounded to the nearest E4M3 value, ties to the even
+ *             mantissa, magnitudes past 448 saturating to 448, sign bit of x
+ *   codes   : one byte per element; a block with Inf/NaN gets scale 0xFF,
+ *             codes 0
+ *   GEMM    : every E4M3 value is an integer times 2^-9, so block sums are
+ *             exact 64-bit integers, scaled by 2^(Xa + Xb - 18).
+ */
+#define MXO_E4M3_MAX_CODE 0x7E
+
+/* Magnitude of E4M3 code c (0..0x7E) from its bit fields. */
+static double e4m3_magnitude(int c) {
+    int e = (c >> 3) & 0xF, m = c & 7;
+    if (e == 0) return ldexp((double)m, -9);
+    return ldexp((double)(8 + m), e - 10);
+}
+
+/* The same magnitude as an integer number of 2^-9 units. */
+static int64_t e4m3_units(int c) {
+    int e = (c >> 3) & 0xF, m = c & 7;
+    if (e == 0) return m;
+    return (int64_t)(8 + m) << (e - 1);
+}
+
+/* Nearest E4M3 magnitude code for a >= 0 (finite): the quantum of the binade
+ * of a (2^-9 below 2^-6) divides a exactly; the quotient rounds to the nearest
+ * integer, ties to even (= even mantissa); past 448 the code saturates. */
+static int e4m3_round(double a) {
+    if (a >= 448.0) return MXO_E4M3_MAX_CODE;
+    int e = a > 0.0 ? floor_log2(a) : -6;
+    if (e < -6) e = -6;
+    double q = nearbyint(ldexp(a, 3 - e));      /* a / 2^(e-3), exact; default mode rounds ties to even */
+    int code = (e + 7) * 8 + (int)q - 8;        /* q = 16 carries into the next binade */
+    return code > MXO_E4M3_MAX_CODE ? MXO_E4M3_MAX_CODE : code;
+}
+
+static uint8_t quantize_block_fp8(const uint16_t* x, int64_t stride, int n, uint8_t codes[MXO_BLOCK]) {
+    double amax = 0.0;
+    for (int i = 0; i < n; ++i) {
+        uint16_t h = x[i * stride];
+        if (!bf16_is_finite(h)) {
+            memset(codes, 0, MXO_BLOCK);
+            return 0xFF;
+        }
+        double a = fabs(bf16_value(h));
+        if (a > amax) amax = a;
+    }
+    int X;
+    if (amax == 0.0) {
+        X = -127;
+    } else {
+        X = floor_log2(amax) - 8;
+        if (X < -127) X = -127;
+        if (X > 127) X = 127;
+    }
+    for (int i = 0; i < MXO_BLOCK; ++i) {
+        if (i >= n) { codes[i] = 0; continue; }
+        uint16_t h = x[i * stride];
+        codes[i] = (uint8_t)(e4m3_round(ldexp(fabs(bf16_value(h)), -X)) | ((h >> 15) << 7));
+    }
+    return (uint8_t)(X + 127);
+}
+
+static void cast_rows_fp8_range(void* p, int64_t lo, int64_t hi) {
+    cast_ctx* c = (cast_ctx*)p;
+    int64_t nb = c->C / MXO_BLOCK;
+    for (int64_t r = lo; r < hi; ++r)
+        for (int64_t b = 0; b < nb; ++b)
+            c->s[r * nb + b] = quantize_block_fp8(c->x + r * c->ldx + b * MXO_BLOCK, 1, MXO_BLOCK,
+                                                  c->q + r * c->C + b * MXO_BLOCK);
+}
+
+/* MXFP8 row copy of x [R, C] (C % 32 == 0): q [R, C] codes, s [R, C/32]. */
+int mxo_cast_rows_fp8(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint8_t* q, uint8_t* s, int nthreads) {
+    if (R < 0 || C < 0 || C % MXO_BLOCK != 0 || ldx < C) return -1;
+    cast_ctx c = {x, R, C, ldx, q, s};
+    parallel_for(R, nthreads, cast_rows_fp8_range, &c);
+    return 0;
+}
+
+static void cast_cols_fp8_range(void* p, int64_t lo, int64_t hi) {
+    cast_ctx* c = (cast_ctx*)p;
+    int64_t nb = (c->R + MXO_BLOCK - 1) / MXO_BLOCK;
+    int64_t Rp = nb * MXO_BLOCK;
+    for (int64_t col = lo; col < hi; ++col)
+        for (int64_t b = 0; b < nb; ++b) {
+            int64_t r0 = b * MXO_BLOCK;
+            int n = (int)((c->R - r0) < MXO_BLOCK ? (c->R - r0) : MXO_BLOCK);
+            c->s[col * nb + b] = quantize_block_fp8(c->x + r0 * c->ldx + col, c->ldx, n, c->q + col * Rp + r0);
+        }
+}
+
+/* MXFP8 column copy of x [R, C]: q [C, Rp], s [C, Rp/32], Rp = ceil(R/32)*32, rows past R +0. */
+int mxo_cast_cols_fp8(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint8_t* q, uint8_t* s, int nthreads) {
+    if (R < 0 || C < 0 || ldx < C) return -1;
+    cast_ctx c = {x, R, C, ldx, q, s};
+    parallel_for(C, nthreads, cast_cols_fp8_range, &c);
+    return 0;
+}
+
+/* out[r, k] = e4m3(q[r, k]) * 2^(s[r, k/32] - 127); NaN for scale 0xFF or a NaN code. */
+int mxo_dequant_fp8(const uint8_t* q, const uint8_t* s, int64_t R, int64_t K, double* out) {
+    if (R < 0 || K < 0 || K % MXO_BLOCK != 0) return -1;
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t k = 0; k < K; ++k) {
+            int code = q[r * K + k];
+            uint8_t sc = s[r * (K / MXO_BLOCK) + k / MXO_BLOCK];
+            if (sc == 0xFF || (code & 0x7F) == 0x7F) { out[r * K + k] = NAN; continue; }
+            double mag = e4m3_magnitude(code & 0x7F);
+            out[r * K + k] = ldexp((code & 0x80) ? -mag : mag, (int)sc - 127);
+        }
+    return 0;
+}
+
+typedef struct {
+    const uint8_t *qa, *sa, *qb, *sb;
+    int64_t M, N, K;
+    double *ref, *absref;
+    int32_t* ub;   /* B as signed 2^-9 units, [N, K] */
+} gemm8_ctx;
+
+static int32_t e4m3_signed_units(uint8_t c) {
+    int32_t v = (int32_t)e4m3_units(c & 0x7F);
+    return (c & 0x80) ? -v : v;
+}
+
+static void unpack8_b_range(void* p, int64_t lo, int64_t hi) {
+    gemm8_ctx* g = (gemm8_ctx*)p;
+    for (int64_t n = lo; n < hi; ++n)
+        for (int64_t k = 0; k < g->K; ++k) g->ub[n * g->K + k] = e4m3_signed_units(g->qb[n * g->K + k]);
+}
+
+static void gemm8_rows_range(void* p, int64_t lo, int64_t hi) {
+    gemm8_ctx* g = (gemm8_ctx*)p;
+    int64_t nb = g->K / MXO_BLOCK;
+    int32_t* ua = (int32_t*)malloc((size_t)(g->K > 0 ? g->K : 1) * sizeof(int32_t));
+    if (!ua) return;
+    for (int64_t m = lo; m < hi; ++m) {
+        for (int64_t k = 0; k < g->K; ++k) ua[k] = e4m3_signed_units(g->qa[m * g->K + k]);
+        for (int64_t n = 0; n < g->N; ++n) {
+            double acc = 0.0, aacc = 0.0;
+            const int32_t* ub = g->ub + n * g->K;
+            for (int64_t b = 0; b < nb; ++b) {
+                uint8_t xa = g->sa[m * nb + b], xb = g->sb[n * nb + b];
+                if (xa == 0xFF || xb == 0xFF) { acc = NAN; aacc = NAN; continue; }
+                int64_t dot = 0, adot = 0;
+                for (int i = 0; i < MXO_BLOCK; ++i) {
+                    int64_t prod = (int64_t)ua[b * MXO_BLOCK + i] * (int64_t)ub[b * MXO_BLOCK + i];
+                    dot += prod;
+                    adot += prod < 0 ? -prod : prod;
+                }
+                int e = (int)xa + (int)xb - 254 - 18;
+                acc += ldexp((double)dot, e);
+                aacc += ldexp((double)adot, e);
+            }
+            g->ref[m * g->N + n] = acc;
+            g->absref[m * g->N + n] = aacc;
+        }
+    }
+    free(ua);
+}
+
+/* ref / absref [M, N] of out = A . B^T on MXFP8 operands (canonical row-major codes). */
+int mxo_gemm_fp8(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb, int64_t M, int64_t N,
+                 int64_t K, double* ref, double* absref, int nthreads) {
+    if (M < 0 || N < 0 || K < 0 || K % MXO_BLOCK != 0) return -1;
+    gemm8_ctx g = {qa, sa, qb, sb, M, N, K, ref, absref, NULL};
+    g.ub = (int32_t*)malloc((size_t)(N > 0 ? N : 1) * (size_t)(K > 0 ? K : 1) * sizeof(int32_t));
+    if (!g.ub) return -1;
+    parallel_for(N, nthreads, unpack8_b_range, &g);
+    parallel_for(M, nthreads, gemm8_rows_range, &g);
+    free(g.ub);
+    return 0;
+}
+
 /* ---- dequantization ---- */
 
 /* out[r, k] = e2m1(q[r,k]) * 2^(s[r, k/32] - 127), NaN for scale 0xFF.  K % 32 == 0. */

@@ -41,8 +41,13 @@ def lib():
         L.mxo_cast_rows_hadamard.argtypes = [p, i64, i64, i64, i32, p, p, i32]
         L.mxo_cast_cols_hadamard.argtypes = [p, i64, i64, i64, i32, p, p, i32]
         L.mxo_fwht32.argtypes = [p, p, i64]
+        L.mxo_cast_rows_fp8.argtypes = [p, i64, i64, i64, p, p, i32]
+        L.mxo_cast_cols_fp8.argtypes = [p, i64, i64, i64, p, p, i32]
+        L.mxo_dequant_fp8.argtypes = [p, p, i64, i64, p]
+        L.mxo_gemm_fp8.argtypes = [p, p, p, p, i64, i64, i64, p, p, i32]
         for f in (L.mxo_cast_rows, L.mxo_cast_cols, L.mxo_dequant, L.mxo_gemm, L.mxo_gemm_pairs,
-                  L.mxo_cast_rows_hadamard, L.mxo_cast_cols_hadamard, L.mxo_fwht32):
+                  L.mxo_cast_rows_hadamard, L.mxo_cast_cols_hadamard, L.mxo_fwht32, L.mxo_cast_rows_fp8,
+                  L.mxo_cast_cols_fp8, L.mxo_dequant_fp8, L.mxo_gemm_fp8):
             f.restype = i32
         _lib = L
     return _lib

@@ -160,3 +160,43 @@ def quantize_rationals(values, negative=None):
     X = shared_exponent(vals)
     codes = [nearest_e2m1_magnitude(abs(v) / Fraction(2) ** X) | (8 if neg else 0) for v, neg in zip(vals, negative)]
     return X + 127, codes
+
+
+# ---- E4M3 (MXFP8 elements): 1 sign, 4 exponent bits (bias 7), 3 mantissa bits, exponent
+# field 0 subnormal, S.1111.111 NaN, no infinities (OCP 8-bit floating point formats) ----
+
+def e4m3_value(code):
+    """Value of the 8-bit E4M3 code, from its bit fields (None for NaN)."""
+    sign = (code >> 7) & 1
+    e = (code >> 3) & 0xF
+    m = code & 7
+    if e == 0xF and m == 7:
+        return None
+    if e == 0:
+        mag = Fraction(m, 8) * Fraction(2) ** -6
+    else:
+        mag = (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+    return -mag if sign else mag
+
+
+def nearest_e4m3_magnitude(a):
+    """Code 0..0x7E of the E4M3 magnitude nearest to a >= 0 (search over all codes); on a tie
+    the even code wins; past the largest magnitude the nearest is the largest."""
+    best = None
+    for c in range(0x7F):
+        d = abs(a - e4m3_value(c))
+        if best is None or d < best[0] or (d == best[0] and c % 2 == 0):
+            best = (d, c)
+    return best[1]
+
+
+def quantize_block_fp8(bits):
+    """MXFP8 block: (scale byte, 32 codes); X = floor(log2 amax) - 8 clamped to [-127, 127]."""
+    bits = list(bits) + [0] * (BLOCK - len(bits))
+    vals = [bf16_value(h) for h in bits]
+    if any(v is None for v in vals):
+        return 0xFF, [0] * BLOCK
+    amax = max(abs(v) for v in vals)
+    X = -127 if amax == 0 else min(127, max(-127, floor_log2(amax) - 8))
+    codes = [nearest_e4m3_magnitude(abs(v) / Fraction(2) ** X) | (((h >> 15) & 1) << 7) for h, v in zip(bits, vals)]
+    return X + 127, codes
