@@ -49,6 +49,15 @@
  *   The row copy of x[R, C] is the MX operand (R rows, K = C).  The column
  *   copy is the MX operand (C rows, K = Rp) with Rp = ceil(R/32)*32: row c of
  *   it quantizes column c of x in blocks of 32 rows, rows R..Rp-1 taken as +0.
+ *
+ * MXFP8 operand (the FP8 dB variant, see MXFP4_STEP_FP8_WGRAD): the same
+ * block scales (X = floor(log2 amax) - 8, byte X + 127, same scale tiles and
+ * byte positions as above), E4M3 elements x / 2^X rounded to nearest even
+ * and saturating at +-448, one code per byte.  Codes in 1 KB tiles of 16
+ * rows x 64 elements: with KT8 = ceil(K/64), element (r, k) is byte
+ *         ((r/16) * KT8 + k/64) * 1024 + (r%16) * 64 + k%64.
+ *   Size: ceil(R/16) * KT8 * 1024 bytes.  A block holding Inf/NaN gets scale
+ *   0xFF and codes 0, as for MXFP4.
  */
 #ifndef MXFP4_H
 #define MXFP4_H
@@ -159,6 +168,35 @@ int mxfp4_gemm_nn(const void* a_q, const void* a_s, const void* bcol_q, const vo
                   int64_t K, void* out, int64_t ldo, hipStream_t stream);
 
 /*
+ * F3 -- MXFP8 (E4M3) operands for the FP8 dB of the jax-aiter README,
+ * "MXFP4 training architecture" (its backward runs dB as an FP8 dot while
+ * the forward pass and dA stay FP4).  Argument rules, alignment and errors
+ * as for the MXFP4 counterparts above; operands in the MXFP8 format above.
+ *
+ * mxfp8_operand_layout_of : sizes of an MXFP8 operand (code_k_tiles =
+ *   ceil(k/64)); host only.
+ * mxfp8_cast              : row copy of x as MXFP8.
+ * mxfp8_cast_dual         : row and column copies, both MXFP8.
+ * mxfp4_cast_dual_fp8col  : MXFP4 row copy and MXFP8 column copy in one pass
+ *   (the activation / dOut cast of the FP8-dB step: the row copy feeds an
+ *   FP4 product, the column copy the FP8 dB).
+ * mxfp8_gemm_nt           : out[M, N] = bf16( A[M, K] . B[N, K]^T ) on two
+ *   MXFP8 operands (fp32 accumulation, nearest-even bf16 output).
+ */
+int mxfp8_operand_layout_of(int64_t rows, int64_t k, mxfp4_operand_layout* out);
+
+int mxfp8_cast(const void* x, int64_t rows, int64_t cols, int64_t ldx, void* q, void* s, hipStream_t stream);
+
+int mxfp8_cast_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx, void* q_row, void* s_row, void* q_col,
+                    void* s_col, hipStream_t stream);
+
+int mxfp4_cast_dual_fp8col(const void* x, int64_t rows, int64_t cols, int64_t ldx, void* q_row, void* s_row,
+                           void* q_col, void* s_col, hipStream_t stream);
+
+int mxfp8_gemm_nt(const void* a_q, const void* a_s, const void* b_q, const void* b_s, int64_t M, int64_t N, int64_t K,
+                  void* out, int64_t ldo, hipStream_t stream);
+
+/*
  * A7 -- workspace for gemm_fp4_bf16_fwd/bwd with activations [M, K] and
  * weights [N, K].  training != 0 sizes for fwd + bwd: it holds the row copies
  * of A and W, the saved column copies of A and W that the backward pass reads,
@@ -241,7 +279,15 @@ int gemm_fp4_bf16_bwd_qw(const void* dout, const void* w_col_q, const void* w_co
  *     w_row_s in the forward, w_col_q / w_col_s in the backward, made by
  *     mxfp4_cast_dual, or by mxfp4_cast_hadamard with transform_col = 1,
  *     shift 0 under HADAMARD_GRAD); the workspace is
- *     gemm_fp4_bf16_workspace_bytes_qw's, else gemm_fp4_bf16_workspace_bytes'.
+ *     gemm_fp4_bf16_workspace_bytes_qw's, else gemm_fp4_bf16_workspace_bytes';
+ *   MXFP4_STEP_FP8_WGRAD     : F3, dB in MXFP8 (README "MXFP4 training
+ *     architecture": the backward's dB is an FP8 dot).  Needs TRAINING in the
+ *     forward; the column copies of A and dOut are MXFP8 (made in the same
+ *     passes as the MXFP4 row copies) and dB is mxfp8_gemm_nt on them; the
+ *     forward product and dA are unchanged.  Not combinable with
+ *     HADAMARD_GRAD (MXFP4_EINVAL).
+ * gemm_fp4_bf16_workspace_bytes_ex sizes the workspace for any flag set
+ * (0 for invalid sizes or flags).
  * The backward pass takes the forward's flags.  Unknown flags: MXFP4_EINVAL.
  * gemm_fp4_bf16_fwd / _bwd / _fwd_qw / _bwd_qw are these with HADAMARD_GRAD
  * clear.
@@ -249,6 +295,9 @@ int gemm_fp4_bf16_bwd_qw(const void* dout, const void* w_col_q, const void* w_co
 #define MXFP4_STEP_TRAINING 1u
 #define MXFP4_STEP_HADAMARD_GRAD 2u
 #define MXFP4_STEP_QUANTIZED_W 4u
+#define MXFP4_STEP_FP8_WGRAD 8u
+
+size_t gemm_fp4_bf16_workspace_bytes_ex(int64_t M, int64_t N, int64_t K, unsigned flags);
 
 int gemm_fp4_bf16_fwd_ex(const void* a, const void* w, const void* w_row_q, const void* w_row_s, int64_t M, int64_t N,
                          int64_t K, void* out, void* ws, size_t ws_bytes, unsigned flags, hipStream_t stream);

@@ -35,9 +35,15 @@ SIGNATURES = [
     ("mxfp4_cast_hadamard", _i32, [_p, _i64, _i64, _i64, _p, _p, _p, _p, _i32, _i32, _i32, _p]),
     ("gemm_fp4_bf16_fwd_ex", _i32, [_p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _sz, ctypes.c_uint, _p]),
     ("gemm_fp4_bf16_bwd_ex", _i32, [_p, _p, _p, _i64, _i64, _i64, _p, _sz, _p, _p, ctypes.c_uint, _p]),
+    ("mxfp8_operand_layout_of", _i32, [_i64, _i64, ctypes.POINTER(OperandLayout)]),
+    ("mxfp8_cast", _i32, [_p, _i64, _i64, _i64, _p, _p, _p]),
+    ("mxfp8_cast_dual", _i32, [_p, _i64, _i64, _i64, _p, _p, _p, _p, _p]),
+    ("mxfp4_cast_dual_fp8col", _i32, [_p, _i64, _i64, _i64, _p, _p, _p, _p, _p]),
+    ("mxfp8_gemm_nt", _i32, [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _p]),
+    ("gemm_fp4_bf16_workspace_bytes_ex", _sz, [_i64, _i64, _i64, ctypes.c_uint]),
 ]
 
-STEP_TRAINING, STEP_HADAMARD_GRAD, STEP_QUANTIZED_W = 1, 2, 4
+STEP_TRAINING, STEP_HADAMARD_GRAD, STEP_QUANTIZED_W, STEP_FP8_WGRAD = 1, 2, 4, 8
 
 STATUS = {0: "MXFP4_OK", -1: "MXFP4_EINVAL", -2: "MXFP4_EALIGN", -3: "MXFP4_EDEVICE",
           -4: "MXFP4_ELAUNCH", -5: "MXFP4_ERANGE", -6: "MXFP4_ESPACE"}
@@ -77,7 +83,11 @@ def check(status, where):
         raise Mxfp4Error(status, where)
 
 
-def operand_layout(rows, k):
+def operand_layout(rows, k, fmt=4):
+    """Sizes of an MX operand: fmt 4 = MXFP4, 8 = MXFP8."""
     out = OperandLayout()
-    check(lib().mxfp4_operand_layout_of(int(rows), int(k), ctypes.byref(out)), "mxfp4_operand_layout_of")
+    name = "mxfp8_operand_layout_of" if fmt == 8 else "mxfp4_operand_layout_of"
+    if fmt not in (4, 8):
+        raise ValueError("fmt must be 4 or 8")
+    check(getattr(lib(), name)(int(rows), int(k), ctypes.byref(out)), name)
     return out

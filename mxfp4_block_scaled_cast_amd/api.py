@@ -5,7 +5,10 @@ cast and GEMM runs in the HIP kernels behind include/mxfp4.h.  Names follow
 jax-aiter's MXFP4 path (README, "Supported ops" and "Quick start"):
 ``cast`` / ``cast_dual`` (CastMxfp4JA / CastMxfp4DualJA), ``gemm_nt`` (the
 low-level gemm_fp4 on pre-quantized operands), ``gemm_nn`` (the dA form),
-and the differentiable ``gemm_fp4_bf16``.
+and the differentiable ``gemm_fp4_bf16``.  The MXFP8 functions
+(``cast_fp8``, ``cast_fp8_dual``, ``cast_dual_fp8col``, ``gemm_fp8_nt``)
+and the ``fp8_wgrad`` step option serve the FP8 dB that the README's
+"MXFP4 training architecture" section describes.
 """
 from dataclasses import dataclass
 from typing import Optional, Tuple
@@ -17,11 +20,13 @@ from . import _native as N
 
 @dataclass
 class MxOperand:
-    """One quantized copy in the tiled MX layout: E2M1 codes q and E8M0 scales s (flat uint8 buffers)."""
+    """One quantized copy in the tiled MX layout: element codes q and E8M0 scales s (flat
+    uint8 buffers); fmt 4 = MXFP4 (E2M1, two per byte), 8 = MXFP8 (E4M3, one per byte)."""
     q: torch.Tensor
     s: torch.Tensor
     rows: int
     k: int
+    fmt: int = 4
 
 
 @dataclass
@@ -48,17 +53,24 @@ def _check_bf16_matrix(x, name):
         raise ValueError("%s must have a unit stride along its last dimension" % name)
 
 
-def empty_operand(rows, k, device):
-    L = N.operand_layout(rows, k)
+def empty_operand(rows, k, device, fmt=4):
+    L = N.operand_layout(rows, k, fmt)
     q = torch.empty((L.q_bytes,), dtype=torch.uint8, device=device)
     s = torch.empty((L.s_bytes,), dtype=torch.uint8, device=device)
-    return MxOperand(q, s, rows, k)
+    return MxOperand(q, s, rows, k, fmt)
+
+
+def _check_out_operand(op, rows, k, fmt, name):
+    if op.rows != rows or op.k != k or op.fmt != fmt:
+        raise ValueError("%s must be an MXFP%d operand of %d rows, k=%d" % (name, fmt, rows, k))
 
 
 def cast(x, out: Optional[MxOperand] = None) -> MxOperand:
     """Row copy of bf16 x [R, C] (C % 32 == 0)."""
     _check_bf16_matrix(x, "x")
     R, C = x.shape
+    if out is not None:
+        _check_out_operand(out, R, C, 4, "out")
     op = out if out is not None else empty_operand(R, C, x.device)
     st = N.lib().mxfp4_cast(x.data_ptr(), R, C, x.stride(0), op.q.data_ptr(), op.s.data_ptr(), _stream(x.device))
     N.check(st, "mxfp4_cast")
@@ -70,6 +82,10 @@ def cast_dual(x, row: Optional[MxOperand] = None, col: Optional[MxOperand] = Non
     _check_bf16_matrix(x, "x")
     R, C = x.shape
     Rp = -(-R // 32) * 32
+    if row is not None:
+        _check_out_operand(row, R, C, 4, "row")
+    if col is not None:
+        _check_out_operand(col, C, Rp, 4, "col")
     row = row if row is not None else empty_operand(R, C, x.device)
     col = col if col is not None else empty_operand(C, Rp, x.device)
     st = N.lib().mxfp4_cast_dual(x.data_ptr(), R, C, x.stride(0), row.q.data_ptr(), row.s.data_ptr(),
@@ -98,6 +114,38 @@ def cast_hadamard(x, transform_row=True, transform_col=True, shift=0, columnwise
     return Mxfp4Tensor(row, col, (R, C), bool(transform_row), bool(transform_col and columnwise))
 
 
+def cast_fp8(x) -> MxOperand:
+    """MXFP8 (E4M3) row copy of bf16 x [R, C] (C % 32 == 0)."""
+    _check_bf16_matrix(x, "x")
+    R, C = x.shape
+    op = empty_operand(R, C, x.device, 8)
+    st = N.lib().mxfp8_cast(x.data_ptr(), R, C, x.stride(0), op.q.data_ptr(), op.s.data_ptr(), _stream(x.device))
+    N.check(st, "mxfp8_cast")
+    return op
+
+
+def _cast_dual_formats(x, row_fmt, fn, name) -> Mxfp4Tensor:
+    _check_bf16_matrix(x, "x")
+    R, C = x.shape
+    Rp = -(-R // 32) * 32
+    row = empty_operand(R, C, x.device, row_fmt)
+    col = empty_operand(C, Rp, x.device, 8)
+    st = fn(x.data_ptr(), R, C, x.stride(0), row.q.data_ptr(), row.s.data_ptr(), col.q.data_ptr(), col.s.data_ptr(),
+            _stream(x.device))
+    N.check(st, name)
+    return Mxfp4Tensor(row, col, (R, C))
+
+
+def cast_fp8_dual(x) -> Mxfp4Tensor:
+    """MXFP8 row and column copies of bf16 x [R, C] from one read of x."""
+    return _cast_dual_formats(x, 8, N.lib().mxfp8_cast_dual, "mxfp8_cast_dual")
+
+
+def cast_dual_fp8col(x) -> Mxfp4Tensor:
+    """MXFP4 row copy and MXFP8 column copy of bf16 x [R, C] from one read of x."""
+    return _cast_dual_formats(x, 4, N.lib().mxfp4_cast_dual_fp8col, "mxfp4_cast_dual_fp8col")
+
+
 def _gemm(fn, name, a: MxOperand, b: MxOperand, out):
     if a.k != b.k:
         raise ValueError("contraction lengths differ: %d vs %d" % (a.k, b.k))
@@ -112,14 +160,27 @@ def _gemm(fn, name, a: MxOperand, b: MxOperand, out):
     return out
 
 
+def _check_formats(a, b, fmt):
+    if a.fmt != fmt or b.fmt != fmt:
+        raise ValueError("operands are MXFP%d / MXFP%d, this product takes MXFP%d" % (a.fmt, b.fmt, fmt))
+
+
 def gemm_nt(a: MxOperand, b: MxOperand, out=None):
-    """out[M, N] = dq(a)[M, K] . dq(b)[N, K]^T in bf16."""
+    """out[M, N] = dq(a)[M, K] . dq(b)[N, K]^T in bf16 (two MXFP4 operands)."""
+    _check_formats(a, b, 4)
     return _gemm(N.lib().mxfp4_gemm_nt, "mxfp4_gemm_nt", a, b, out)
 
 
 def gemm_nn(a: MxOperand, bcol: MxOperand, out=None):
     """out[M, N] = dq(a)[M, K] . B[K, N], B given by its column copy (N rows, contraction K)."""
+    _check_formats(a, bcol, 4)
     return _gemm(N.lib().mxfp4_gemm_nn, "mxfp4_gemm_nn", a, bcol, out)
+
+
+def gemm_fp8_nt(a: MxOperand, b: MxOperand, out=None):
+    """out[M, N] = dq(a)[M, K] . dq(b)[N, K]^T in bf16 (two MXFP8 operands)."""
+    _check_formats(a, b, 8)
+    return _gemm(N.lib().mxfp8_gemm_nt, "mxfp8_gemm_nt", a, b, out)
 
 
 def workspace_bytes(M, Nn, K, training=True):
@@ -130,11 +191,19 @@ def workspace_bytes_qw(M, Nn, K, training=True):
     return int(N.lib().gemm_fp4_bf16_workspace_bytes_qw(M, Nn, K, 1 if training else 0))
 
 
-def _flags(training, hadamard_grad, quantized_w):
+def workspace_bytes_ex(M, Nn, K, flags):
+    return int(N.lib().gemm_fp4_bf16_workspace_bytes_ex(M, Nn, K, int(flags)))
+
+
+def _flags(training, hadamard_grad, quantized_w, fp8_wgrad=False):
     if hadamard_grad and not training:
         raise ValueError("the Hadamard gradient recipe only applies to training")
+    if fp8_wgrad and not training:
+        raise ValueError("the FP8 wgrad only applies to training")
+    if fp8_wgrad and hadamard_grad:
+        raise ValueError("the Hadamard recipe and the FP8 wgrad do not combine")
     return ((N.STEP_TRAINING if training else 0) | (N.STEP_HADAMARD_GRAD if hadamard_grad else 0) |
-            (N.STEP_QUANTIZED_W if quantized_w else 0))
+            (N.STEP_QUANTIZED_W if quantized_w else 0) | (N.STEP_FP8_WGRAD if fp8_wgrad else 0))
 
 
 def _check_weight_fp4(w_fp4, Nn, K, training, hadamard_grad):
@@ -147,7 +216,7 @@ def _check_weight_fp4(w_fp4, Nn, K, training, hadamard_grad):
                          ("carries" if w_fp4.hadamard_col else "lacks", bool(hadamard_grad)))
 
 
-def _fwd(a, w, w_fp4, training, ws, out, hadamard_grad):
+def _fwd(a, w, w_fp4, training, ws, out, hadamard_grad, fp8_wgrad=False):
     _check_bf16_matrix(a, "a")
     if not a.is_contiguous():
         raise ValueError("a must be contiguous")
@@ -159,12 +228,11 @@ def _fwd(a, w, w_fp4, training, ws, out, hadamard_grad):
         if w.shape[1] != K:
             raise ValueError("a and w disagree on K")
         Nn = w.shape[0]
-        nbytes = workspace_bytes(M, Nn, K, training)
     else:
         Nn = w_fp4.shape[0]
         _check_weight_fp4(w_fp4, Nn, K, training, hadamard_grad)
-        nbytes = workspace_bytes_qw(M, Nn, K, training)
-    flags = _flags(training, hadamard_grad, w_fp4 is not None)
+    flags = _flags(training, hadamard_grad, w_fp4 is not None, fp8_wgrad)
+    nbytes = workspace_bytes_ex(M, Nn, K, flags)
     if ws is None:
         ws = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=a.device)
     if out is None:
@@ -178,7 +246,7 @@ def _fwd(a, w, w_fp4, training, ws, out, hadamard_grad):
     return out, ws
 
 
-def _bwd(dout, w_fp4, M, Nn, K, ws, need_da, need_dw, da, dw, hadamard_grad):
+def _bwd(dout, w_fp4, M, Nn, K, ws, need_da, need_dw, da, dw, hadamard_grad, fp8_wgrad=False):
     _check_bf16_matrix(dout, "dout")
     if not dout.is_contiguous():
         dout = dout.contiguous()
@@ -190,55 +258,61 @@ def _bwd(dout, w_fp4, M, Nn, K, ws, need_da, need_dw, da, dw, hadamard_grad):
     st = N.lib().gemm_fp4_bf16_bwd_ex(dout.data_ptr(), c.q.data_ptr() if c is not None else None,
                                       c.s.data_ptr() if c is not None else None, M, Nn, K, ws.data_ptr(), ws.numel(),
                                       da.data_ptr() if need_da else None, dw.data_ptr() if need_dw else None,
-                                      _flags(True, hadamard_grad, w_fp4 is not None), _stream(dout.device))
+                                      _flags(True, hadamard_grad, w_fp4 is not None, fp8_wgrad),
+                                      _stream(dout.device))
     N.check(st, "gemm_fp4_bf16_bwd")
     return (da if need_da else None), (dw if need_dw else None)
 
 
-def gemm_fp4_bf16_fwd(a, w, training=True, ws=None, out=None, hadamard_grad=False):
+def gemm_fp4_bf16_fwd(a, w, training=True, ws=None, out=None, hadamard_grad=False, fp8_wgrad=False):
     """Forward of gemm_fp4_bf16 on 2-D contiguous bf16 a [M, K], w [N, K] -> (out [M, N], ws)."""
-    return _fwd(a, w, None, training, ws, out, hadamard_grad)
+    return _fwd(a, w, None, training, ws, out, hadamard_grad, fp8_wgrad)
 
 
-def gemm_fp4_bf16_bwd(dout, M, Nn, K, ws, need_da=True, need_dw=True, da=None, dw=None, hadamard_grad=False):
-    """Backward of gemm_fp4_bf16 from the workspace of a training forward -> (da, dw)."""
-    return _bwd(dout, None, M, Nn, K, ws, need_da, need_dw, da, dw, hadamard_grad)
+def gemm_fp4_bf16_bwd(dout, M, Nn, K, ws, need_da=True, need_dw=True, da=None, dw=None, hadamard_grad=False,
+                      fp8_wgrad=False):
+    """Backward of gemm_fp4_bf16 from the workspace of a training forward -> (da, dw).
+    The options must be the forward's."""
+    return _bwd(dout, None, M, Nn, K, ws, need_da, need_dw, da, dw, hadamard_grad, fp8_wgrad)
 
 
-def gemm_fp4_bf16_fwd_qw(a, w_fp4, training=True, ws=None, out=None, hadamard_grad=False):
+def gemm_fp4_bf16_fwd_qw(a, w_fp4, training=True, ws=None, out=None, hadamard_grad=False, fp8_wgrad=False):
     """Forward with a pre-quantized weight (Mxfp4Tensor of W [N, K]) -> (out [M, N], ws)."""
-    return _fwd(a, None, w_fp4, training, ws, out, hadamard_grad)
+    return _fwd(a, None, w_fp4, training, ws, out, hadamard_grad, fp8_wgrad)
 
 
 def gemm_fp4_bf16_bwd_qw(dout, w_fp4, M, Nn, K, ws, need_da=True, need_dw=True, da=None, dw=None,
-                         hadamard_grad=False):
+                         hadamard_grad=False, fp8_wgrad=False):
     """Backward of gemm_fp4_bf16_fwd_qw (W's column copy from w_fp4) -> (da, dw)."""
-    return _bwd(dout, w_fp4, M, Nn, K, ws, need_da, need_dw, da, dw, hadamard_grad)
+    return _bwd(dout, w_fp4, M, Nn, K, ws, need_da, need_dw, da, dw, hadamard_grad, fp8_wgrad)
 
 
 class _GemmFp4Bf16(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, a, w, w_fp4, hadamard_grad):
+    def forward(ctx, a, w, w_fp4, hadamard_grad, fp8_wgrad):
         training = bool(ctx.needs_input_grad[0] or ctx.needs_input_grad[1])
         had = bool(hadamard_grad) and training
-        out, ws = _fwd(a, w if w_fp4 is None else None, w_fp4, training, None, None, had)
+        f8 = bool(fp8_wgrad) and training
+        out, ws = _fwd(a, w if w_fp4 is None else None, w_fp4, training, None, None, had, f8)
         ctx.dims = (a.shape[0], w.shape[0], a.shape[1])
         ctx.ws = ws if training else None
         ctx.w_fp4 = w_fp4
         ctx.hadamard = had
+        ctx.fp8_wgrad = f8
         return out
 
     @staticmethod
     def backward(ctx, dout):
         M, Nn, K = ctx.dims
         da, dw = _bwd(dout, ctx.w_fp4, M, Nn, K, ctx.ws, ctx.needs_input_grad[0], ctx.needs_input_grad[1], None,
-                      None, ctx.hadamard)
+                      None, ctx.hadamard, ctx.fp8_wgrad)
         ctx.ws = None
         ctx.w_fp4 = None
-        return da, dw, None, None
+        return da, dw, None, None, None
 
 
-def gemm_fp4_bf16(a, w, w_fp4: Optional[Mxfp4Tensor] = None, hadamard_grad: bool = False):
+def gemm_fp4_bf16(a, w, w_fp4: Optional[Mxfp4Tensor] = None, hadamard_grad: bool = False,
+                  fp8_wgrad: bool = False):
     """BF16 in/out MXFP4 GEMM, out = a . w^T, differentiable (FP4 forward, FP4 dA, FP4 dB).
 
     a: [..., K] bfloat16, w: [N, K] bfloat16 -> [..., N] bfloat16.
@@ -247,8 +321,12 @@ def gemm_fp4_bf16(a, w, w_fp4: Optional[Mxfp4Tensor] = None, hadamard_grad: bool
     hadamard_grad: the README's gradient recipe -- dA and dB contract Walsh-Hadamard
     transformed operands (dOut's copies and the column copies of a and w); a w_fp4 then
     has to come from a weight quantizer with hadamard=True.
+    fp8_wgrad: dB as an MXFP8 product (the FP8 dB of the README's training architecture);
+    the forward product and dA stay MXFP4.  Does not combine with hadamard_grad.
     """
     lead = a.shape[:-1]
     a2 = a.reshape(-1, a.shape[-1]).contiguous()
-    out = _GemmFp4Bf16.apply(a2, w.contiguous(), w_fp4, hadamard_grad)
+    if hadamard_grad and fp8_wgrad:
+        raise ValueError("the Hadamard recipe and the FP8 wgrad do not combine")
+    out = _GemmFp4Bf16.apply(a2, w.contiguous(), w_fp4, hadamard_grad, fp8_wgrad)
     return out.reshape(*lead, w.shape[0])

@@ -12,6 +12,9 @@
 // transform along its contraction dimension: the column copies of A and W
 // (forward casts, divisor 1) and both copies of dOut (divisor 32 = 2^5, so
 // the products are unchanged: H H = 32 I).
+// With the FP8 wgrad option (the dB of the "MXFP4 training architecture"
+// section runs as an FP8 product) the column copies of A and dOut are MXFP8
+// and dB is the MXFP8 GEMM; the forward pass and dA stay MXFP4.
 #include <mutex>
 #include <string.h>
 
@@ -24,6 +27,11 @@ extern "C" hipError_t mx_launch_cast_h(const void* x, int64_t R, int64_t C, int6
                                        int hshift, hipStream_t stream);
 extern "C" hipError_t mx_launch_gemm(const void* aq, const void* as, const void* bq, const void* bs, int64_t M,
                                      int64_t N, int64_t K, void* out, int64_t ldo, hipStream_t stream);
+extern "C" hipError_t mx_launch_cast_f(const void* x, int64_t R, int64_t C, int64_t ldx, void* q_row, void* s_row,
+                                       void* q_col, void* s_col, bool dual, int row_fmt, int col_fmt,
+                                       bool transform_row, bool transform_col, int hshift, hipStream_t stream);
+extern "C" hipError_t mx_launch_gemm_f(const void* aq, const void* as, const void* bq, const void* bs, int64_t M,
+                                       int64_t N, int64_t K, void* out, int64_t ldo, int fmt, hipStream_t stream);
 
 namespace {
 
@@ -61,6 +69,11 @@ OperandSizes operand_sizes(int64_t rows, int64_t k) {
     return {((rows + 15) / 16) * ((k + 127) / 128) * 1024, ((rows + 127) / 128) * ((k + 255) / 256) * 1024};
 }
 
+// MXFP8 operand: code tiles of 16 rows x 64 elements (one byte each), same scale tiles.
+OperandSizes operand_sizes8(int64_t rows, int64_t k) {
+    return {((rows + 15) / 16) * ((k + 63) / 64) * 1024, ((rows + 127) / 128) * ((k + 255) / 256) * 1024};
+}
+
 int validate_cast(const void* x, int64_t rows, int64_t cols, int64_t ldx, const void* q, const void* s) {
     if (rows < 0 || cols < 0) return MXFP4_EINVAL;
     if (cols % 32 != 0) return MXFP4_EINVAL;
@@ -96,7 +109,9 @@ struct Workspace {
 };
 
 // with_w == false: W's copies come from the caller (pre-quantized weight), no W slots.
-Workspace workspace_layout(int64_t M, int64_t N, int64_t K, bool training, bool with_w = true) {
+// fp8_wgrad: the column copies of A and dOut (dB's operands) are MXFP8.
+Workspace workspace_layout(int64_t M, int64_t N, int64_t K, bool training, bool with_w = true,
+                           bool fp8_wgrad = false) {
     Workspace w{};
     int64_t off = 0;
     auto take = [&off](int64_t bytes) {
@@ -111,8 +126,10 @@ Workspace workspace_layout(int64_t M, int64_t N, int64_t K, bool training, bool 
     w.w_row_s = take(with_w ? w_row.s : 0);
     if (training) {
         const int64_t Mp = round_up(M, 32), Np = round_up(N, 32);
-        const OperandSizes a_col = operand_sizes(K, Mp), w_col = operand_sizes(K, Np);
-        const OperandSizes g_row = operand_sizes(M, N), g_col = operand_sizes(N, Mp);
+        const OperandSizes a_col = fp8_wgrad ? operand_sizes8(K, Mp) : operand_sizes(K, Mp);
+        const OperandSizes w_col = operand_sizes(K, Np);
+        const OperandSizes g_row = operand_sizes(M, N);
+        const OperandSizes g_col = fp8_wgrad ? operand_sizes8(N, Mp) : operand_sizes(N, Mp);
         w.a_col_q = take(a_col.q);
         w.a_col_s = take(a_col.s);
         w.w_col_q = take(with_w ? w_col.q : 0);
@@ -129,7 +146,14 @@ Workspace workspace_layout(int64_t M, int64_t N, int64_t K, bool training, bool 
 // 2^5 = 32: H H = 32 I for the 32-point Walsh-Hadamard matrix.
 constexpr int kHadamardShift = 5;
 
-constexpr unsigned kStepFlags = MXFP4_STEP_TRAINING | MXFP4_STEP_HADAMARD_GRAD | MXFP4_STEP_QUANTIZED_W;
+constexpr unsigned kStepFlags =
+    MXFP4_STEP_TRAINING | MXFP4_STEP_HADAMARD_GRAD | MXFP4_STEP_QUANTIZED_W | MXFP4_STEP_FP8_WGRAD;
+
+// Flags valid for a step: known bits; the transform goes with MXFP4 copies only.
+bool step_flags_ok(unsigned flags) {
+    if (flags & ~kStepFlags) return false;
+    return !((flags & MXFP4_STEP_HADAMARD_GRAD) && (flags & MXFP4_STEP_FP8_WGRAD));
+}
 
 int validate_step_sizes(int64_t M, int64_t N, int64_t K, bool training) {
     if (M < 0 || N < 0 || K < 0 || K % 32 != 0) return MXFP4_EINVAL;
@@ -218,6 +242,58 @@ int mxfp4_gemm_nn(const void* a_q, const void* a_s, const void* bcol_q, const vo
     return mxfp4_gemm_nt(a_q, a_s, bcol_q, bcol_s, M, N, K, out, ldo, stream);
 }
 
+int mxfp8_operand_layout_of(int64_t rows, int64_t k, mxfp4_operand_layout* out) {
+    if (!out || rows < 0 || k < 0 || k % 32 != 0) return MXFP4_EINVAL;
+    const OperandSizes sz = operand_sizes8(rows, k);
+    out->rows = rows;
+    out->k = k;
+    out->q_bytes = sz.q;
+    out->s_bytes = sz.s;
+    out->code_row_tiles = (rows + 15) / 16;
+    out->code_k_tiles = (k + 63) / 64;
+    out->scale_row_tiles = (rows + 127) / 128;
+    out->scale_k_tiles = (k + 255) / 256;
+    return MXFP4_OK;
+}
+
+int mxfp8_cast(const void* x, int64_t rows, int64_t cols, int64_t ldx, void* q, void* s, hipStream_t stream) {
+    int st = validate_cast(x, rows, cols, ldx, q, s);
+    if (st != MXFP4_OK || rows == 0 || cols == 0) return st;
+    if ((st = check_device()) != MXFP4_OK) return st;
+    return status_of(mx_launch_cast_f(x, rows, cols, ldx, q, s, nullptr, nullptr, false, 8, 8, false, false, 0, stream));
+}
+
+namespace {
+int cast_dual_formats(const void* x, int64_t rows, int64_t cols, int64_t ldx, void* q_row, void* s_row, void* q_col,
+                      void* s_col, int row_fmt, int col_fmt, hipStream_t stream) {
+    int st = validate_cast(x, rows, cols, ldx, q_row, s_row);
+    if (st != MXFP4_OK || rows == 0 || cols == 0) return st;
+    if (!q_col || !s_col) return MXFP4_EINVAL;
+    if (!aligned16(q_col) || !aligned16(s_col)) return MXFP4_EALIGN;
+    if ((st = check_device()) != MXFP4_OK) return st;
+    return status_of(
+        mx_launch_cast_f(x, rows, cols, ldx, q_row, s_row, q_col, s_col, true, row_fmt, col_fmt, false, false, 0, stream));
+}
+}  // namespace
+
+int mxfp8_cast_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx, void* q_row, void* s_row, void* q_col,
+                    void* s_col, hipStream_t stream) {
+    return cast_dual_formats(x, rows, cols, ldx, q_row, s_row, q_col, s_col, 8, 8, stream);
+}
+
+int mxfp4_cast_dual_fp8col(const void* x, int64_t rows, int64_t cols, int64_t ldx, void* q_row, void* s_row,
+                           void* q_col, void* s_col, hipStream_t stream) {
+    return cast_dual_formats(x, rows, cols, ldx, q_row, s_row, q_col, s_col, 4, 8, stream);
+}
+
+int mxfp8_gemm_nt(const void* a_q, const void* a_s, const void* b_q, const void* b_s, int64_t M, int64_t N, int64_t K,
+                  void* out, int64_t ldo, hipStream_t stream) {
+    int st = validate_gemm(a_q, a_s, b_q, b_s, M, N, K, out, ldo);
+    if (st != MXFP4_OK || M == 0 || N == 0) return st;
+    if ((st = check_device()) != MXFP4_OK) return st;
+    return status_of(mx_launch_gemm_f(a_q, a_s, b_q, b_s, M, N, K, out, ldo, 8, stream));
+}
+
 size_t gemm_fp4_bf16_workspace_bytes(int64_t M, int64_t N, int64_t K, int training) {
     if (validate_step_sizes(M, N, K, training != 0) != MXFP4_OK) return 0;
     return (size_t)workspace_layout(M, N, K, training != 0).total;
@@ -228,6 +304,14 @@ size_t gemm_fp4_bf16_workspace_bytes_qw(int64_t M, int64_t N, int64_t K, int tra
     return (size_t)workspace_layout(M, N, K, training != 0, false).total;
 }
 
+size_t gemm_fp4_bf16_workspace_bytes_ex(int64_t M, int64_t N, int64_t K, unsigned flags) {
+    const bool train = (flags & MXFP4_STEP_TRAINING) != 0;
+    if (!step_flags_ok(flags) || validate_step_sizes(M, N, K, train) != MXFP4_OK) return 0;
+    return (size_t)workspace_layout(M, N, K, train, (flags & MXFP4_STEP_QUANTIZED_W) == 0,
+                                    (flags & MXFP4_STEP_FP8_WGRAD) != 0)
+        .total;
+}
+
 }  // extern "C"
 
 namespace {
@@ -235,14 +319,16 @@ namespace {
 // Forward: cast A (dual when training, its column copy kept in ws), then the
 // GEMM with W's row copy -- cast here from bf16 w (own_w), or given.
 int step_fwd(const void* a, bool own_w, const void* w, const void* w_row_q, const void* w_row_s, int64_t M, int64_t N,
-             int64_t K, void* out, void* ws, size_t ws_bytes, bool train, bool hadamard, hipStream_t stream) {
-    if (hadamard && !train) return MXFP4_EINVAL;  // the transform only concerns the backward operands
+             int64_t K, void* out, void* ws, size_t ws_bytes, bool train, bool hadamard, bool fp8_wgrad,
+             hipStream_t stream) {
+    // the transform and the FP8 wgrad only concern the backward operands
+    if ((hadamard || fp8_wgrad) && !train) return MXFP4_EINVAL;
     int st = validate_step_sizes(M, N, K, train);
     if (st != MXFP4_OK) return st;
     if (M == 0 || N == 0) return MXFP4_OK;
     if (!out) return MXFP4_EINVAL;
     if ((reinterpret_cast<uintptr_t>(out) & 1u) != 0) return MXFP4_EALIGN;
-    const Workspace L = workspace_layout(M, N, K, train, own_w);
+    const Workspace L = workspace_layout(M, N, K, train, own_w, fp8_wgrad);
     char* base = static_cast<char*>(ws);
     const void* wq = own_w ? base + L.w_row_q : w_row_q;
     const void* wsc = own_w ? base + L.w_row_s : w_row_s;
@@ -256,8 +342,10 @@ int step_fwd(const void* a, bool own_w, const void* w, const void* w_row_q, cons
     hipError_t e = hipSuccess;
     if (K > 0) {
         // with the Hadamard recipe the column copies (dB's and dA's B operands) carry the transform
-        e = mx_launch_cast_h(a, M, K, K, base + L.a_row_q, base + L.a_row_s, train ? base + L.a_col_q : nullptr,
-                             train ? base + L.a_col_s : nullptr, train, false, hadamard, 0, stream);
+        // with the FP8 wgrad A's column copy (dB's B operand) is MXFP8
+        e = mx_launch_cast_f(a, M, K, K, base + L.a_row_q, base + L.a_row_s, train ? base + L.a_col_q : nullptr,
+                             train ? base + L.a_col_s : nullptr, train, 4, fp8_wgrad ? 8 : 4, false, hadamard, 0,
+                             stream);
         if (e == hipSuccess && own_w)
             e = mx_launch_cast_h(w, N, K, K, base + L.w_row_q, base + L.w_row_s, train ? base + L.w_col_q : nullptr,
                                  train ? base + L.w_col_s : nullptr, train, false, hadamard, 0, stream);
@@ -269,14 +357,14 @@ int step_fwd(const void* a, bool own_w, const void* w, const void* w_row_q, cons
 // Backward: cast dOut (dual), dA = dOut . W on W's column copy (from ws, or
 // given), dW = dOut^T . A on the column copies of dOut and A.
 int step_bwd(const void* dout, bool own_w, const void* w_col_q, const void* w_col_s, int64_t M, int64_t N, int64_t K,
-             void* ws, size_t ws_bytes, void* da, void* dw, bool hadamard, hipStream_t stream) {
+             void* ws, size_t ws_bytes, void* da, void* dw, bool hadamard, bool fp8_wgrad, hipStream_t stream) {
     int st = validate_step_sizes(M, N, K, true);
     if (st != MXFP4_OK) return st;
     if (!ws || (!da && !dw)) return ws ? MXFP4_OK : MXFP4_EINVAL;
     if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return MXFP4_EALIGN;
     if ((da && (reinterpret_cast<uintptr_t>(da) & 1u)) || (dw && (reinterpret_cast<uintptr_t>(dw) & 1u)))
         return MXFP4_EALIGN;
-    const Workspace L = workspace_layout(M, N, K, true, own_w);
+    const Workspace L = workspace_layout(M, N, K, true, own_w, fp8_wgrad);
     if ((int64_t)ws_bytes < L.total) return MXFP4_ESPACE;
     if (K == 0) return MXFP4_OK;  // dA [M, 0] and dW [N, 0] have no elements
     if (M == 0 || N == 0) {
@@ -299,12 +387,15 @@ int step_bwd(const void* dout, bool own_w, const void* w_col_q, const void* w_co
     const void* wq = own_w ? base + L.w_col_q : w_col_q;
     const void* wsc = own_w ? base + L.w_col_s : w_col_s;
     // Hadamard recipe: both copies of dOut transformed and divided by 32 (kHadamardShift)
-    hipError_t e = mx_launch_cast_h(dout, M, N, N, base + L.g_row_q, base + L.g_row_s, base + L.g_col_q,
-                                    base + L.g_col_s, true, hadamard, hadamard, hadamard ? kHadamardShift : 0, stream);
+    // FP8 wgrad: dOut's column copy (dB's A operand) is MXFP8, and dB the MXFP8 GEMM
+    const int wfmt = fp8_wgrad ? 8 : 4;
+    hipError_t e = mx_launch_cast_f(dout, M, N, N, base + L.g_row_q, base + L.g_row_s, base + L.g_col_q,
+                                    base + L.g_col_s, true, 4, wfmt, hadamard, hadamard,
+                                    hadamard ? kHadamardShift : 0, stream);
     if (e == hipSuccess && da) e = mx_launch_gemm(base + L.g_row_q, base + L.g_row_s, wq, wsc, M, K, N, da, K, stream);
     if (e == hipSuccess && dw)
-        e = mx_launch_gemm(base + L.g_col_q, base + L.g_col_s, base + L.a_col_q, base + L.a_col_s, N, K, Mp, dw, K,
-                           stream);
+        e = mx_launch_gemm_f(base + L.g_col_q, base + L.g_col_s, base + L.a_col_q, base + L.a_col_s, N, K, Mp, dw, K,
+                             wfmt, stream);
     return status_of(e);
 }
 
@@ -314,40 +405,40 @@ extern "C" {
 
 int gemm_fp4_bf16_fwd(const void* a, const void* w, int64_t M, int64_t N, int64_t K, void* out, void* ws,
                       size_t ws_bytes, int training, hipStream_t stream) {
-    return step_fwd(a, true, w, nullptr, nullptr, M, N, K, out, ws, ws_bytes, training != 0, false, stream);
+    return step_fwd(a, true, w, nullptr, nullptr, M, N, K, out, ws, ws_bytes, training != 0, false, false, stream);
 }
 
 int gemm_fp4_bf16_bwd(const void* dout, int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes, void* da,
                       void* dw, hipStream_t stream) {
-    return step_bwd(dout, true, nullptr, nullptr, M, N, K, ws, ws_bytes, da, dw, false, stream);
+    return step_bwd(dout, true, nullptr, nullptr, M, N, K, ws, ws_bytes, da, dw, false, false, stream);
 }
 
 int gemm_fp4_bf16_fwd_qw(const void* a, const void* w_row_q, const void* w_row_s, int64_t M, int64_t N, int64_t K,
                          void* out, void* ws, size_t ws_bytes, int training, hipStream_t stream) {
-    return step_fwd(a, false, nullptr, w_row_q, w_row_s, M, N, K, out, ws, ws_bytes, training != 0, false, stream);
+    return step_fwd(a, false, nullptr, w_row_q, w_row_s, M, N, K, out, ws, ws_bytes, training != 0, false, false, stream);
 }
 
 int gemm_fp4_bf16_bwd_qw(const void* dout, const void* w_col_q, const void* w_col_s, int64_t M, int64_t N, int64_t K,
                          void* ws, size_t ws_bytes, void* da, void* dw, hipStream_t stream) {
-    return step_bwd(dout, false, w_col_q, w_col_s, M, N, K, ws, ws_bytes, da, dw, false, stream);
+    return step_bwd(dout, false, w_col_q, w_col_s, M, N, K, ws, ws_bytes, da, dw, false, false, stream);
 }
 
 int gemm_fp4_bf16_fwd_ex(const void* a, const void* w, const void* w_row_q, const void* w_row_s, int64_t M, int64_t N,
                          int64_t K, void* out, void* ws, size_t ws_bytes, unsigned flags, hipStream_t stream) {
-    if (flags & ~kStepFlags) return MXFP4_EINVAL;
+    if (!step_flags_ok(flags)) return MXFP4_EINVAL;
     const bool qw = (flags & MXFP4_STEP_QUANTIZED_W) != 0;
     if (qw ? w != nullptr : (w_row_q != nullptr || w_row_s != nullptr)) return MXFP4_EINVAL;
     return step_fwd(a, !qw, w, w_row_q, w_row_s, M, N, K, out, ws, ws_bytes, (flags & MXFP4_STEP_TRAINING) != 0,
-                    (flags & MXFP4_STEP_HADAMARD_GRAD) != 0, stream);
+                    (flags & MXFP4_STEP_HADAMARD_GRAD) != 0, (flags & MXFP4_STEP_FP8_WGRAD) != 0, stream);
 }
 
 int gemm_fp4_bf16_bwd_ex(const void* dout, const void* w_col_q, const void* w_col_s, int64_t M, int64_t N, int64_t K,
                          void* ws, size_t ws_bytes, void* da, void* dw, unsigned flags, hipStream_t stream) {
-    if (flags & ~kStepFlags) return MXFP4_EINVAL;
+    if (!step_flags_ok(flags)) return MXFP4_EINVAL;
     const bool qw = (flags & MXFP4_STEP_QUANTIZED_W) != 0;
     if (!qw && (w_col_q || w_col_s)) return MXFP4_EINVAL;
     return step_bwd(dout, !qw, w_col_q, w_col_s, M, N, K, ws, ws_bytes, da, dw,
-                    (flags & MXFP4_STEP_HADAMARD_GRAD) != 0, stream);
+                    (flags & MXFP4_STEP_HADAMARD_GRAD) != 0, (flags & MXFP4_STEP_FP8_WGRAD) != 0, stream);
 }
 
 }  // extern "C"

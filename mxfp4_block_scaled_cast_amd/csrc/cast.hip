@@ -82,11 +82,16 @@ __device__ __forceinline__ float butterfly_lanes(float own, bool upper) {
     return upper ? other - own : own + other;
 }
 
-template <int TILE_R, bool DUAL, bool HROW, bool HCOL>
+// ROWF / COLF: element format of the row / column copy, 4 = MXFP4 (E2M1),
+// 8 = MXFP8 (E4M3, one byte per code, X = floor(log2 amax) - 8, saturating
+// at 448; the transform is only offered with MXFP4).
+template <int TILE_R, bool DUAL, bool HROW, bool HCOL, int ROWF, int COLF>
 __global__ __launch_bounds__(256, 4) void cast_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C, int64_t ldx,
                                                    uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
                                                    uint8_t* __restrict__ q_col, uint8_t* __restrict__ s_col,
                                                    int n_rtiles, int n_ctiles, int hshift) {
+    static_assert((ROWF == 4 || ROWF == 8) && (COLF == 4 || COLF == 8), "MXFP4 or MXFP8");
+    static_assert(!(HROW && ROWF == 8) && !(HCOL && COLF == 8), "the transform goes with MXFP4 copies");
     constexpr int NI = TILE_R / 8;  // 16-byte loads per thread
     const int t = threadIdx.x;
     const int tile = xcd_remap(blockIdx.x, n_rtiles * n_ctiles);
@@ -98,6 +103,7 @@ __global__ __launch_bounds__(256, 4) void cast_kernel(const uint16_t* __restrict
     const int64_t row16 = (R + 15) & ~(int64_t)15;     // code rows of the row copy (padded)
     const int64_t row128 = (R + 127) & ~(int64_t)127;  // scale rows of the row copy (padded)
     const int64_t kt128_row = (C + 127) >> 7;          // 128-wide code tiles of the row copy
+    const int64_t kt64_row = (C + 63) >> 6;            // 64-wide (MXFP8) code tiles of the row copy
     const int64_t kt256_row = (C + 255) >> 8;          // 256-wide scale tiles of the row copy
     const int cl = t & 31;                              // 16-byte column chunk within the tile
     const int64_t col = c0 + cl * 8;
@@ -118,6 +124,24 @@ __global__ __launch_bounds__(256, 4) void cast_kernel(const uint16_t* __restrict
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const int64_t row = r0 + i * 8 + (t >> 5);
+        if constexpr (ROWF == 8) {
+            unsigned m = pk_max_u16(v[i].x & 0x7FFF7FFFu, v[i].y & 0x7FFF7FFFu);
+            m = pk_max_u16(m, v[i].z & 0x7FFF7FFFu);
+            m = pk_max_u16(m, v[i].w & 0x7FFF7FFFu);
+            unsigned amax = (m & 0xFFFFu) > (m >> 16) ? (m & 0xFFFFu) : (m >> 16);
+            amax = quad_max_u32(amax);
+            const unsigned sb8 = scale_byte_fp8_from_amax(amax);
+            const unsigned lim = e4m3_limit_bf16(sb8);
+            uint2 c8 = cvt8_e4m3(v[i], scale_value(sb8), lim | (lim << 16));
+            if (sb8 == 255u) c8 = uint2{0u, 0u};
+            if (row < row16 && col < kt64_row * 64) {
+                *reinterpret_cast<uint2*>(q_row + code8_offset(row, col, kt64_row)) = c8;
+            }
+            if ((cl & 3) == 0 && row < row128) {
+                s_row[scale_offset(row, col >> 5, kt256_row)] = (uint8_t)sb8;
+            }
+            continue;
+        }
         unsigned sb, codes;
         if constexpr (HROW) {
             // this lane holds elements 8q .. 8q+7 of its block, q = lane % 4
@@ -172,6 +196,7 @@ __global__ __launch_bounds__(256, 4) void cast_kernel(const uint16_t* __restrict
 
         const int64_t Rp = (R + 31) & ~(int64_t)31;  // contraction length of the column copy
         const int64_t kt128_col = (Rp + 127) >> 7;
+        const int64_t kt64_col = (Rp + 63) >> 6;
         const int64_t kt256_col = (Rp + 255) >> 8;
         const int64_t col16 = (C + 15) & ~(int64_t)15;
         const int64_t col128 = (C + 127) & ~(int64_t)127;
@@ -184,6 +209,53 @@ __global__ __launch_bounds__(256, 4) void cast_kernel(const uint16_t* __restrict
             const int64_t c = c0 + cp * 2;
             const int64_t rblk = r0 + rb * 32;      // first row of the block
             if (rblk >= kt256_col * 256) continue;  // beyond the padded scale region
+            if constexpr (COLF == 8) {
+                const unsigned* strip = &lds[rb * 32 * 128 + cp];
+                unsigned m = strip[0] & 0x7FFF7FFFu;
+#pragma unroll
+                for (int r = 1; r < 32; ++r) m = pk_max_u16(m, strip[r * 128] & 0x7FFF7FFFu);
+                const unsigned sb0 = scale_byte_fp8_from_amax(m & 0xFFFFu);
+                const unsigned sb1 = scale_byte_fp8_from_amax(m >> 16);
+                const float f0 = scale_value(sb0), f1 = scale_value(sb1);
+                const unsigned l0 = e4m3_limit_bf16(sb0), l1 = e4m3_limit_bf16(sb1);
+                const unsigned lim0 = l0 | (l0 << 16), lim1 = l1 | (l1 << 16);
+                typedef short s16x2 __attribute__((ext_vector_type(2)));
+                unsigned o0[8], o1[8];
+#pragma unroll
+                for (int w = 0; w < 8; ++w) {
+                    // rows 4w .. 4w+3: two pairs per column, one dword of four codes
+                    const unsigned d0 = strip[(4 * w + 0) * 128], d1 = strip[(4 * w + 1) * 128];
+                    const unsigned d2 = strip[(4 * w + 2) * 128], d3 = strip[(4 * w + 3) * 128];
+                    s16x2 a0 = {0, 0}, a1 = {0, 0};
+                    a0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(
+                        a0, __builtin_bit_cast(bf16x2, clamp_pair_bf16(__builtin_amdgcn_perm(d1, d0, 0x05040100u), lim0)),
+                        f0, false);
+                    a0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(
+                        a0, __builtin_bit_cast(bf16x2, clamp_pair_bf16(__builtin_amdgcn_perm(d3, d2, 0x05040100u), lim0)),
+                        f0, true);
+                    a1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(
+                        a1, __builtin_bit_cast(bf16x2, clamp_pair_bf16(__builtin_amdgcn_perm(d1, d0, 0x07060302u), lim1)),
+                        f1, false);
+                    a1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(
+                        a1, __builtin_bit_cast(bf16x2, clamp_pair_bf16(__builtin_amdgcn_perm(d3, d2, 0x07060302u), lim1)),
+                        f1, true);
+                    o0[w] = sb0 == 255u ? 0u : __builtin_bit_cast(unsigned, a0);
+                    o1[w] = sb1 == 255u ? 0u : __builtin_bit_cast(unsigned, a1);
+                }
+                if (c < col16 && rblk < kt64_col * 64) {
+                    u32x4* p0 = reinterpret_cast<u32x4*>(q_col + code8_offset(c, rblk, kt64_col));
+                    u32x4* p1 = reinterpret_cast<u32x4*>(q_col + code8_offset(c + 1, rblk, kt64_col));
+                    p0[0] = u32x4{o0[0], o0[1], o0[2], o0[3]};
+                    p0[1] = u32x4{o0[4], o0[5], o0[6], o0[7]};
+                    p1[0] = u32x4{o1[0], o1[1], o1[2], o1[3]};
+                    p1[1] = u32x4{o1[4], o1[5], o1[6], o1[7]};
+                }
+                if (c < col128) {
+                    s_col[scale_offset(c, rblk >> 5, kt256_col)] = (uint8_t)sb0;
+                    s_col[scale_offset(c + 1, rblk >> 5, kt256_col)] = (uint8_t)sb1;
+                }
+                continue;
+            }
             u32x4 o0, o1;
             unsigned sb0, sb1;
             if constexpr (HCOL) {
@@ -267,9 +339,9 @@ __global__ __launch_bounds__(256, 4) void cast_kernel(const uint16_t* __restrict
 // Launchers (internal, called by the C ABI layer after validation).
 // transform_row / transform_col: Walsh-Hadamard on the row / column copy, the
 // transformed copies divided by 2^hshift.
-extern "C" hipError_t mx_launch_cast_h(const void* x, int64_t R, int64_t C, int64_t ldx, void* q_row, void* s_row,
-                                       void* q_col, void* s_col, bool dual, bool transform_row, bool transform_col,
-                                       int hshift, hipStream_t stream) {
+extern "C" hipError_t mx_launch_cast_f(const void* x, int64_t R, int64_t C, int64_t ldx, void* q_row, void* s_row,
+                                       void* q_col, void* s_col, bool dual, int row_fmt, int col_fmt, bool transform_row,
+                                       bool transform_col, int hshift, hipStream_t stream) {
     constexpr int TILE_R = 64;
     // rows covered: the row copy's padded scale rows (a multiple of 128), and for
     // the dual cast the column copy's padded contraction (a multiple of 256)
@@ -284,24 +356,42 @@ extern "C" hipError_t mx_launch_cast_h(const void* x, int64_t R, int64_t C, int6
     uint8_t *qr = static_cast<uint8_t*>(q_row), *sr = static_cast<uint8_t*>(s_row);
     uint8_t *qc = static_cast<uint8_t*>(q_col), *scl = static_cast<uint8_t*>(s_col);
     const int nr = (int)n_rtiles, nc = (int)n_ctiles;
-#define MX_CAST(D, HR, HC)                                                                                  \
-    hipLaunchKernelGGL((mx::cast_kernel<TILE_R, D, HR, HC>), grid, block, 0, stream, xb, R, C, ldx, qr, sr, \
-                       D ? qc : nullptr, D ? scl : nullptr, nr, nc, hshift)
-    if (!dual) {
-        if (transform_row) MX_CAST(false, true, false);
-        else MX_CAST(false, false, false);
+#define MX_CAST(D, HR, HC, RF, CF)                                                                         \
+    hipLaunchKernelGGL((mx::cast_kernel<TILE_R, D, HR, HC, RF, CF>), grid, block, 0, stream, xb, R, C, ldx, qr, \
+                       sr, D ? qc : nullptr, D ? scl : nullptr, nr, nc, hshift)
+    if (row_fmt == 8 || col_fmt == 8) {
+        if (transform_row || transform_col) return hipErrorInvalidValue;
+        if (!dual) {
+            if (row_fmt != 8) return hipErrorInvalidValue;
+            MX_CAST(false, false, false, 8, 4);
+        } else if (row_fmt == 8) {
+            if (col_fmt != 8) return hipErrorInvalidValue;
+            MX_CAST(true, false, false, 8, 8);
+        } else {
+            MX_CAST(true, false, false, 4, 8);
+        }
+    } else if (!dual) {
+        if (transform_row) MX_CAST(false, true, false, 4, 4);
+        else MX_CAST(false, false, false, 4, 4);
     } else if (transform_row) {
-        if (transform_col) MX_CAST(true, true, true);
-        else MX_CAST(true, true, false);
+        if (transform_col) MX_CAST(true, true, true, 4, 4);
+        else MX_CAST(true, true, false, 4, 4);
     } else {
-        if (transform_col) MX_CAST(true, false, true);
-        else MX_CAST(true, false, false);
+        if (transform_col) MX_CAST(true, false, true, 4, 4);
+        else MX_CAST(true, false, false, 4, 4);
     }
 #undef MX_CAST
     return hipGetLastError();
 }
 
+extern "C" hipError_t mx_launch_cast_h(const void* x, int64_t R, int64_t C, int64_t ldx, void* q_row, void* s_row,
+                                       void* q_col, void* s_col, bool dual, bool transform_row, bool transform_col,
+                                       int hshift, hipStream_t stream) {
+    return mx_launch_cast_f(x, R, C, ldx, q_row, s_row, q_col, s_col, dual, 4, 4, transform_row, transform_col, hshift,
+                            stream);
+}
+
 extern "C" hipError_t mx_launch_cast(const void* x, int64_t R, int64_t C, int64_t ldx, void* q_row, void* s_row,
                                      void* q_col, void* s_col, bool dual, hipStream_t stream) {
-    return mx_launch_cast_h(x, R, C, ldx, q_row, s_row, q_col, s_col, dual, false, false, 0, stream);
+    return mx_launch_cast_f(x, R, C, ldx, q_row, s_row, q_col, s_col, dual, 4, 4, false, false, 0, stream);
 }

@@ -13,6 +13,13 @@
 // `opsel` of a dword; the MX operand scale layout packs the four blocks a
 // lane needs over a 256-wide K range into one dword.  Accumulation is fp32;
 // the epilogue rounds to bf16 (nearest even).
+//
+// The same kernels also run the MXFP8 product of the FP8 dB variant (format
+// code 0, E4M3 on both sides): an FP8 code tile has the FP4 tile's geometry
+// in bytes (64 bytes per row = one 64-wide K step), so loads, LDS stages and
+// swizzle are shared; lane half h supplies K elements 16h .. 16h+15 and
+// 32+16h .. 47+16h of the step (two 16-byte pieces), while the scale of K
+// block b still comes from lane half b % 2.
 #include <stdlib.h>
 
 #include <algorithm>
@@ -44,6 +51,7 @@ namespace mx {
 // Reference-shaped kernel: each wave computes a 32x32 output tile reading its
 // operands straight from global memory (no LDS), one 64-wide K step at a
 // time.  Only used when MXFP4_GEMM_DIRECT=1 (a cross-check of the others).
+template <int FMT>
 __global__ __launch_bounds__(256) void gemm_direct_kernel(const uint8_t* __restrict__ aq,
                                                           const uint8_t* __restrict__ as,
                                                           const uint8_t* __restrict__ bq,
@@ -56,7 +64,8 @@ __global__ __launch_bounds__(256) void gemm_direct_kernel(const uint8_t* __restr
     const int ra = m0 + (lane & 31);
     const int rb = n0 + (lane & 31);
     const int half = lane >> 5;
-    const int64_t kt128 = (K + 127) >> 7, kt256 = (K + 255) >> 8;
+    const int64_t kt128 = (K + 127) >> 7, kt64 = (K + 63) >> 6, kt256 = (K + 255) >> 8;
+    constexpr int CODE = FMT == 8 ? 0 : 4;  // MFMA format code: E4M3 or E2M1
 
     f32x16 acc = {};
     for (int k0 = 0; k0 < K; k0 += 64) {
@@ -64,18 +73,27 @@ __global__ __launch_bounds__(256) void gemm_direct_kernel(const uint8_t* __restr
         v8i a = {}, b = {};
         int sa = 0, sb = 0;
         if (kk < K) {
+            // FP8 lane operand: K k0+16h .. +15 and k0+32+16h .. +15 (the layout pads to 64)
             if (ra < M) {
-                const u32x4 v = *reinterpret_cast<const u32x4*>(aq + code_offset(ra, kk, kt128));
-                a[0] = (int)v.x; a[1] = (int)v.y; a[2] = (int)v.z; a[3] = (int)v.w;
+                if constexpr (FMT == 8) {
+                    const uint8_t* p = aq + code8_offset(ra, k0 + half * 16, kt64);
+                    a = as_operand8(*reinterpret_cast<const u32x4*>(p), *reinterpret_cast<const u32x4*>(p + 32));
+                } else {
+                    a = as_operand(*reinterpret_cast<const u32x4*>(aq + code_offset(ra, kk, kt128)));
+                }
                 sa = as[scale_offset(ra, kk >> 5, kt256)];
             }
             if (rb < N) {
-                const u32x4 v = *reinterpret_cast<const u32x4*>(bq + code_offset(rb, kk, kt128));
-                b[0] = (int)v.x; b[1] = (int)v.y; b[2] = (int)v.z; b[3] = (int)v.w;
+                if constexpr (FMT == 8) {
+                    const uint8_t* p = bq + code8_offset(rb, k0 + half * 16, kt64);
+                    b = as_operand8(*reinterpret_cast<const u32x4*>(p), *reinterpret_cast<const u32x4*>(p + 32));
+                } else {
+                    b = as_operand(*reinterpret_cast<const u32x4*>(bq + code_offset(rb, kk, kt128)));
+                }
                 sb = bs[scale_offset(rb, kk >> 5, kt256)];
             }
         }
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 4, 4, 0, sa, 0, sb);
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, CODE, CODE, 0, sa, 0, sb);
     }
     const int n = n0 + (lane & 31);
     if (n < N) {
@@ -112,7 +130,7 @@ __global__ __launch_bounds__(256) void gemm_direct_kernel(const uint8_t* __restr
 template <int NB>
 constexpr int skinny_max_waves() { return NB == 1 ? 16 : 8; }
 
-template <int NB>
+template <int NB, int FMT>
 __global__ __launch_bounds__(64 * skinny_max_waves<NB>()) void gemm_skinny_kernel(
     const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as, const uint8_t* __restrict__ bq,
     const uint8_t* __restrict__ bs, int Ma, int Nb, int K, uint16_t* __restrict__ out, int64_t ld_i, int64_t ld_j,
@@ -124,7 +142,8 @@ __global__ __launch_bounds__(64 * skinny_max_waves<NB>()) void gemm_skinny_kerne
     const int half = lane >> 5;
     const int i0 = (blockIdx.x / tiles_b) * 32;
     const int j0 = (blockIdx.x % tiles_b) * (32 * NB);
-    const int64_t kt128 = (K + 127) >> 7, kt256 = (K + 255) >> 8;
+    const int64_t kt128 = (K + 127) >> 7, kt64 = (K + 63) >> 6, kt256 = (K + 255) >> 8;
+    const int64_t k_pad = FMT == 8 ? kt64 * 64 : kt128 * 128;  // K padded to whole code tiles
 
     const int ia = i0 + (lane & 31);
     const bool a_ok = ia < Ma;
@@ -144,19 +163,29 @@ __global__ __launch_bounds__(64 * skinny_max_waves<NB>()) void gemm_skinny_kerne
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16{};
 
+    // lane fragment of (row, 64-wide step at k0): FP4, the 16 bytes of K k0+32h .. +31; FP8,
+    // K k0+16h .. +15 and k0+32+16h .. +15 (16 bytes each)
+    auto load = [&](const uint8_t* q, int64_t row, int64_t k0, bool ok) -> v8i {
+        if (!ok) return v8i{};
+        if constexpr (FMT == 8) {
+            const uint8_t* p = q + code8_offset(row, k0 + half * 16, kt64);
+            return as_operand8(*reinterpret_cast<const u32x4*>(p), *reinterpret_cast<const u32x4*>(p + 32));
+        } else {
+            return as_operand(*reinterpret_cast<const u32x4*>(q + code_offset(row, k0 + half * 32, kt128)));
+        }
+    };
+    constexpr int CODE = FMT == 8 ? 0 : 4;
+
     for (int c = c_begin; c < c_end; ++c) {
-        u32x4 av[4], bv[NB][4];
+        v8i av[4], bv[NB][4];
         unsigned sa = 0u, sb[NB];
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-            const int64_t kk = (int64_t)c * 256 + st * 64 + half * 32;
-            const bool k_ok = (int64_t)c * 256 + st * 64 < kt128 * 128;
-            av[st] = (a_ok && k_ok) ? *reinterpret_cast<const u32x4*>(aq + code_offset(ia, kk, kt128))
-                                    : u32x4{0u, 0u, 0u, 0u};
+            const int64_t k0 = (int64_t)c * 256 + st * 64;
+            const bool k_ok = k0 < k_pad;
+            av[st] = load(aq, ia, k0, a_ok && k_ok);
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-                bv[nb][st] = (b_ok[nb] && k_ok) ? *reinterpret_cast<const u32x4*>(bq + code_offset(jb[nb], kk, kt128))
-                                                : u32x4{0u, 0u, 0u, 0u};
+            for (int nb = 0; nb < NB; ++nb) bv[nb][st] = load(bq, jb[nb], k0, b_ok[nb] && k_ok);
         }
         // scale dword of (row, half): blocks c*8 + half + 2*st, st = 0..3
         if (a_ok) sa = *reinterpret_cast<const unsigned*>(as + scale_offset(ia, (int64_t)c * 8 + half, kt256));
@@ -166,7 +195,7 @@ __global__ __launch_bounds__(64 * skinny_max_waves<NB>()) void gemm_skinny_kerne
                               : 0u;
 #define MX_SKINNY_STEP(ST)                                                                                         \
     _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) acc[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4( \
-        as_operand(av[ST]), as_operand(bv[nb][ST]), acc[nb], 4, 4, ST, (int)sa, ST, (int)sb[nb]);
+        av[ST], bv[nb][ST], acc[nb], CODE, CODE, ST, (int)sa, ST, (int)sb[nb]);
         MX_SKINNY_STEP(0) MX_SKINNY_STEP(1) MX_SKINNY_STEP(2) MX_SKINNY_STEP(3)
 #undef MX_SKINNY_STEP
     }
@@ -201,6 +230,7 @@ __global__ __launch_bounds__(64 * skinny_max_waves<NB>()) void gemm_skinny_kerne
 }
 
 // Launch the skinny kernel for out[M, N] = a . b^T.
+template <int FMT>
 static hipError_t launch_skinny(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t M,
                                 int64_t N, int64_t K, uint16_t* out, int64_t ldo, hipStream_t stream) {
     // the smaller side is A (32-row groups), the larger one B (32*NB-row groups)
@@ -214,7 +244,8 @@ static hipError_t launch_skinny(const uint8_t* aq, const uint8_t* as, const uint
     const int64_t tiles_a = (Ma + 31) / 32;
     int nb = 1, W = 1;
     int64_t tiles_b = 0;
-    for (int cand = 4; cand >= 1; cand /= 2) {
+    // (FP8 fragments are twice as wide: NB = 4 would not fit the registers)
+    for (int cand = FMT == 8 ? 2 : 4; cand >= 1; cand /= 2) {
         if (cand > 1 && Nb < 32 * cand) continue;
         const int wmax = cand == 1 ? 16 : 8;
         int w = 1;
@@ -230,15 +261,11 @@ static hipError_t launch_skinny(const uint8_t* aq, const uint8_t* as, const uint
     const size_t lds = W > 1 ? (size_t)W * nb * 16 * 64 * sizeof(float) : 0;
     const dim3 grid((unsigned)tiles), block((unsigned)(64 * W));
     const uint8_t *pa = swap ? bq : aq, *psa = swap ? bs : as, *pb = swap ? aq : bq, *psb = swap ? as : bs;
-    if (nb == 4)
-        hipLaunchKernelGGL(mx::gemm_skinny_kernel<4>, grid, block, lds, stream, pa, psa, pb, psb, (int)Ma, (int)Nb,
-                           (int)K, out, ld_i, ld_j, (int)tiles_b);
-    else if (nb == 2)
-        hipLaunchKernelGGL(mx::gemm_skinny_kernel<2>, grid, block, lds, stream, pa, psa, pb, psb, (int)Ma, (int)Nb,
-                           (int)K, out, ld_i, ld_j, (int)tiles_b);
-    else
-        hipLaunchKernelGGL(mx::gemm_skinny_kernel<1>, grid, block, lds, stream, pa, psa, pb, psb, (int)Ma, (int)Nb,
-                           (int)K, out, ld_i, ld_j, (int)tiles_b);
+    auto kern = nb == 2 ? mx::gemm_skinny_kernel<2, FMT> : mx::gemm_skinny_kernel<1, FMT>;
+    if constexpr (FMT == 4)
+        if (nb == 4) kern = mx::gemm_skinny_kernel<4, FMT>;
+    hipLaunchKernelGGL(kern, grid, block, lds, stream, pa, psa, pb, psb, (int)Ma, (int)Nb, (int)K, out, ld_i, ld_j,
+                       (int)tiles_b);
     return hipGetLastError();
 }
 
@@ -396,7 +423,10 @@ struct DmaPlan {
 // Instruction Q (0..8) of the DMA of K tile kt of source S into stage ST:
 // 0-3 A codes, 4-7 B codes, 8 scales.  P.code_base / P.scale_base are this
 // wave's LDS bases (wave-uniform SGPRs); the rest of the address is constant.
-template <int ST, int Q>
+// FMT 4: K tile = 128 FP4 elements, the scale tile (256 elements) spans 2 K
+// tiles; FMT 8: K tile = 64 FP8 elements (the same 64 bytes per row), the
+// scale tile spans 4 K tiles.
+template <int ST, int Q, int FMT = 4>
 __device__ __forceinline__ void dma_one(const DmaPlan& P, const TileSrc& S, int kt, bool valid) {
     // a tile past K goes through a descriptor with num_records 0: every lane reads zero
     if constexpr (Q < 4) {
@@ -410,21 +440,21 @@ __device__ __forceinline__ void dma_one(const DmaPlan& P, const TileSrc& S, int 
     } else {
         i32x4 r = S.rs;
         r.z = __builtin_amdgcn_readfirstlane(valid ? r.z : 0);
-        dma16_at<ST * STAGE>(r, P.vs, (kt >> 1) * 1024, P.scale_base);
+        dma16_at<ST * STAGE>(r, P.vs, (kt >> (FMT == 8 ? 2 : 1)) * 1024, P.scale_base);
     }
 }
 
-template <int ST>
+template <int ST, int FMT = 4>
 __device__ __forceinline__ void dma_tile_all(const DmaPlan& P, const TileSrc& S, int kt, bool valid) {
-    dma_one<ST, 0>(P, S, kt, valid);
-    dma_one<ST, 1>(P, S, kt, valid);
-    dma_one<ST, 2>(P, S, kt, valid);
-    dma_one<ST, 3>(P, S, kt, valid);
-    dma_one<ST, 4>(P, S, kt, valid);
-    dma_one<ST, 5>(P, S, kt, valid);
-    dma_one<ST, 6>(P, S, kt, valid);
-    dma_one<ST, 7>(P, S, kt, valid);
-    dma_one<ST, 8>(P, S, kt, valid);
+    dma_one<ST, 0, FMT>(P, S, kt, valid);
+    dma_one<ST, 1, FMT>(P, S, kt, valid);
+    dma_one<ST, 2, FMT>(P, S, kt, valid);
+    dma_one<ST, 3, FMT>(P, S, kt, valid);
+    dma_one<ST, 4, FMT>(P, S, kt, valid);
+    dma_one<ST, 5, FMT>(P, S, kt, valid);
+    dma_one<ST, 6, FMT>(P, S, kt, valid);
+    dma_one<ST, 7, FMT>(P, S, kt, valid);
+    dma_one<ST, 8, FMT>(P, S, kt, valid);
 }
 
 // Operand descriptors of the output tile at (m0, n0), rebased at the tile and
@@ -472,8 +502,67 @@ __device__ __forceinline__ int lds32(lds_cptr p) {
     return *reinterpret_cast<const __attribute__((address_space(3))) int*>(p);
 }
 
-// LDS read q (0..23) of a tile: scales first, then the step-0 fragments, then step 1.
-__device__ __forceinline__ void read_one(TileRegs& T, const ReadPlan& R, lds_cptr stage, int q) {
+// K tiles of the operands: 128 FP4 or 64 FP8 elements, 64 bytes per row either way.
+template <int FMT>
+__device__ __forceinline__ int k_tiles(int K) { return FMT == 8 ? (K + 63) >> 6 : (K + 127) >> 7; }
+
+// DMA addressing of a wave.  Code DMA: instruction q of wave w moves 16-row
+// tile 4w + q; lane l takes row l/4 of it, physical chunk l%4, i.e. logical
+// chunk (l%4) ^ swz64(l/4).  Waves 0, 1 copy the A scale tiles (rows 0-127,
+// 128-255 of the output tile), waves 2, 3 the B ones.
+__device__ __forceinline__ DmaPlan dma_plan(int lane, int wave, int nkt, int kt2, lds_cptr lds) {
+    DmaPlan P;
+    P.wave = wave;
+    P.scale_region = (wave >= 2 ? ST_SB : ST_SA) + (wave & 1) * 1024;
+    const int chunk = (lane & 3) ^ swz64(lane >> 2);
+    P.tstep = nkt * 1024;
+    P.va = wave * 4 * P.tstep + (lane >> 2) * 64 + chunk * 16;
+    P.vb = P.va;
+    P.vs = (wave & 1) * kt2 * 1024 + lane * 16;
+    P.lds0 = (unsigned)(uintptr_t)lds;
+    P.code_base = __builtin_amdgcn_readfirstlane(P.lds0 + (unsigned)(wave * 4 * 1024));
+    P.scale_base = __builtin_amdgcn_readfirstlane(P.lds0 + (unsigned)P.scale_region);
+    return P;
+}
+
+// LDS read addressing of a lane: fragment row lane%32 of the wave's 128-row
+// blocks, at the 16-byte chunks c = 2*st + h (h = lane/32, st = 0, 1) of its
+// 64-byte tile row.  FP4: chunk c holds K elements 32c .. 32c+31 of the
+// tile, the lane's whole operand for K step st.  FP8: the tile is one K
+// step and the 32x32x64 FP8 operand of lane half h is K elements 16h ..
+// 16h+15 (registers 0-3) and 32+16h .. 47+16h (registers 4-7), i.e. chunks h
+// and 2 + h -- the same two chunks.  Scales: the dword of (row, half); the
+// scale of K block b (32 elements) comes from the lanes of half b % 2.
+__device__ __forceinline__ ReadPlan read_plan(int lane, int wm, int wn) {
+    ReadPlan R;
+    const int frow = lane & 31;
+    const int sw = swz64(frow);
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        const int c = 2 * st + (lane >> 5);
+        R.a_off[st] = (wm * 128 + frow) * PROWB + ((c ^ sw) << 4);
+        R.b_off[st] = (wn * 128 + frow) * PROWB + ((c ^ sw) << 4);
+    }
+    const int s_lane = frow * 8 + (lane >> 5) * 4;
+    R.sa_off = wm * 4 * 256 + s_lane;
+    R.sb_off = wn * 4 * 256 + s_lane;
+    return R;
+}
+
+// Order of the FP8 fragment reads (slots 8..23 of read_one): an MFMA needs
+// both halves of its A and B fragments, so they come in the order the MFMAs
+// (i-major) first use them.
+__device__ __forceinline__ constexpr int read8_slot(int q) {
+    constexpr int order[24] = {0,  1,  2,  3,  4,  5,  6,  7,  8,  16, 12, 20,
+                               13, 21, 14, 22, 15, 23, 9,  17, 10, 18, 11, 19};
+    return order[q];
+}
+
+// LDS read q (0..23) of a tile: scales first, then (FP4) the step-0
+// fragments, then step 1; FP8 reads the same slots in read8_slot order.
+template <int FMT = 4>
+__device__ __forceinline__ void read_one(TileRegs& T, const ReadPlan& R, lds_cptr stage, int q0) {
+    const int q = FMT == 8 ? read8_slot(q0) : q0;
     if (q < 4) T.sa[q] = lds32(stage + ST_SA + R.sa_off + q * 256);
     else if (q < 8) T.sb[q - 4] = lds32(stage + ST_SB + R.sb_off + (q - 4) * 256);
     else if (q < 12) T.a0[q - 8] = lds128(stage + ST_A + R.a_off[0] + (q - 8) * 32 * PROWB);
@@ -494,6 +583,17 @@ __device__ __forceinline__ void mfma_one(f32x16 (&acc)[4][4], const u32x4 (&a)[4
                                                                 OPSEL, sb[j], OPSEL, sa[i]);
 }
 
+// FP8 MFMA q (0..15) of a K tile: (i, j) = (q / 4, q % 4), operands from the
+// two 16-byte chunks the lane read (see read_plan), format code 0 (E4M3) on
+// both sides.
+template <int OPSEL>
+__device__ __forceinline__ void mfma8_one(f32x16 (&acc)[4][4], const TileRegs& T, int q) {
+    const int i = q >> 2, j = q & 3;
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(as_operand8(T.b0[j], T.b1[j]),
+                                                                as_operand8(T.a0[i], T.a1[i]), acc[i][j], 0, 0,
+                                                                OPSEL, T.sb[j], OPSEL, T.sa[i]);
+}
+
 constexpr int kEpiStores = 32;  // 16-byte output stores per wave per tile (persistent kernel)
 
 // Iteration kt = 4t + U of the main loop (see the schedule above).  The DMA
@@ -502,59 +602,91 @@ constexpr int kEpiStores = 32;  // 16-byte output stores per wave per tile (pers
 // stage U.  With POST (first trip after an epilogue) the waits of the first
 // three iterations also let the epilogue's stores, issued after the DMA of K
 // tile 3, be outstanding.
-template <int U, bool POST = false, bool LAST = false>
+template <int U, bool POST = false, bool LAST = false, int FMT = 4>
 __device__ __forceinline__ void pipe_iter(f32x16 (&acc)[4][4], TileRegs& cur, TileRegs& nxt, const DmaPlan& P,
                                           const TileSrc& Scur, const TileSrc& Snext, bool next_ok,
                                           const ReadPlan& R, lds_cptr lds, int kt, int nkt) {
-    constexpr int OP = (U & 1) * 2;  // tile kt uses bytes 2*(kt%2) and 2*(kt%2)+1 of its scale dwords
     constexpr int DST = U;
     constexpr int WAIT = 2 * kDmaPerTile + ((POST && U < 3) ? kEpiStores : 0);
     const TileSrc& S = LAST ? Snext : Scur;
     const int dkt = LAST ? U : kt + NST;
     const bool valid = LAST ? (next_ok && U < nkt) : (kt + NST < nkt);
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-        mfma_one<OP>(acc, cur.a0, cur.b0, cur.sa, cur.sb, q);
-        order_point();
-    }
-    // tile kt+1 has landed (tiles kt+2 and kt+3 may be in flight), this wave's
-    // LDS reads are done, and after the barrier nobody reads stage U any more
-    wait_vmcnt<WAIT, true>();
-    __syncthreads();
     lds_cptr next = lds + ((U + 1) % NST) * STAGE;
+    if constexpr (FMT == 4) {
+        constexpr int OP = (U & 1) * 2;  // tile kt uses bytes 2*(kt%2) and 2*(kt%2)+1 of its scale dwords
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-        // the step-0 data of tile kt+1 (reads 0..15) goes first: it is needed first
-        const int r0 = (q * 3) / 2, r1 = ((q + 1) * 3) / 2;
+        for (int q = 0; q < 16; ++q) {
+            mfma_one<OP>(acc, cur.a0, cur.b0, cur.sa, cur.sb, q);
+            order_point();
+        }
+        // tile kt+1 has landed (tiles kt+2 and kt+3 may be in flight), this wave's
+        // LDS reads are done, and after the barrier nobody reads stage U any more
+        wait_vmcnt<WAIT, true>();
+        __syncthreads();
 #pragma unroll
-        for (int r = r0; r < r1; ++r) read_one(nxt, R, next, r);
-        // DMA instructions 0..7 before the odd MFMAs, 8 (scales) before MFMA 14
-        if (q == 1) dma_one<DST, 0>(P, S, dkt, valid);
-        if (q == 3) dma_one<DST, 1>(P, S, dkt, valid);
-        if (q == 5) dma_one<DST, 2>(P, S, dkt, valid);
-        if (q == 7) dma_one<DST, 3>(P, S, dkt, valid);
-        if (q == 9) dma_one<DST, 4>(P, S, dkt, valid);
-        if (q == 11) dma_one<DST, 5>(P, S, dkt, valid);
-        if (q == 13) dma_one<DST, 6>(P, S, dkt, valid);
-        if (q == 14) dma_one<DST, 8>(P, S, dkt, valid);
-        if (q == 15) dma_one<DST, 7>(P, S, dkt, valid);
-        mfma_one<OP + 1>(acc, cur.a1, cur.b1, cur.sa, cur.sb, q);
-        order_point();
+        for (int q = 0; q < 16; ++q) {
+            // the step-0 data of tile kt+1 (reads 0..15) goes first: it is needed first
+            const int r0 = (q * 3) / 2, r1 = ((q + 1) * 3) / 2;
+#pragma unroll
+            for (int r = r0; r < r1; ++r) read_one<FMT>(nxt, R, next, r);
+            // DMA instructions 0..7 before the odd MFMAs, 8 (scales) before MFMA 14
+            if (q == 1) dma_one<DST, 0, FMT>(P, S, dkt, valid);
+            if (q == 3) dma_one<DST, 1, FMT>(P, S, dkt, valid);
+            if (q == 5) dma_one<DST, 2, FMT>(P, S, dkt, valid);
+            if (q == 7) dma_one<DST, 3, FMT>(P, S, dkt, valid);
+            if (q == 9) dma_one<DST, 4, FMT>(P, S, dkt, valid);
+            if (q == 11) dma_one<DST, 5, FMT>(P, S, dkt, valid);
+            if (q == 13) dma_one<DST, 6, FMT>(P, S, dkt, valid);
+            if (q == 14) dma_one<DST, 8, FMT>(P, S, dkt, valid);
+            if (q == 15) dma_one<DST, 7, FMT>(P, S, dkt, valid);
+            mfma_one<OP + 1>(acc, cur.a1, cur.b1, cur.sa, cur.sb, q);
+            order_point();
+        }
+    } else {
+        // FP8: one 64-wide K step per tile, each MFMA twice as long; a0/a1 (b0/b1) are registers
+        // 0-3 / 4-7 of a lane's 32-byte operand; tile kt uses byte kt%4 of its scale dwords
+        constexpr int OP = U;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            mfma8_one<OP>(acc, cur, q);
+            order_point();
+        }
+        wait_vmcnt<WAIT, true>();
+        __syncthreads();
+#pragma unroll
+        for (int q = 8; q < 16; ++q) {
+            // all 24 reads of tile kt+1 (every MFMA of the next tile needs both halves)
+#pragma unroll
+            for (int r = (q - 8) * 3; r < (q - 7) * 3; ++r) read_one<FMT>(nxt, R, next, r);
+            if (q == 8) dma_one<DST, 0, FMT>(P, S, dkt, valid);
+            if (q == 9) dma_one<DST, 1, FMT>(P, S, dkt, valid);
+            if (q == 10) dma_one<DST, 2, FMT>(P, S, dkt, valid);
+            if (q == 11) dma_one<DST, 3, FMT>(P, S, dkt, valid);
+            if (q == 12) dma_one<DST, 4, FMT>(P, S, dkt, valid);
+            if (q == 13) dma_one<DST, 5, FMT>(P, S, dkt, valid);
+            if (q == 14) dma_one<DST, 6, FMT>(P, S, dkt, valid);
+            if (q == 15) {
+                dma_one<DST, 7, FMT>(P, S, dkt, valid);
+                dma_one<DST, 8, FMT>(P, S, dkt, valid);
+            }
+            mfma8_one<OP>(acc, cur, q);
+            order_point();
+        }
     }
 }
 
 // Four iterations kt0 .. kt0+3 (kt0 a multiple of 4).
-template <bool POST, bool LAST>
+template <bool POST, bool LAST, int FMT = 4>
 __device__ __forceinline__ void pipe_trip(f32x16 (&acc)[4][4], TileRegs& r0, TileRegs& r1, const DmaPlan& P,
                                           const TileSrc& Scur, const TileSrc& Snext, bool next_ok,
                                           const ReadPlan& R, lds_cptr lds, int kt0, int nkt) {
-    pipe_iter<0, POST, LAST>(acc, r0, r1, P, Scur, Snext, next_ok, R, lds, kt0 + 0, nkt);
-    pipe_iter<1, POST, LAST>(acc, r1, r0, P, Scur, Snext, next_ok, R, lds, kt0 + 1, nkt);
-    pipe_iter<2, POST, LAST>(acc, r0, r1, P, Scur, Snext, next_ok, R, lds, kt0 + 2, nkt);
-    pipe_iter<3, POST, LAST>(acc, r1, r0, P, Scur, Snext, next_ok, R, lds, kt0 + 3, nkt);
+    pipe_iter<0, POST, LAST, FMT>(acc, r0, r1, P, Scur, Snext, next_ok, R, lds, kt0 + 0, nkt);
+    pipe_iter<1, POST, LAST, FMT>(acc, r1, r0, P, Scur, Snext, next_ok, R, lds, kt0 + 1, nkt);
+    pipe_iter<2, POST, LAST, FMT>(acc, r0, r1, P, Scur, Snext, next_ok, R, lds, kt0 + 2, nkt);
+    pipe_iter<3, POST, LAST, FMT>(acc, r1, r0, P, Scur, Snext, next_ok, R, lds, kt0 + 3, nkt);
 }
 
-template <bool VEC_STORE>
+template <bool VEC_STORE, int FMT>
 __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __restrict__ aq,
                                                            const uint8_t* __restrict__ as,
                                                            const uint8_t* __restrict__ bq,
@@ -580,39 +712,11 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
     const int tn = local / gsize;
     const int64_t m0 = (int64_t)tm * PBM, n0 = (int64_t)tn * PBN;
 
-    const int nkt = (K + PBK - 1) / PBK;   // 128-wide K tiles (= code tiles per 16-row group)
-    const int kt2 = (K + 255) >> 8;         // 256-wide scale tiles per 128-row group
-    DmaPlan P;
-    P.wave = wave;
-    // waves 0, 1 copy the A scale tiles (rows 0-127, 128-255 of the tile), waves 2, 3 the B ones
-    P.scale_region = (wave >= 2 ? ST_SB : ST_SA) + (wave & 1) * 1024;
+    const int nkt = k_tiles<FMT>(K);   // K tiles (= code tiles per 16-row group)
+    const int kt2 = (K + 255) >> 8;     // 256-wide scale tiles per 128-row group
+    const DmaPlan P = dma_plan(lane, wave, nkt, kt2, lds);
+    const ReadPlan R = read_plan(lane, wm, wn);
     const TileSrc S = tile_src(aq, as, bq, bs, M, N, nkt, kt2, m0, n0, wave);
-    {
-        // code DMA: instruction q of wave w moves 16-row tile 4w + q; lane l takes row l/4 of it,
-        // physical chunk l%4, i.e. logical chunk (l%4) ^ swz64(l/4)
-        const int chunk = (lane & 3) ^ swz64(lane >> 2);
-        P.tstep = nkt * 1024;
-        P.va = wave * 4 * P.tstep + (lane >> 2) * 64 + chunk * 16;
-        P.vb = P.va;
-        P.vs = (wave & 1) * kt2 * 1024 + lane * 16;
-        P.lds0 = (unsigned)(uintptr_t)lds;
-        P.code_base = __builtin_amdgcn_readfirstlane(P.lds0 + (unsigned)(wave * 4 * 1024));
-        P.scale_base = __builtin_amdgcn_readfirstlane(P.lds0 + (unsigned)P.scale_region);
-    }
-    ReadPlan R;
-    {
-        const int frow = lane & 31;
-        const int sw = swz64(frow);
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            const int c = 2 * st + (lane >> 5);
-            R.a_off[st] = (wm * 128 + frow) * PROWB + ((c ^ sw) << 4);
-            R.b_off[st] = (wn * 128 + frow) * PROWB + ((c ^ sw) << 4);
-        }
-        const int s_lane = frow * 8 + (lane >> 5) * 4;
-        R.sa_off = wm * 4 * 256 + s_lane;
-        R.sb_off = wn * 4 * 256 + s_lane;
-    }
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -621,19 +725,19 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
     // prologue: tiles 0..3 in flight, then tile 0 into registers
-    dma_tile_all<0>(P, S, 0, 0 < nkt);
-    dma_tile_all<1>(P, S, 1, 1 < nkt);
-    dma_tile_all<2>(P, S, 2, 2 < nkt);
-    dma_tile_all<3>(P, S, 3, 3 < nkt);
+    dma_tile_all<0, FMT>(P, S, 0, 0 < nkt);
+    dma_tile_all<1, FMT>(P, S, 1, 1 < nkt);
+    dma_tile_all<2, FMT>(P, S, 2, 2 < nkt);
+    dma_tile_all<3, FMT>(P, S, 3, 3 < nkt);
     wait_vmcnt<(NST - 1) * kDmaPerTile, true>();
     __syncthreads();
     TileRegs r0, r1;
 #pragma unroll
-    for (int q = 0; q < 24; ++q) read_one(r0, R, lds, q);
+    for (int q = 0; q < 24; ++q) read_one<FMT>(r0, R, lds, q);
     order_point();
 
     const int trips = (nkt + NST - 1) / NST;
-    for (int tr = 0; tr < trips; ++tr) pipe_trip<false, false>(acc, r0, r1, P, S, S, false, R, lds, tr * NST, nkt);
+    for (int tr = 0; tr < trips; ++tr) pipe_trip<false, false, FMT>(acc, r0, r1, P, S, S, false, R, lds, tr * NST, nkt);
     // drain the DMA of the (empty) tiles past the end before the workgroup can exit
     wait_vmcnt<0>();
 
@@ -763,7 +867,7 @@ __device__ __forceinline__ void persist_epilogue(const f32x16 (&acc)[4][4], uint
     }
 }
 
-template <bool SINGLE>
+template <bool SINGLE, int FMT>
 __global__ __launch_bounds__(256, 1) void gemm_persist_kernel(const uint8_t* __restrict__ aq,
                                                               const uint8_t* __restrict__ as,
                                                               const uint8_t* __restrict__ bq,
@@ -781,37 +885,11 @@ __global__ __launch_bounds__(256, 1) void gemm_persist_kernel(const uint8_t* __r
     const int G = gridDim.x;
     const int slot = xcd_remap(blockIdx.x, G);  // each XCD takes a contiguous range of slots per round
 
-    const int nkt = (K + PBK - 1) / PBK;
+    const int nkt = k_tiles<FMT>(K);
     const int trips = (nkt + NST - 1) / NST;  // 1 with SINGLE, else >= 2; K tiles past nkt read as zero
     const int kt2 = (K + 255) >> 8;
-
-    DmaPlan P;
-    P.wave = wave;
-    P.scale_region = (wave >= 2 ? ST_SB : ST_SA) + (wave & 1) * 1024;
-    {
-        const int chunk = (lane & 3) ^ swz64(lane >> 2);
-        P.tstep = nkt * 1024;
-        P.va = wave * 4 * P.tstep + (lane >> 2) * 64 + chunk * 16;
-        P.vb = P.va;
-        P.vs = (wave & 1) * kt2 * 1024 + lane * 16;
-        P.lds0 = (unsigned)(uintptr_t)lds;
-        P.code_base = __builtin_amdgcn_readfirstlane(P.lds0 + (unsigned)(wave * 4 * 1024));
-        P.scale_base = __builtin_amdgcn_readfirstlane(P.lds0 + (unsigned)P.scale_region);
-    }
-    ReadPlan R;
-    {
-        const int frow = lane & 31;
-        const int sw = swz64(frow);
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            const int c = 2 * st + (lane >> 5);
-            R.a_off[st] = (wm * 128 + frow) * PROWB + ((c ^ sw) << 4);
-            R.b_off[st] = (wn * 128 + frow) * PROWB + ((c ^ sw) << 4);
-        }
-        const int s_lane = frow * 8 + (lane >> 5) * 4;
-        R.sa_off = wm * 4 * 256 + s_lane;
-        R.sb_off = wn * 4 * 256 + s_lane;
-    }
+    const DmaPlan P = dma_plan(lane, wave, nkt, kt2, lds);
+    const ReadPlan R = read_plan(lane, wm, wn);
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -825,15 +903,15 @@ __global__ __launch_bounds__(256, 1) void gemm_persist_kernel(const uint8_t* __r
     TileSrc S = tile_src(aq, as, bq, bs, M, N, nkt, kt2, m0, n0, wave);
 
     // first tile: K tiles 0..3 in flight, K tile 0 into registers, then its first trip
-    dma_tile_all<0>(P, S, 0, 0 < nkt);
-    dma_tile_all<1>(P, S, 1, 1 < nkt);
-    dma_tile_all<2>(P, S, 2, 2 < nkt);
-    dma_tile_all<3>(P, S, 3, 3 < nkt);
+    dma_tile_all<0, FMT>(P, S, 0, 0 < nkt);
+    dma_tile_all<1, FMT>(P, S, 1, 1 < nkt);
+    dma_tile_all<2, FMT>(P, S, 2, 2 < nkt);
+    dma_tile_all<3, FMT>(P, S, 3, 3 < nkt);
     wait_vmcnt<(NST - 1) * kDmaPerTile, true>();
     __syncthreads();
     TileRegs r0, r1;
 #pragma unroll
-    for (int q = 0; q < 24; ++q) read_one(r0, R, lds, q);
+    for (int q = 0; q < 24; ++q) read_one<FMT>(r0, R, lds, q);
     order_point();
 
     // one tile's last trip, then its epilogue; returns false after the last tile
@@ -849,7 +927,7 @@ __global__ __launch_bounds__(256, 1) void gemm_persist_kernel(const uint8_t* __r
         m0 = (int64_t)tm * PBM;
         n0 = (int64_t)tn * PBN;
         const TileSrc Sn = tile_src(aq, as, bq, bs, M, N, nkt, kt2, m0, n0, wave);
-        pipe_trip<POST, true>(acc, r0, r1, P, S, Sn, more, R, lds, kt0, nkt);
+        pipe_trip<POST, true, FMT>(acc, r0, r1, P, S, Sn, more, R, lds, kt0, nkt);
         S = Sn;
 
         // stage 0 (the next tile's K tile 0, now in r0) is free until the next
@@ -873,15 +951,15 @@ __global__ __launch_bounds__(256, 1) void gemm_persist_kernel(const uint8_t* __r
                 if (!finish_tile(t, std::true_type{}, 0)) break;
         }
     } else {
-        pipe_trip<false, false>(acc, r0, r1, P, S, S, false, R, lds, 0, nkt);
+        pipe_trip<false, false, FMT>(acc, r0, r1, P, S, S, false, R, lds, 0, nkt);
         for (int t = slot;;) {
             // trip 0 of tile t is done; K tiles 4..7 are in flight or landed
             for (int tr = 1; tr < trips - 1; ++tr)
-                pipe_trip<false, false>(acc, r0, r1, P, S, S, false, R, lds, tr * NST, nkt);
+                pipe_trip<false, false, FMT>(acc, r0, r1, P, S, S, false, R, lds, tr * NST, nkt);
             if (!finish_tile(t, std::false_type{}, (trips - 1) * NST)) break;
             t += G;
             // trip 0 of the next tile; its first three waits allow for the 32 stores
-            pipe_trip<true, false>(acc, r0, r1, P, S, S, false, R, lds, 0, nkt);
+            pipe_trip<true, false, FMT>(acc, r0, r1, P, S, S, false, R, lds, 0, nkt);
         }
     }
     // drain the last (empty) prefetch and the last stores
@@ -890,47 +968,59 @@ __global__ __launch_bounds__(256, 1) void gemm_persist_kernel(const uint8_t* __r
 
 }  // namespace mx
 
-extern "C" hipError_t mx_launch_gemm(const void* aq, const void* as, const void* bq, const void* bs, int64_t M,
-                                     int64_t N, int64_t K, void* out, int64_t ldo, hipStream_t stream) {
+namespace mx {
+
+template <int FMT>
+static hipError_t launch_gemm(const uint8_t* a8, const uint8_t* as8, const uint8_t* b8, const uint8_t* bs8, int64_t M,
+                              int64_t N, int64_t K, uint16_t* o16, int64_t ldo, hipStream_t stream) {
+    if (getenv_direct() != 0) {
+        if ((M + 63) / 64 > 65535 || (N + 63) / 64 > 0x7FFFFFFF) return hipErrorInvalidValue;
+        const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64)), block(256);
+        hipLaunchKernelGGL(gemm_direct_kernel<FMT>, grid, block, 0, stream, a8, as8, b8, bs8, (int)M, (int)N, (int)K,
+                           o16, ldo);
+        return hipGetLastError();
+    }
+    const int64_t tiles_m = (M + PBM - 1) / PBM, tiles_n = (N + PBN - 1) / PBN;
+    // 256 x 256 tiles need both sides >= 128 and enough tiles to fill half the CUs
+    const bool tiled = K > 0 && M >= 128 && N >= 128 && tiles_m * tiles_n * 2 >= num_cus();
+    if (!tiled) return launch_skinny<FMT>(a8, as8, b8, bs8, M, N, K, o16, ldo, stream);
+    if (tiles_m * tiles_n > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const int group_m = 8;
+    const int64_t nkt = FMT == 8 ? (K + 63) / 64 : (K + 127) / 128;
+    // persistent kernel: needs 16-byte aligned output rows, N % 8 == 0, and a tile's output
+    // bytes (256 rows) addressable by a 31-bit buffer offset
+    const bool persist = (reinterpret_cast<uintptr_t>(o16) & 15u) == 0 && (ldo & 7) == 0 && (N & 7) == 0 &&
+                         (int64_t)PBM * ldo * 2 < 0x7FFFFFF0ll && getenv_persist() != 0;
+    if (persist) {
+        const int64_t grid = std::min<int64_t>(tiles_m * tiles_n, num_cus());
+        auto kern = nkt <= NST ? gemm_persist_kernel<true, FMT> : gemm_persist_kernel<false, FMT>;
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, stream, a8, as8, b8, bs8, (int)M, (int)N, (int)K,
+                           o16, ldo, (int)tiles_m, (int)tiles_n, group_m);
+        return hipGetLastError();
+    }
+    // 8-byte output stores need an 8-byte aligned start for every row
+    const bool vec = (reinterpret_cast<uintptr_t>(o16) & 7u) == 0 && (ldo & 3) == 0;
+    auto kern = vec ? gemm_pipe_kernel<true, FMT> : gemm_pipe_kernel<false, FMT>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, stream, a8, as8, b8, bs8, (int)M,
+                       (int)N, (int)K, o16, ldo, (int)tiles_m, (int)tiles_n, group_m);
+    return hipGetLastError();
+}
+
+}  // namespace mx
+
+// fmt 4: both operands MXFP4; fmt 8: both MXFP8 (E4M3).
+extern "C" hipError_t mx_launch_gemm_f(const void* aq, const void* as, const void* bq, const void* bs, int64_t M,
+                                       int64_t N, int64_t K, void* out, int64_t ldo, int fmt, hipStream_t stream) {
     if (M == 0 || N == 0) return hipSuccess;
     const uint8_t *a8 = static_cast<const uint8_t*>(aq), *as8 = static_cast<const uint8_t*>(as);
     const uint8_t *b8 = static_cast<const uint8_t*>(bq), *bs8 = static_cast<const uint8_t*>(bs);
     uint16_t* o16 = static_cast<uint16_t*>(out);
-    if (getenv_direct() != 0) {
-        if ((M + 63) / 64 > 65535 || (N + 63) / 64 > 0x7FFFFFFF) return hipErrorInvalidValue;
-        const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64)), block(256);
-        hipLaunchKernelGGL(mx::gemm_direct_kernel, grid, block, 0, stream, a8, as8, b8, bs8, (int)M, (int)N, (int)K,
-                           o16, ldo);
-        return hipGetLastError();
-    }
-    const int64_t tiles_m = (M + mx::PBM - 1) / mx::PBM, tiles_n = (N + mx::PBN - 1) / mx::PBN;
-    // 256 x 256 tiles need both sides >= 128 and enough tiles to fill half the CUs
-    const bool tiled = K > 0 && M >= 128 && N >= 128 && tiles_m * tiles_n * 2 >= mx::num_cus();
-    if (!tiled) return mx::launch_skinny(a8, as8, b8, bs8, M, N, K, o16, ldo, stream);
-    {
-        if (tiles_m * tiles_n > 0x7FFFFFFF) return hipErrorInvalidValue;
-        const int group_m = 8;
-        const int64_t nkt = (K + mx::PBK - 1) / mx::PBK;
-        // persistent kernel: needs 16-byte aligned output rows, N % 8 == 0, and a tile's output
-        // bytes (256 rows) addressable by a 31-bit buffer offset
-        const bool persist = (reinterpret_cast<uintptr_t>(out) & 15u) == 0 && (ldo & 7) == 0 && (N & 7) == 0 &&
-                             (int64_t)mx::PBM * ldo * 2 < 0x7FFFFFF0ll && getenv_persist() != 0;
-        if (persist) {
-            const int64_t grid = std::min<int64_t>(tiles_m * tiles_n, mx::num_cus());
-            auto kern = nkt <= mx::NST ? mx::gemm_persist_kernel<true> : mx::gemm_persist_kernel<false>;
-            hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, stream,
-                               static_cast<const uint8_t*>(aq), static_cast<const uint8_t*>(as),
-                               static_cast<const uint8_t*>(bq), static_cast<const uint8_t*>(bs), (int)M, (int)N,
-                               (int)K, static_cast<uint16_t*>(out), ldo, (int)tiles_m, (int)tiles_n, group_m);
-            return hipGetLastError();
-        }
-        // 8-byte output stores need an 8-byte aligned start for every row
-        const bool vec = (reinterpret_cast<uintptr_t>(out) & 7u) == 0 && (ldo & 3) == 0;
-        auto kern = vec ? mx::gemm_pipe_kernel<true> : mx::gemm_pipe_kernel<false>;
-        hipLaunchKernelGGL(kern, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, stream,
-                           static_cast<const uint8_t*>(aq), static_cast<const uint8_t*>(as),
-                           static_cast<const uint8_t*>(bq), static_cast<const uint8_t*>(bs), (int)M, (int)N, (int)K,
-                           static_cast<uint16_t*>(out), ldo, (int)tiles_m, (int)tiles_n, group_m);
-        return hipGetLastError();
-    }
+    if (fmt == 8) return mx::launch_gemm<8>(a8, as8, b8, bs8, M, N, K, o16, ldo, stream);
+    if (fmt == 4) return mx::launch_gemm<4>(a8, as8, b8, bs8, M, N, K, o16, ldo, stream);
+    return hipErrorInvalidValue;
+}
+
+extern "C" hipError_t mx_launch_gemm(const void* aq, const void* as, const void* bq, const void* bs, int64_t M,
+                                     int64_t N, int64_t K, void* out, int64_t ldo, hipStream_t stream) {
+    return mx_launch_gemm_f(aq, as, bq, bs, M, N, K, out, ldo, 4, stream);
 }

@@ -9,6 +9,10 @@ length `k`:
 * scales: 1 KB tiles of 128 rows x 256 elements; the scale of (r, block b)
   sits at ((r//128) * KT2 + b//8) * 1024 + ((r//32)%4) * 256 + (r%32) * 8
   + (b%2) * 4 + (b%8)//2 with KT2 = ceil(k/256).
+
+MXFP8 operands keep the scales and store one E4M3 code per byte in 1 KB
+tiles of 16 rows x 64 elements: element k of row r at ((r//16) * KT8 +
+k//64) * 1024 + (r%16) * 64 + k%64 with KT8 = ceil(k/64).
 """
 import numpy as np
 
@@ -70,6 +74,40 @@ def scales_from_rowmajor(s, rows, k):
     out = np.zeros(scale_bytes(rows, k), np.uint8)
     out[scale_offsets(rows, k)] = np.asarray(s, np.uint8)
     return out
+
+
+def code8_bytes(rows, k):
+    return -(-rows // 16) * (-(-k // 64)) * 1024
+
+
+def code8_offsets(rows, k):
+    """int64 [rows, k]: device byte offset of each MXFP8 code."""
+    _check(k)
+    kt = -(-k // 64)
+    r = np.arange(rows, dtype=np.int64)[:, None]
+    e = np.arange(k, dtype=np.int64)[None, :]
+    return ((r // 16) * kt + e // 64) * 1024 + (r % 16) * 64 + e % 64
+
+
+def codes8_to_rowmajor(q_dev, rows, k):
+    """Device MXFP8 code bytes -> uint8 [rows, k]."""
+    q_dev = np.asarray(q_dev, np.uint8).reshape(-1)
+    if q_dev.size < code8_bytes(rows, k):
+        raise ValueError("code buffer too small")
+    return q_dev[code8_offsets(rows, k)]
+
+
+def codes8_from_rowmajor(q, rows, k):
+    out = np.zeros(code8_bytes(rows, k), np.uint8)
+    out[code8_offsets(rows, k)] = np.asarray(q, np.uint8)
+    return out
+
+
+def code8_padding_mask(rows, k):
+    """True at device MXFP8 code bytes that no (row, element) maps to."""
+    m = np.ones(code8_bytes(rows, k), bool)
+    m[code8_offsets(rows, k)] = False
+    return m
 
 
 def code_padding_mask(rows, k):

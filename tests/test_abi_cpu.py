@@ -191,3 +191,71 @@ def test_layout_dword_holds_four_consecutive_k_steps():
         for h in range(2):
             dword = [off[r, h + 2 * t] for t in range(4)]
             assert dword == [(r // 32) * 256 + (r % 32) * 8 + h * 4 + t for t in range(4)]
+
+
+@pytest.mark.parametrize("rows,k", [(1, 32), (17, 32), (32, 256), (33, 288), (8192, 4096)])
+def test_fp8_operand_layout(rows, k):
+    L = N.operand_layout(rows, k, 8)
+    assert L.code_row_tiles == -(-rows // 16) and L.code_k_tiles == -(-k // 64)
+    assert L.scale_row_tiles == -(-rows // 128) and L.scale_k_tiles == -(-k // 256)
+    assert L.q_bytes == L.code_row_tiles * L.code_k_tiles * 1024 == layout.code8_bytes(rows, k)
+    assert L.s_bytes == layout.scale_bytes(rows, k)
+    out = N.OperandLayout()
+    assert N.lib().mxfp8_operand_layout_of(4, 48, ctypes.byref(out)) == -1
+
+
+def test_fp8_layout_offsets_are_a_bijection_and_tile_kilobytes():
+    rng = np.random.default_rng(1)
+    for rows, k in ((1, 32), (17, 96), (64, 256), (100, 800), (257, 4096)):
+        off = layout.code8_offsets(rows, k).ravel()
+        assert off.min() >= 0 and off.max() < layout.code8_bytes(rows, k)
+        assert np.unique(off).size == off.size
+        q = rng.integers(0, 255, (rows, k)).astype(np.uint8)
+        assert np.array_equal(layout.codes8_to_rowmajor(layout.codes8_from_rowmajor(q, rows, k), rows, k), q)
+    # a 16-row x 64-element code tile is one aligned kilobyte, rows of 64 consecutive bytes
+    off = layout.code8_offsets(32, 256)
+    for r0 in (0, 16):
+        for k0 in (0, 64, 128, 192):
+            blk = off[r0:r0 + 16, k0:k0 + 64]
+            assert blk.min() % 1024 == 0 and np.array_equal(blk.ravel(), blk.min() + np.arange(1024))
+
+
+def test_fp8_argument_validation():
+    L = N.lib()
+    assert L.mxfp8_cast(FAKE, 4, 33, 40, FAKE, FAKE, None) == -1
+    assert L.mxfp8_cast(FAKE + 2, 4, 32, 32, FAKE, FAKE, None) == -2
+    assert L.mxfp8_cast(FAKE, 0, 32, 32, None, None, None) == 0
+    for f in (L.mxfp8_cast_dual, L.mxfp4_cast_dual_fp8col):
+        assert f(FAKE, 4, 32, 32, FAKE, FAKE, None, FAKE, None) == -1
+        assert f(FAKE, 4, 32, 32, FAKE, FAKE, FAKE + 4, FAKE, None) == -2
+        assert f(FAKE, 4, 48, 48, FAKE, FAKE, FAKE, FAKE, None) == -1
+    g = L.mxfp8_gemm_nt
+    assert g(FAKE, FAKE, FAKE, FAKE, 4, 4, 48, FAKE, 4, None) == -1
+    assert g(FAKE + 4, FAKE, FAKE, FAKE, 4, 4, 32, FAKE, 4, None) == -2
+    assert g(FAKE, FAKE, FAKE, FAKE, 0, 4, 32, None, 4, None) == 0
+
+
+def test_fp8_wgrad_flags_and_workspace():
+    L = N.lib()
+    T, H, Q, F = N.STEP_TRAINING, N.STEP_HADAMARD_GRAD, N.STEP_QUANTIZED_W, N.STEP_FP8_WGRAD
+
+    def op(rows, k, fmt=4):
+        return (layout.code8_bytes(rows, k) if fmt == 8 else layout.code_bytes(rows, k)) + layout.scale_bytes(rows, k)
+    M, Nn, K = 17, 96, 64
+    Mp = 32
+    base = op(M, K) + op(Nn, K) + op(K, Nn) + op(M, Nn)
+    assert L.gemm_fp4_bf16_workspace_bytes_ex(M, Nn, K, T) == base + op(K, Mp) + op(Nn, Mp)
+    assert L.gemm_fp4_bf16_workspace_bytes_ex(M, Nn, K, T | F) == base + op(K, Mp, 8) + op(Nn, Mp, 8)
+    assert L.gemm_fp4_bf16_workspace_bytes_ex(M, Nn, K, T | F | Q) == \
+        base + op(K, Mp, 8) + op(Nn, Mp, 8) - op(Nn, K) - op(K, Nn)
+    assert L.gemm_fp4_bf16_workspace_bytes_ex(M, Nn, K, 0) == L.gemm_fp4_bf16_workspace_bytes(M, Nn, K, 0)
+    assert L.gemm_fp4_bf16_workspace_bytes_ex(M, Nn, K, T | H) == L.gemm_fp4_bf16_workspace_bytes(M, Nn, K, 1)
+    assert L.gemm_fp4_bf16_workspace_bytes_ex(M, Nn, K, T | H | F) == 0      # the transform is MXFP4-only
+    assert L.gemm_fp4_bf16_workspace_bytes_ex(M, Nn, K, 16) == 0             # unknown flag
+    need = L.gemm_fp4_bf16_workspace_bytes_ex(64, 64, 64, T | F)
+    fwd, bwd = L.gemm_fp4_bf16_fwd_ex, L.gemm_fp4_bf16_bwd_ex
+    assert fwd(FAKE, FAKE, None, None, 64, 64, 64, FAKE, FAKE, need, T | H | F, None) == -1
+    assert fwd(FAKE, FAKE, None, None, 64, 64, 64, FAKE, FAKE, need, F, None) == -1   # needs training
+    assert fwd(FAKE, FAKE, None, None, 64, 64, 64, FAKE, FAKE, need - 1, T | F, None) == -6
+    assert bwd(FAKE, None, None, 64, 64, 64, FAKE, need - 1, FAKE, FAKE, T | F, None) == -6
+    assert bwd(FAKE, None, None, 64, 64, 64, FAKE, need, FAKE, FAKE, T | H | F, None) == -1
