@@ -9,11 +9,12 @@ every kernel launched through the C ABI on torch's current stream, inputs
 resident in HBM before timing starts.
 
 Prints ONE JSON line.  `value` is the whole step's throughput (6*M*N*K
-summed over the projections, divided by the step time including the casts).
+summed over the projections, divided by the step time including the casts),
+from K steps after W warm-up steps with nothing between the launches.
 `roofline` describes the dominant kernel (the GEMM): algorithmic FLOPs per
 launch over its average launch time, timed with events on the launch stream
-inside the timed region.  `cpu_baseline` times the CPU oracle on a bounded
-slab of the same workload.
+over a second pass of K steps that records an event after every launch.
+`cpu_baseline` times the CPU oracle on a bounded slab of the same workload.
 """
 import argparse
 import json
@@ -26,6 +27,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 FP4_PEAK_TFLOPS = 10100.0   # MI355X dense MXFP4 MFMA
+FP8_PEAK_TFLOPS = 5000.0    # MI355X dense FP8 MFMA
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
 METRIC = "MXFP4 GEMM TFLOP/s + % of MI355X FP4 peak (fwd+dA+dB), cast GB/s"
 
@@ -45,8 +47,10 @@ WORKLOADS = {
 def parse():
     p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=10)
-    p.add_argument("--warmup", type=int, default=3)
+    # defaults: 100 timed steps after 50 warm-up steps (the chip's clock and power settle over the
+    # first ~50 ms of back-to-back steps); the ragged sweep: 5 after 2 per combination
+    p.add_argument("--steps", type=int, default=None)
+    p.add_argument("--warmup", type=int, default=None)
     p.add_argument("--workload", default="llama8b_mlp", choices=sorted(WORKLOADS))
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target wall time of the CPU-oracle sample (0 skips the CPU baseline)")
@@ -54,11 +58,18 @@ def parse():
                    help="weights quantized once before timing (WeightWorkspace reuse): the step skips W's dual cast")
     p.add_argument("--hadamard-grad", action="store_true",
                    help="the Hadamard gradient recipe: column copies of A and W and both copies of dOut transformed")
+    p.add_argument("--fp8-wgrad", action="store_true",
+                   help="dB as an MXFP8 GEMM (column copies of A and dOut in MXFP8), as in the FP8 dB variant")
     p.add_argument("--no-kernel-events", action="store_true",
                    help="time only the whole step (no per-kernel events)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device copy of COPY_BYTES (for scaling HBM counters), then exit")
-    return p.parse_args()
+    a = p.parse_args()
+    if a.steps is None:
+        a.steps = 5 if a.workload == "ragged" else 100
+    if a.warmup is None:
+        a.warmup = 2 if a.workload == "ragged" else 50
+    return a
 
 
 COPY_BYTES = 1 << 30  # plain copy used to calibrate FETCH_SIZE / WRITE_SIZE
@@ -91,23 +102,29 @@ def measured_traffic():
         return None
 
 
-def gemm_roofline(m, n, k):
-    """Algorithmic FLOPs and minimum HBM bytes of out[m, n] = sum over k, and the bound they imply."""
+def gemm_roofline(m, n, k, fmt=4):
+    """Algorithmic FLOPs and minimum HBM bytes of out[m, n] = sum over k (MXFP4 or, fmt 8, MXFP8
+    operands), and the bound they imply."""
     flops = 2.0 * m * n * k
-    nbytes = m * k / 2 + n * k / 2 + (m + n) * k / 32 + 2.0 * m * n
-    t_mfma = flops / (FP4_PEAK_TFLOPS * 1e12)
+    code = 0.5 if fmt == 4 else 1.0
+    nbytes = m * k * code + n * k * code + (m + n) * k / 32 + 2.0 * m * n
+    t_mfma = flops / ((FP4_PEAK_TFLOPS if fmt == 4 else FP8_PEAK_TFLOPS) * 1e12)
     t_hbm = nbytes / (HBM_PEAK_GBPS * 1e9)
     return flops, nbytes, ("mfma" if t_mfma >= t_hbm else "hbm"), max(t_mfma, t_hbm)
 
 
-def step_ops(P, L, sp, N, cached_weights=False, hadamard=False):
+def step_ops(P, L, sp, N, cached_weights=False, hadamard=False, fp8_wgrad=False):
     """The training step of one projection: (kind, label, launch, work, roofline-ideal seconds).
     With cached_weights, W's copies are made once beforehand and the step has no W cast.
     With hadamard, the casts apply the gradient recipe's block transform (A and W: column copy;
-    dOut: both copies, divided by 32)."""
+    dOut: both copies, divided by 32).  With fp8_wgrad, A and dOut get MXFP8 column copies and
+    dB is the MXFP8 GEMM (kind "gemm8")."""
 
     def cast_dual(x, row, col, t_row=False, t_col=False, shift=0):
         R, C = x.shape
+        if col.fmt == 8:
+            return lambda: L.mxfp4_cast_dual_fp8col(x.data_ptr(), R, C, C, row.q.data_ptr(), row.s.data_ptr(),
+                                                    col.q.data_ptr(), col.s.data_ptr(), sp)
         if hadamard:
             return lambda: L.mxfp4_cast_hadamard(x.data_ptr(), R, C, C, row.q.data_ptr(), row.s.data_ptr(),
                                                  col.q.data_ptr(), col.s.data_ptr(), int(t_row), int(t_col), shift, sp)
@@ -125,27 +142,33 @@ def step_ops(P, L, sp, N, cached_weights=False, hadamard=False):
     if not cached_weights:
         casts.append(("cast_dual(W)", P["w"], P["w_row"], P["w_col"]))
     for label, x, row, col in casts:
-        nb = 3.0625 * x.shape[0] * x.shape[1]
+        # bytes per element: bf16 read, FP4 row codes, column codes (FP4 or FP8), two scale bytes per 32
+        nb = (2.5 + (1.0 if col.fmt == 8 else 0.5) + 2.0 / 32) * x.shape[0] * x.shape[1]
         ops.append(("cast", name + "." + label, cast_dual(x, row, col, False, True, 0), nb, nb / (HBM_PEAK_GBPS * 1e9)))
     fl, _, _, t = gemm_roofline(M, Nn, K)
     ops.append(("gemm", name + ".fwd", gemm(L.mxfp4_gemm_nt, P["a_row"], P["w_row"], P["out"]), fl, t))
-    nb = 3.0625 * M * Nn
+    nb = (2.5 + (1.0 if fp8_wgrad else 0.5) + 2.0 / 32) * M * Nn
     ops.append(("cast", name + ".cast_dual(dOut)", cast_dual(P["g"], P["g_row"], P["g_col"], True, True, 5), nb,
                 nb / (HBM_PEAK_GBPS * 1e9)))
     fl, _, _, t = gemm_roofline(M, K, Nn)
     ops.append(("gemm", name + ".dA", gemm(L.mxfp4_gemm_nn, P["g_row"], P["w_col"], P["da"]), fl, t))
-    fl, _, _, t = gemm_roofline(Nn, K, M)
-    ops.append(("gemm", name + ".dB", gemm(L.mxfp4_gemm_nt, P["g_col"], P["a_col"], P["dw"]), fl, t))
+    fl, _, _, t = gemm_roofline(Nn, K, M, fmt=8 if fp8_wgrad else 4)
+    if fp8_wgrad:
+        ops.append(("gemm8", name + ".dB(fp8)", gemm(L.mxfp8_gemm_nt, P["g_col"], P["a_col"], P["dw"]), fl, t))
+    else:
+        ops.append(("gemm", name + ".dB", gemm(L.mxfp4_gemm_nt, P["g_col"], P["a_col"], P["dw"]), fl, t))
     return ops
 
 
-def alloc_projection(name, M, Nn, K, a, w, g, mx, torch, dev):
-    """Device operands of one projection's step (a, w, g: bf16 device tensors)."""
+def alloc_projection(name, M, Nn, K, a, w, g, mx, torch, dev, fp8_wgrad=False):
+    """Device operands of one projection's step (a, w, g: bf16 device tensors); with fp8_wgrad
+    the column copies of A and dOut (dB's operands) are MXFP8."""
     Mp = -(-M // 32) * 32
+    cf = 8 if fp8_wgrad else 4
     P = dict(name=name, M=M, N=Nn, K=K, Mp=Mp, a=a, w=w, g=g)
-    P["a_row"], P["a_col"] = mx.empty_operand(M, K, dev), mx.empty_operand(K, Mp, dev)
+    P["a_row"], P["a_col"] = mx.empty_operand(M, K, dev), mx.empty_operand(K, Mp, dev, cf)
     P["w_row"], P["w_col"] = mx.empty_operand(Nn, K, dev), mx.empty_operand(K, Nn, dev)
-    P["g_row"], P["g_col"] = mx.empty_operand(M, Nn, dev), mx.empty_operand(Nn, Mp, dev)
+    P["g_row"], P["g_col"] = mx.empty_operand(M, Nn, dev), mx.empty_operand(Nn, Mp, dev, cf)
     P["out"] = torch.empty((M, Nn), dtype=torch.bfloat16, device=dev)
     P["da"] = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
     P["dw"] = torch.empty((Nn, K), dtype=torch.bfloat16, device=dev)
@@ -337,7 +360,8 @@ def main():
         a, w, g = W.projection_inputs(args.workload, idx, M, Nn, K)
         if idx == 0:
             host_inputs = {"a": a, "w": w, "M": M, "N": Nn, "K": K, "name": name}
-        projs.append(alloc_projection(name, M, Nn, K, to_dev(a), to_dev(w), to_dev(g), mx, torch, dev))
+        projs.append(alloc_projection(name, M, Nn, K, to_dev(a), to_dev(w), to_dev(g), mx, torch, dev,
+                                      args.fp8_wgrad))
         del a, w, g
     torch.cuda.synchronize()
     setup_s = time.time() - t0
@@ -348,7 +372,8 @@ def main():
     step_flops = 0.0
     for P in projs:
         step_flops += 6.0 * P["M"] * P["N"] * P["K"]
-        ops += step_ops(P, L, sp, N, cached_weights=args.cached_weights, hadamard=args.hadamard_grad)
+        ops += step_ops(P, L, sp, N, cached_weights=args.cached_weights, hadamard=args.hadamard_grad,
+                        fp8_wgrad=args.fp8_wgrad)
         if args.cached_weights:
             # the WeightWorkspace fill: W's dual cast once, outside the timed region
             R, C = P["w"].shape
@@ -356,21 +381,36 @@ def main():
                                           P["w_row"].s.data_ptr(), P["w_col"].q.data_ptr(), P["w_col"].s.data_ptr(),
                                           0, int(args.hadamard_grad), 0, sp), "mxfp4_cast_hadamard")
 
+    if args.fp8_wgrad and args.hadamard_grad:
+        sys.stderr.write("--fp8-wgrad and --hadamard-grad do not combine (the transform is MXFP4-only)\n")
+        sys.exit(2)
     use_events = not args.no_kernel_events
-    ms_per_step, per = time_ops(ops, args.steps, args.warmup, stream, torch, N, per_kernel=use_events)
+    # the timed region: K steps bracketed by two events, nothing between the launches
+    ms_per_step, _ = time_ops(ops, args.steps, args.warmup, stream, torch, N, per_kernel=False)
+    per = None
+    if use_events:
+        # per-kernel durations: the same K steps again with an event after every launch
+        # (each event adds a few microseconds between launches, so the step time above
+        # comes from the uninstrumented pass)
+        _, per = time_ops(ops, args.steps, 0, stream, torch, N, per_kernel=True)
 
     per_op = {}
     gemm_ms = cast_ms = 0.0
     gemm_launches = 0
     gemm_work = cast_bytes = 0.0
+    gemm8_ms = gemm8_work = 0.0
     if use_events:
         for (kind, label, _, work, _), ts in zip(ops, per):
             avg = sum(ts) / len(ts)
             rate = work / (avg * 1e-3)
+            is_gemm = kind in ("gemm", "gemm8")
             per_op[label] = {"ms": round(avg, 4),
-                             ("tflops" if kind == "gemm" else "gbps"): round(rate / (1e12 if kind == "gemm" else 1e9), 1),
+                             ("tflops" if is_gemm else "gbps"): round(rate / (1e12 if is_gemm else 1e9), 1),
                              **percentiles(ts)}
-            if kind == "gemm":
+            if kind == "gemm8":
+                gemm8_ms += avg
+                gemm8_work += work
+            elif kind == "gemm":
                 gemm_ms += avg
                 gemm_launches += 1
                 gemm_work += work
@@ -390,11 +430,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4",
+        "dtype": "mxfp4+mxfp8" if args.fp8_wgrad else "mxfp4",
         "data": "synthetic",
         "config": {"workload": WORKLOADS[args.workload] + (
                        "; weights quantized once (cached), no W cast in the step" if args.cached_weights else "") + (
-                       "; Hadamard gradient recipe" if args.hadamard_grad else ""),
+                       "; Hadamard gradient recipe" if args.hadamard_grad else "") + (
+                       "; dB as an MXFP8 GEMM (FP8 wgrad)" if args.fp8_wgrad else ""),
                    "projections": [[P["name"], P["M"], P["N"], P["K"]] for P in projs],
                    "step_tflop": round(step_flops / 1e12, 4)},
         "frac_of_fp4_peak": round(value / FP4_PEAK_TFLOPS, 4),
@@ -408,11 +449,18 @@ def main():
         result["cast_gbps"] = round(cast_gbps, 1)
         result["cast_frac_of_hbm"] = round(cast_gbps / HBM_PEAK_GBPS, 4)
         result["per_kernel"] = per_op
-        result["roofline"] = {"kernel": "mxfp4 block-scaled GEMM (fwd, dA, dB launches)",
+        if gemm8_ms > 0:
+            t8 = gemm8_work / (gemm8_ms * 1e-3) / 1e12
+            result["fp8_gemm"] = {"kernel": "mxfp8 block-scaled GEMM (dB launches)", "achieved": round(t8, 1),
+                                  "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(t8 / FP8_PEAK_TFLOPS, 4)}
+        result["roofline"] = {"kernel": "mxfp4 block-scaled GEMM (%s launches)" % (
+                                  "fwd, dA" if gemm8_ms > 0 else "fwd, dA, dB"),
                               "bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": FP4_PEAK_TFLOPS,
                               "unit": "TFLOP/s", "frac": round(gemm_tflops / FP4_PEAK_TFLOPS, 4),
                               "avg_launch_ms": round(avg_gemm_ms, 4),
-                              "flop_per_launch": gemm_work / gemm_launches, "traffic": measured_traffic()}
+                              "flop_per_launch": gemm_work / gemm_launches,
+                              # counters were taken over the default step's six MXFP4 launches
+                              "traffic": None if gemm8_ms > 0 else measured_traffic()}
         # sustained clock and power over ~0.5 s of further steps (not part of the timed region)
         with ClockSampler() as cs:
             t_end = time.time() + 0.5

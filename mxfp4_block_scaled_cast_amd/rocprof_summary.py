@@ -42,7 +42,18 @@ def source_hash(paths):
     return h.hexdigest()[:16]
 
 
-def kernel_stats(csv_path, out_md, command, include=None):
+def window_average(trace_csv, kernel_regex, start, count):
+    """Average duration (us) of dispatches start .. start+count-1, in start order, of the kernels
+    matching kernel_regex in a --kernel-trace CSV (e.g. the dispatches of one timed pass)."""
+    rows = [r for r in csv.DictReader(open(trace_csv)) if re.search(kernel_regex, r["Kernel_Name"])]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    sel = rows[start:start + count]
+    if len(sel) < count:
+        raise SystemExit("only %d dispatches of %r after %d" % (len(sel), kernel_regex, start))
+    return statistics.mean((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in sel)
+
+
+def kernel_stats(csv_path, out_md, command, include=None, trace=None, windows=(), note=None):
     rows = [r for r in csv.DictReader(open(csv_path)) if include is None or re.search(include, r["Name"])]
     lines = ["# rocprofv3 kernel statistics", "", "Command:", "", "```", command, "```", "",
              "| kernel | calls | total ms | average us | min us | max us | % |", "|---|---|---|---|---|---|---|"]
@@ -52,6 +63,15 @@ def kernel_stats(csv_path, out_md, command, include=None):
         lines.append("| %s | %s | %.3f | %.1f | %.1f | %.1f | %.1f |" % (
             name, r["Calls"], float(r["TotalDurationNs"]) / 1e6, float(r["AverageNs"]) / 1e3,
             float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    if windows:
+        lines += ["", "| kernel | dispatches (in start order) | average us |", "|---|---|---|"]
+        for spec in windows:
+            regex, rng = spec.rsplit("@", 1)
+            start, count = (int(x) for x in rng.split(":"))
+            lines.append("| %s | %d .. %d | %.1f |" % (regex, start, start + count - 1,
+                                                       window_average(trace, regex, start, count)))
+    if note:
+        lines += ["", note]
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -116,6 +136,10 @@ def main():
     k.add_argument("out")
     k.add_argument("--command", required=True)
     k.add_argument("--include", default=None, help="only kernels whose name matches this regex")
+    k.add_argument("--trace", default=None, help="the run's kernel_trace CSV (for --window)")
+    k.add_argument("--window", action="append", default=[],
+                   help="REGEX@START:COUNT: average duration of those dispatches of the matching kernels")
+    k.add_argument("--note", default=None, help="text appended to the summary")
     w = sub.add_parser("sweep-table")
     w.add_argument("json")
     w.add_argument("out")
@@ -134,7 +158,7 @@ def main():
     t.add_argument("--command", required=True)
     a = p.parse_args()
     if a.cmd == "kernel-stats":
-        kernel_stats(a.csv, a.out, a.command, a.include)
+        kernel_stats(a.csv, a.out, a.command, a.include, a.trace, a.window, a.note)
     elif a.cmd == "sweep-table":
         sweep_table(a.json, a.out, a.command)
     else:
