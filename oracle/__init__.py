@@ -37,6 +37,13 @@ the 32-point Sylvester Walsh-Hadamard matrix to every block in binary32
 (butterflies of half-width 1, 2, 4, 8, 16, each (u, w) -> (u + w, u - w)),
 divide by 2^shift and quantize by the same rule.  Used on both operands of a
 contraction, with shift 5 on one of them (H H = 32 I).
+
+Producers whose BF16 output feeds the cast (README "Supported ops": SiLU-and-Mul
+is silu(x[:half]) * x[half:], RMSNorm fuses square, mean, rsqrt and scale, Fused
+Add+RMSNorm normalizes x + residual): ``silu_mul``, ``rmsnorm`` -- evaluated in
+fp64 from the bf16 inputs and rounded once to bf16 (``bf16_round``); with a
+residual the sum is rounded to bf16 first (it is the stored residual) and the
+norm applies to that.  A fused producer + cast quantizes exactly these outputs.
 """
 import os
 
@@ -229,3 +236,51 @@ def gemm_pairs(qa, sa, qb, sb, mi, ni, nthreads=None):
     if rc:
         raise RuntimeError("mxo_gemm_pairs failed")
     return ref, absref
+
+
+# ---- producers feeding the cast (README "Supported ops": SiLU-and-Mul, RMSNorm,
+# Fused Add+RMSNorm); each returns BF16 bit patterns, evaluated in fp64 and rounded once
+
+def bf16_round(values):
+    """Nearest-even bf16 bit patterns (uint16) of float64 values, rounded once."""
+    v = np.ascontiguousarray(values, np.float64)
+    out = np.empty(v.shape, np.uint16)
+    if native.lib().mxo_bf16_round(v.ctypes.data, out.ctypes.data, v.size):
+        raise RuntimeError("mxo_bf16_round failed")
+    return out
+
+
+def silu_mul(x_bits, nthreads=None):
+    """y [R, F] = bf16(silu(gate) * up) for x [R, 2F] = [gate | up]."""
+    x = _bits(x_bits)
+    R, C = x.shape
+    if C % 2:
+        raise ValueError("x must have an even number of columns")
+    y = np.empty((R, C // 2), np.uint16)
+    if native.lib().mxo_silu_mul(x.ctypes.data, R, C // 2, C, y.ctypes.data, _threads(nthreads)):
+        raise RuntimeError("mxo_silu_mul failed")
+    return y
+
+
+def rmsnorm(x_bits, gamma_bits, eps, residual_bits=None, nthreads=None):
+    """RMSNorm of x [R, D] (of h = bf16(x + residual) with a residual):
+    (y = bf16(h * rstd * gamma) [R, D], h [R, D] or None, rstd [R] float64)."""
+    x = _bits(x_bits)
+    R, D = x.shape
+    g = np.ascontiguousarray(gamma_bits, np.uint16).reshape(-1)
+    if g.size != D:
+        raise ValueError("gamma must have D entries")
+    res = None
+    if residual_bits is not None:
+        res = _bits(residual_bits)
+        if res.shape != x.shape:
+            raise ValueError("residual must match x")
+    y = np.empty((R, D), np.uint16)
+    h = np.empty((R, D), np.uint16) if res is not None else None
+    rstd = np.empty(R, np.float64)
+    rc = native.lib().mxo_rmsnorm(x.ctypes.data, res.ctypes.data if res is not None else None, g.ctypes.data,
+                                  float(eps), R, D, y.ctypes.data, h.ctypes.data if h is not None else None,
+                                  rstd.ctypes.data, _threads(nthreads))
+    if rc:
+        raise RuntimeError("mxo_rmsnorm failed")
+    return y, h, rstd

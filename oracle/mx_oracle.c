@@ -632,3 +632,103 @@ int mxo_gemm_pairs(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, cons
     parallel_for(npairs, nthreads, gemm_pairs_range, &g);
     return 0;
 }
+
+/* ==== Producers that feed the cast (jax-aiter README, "Supported ops": SiLU-and-Mul,
+ * RMSNorm, Fused Add+RMSNorm).  Each returns its BF16 output; quantizing that output
+ * with the casts above is what a fused producer + cast computes. ==== */
+
+/* Nearest-even bf16 of a double, rounded once (no intermediate binary32):
+ * the grid of the value's binade (2^(e-7), or 2^-133 below 2^-126), RNE by rint,
+ * magnitudes that round past the largest finite bf16 become infinity. */
+static uint16_t bf16_round(double v) {
+    if (isnan(v)) return 0x7FC0;
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (a == 0.0) return sign;
+    if (isinf(a)) return sign | 0x7F80;
+    int e = floor_log2(a);
+    int qexp = e < -126 ? -133 : e - 7;          /* exponent of the grid spacing */
+    double r = rint(ldexp(a, -qexp));            /* integer multiple of the spacing, ties to even */
+    double val = ldexp(r, qexp);
+    if (val == 0.0) return sign;
+    int e2 = floor_log2(val);
+    if (e2 > 127) return sign | 0x7F80;
+    if (e2 < -126) return sign | (uint16_t)r;    /* subnormal: r < 128 */
+    double m = ldexp(val, 7 - e2);               /* in [128, 256) */
+    return sign | (uint16_t)((e2 + 127) << 7) | (uint16_t)((int)m - 128);
+}
+
+int mxo_bf16_round(const double* v, uint16_t* out, int64_t n) {
+    if (n < 0) return -1;
+    for (int64_t i = 0; i < n; ++i) out[i] = bf16_round(v[i]);
+    return 0;
+}
+
+typedef struct {
+    const uint16_t* x;
+    int64_t F, ldx;
+    uint16_t* y;
+} silu_ctx;
+
+static void silu_mul_range(void* p, int64_t lo, int64_t hi) {
+    silu_ctx* c = (silu_ctx*)p;
+    for (int64_t r = lo; r < hi; ++r)
+        for (int64_t j = 0; j < c->F; ++j) {
+            double g = bf16_value(c->x[r * c->ldx + j]);
+            double u = bf16_value(c->x[r * c->ldx + c->F + j]);
+            double silu = g / (1.0 + exp(-g));   /* SiLU(g) = g * sigmoid(g) */
+            c->y[r * c->F + j] = bf16_round(silu * u);
+        }
+}
+
+/* SiLU-and-Mul of x [R, 2F] (finite bf16; gate = columns 0..F-1, up = F..2F-1):
+ * y [R, F] = bf16(silu(gate) * up), evaluated in double. */
+int mxo_silu_mul(const uint16_t* x, int64_t R, int64_t F, int64_t ldx, uint16_t* y, int nthreads) {
+    if (R < 0 || F < 0 || ldx < 2 * F) return -1;
+    silu_ctx c = {x, F, ldx, y};
+    parallel_for(R, nthreads, silu_mul_range, &c);
+    return 0;
+}
+
+typedef struct {
+    const uint16_t *x, *res, *gamma;
+    int64_t D;
+    double eps;
+    uint16_t *y, *h;
+    double* rstd;
+} rms_ctx;
+
+static void rmsnorm_range(void* p, int64_t lo, int64_t hi) {
+    rms_ctx* c = (rms_ctx*)p;
+    int64_t D = c->D;
+    double* hv = (double*)malloc((size_t)(D > 0 ? D : 1) * sizeof(double));
+    for (int64_t r = lo; r < hi; ++r) {
+        double ss = 0.0;
+        for (int64_t j = 0; j < D; ++j) {
+            double v = bf16_value(c->x[r * D + j]);
+            if (c->res) {
+                /* the residual sum is rounded to bf16 (it is also the stored residual) */
+                uint16_t hb = bf16_round(v + bf16_value(c->res[r * D + j]));
+                if (c->h) c->h[r * D + j] = hb;
+                v = bf16_value(hb);
+            }
+            hv[j] = v;
+            ss += v * v;
+        }
+        double rs = 1.0 / sqrt(ss / (double)D + c->eps);
+        if (c->rstd) c->rstd[r] = rs;
+        for (int64_t j = 0; j < D; ++j) c->y[r * D + j] = bf16_round(hv[j] * rs * bf16_value(c->gamma[j]));
+    }
+    free(hv);
+}
+
+/* RMSNorm of x [R, D] (or, with res != NULL, of h = bf16(x + res), written to h
+ * when h != NULL): y = bf16(h * rstd * gamma) with rstd = 1 / sqrt(mean(h^2) + eps),
+ * all in double; rstd [R] written when non-NULL. */
+int mxo_rmsnorm(const uint16_t* x, const uint16_t* res, const uint16_t* gamma, double eps, int64_t R, int64_t D,
+                uint16_t* y, uint16_t* h, double* rstd, int nthreads) {
+    if (R < 0 || D <= 0 || !(eps >= 0.0)) return -1;
+    rms_ctx c = {x, res, gamma, D, eps, y, h, rstd};
+    parallel_for(R, nthreads, rmsnorm_range, &c);
+    return 0;
+}

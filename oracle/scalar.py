@@ -200,3 +200,32 @@ def quantize_block_fp8(bits):
     X = -127 if amax == 0 else min(127, max(-127, floor_log2(amax) - 8))
     codes = [nearest_e4m3_magnitude(abs(v) / Fraction(2) ** X) | (((h >> 15) & 1) << 7) for h, v in zip(bits, vals)]
     return X + 127, codes
+
+
+def bf16_round_exact(q, negative=None):
+    """Bit pattern of the bf16 nearest to the rational q (ties to even mantissa), rounded
+    once; magnitudes at or past the midpoint above the largest finite bf16 give infinity.
+    `negative` gives the sign of a zero q (a rational has none)."""
+    q = Fraction(q)
+    sign = 0x8000 if (q < 0 or (q == 0 and negative)) else 0
+    a = abs(q)
+    if a == 0:
+        return sign
+    e = floor_log2(a)
+    qexp = -133 if e < -126 else e - 7
+    unit = Fraction(2) ** qexp
+    t = a / unit
+    n = t.numerator // t.denominator
+    rem = t - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    val = n * unit
+    if val == 0:
+        return sign
+    e2 = floor_log2(val)
+    if e2 > 127:
+        return sign | 0x7F80
+    if e2 < -126:
+        return sign | n
+    m = val / Fraction(2) ** (e2 - 7)
+    return sign | ((e2 + 127) << 7) | (int(m) - 128)
