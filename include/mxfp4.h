@@ -197,6 +197,44 @@ int mxfp8_gemm_nt(const void* a_q, const void* a_s, const void* b_q, const void*
                   void* out, int64_t ldo, hipStream_t stream);
 
 /*
+ * F4 -- fused producer + cast (jax-aiter README, Supported ops: SiLU-and-Mul
+ * computes silu(x[:half]) * x[half:]; RMSNorm fuses square, mean, rsqrt and
+ * scale; Fused Add+RMSNorm normalizes x + residual in one kernel).  These are
+ * the steps that produce the A operand of the MLP GEMMs; here the cast reads
+ * the producer's inputs and computes its BF16 output in registers, so that
+ * output need never be stored and read back.  The quantized values are
+ * exactly the producer's BF16 output (its exact result rounded once to bf16,
+ * nearest even), so the copies equal mxfp4_cast / mxfp4_cast_dual of that
+ * output bit for bit.
+ *
+ * Output copies (both entry points): q_row / s_row, the MXFP4 row copy,
+ * operand (rows, K) with K the output width; with q_col / s_col (both or
+ * neither) also the column copy, operand (K, ceil(rows/32)*32), in col_fmt 4
+ * (MXFP4) or 8 (MXFP8, the FP8 dB variant); col_fmt is ignored without a
+ * column copy.  y_out: optional bf16 [rows, K] contiguous, 16-byte aligned --
+ * the producer's output itself, for callers that also need it.  Copies are
+ * 16-byte aligned.  Errors as for mxfp4_cast; rows == 0 or K == 0 is a
+ * successful no-op.
+ *
+ * mxfp4_silu_mul_cast: x bf16 [rows, 2f], row stride ldx (>= 2f, % 8 == 0),
+ *   16-byte aligned; gate = columns 0..f-1, up = f..2f-1; f % 32 == 0.
+ *   Output y = bf16(silu(gate) * up) [rows, f], silu(g) = g / (1 + e^-g).
+ * mxfp4_rmsnorm_cast: x bf16 [rows, d] contiguous, d % 32 == 0; gamma bf16
+ *   [d]; 0 <= eps (finite).  Without a residual h = x; with residual (bf16
+ *   [rows, d] contiguous) h = bf16(x + residual), written to residual_out
+ *   (required then).  rstd: double [rows], 8-byte aligned, required: gets
+ *   1 / sqrt(mean(h^2) + eps) (the norm's saved statistic; the cast pass
+ *   reads it).  Output y = bf16(h * rstd * gamma) [rows, d].  Two kernels:
+ *   the row statistics (and residual sum), then the producing cast.
+ */
+int mxfp4_silu_mul_cast(const void* x, int64_t rows, int64_t f, int64_t ldx, void* q_row, void* s_row, void* q_col,
+                        void* s_col, int col_fmt, void* y_out, hipStream_t stream);
+
+int mxfp4_rmsnorm_cast(const void* x, const void* residual, const void* gamma, float eps, int64_t rows, int64_t d,
+                       void* q_row, void* s_row, void* q_col, void* s_col, int col_fmt, void* residual_out,
+                       void* rstd, void* y_out, hipStream_t stream);
+
+/*
  * A7 -- workspace for gemm_fp4_bf16_fwd/bwd with activations [M, K] and
  * weights [N, K].  training != 0 sizes for fwd + bwd: it holds the row copies
  * of A and W, the saved column copies of A and W that the backward pass reads,

@@ -146,6 +146,67 @@ def cast_dual_fp8col(x) -> Mxfp4Tensor:
     return _cast_dual_formats(x, 4, N.lib().mxfp4_cast_dual_fp8col, "mxfp4_cast_dual_fp8col")
 
 
+def _produced_copies(R, K, device, columnwise, col_fmt):
+    if col_fmt not in (4, 8):
+        raise ValueError("col_fmt must be 4 (MXFP4) or 8 (MXFP8)")
+    Rp = -(-R // 32) * 32
+    row = empty_operand(R, K, device)
+    col = empty_operand(K, Rp, device, col_fmt) if columnwise else None
+    return row, col
+
+
+def silu_mul_cast(x, columnwise=True, col_fmt=4, return_y=False):
+    """Fused SiLU-and-mul + cast (README Supported ops: silu(x[:half]) * x[half:]).
+
+    x: bf16 [R, 2F] = [gate | up] with unit column stride.  Returns the Mxfp4Tensor of
+    y = bf16(silu(gate) * up) [R, F] (row copy, and with columnwise the column copy in
+    col_fmt 4 = MXFP4 or 8 = MXFP8), and y itself when return_y (else None)."""
+    _check_bf16_matrix(x, "x")
+    R, C = x.shape
+    if C % 64:
+        raise ValueError("x must have 2F columns with F a multiple of 32")
+    F = C // 2
+    row, col = _produced_copies(R, F, x.device, columnwise, col_fmt)
+    y = torch.empty((R, F), dtype=torch.bfloat16, device=x.device) if return_y else None
+    st = N.lib().mxfp4_silu_mul_cast(x.data_ptr(), R, F, x.stride(0), row.q.data_ptr(), row.s.data_ptr(),
+                                     col.q.data_ptr() if col is not None else None,
+                                     col.s.data_ptr() if col is not None else None, col_fmt,
+                                     y.data_ptr() if y is not None else None, _stream(x.device))
+    N.check(st, "mxfp4_silu_mul_cast")
+    return Mxfp4Tensor(row, col, (R, F)), y
+
+
+def rmsnorm_cast(x, gamma, eps=1e-5, residual=None, columnwise=True, col_fmt=4, return_y=False):
+    """Fused RMSNorm (or Add+RMSNorm with a residual) + cast (README Supported ops).
+
+    x (and residual): bf16 [R, D] contiguous; gamma: bf16 [D].  h = x, or bf16(x + residual);
+    y = bf16(h * rstd * gamma) with rstd = 1 / sqrt(mean(h^2) + eps).  Returns
+    (Mxfp4Tensor of y, h when a residual is given else None, rstd float64 [R], y or None)."""
+    _check_bf16_matrix(x, "x")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    R, D = x.shape
+    if gamma.dtype != torch.bfloat16 or gamma.numel() != D or not gamma.is_contiguous():
+        raise ValueError("gamma must be a contiguous bfloat16 tensor of %d elements" % D)
+    h = None
+    if residual is not None:
+        _check_bf16_matrix(residual, "residual")
+        if residual.shape != x.shape or not residual.is_contiguous():
+            raise ValueError("residual must be contiguous and shaped like x")
+        h = torch.empty_like(x)
+    row, col = _produced_copies(R, D, x.device, columnwise, col_fmt)
+    rstd = torch.empty((R,), dtype=torch.float64, device=x.device)
+    y = torch.empty((R, D), dtype=torch.bfloat16, device=x.device) if return_y else None
+    st = N.lib().mxfp4_rmsnorm_cast(x.data_ptr(), residual.data_ptr() if residual is not None else None,
+                                    gamma.data_ptr(), float(eps), R, D, row.q.data_ptr(), row.s.data_ptr(),
+                                    col.q.data_ptr() if col is not None else None,
+                                    col.s.data_ptr() if col is not None else None, col_fmt,
+                                    h.data_ptr() if h is not None else None, rstd.data_ptr(),
+                                    y.data_ptr() if y is not None else None, _stream(x.device))
+    N.check(st, "mxfp4_rmsnorm_cast")
+    return Mxfp4Tensor(row, col, (R, D)), h, rstd, y
+
+
 def _gemm(fn, name, a: MxOperand, b: MxOperand, out):
     if a.k != b.k:
         raise ValueError("contraction lengths differ: %d vs %d" % (a.k, b.k))

@@ -30,6 +30,13 @@ extern "C" hipError_t mx_launch_gemm(const void* aq, const void* as, const void*
 extern "C" hipError_t mx_launch_cast_f(const void* x, int64_t R, int64_t C, int64_t ldx, void* q_row, void* s_row,
                                        void* q_col, void* s_col, bool dual, int row_fmt, int col_fmt,
                                        bool transform_row, bool transform_col, int hshift, hipStream_t stream);
+extern "C" hipError_t mx_launch_silu_mul_cast(const void* x, int64_t R, int64_t F, int64_t ldx, void* q_row,
+                                              void* s_row, void* q_col, void* s_col, bool dual, int col_fmt,
+                                              void* y_out, hipStream_t stream);
+extern "C" hipError_t mx_launch_rmsnorm_cast(const void* x, const void* residual, const void* gamma, float eps,
+                                             int64_t R, int64_t D, void* q_row, void* s_row, void* q_col, void* s_col,
+                                             bool dual, int col_fmt, void* h_out, void* rstd, void* y_out,
+                                             hipStream_t stream);
 extern "C" hipError_t mx_launch_gemm_f(const void* aq, const void* as, const void* bq, const void* bs, int64_t M,
                                        int64_t N, int64_t K, void* out, int64_t ldo, int fmt, hipStream_t stream);
 
@@ -292,6 +299,54 @@ int mxfp8_gemm_nt(const void* a_q, const void* a_s, const void* b_q, const void*
     if (st != MXFP4_OK || M == 0 || N == 0) return st;
     if ((st = check_device()) != MXFP4_OK) return st;
     return status_of(mx_launch_gemm_f(a_q, a_s, b_q, b_s, M, N, K, out, ldo, 8, stream));
+}
+
+namespace {
+// Output copies of a fused producer + cast: the MXFP4 row copy, and the column
+// copy (both pointers or neither) in col_fmt 4 or 8.
+int validate_copies(const void* q_row, const void* s_row, const void* q_col, const void* s_col, int col_fmt,
+                    bool& dual) {
+    if (!q_row || !s_row) return MXFP4_EINVAL;
+    if ((q_col == nullptr) != (s_col == nullptr)) return MXFP4_EINVAL;
+    dual = q_col != nullptr;
+    if (dual && col_fmt != 4 && col_fmt != 8) return MXFP4_EINVAL;
+    if (!aligned16(q_row) || !aligned16(s_row) || (dual && (!aligned16(q_col) || !aligned16(s_col))))
+        return MXFP4_EALIGN;
+    return MXFP4_OK;
+}
+}  // namespace
+
+int mxfp4_silu_mul_cast(const void* x, int64_t rows, int64_t f, int64_t ldx, void* q_row, void* s_row, void* q_col,
+                        void* s_col, int col_fmt, void* y_out, hipStream_t stream) {
+    if (rows < 0 || f < 0 || f % 32 != 0) return MXFP4_EINVAL;
+    if (rows > kMaxDim || 2 * f > kMaxDim) return MXFP4_ERANGE;
+    if (rows == 0 || f == 0) return MXFP4_OK;
+    if (!x || ldx < 2 * f) return MXFP4_EINVAL;
+    bool dual = false;
+    int st = validate_copies(q_row, s_row, q_col, s_col, col_fmt, dual);
+    if (st != MXFP4_OK) return st;
+    if (!aligned16(x) || ldx % 8 != 0 || (y_out && !aligned16(y_out))) return MXFP4_EALIGN;
+    if ((st = check_device()) != MXFP4_OK) return st;
+    return status_of(mx_launch_silu_mul_cast(x, rows, f, ldx, q_row, s_row, q_col, s_col, dual, col_fmt, y_out,
+                                             stream));
+}
+
+int mxfp4_rmsnorm_cast(const void* x, const void* residual, const void* gamma, float eps, int64_t rows, int64_t d,
+                       void* q_row, void* s_row, void* q_col, void* s_col, int col_fmt, void* residual_out,
+                       void* rstd, void* y_out, hipStream_t stream) {
+    if (rows < 0 || d < 0 || d % 32 != 0 || !(eps >= 0.0f) || eps > 3.0e38f) return MXFP4_EINVAL;
+    if (rows > kMaxDim || d > kMaxDim) return MXFP4_ERANGE;
+    if (rows == 0 || d == 0) return MXFP4_OK;
+    if (!x || !gamma || !rstd || (residual && !residual_out)) return MXFP4_EINVAL;
+    bool dual = false;
+    int st = validate_copies(q_row, s_row, q_col, s_col, col_fmt, dual);
+    if (st != MXFP4_OK) return st;
+    if (!aligned16(x) || !aligned16(gamma) || (reinterpret_cast<uintptr_t>(rstd) & 7u) != 0 ||
+        (residual && (!aligned16(residual) || !aligned16(residual_out))) || (y_out && !aligned16(y_out)))
+        return MXFP4_EALIGN;
+    if ((st = check_device()) != MXFP4_OK) return st;
+    return status_of(mx_launch_rmsnorm_cast(x, residual, gamma, eps, rows, d, q_row, s_row, q_col, s_col, dual,
+                                            col_fmt, residual ? residual_out : nullptr, rstd, y_out, stream));
 }
 
 size_t gemm_fp4_bf16_workspace_bytes(int64_t M, int64_t N, int64_t K, int training) {

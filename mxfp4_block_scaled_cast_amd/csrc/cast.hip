@@ -60,6 +60,82 @@ __device__ __forceinline__ unsigned cvt_pair_f32(unsigned old, float lo, float h
 __device__ __forceinline__ float bf16_lo(unsigned pair) { return __builtin_bit_cast(float, pair << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned pair) { return __builtin_bit_cast(float, pair & 0xFFFF0000u); }
 
+// ---------------------------------------------------------------------------
+// Producers: the values the cast quantizes can be computed in registers from
+// the kernel's inputs instead of read from HBM (jax-aiter README, Supported
+// ops: SiLU-and-Mul is silu(x[:half]) * x[half:]; RMSNorm fuses square, mean,
+// rsqrt and scale; Fused Add+RMSNorm normalizes x + residual).  The produced
+// values are the producer's BF16 output -- its exact result rounded once to
+// bf16 -- so the fused kernel quantizes exactly what the producer would have
+// stored.  PROD_RMS scales rows by a per-row rstd the statistics kernel below
+// computed in fp64.
+// ---------------------------------------------------------------------------
+enum : int { PROD_LOAD = 0, PROD_SILU_MUL = 1, PROD_RMS = 2 };
+
+struct ProdArgs {
+    int64_t up_offset;      // SiLU-and-mul: elements from a gate value to its up value
+    const uint16_t* gamma;  // RMS: gamma [C]
+    const double* rstd;     // RMS: 1 / sqrt(mean(h^2) + eps) per row
+    uint16_t* y_out;        // optional: the produced bf16 values [R, C], row stride C
+};
+
+// bf16 bits (nearest even) of a double, rounded once: the significand is cut at
+// the bf16 grid of the value's binade (2^(e-7), or 2^-133 below 2^-126); past
+// the largest finite bf16 the result is infinity; NaN gives the quiet NaN 0x7FC0.
+__device__ __forceinline__ unsigned bf16_from_f64(double v) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const unsigned sign = (unsigned)(b >> 48) & 0x8000u;
+    const int e = (int)((b >> 52) & 0x7FF);
+    const uint64_t mant = b & 0xFFFFFFFFFFFFFull;
+    if (e == 0x7FF) return mant ? 0x7FC0u : (sign | 0x7F80u);
+    if (e == 0) return sign;  // double subnormals lie far below half the smallest bf16
+    const int ue = e - 1023;
+    if (ue > 127) return sign | 0x7F80u;
+    const uint64_t sig = mant | (1ull << 52);
+    const int q = ue >= -126 ? ue - 7 : -133;  // exponent of the bf16 grid spacing
+    const int sh = q - ue + 52;                // >= 45
+    if (sh > 63) return sign;
+    uint64_t n = sig >> sh;
+    const uint64_t rem = sig & ((1ull << sh) - 1), half = 1ull << (sh - 1);
+    if (rem > half || (rem == half && (n & 1))) ++n;
+    if (ue < -126) return sign | (unsigned)n;  // subnormal (n = 128 is the smallest normal)
+    // n in [128, 256]: 256 carries into the exponent field (to infinity from the top binade)
+    return sign | ((unsigned)((ue + 127) << 7) + (unsigned)n - 128u);
+}
+
+// bf16(silu(g) * u), rounded once.  The binary32 evaluation is within 2^-21 |y|
+// of the exact value (a few roundings and expf's error); unless that interval
+// may hold a bf16 rounding midpoint (the low half of the binary32 pattern near
+// 0x8000), the result is not finite, or e^-g overflows (g < -80), it rounds
+// like the exact value; otherwise the double evaluation decides.
+__device__ __forceinline__ unsigned silu_mul_bf16(float g, float u) {
+    const float y = g / (1.0f + expf(-g)) * u;
+    const unsigned low = __builtin_bit_cast(unsigned, y) & 0xFFFFu;
+    if ((low - 0x7FF0u) > 0x20u && g > -80.0f && __builtin_isfinite(y)) return f32_to_bf16_rne(y);
+    const double gd = g;
+    return bf16_from_f64(gd / (1.0 + exp(-gd)) * (double)u);
+}
+
+// 8 gate / 8 up bf16 values -> 8 bf16 outputs.
+__device__ __forceinline__ u32x4 silu_mul8(u32x4 g, u32x4 u) {
+    u32x4 r;
+#define MX_SM(F) r.F = silu_mul_bf16(bf16_lo(g.F), bf16_lo(u.F)) | (silu_mul_bf16(bf16_hi(g.F), bf16_hi(u.F)) << 16);
+    MX_SM(x) MX_SM(y) MX_SM(z) MX_SM(w)
+#undef MX_SM
+    return r;
+}
+
+// 8 bf16 h -> bf16(h * rstd * gamma) in double, rounded once.
+__device__ __forceinline__ u32x4 rms8(u32x4 h, double rs, u32x4 gm) {
+    u32x4 r;
+#define MX_RMS(F)                                                                                  \
+    r.F = bf16_from_f64((double)bf16_lo(h.F) * rs * (double)bf16_lo(gm.F)) |                       \
+          (bf16_from_f64((double)bf16_hi(h.F) * rs * (double)bf16_hi(gm.F)) << 16);
+    MX_RMS(x) MX_RMS(y) MX_RMS(z) MX_RMS(w)
+#undef MX_RMS
+    return r;
+}
+
 // Half-width H butterflies inside an array of N values (N a multiple of 2H).
 template <int H, int N>
 __device__ __forceinline__ void butterflies(float (&f)[N]) {
@@ -85,11 +161,12 @@ __device__ __forceinline__ float butterfly_lanes(float own, bool upper) {
 // ROWF / COLF: element format of the row / column copy, 4 = MXFP4 (E2M1),
 // 8 = MXFP8 (E4M3, one byte per code, X = floor(log2 amax) - 8, saturating
 // at 448; the transform is only offered with MXFP4).
-template <int TILE_R, bool DUAL, bool HROW, bool HCOL, int ROWF, int COLF>
+// PROD: where the quantized values come from (PROD_LOAD: x itself).
+template <int TILE_R, bool DUAL, bool HROW, bool HCOL, int ROWF, int COLF, int PROD = PROD_LOAD>
 __global__ __launch_bounds__(256, 4) void cast_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C, int64_t ldx,
                                                    uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
                                                    uint8_t* __restrict__ q_col, uint8_t* __restrict__ s_col,
-                                                   int n_rtiles, int n_ctiles, int hshift) {
+                                                   int n_rtiles, int n_ctiles, int hshift, ProdArgs P) {
     static_assert((ROWF == 4 || ROWF == 8) && (COLF == 4 || COLF == 8), "MXFP4 or MXFP8");
     static_assert(!(HROW && ROWF == 8) && !(HCOL && COLF == 8), "the transform goes with MXFP4 copies");
     constexpr int NI = TILE_R / 8;  // 16-byte loads per thread
@@ -110,11 +187,23 @@ __global__ __launch_bounds__(256, 4) void cast_kernel(const uint16_t* __restrict
     const bool col_ok = col < C;
 
     u32x4 v[NI];
+    u32x4 gm = {0u, 0u, 0u, 0u};
+    if constexpr (PROD == PROD_RMS)
+        if (col_ok) gm = *reinterpret_cast<const u32x4*>(P.gamma + col);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const int64_t row = r0 + i * 8 + (t >> 5);
         if (col_ok && row < R) {
-            v[i] = *reinterpret_cast<const u32x4*>(x + row * ldx + col);
+            const u32x4 a = *reinterpret_cast<const u32x4*>(x + row * ldx + col);
+            if constexpr (PROD == PROD_SILU_MUL) {
+                v[i] = silu_mul8(a, *reinterpret_cast<const u32x4*>(x + row * ldx + P.up_offset + col));
+            } else if constexpr (PROD == PROD_RMS) {
+                v[i] = rms8(a, P.rstd[row], gm);
+            } else {
+                v[i] = a;
+            }
+            if constexpr (PROD != PROD_LOAD)
+                if (P.y_out) *reinterpret_cast<u32x4*>(P.y_out + row * C + col) = v[i];
         } else {
             v[i] = u32x4{0u, 0u, 0u, 0u};
         }
@@ -356,9 +445,10 @@ extern "C" hipError_t mx_launch_cast_f(const void* x, int64_t R, int64_t C, int6
     uint8_t *qr = static_cast<uint8_t*>(q_row), *sr = static_cast<uint8_t*>(s_row);
     uint8_t *qc = static_cast<uint8_t*>(q_col), *scl = static_cast<uint8_t*>(s_col);
     const int nr = (int)n_rtiles, nc = (int)n_ctiles;
+    const mx::ProdArgs P{};
 #define MX_CAST(D, HR, HC, RF, CF)                                                                         \
     hipLaunchKernelGGL((mx::cast_kernel<TILE_R, D, HR, HC, RF, CF>), grid, block, 0, stream, xb, R, C, ldx, qr, \
-                       sr, D ? qc : nullptr, D ? scl : nullptr, nr, nc, hshift)
+                       sr, D ? qc : nullptr, D ? scl : nullptr, nr, nc, hshift, P)
     if (row_fmt == 8 || col_fmt == 8) {
         if (transform_row || transform_col) return hipErrorInvalidValue;
         if (!dual) {
@@ -394,4 +484,119 @@ extern "C" hipError_t mx_launch_cast_h(const void* x, int64_t R, int64_t C, int6
 extern "C" hipError_t mx_launch_cast(const void* x, int64_t R, int64_t C, int64_t ldx, void* q_row, void* s_row,
                                      void* q_col, void* s_col, bool dual, hipStream_t stream) {
     return mx_launch_cast_f(x, R, C, ldx, q_row, s_row, q_col, s_col, dual, 4, 4, false, false, 0, stream);
+}
+
+namespace mx {
+
+// Row statistics of RMSNorm (and the residual sum of Add+RMSNorm): one wave per
+// row, 16-byte loads.  With a residual, h = bf16(x + r): the binary32 sum of two
+// bf16 values is exact when their exponents differ by at most 15, and otherwise
+// lies too close to the larger one for a bf16 midpoint to fall in between, so
+// its nearest-even bf16 is the exactly rounded sum; h is stored (the residual
+// output, and the input of the cast pass).  The squares of h (exact in double,
+// tiny values included) are accumulated in double; rstd = 1 / sqrt(ss / D +
+// eps) in double.
+__global__ __launch_bounds__(256) void rms_stats_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ res,
+                                                        uint16_t* __restrict__ h_out, int64_t R, int64_t D, float eps,
+                                                        double* __restrict__ rstd) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= R) return;
+    const uint16_t* xr = x + row * D;
+    double ss = 0.0;
+    for (int64_t c = lane * 8; c < D; c += 512) {
+        u32x4 h = *reinterpret_cast<const u32x4*>(xr + c);
+        if (res) {
+            const u32x4 r = *reinterpret_cast<const u32x4*>(res + row * D + c);
+#define MX_ADD(F) h.F = f32x2_to_bf16x2_rne(bf16_lo(h.F) + bf16_lo(r.F), bf16_hi(h.F) + bf16_hi(r.F));
+            MX_ADD(x) MX_ADD(y) MX_ADD(z) MX_ADD(w)
+#undef MX_ADD
+            *reinterpret_cast<u32x4*>(h_out + row * D + c) = h;
+        }
+#define MX_SQ(F)                                                  \
+    {                                                             \
+        const double lo = bf16_lo(h.F), hi = bf16_hi(h.F);        \
+        ss = __builtin_fma(lo, lo, ss);                           \
+        ss = __builtin_fma(hi, hi, ss);                           \
+    }
+        MX_SQ(x) MX_SQ(y) MX_SQ(z) MX_SQ(w)
+#undef MX_SQ
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    if (lane == 0) rstd[row] = 1.0 / sqrt(ss / (double)D + (double)eps);
+}
+
+// Grid of the cast kernel over x [R, C] (TILE_R = 64 rows x 256 columns per
+// workgroup), covering the padded rows of the copies it writes.
+static bool cast_grid(int64_t R, int64_t C, bool dual, int& nr, int& nc) {
+    const int64_t rows_cover = dual ? ((R + 255) & ~(int64_t)255) : ((R + 127) & ~(int64_t)127);
+    const int64_t n_rtiles = (rows_cover + 63) / 64, n_ctiles = (C + 255) / 256;
+    if (n_rtiles * n_ctiles > 0x7FFFFFFF) return false;
+    nr = (int)n_rtiles;
+    nc = (int)n_ctiles;
+    return true;
+}
+
+template <int PROD>
+static hipError_t launch_produced_cast(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, void* q_row,
+                                       void* s_row, void* q_col, void* s_col, bool dual, int col_fmt,
+                                       const ProdArgs& P, hipStream_t stream) {
+    int nr = 0, nc = 0;
+    if (!cast_grid(R, C, dual, nr, nc)) return hipErrorInvalidValue;
+    if ((int64_t)nr * nc == 0) return hipSuccess;
+    const dim3 grid((unsigned)((int64_t)nr * nc)), block(256);
+    uint8_t *qr = static_cast<uint8_t*>(q_row), *sr = static_cast<uint8_t*>(s_row);
+    uint8_t *qc = static_cast<uint8_t*>(q_col), *scl = static_cast<uint8_t*>(s_col);
+    if (!dual)
+        hipLaunchKernelGGL((cast_kernel<64, false, false, false, 4, 4, PROD>), grid, block, 0, stream, x, R, C, ldx,
+                           qr, sr, nullptr, nullptr, nr, nc, 0, P);
+    else if (col_fmt == 8)
+        hipLaunchKernelGGL((cast_kernel<64, true, false, false, 4, 8, PROD>), grid, block, 0, stream, x, R, C, ldx, qr,
+                           sr, qc, scl, nr, nc, 0, P);
+    else
+        hipLaunchKernelGGL((cast_kernel<64, true, false, false, 4, 4, PROD>), grid, block, 0, stream, x, R, C, ldx, qr,
+                           sr, qc, scl, nr, nc, 0, P);
+    return hipGetLastError();
+}
+
+}  // namespace mx
+
+// SiLU-and-mul + cast: x [R, 2F] (row stride ldx; gate = columns 0..F-1, up =
+// F..2F-1) -> MXFP4 row copy (and, dual, the column copy in col_fmt) of
+// bf16(silu(gate) * up), optionally also written to y_out [R, F].
+extern "C" hipError_t mx_launch_silu_mul_cast(const void* x, int64_t R, int64_t F, int64_t ldx, void* q_row,
+                                              void* s_row, void* q_col, void* s_col, bool dual, int col_fmt,
+                                              void* y_out, hipStream_t stream) {
+    mx::ProdArgs P{};
+    P.up_offset = F;
+    P.y_out = static_cast<uint16_t*>(y_out);
+    return mx::launch_produced_cast<mx::PROD_SILU_MUL>(static_cast<const uint16_t*>(x), R, F, ldx, q_row, s_row,
+                                                       q_col, s_col, dual, col_fmt, P, stream);
+}
+
+// RMSNorm (+ residual) + cast: the statistics kernel (rstd [R] in double; with a
+// residual, h = bf16(x + residual) into h_out), then the cast of
+// bf16(h * rstd * gamma) -- h read back from h_out, or x itself without a
+// residual -- optionally also written to y_out [R, D].
+extern "C" hipError_t mx_launch_rmsnorm_cast(const void* x, const void* residual, const void* gamma, float eps,
+                                             int64_t R, int64_t D, void* q_row, void* s_row, void* q_col, void* s_col,
+                                             bool dual, int col_fmt, void* h_out, void* rstd, void* y_out,
+                                             hipStream_t stream) {
+    if (R == 0 || D == 0) return hipSuccess;
+    const int64_t blocks = (R + 3) / 4;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    const uint16_t* rb = static_cast<const uint16_t*>(residual);
+    uint16_t* hb = static_cast<uint16_t*>(h_out);
+    double* rs = static_cast<double*>(rstd);
+    hipLaunchKernelGGL(mx::rms_stats_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, xb, rb, hb, R, D, eps, rs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    mx::ProdArgs P{};
+    P.gamma = static_cast<const uint16_t*>(gamma);
+    P.rstd = rs;
+    P.y_out = static_cast<uint16_t*>(y_out);
+    return mx::launch_produced_cast<mx::PROD_RMS>(rb ? hb : xb, R, D, D, q_row, s_row, q_col, s_col, dual, col_fmt, P,
+                                                  stream);
 }

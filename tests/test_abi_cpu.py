@@ -259,3 +259,36 @@ def test_fp8_wgrad_flags_and_workspace():
     assert fwd(FAKE, FAKE, None, None, 64, 64, 64, FAKE, FAKE, need - 1, T | F, None) == -6
     assert bwd(FAKE, None, None, 64, 64, 64, FAKE, need - 1, FAKE, FAKE, T | F, None) == -6
     assert bwd(FAKE, None, None, 64, 64, 64, FAKE, need, FAKE, FAKE, T | H | F, None) == -1
+
+
+def test_fused_producer_cast_argument_validation():
+    L = N.lib()
+    s = L.mxfp4_silu_mul_cast
+    assert s(FAKE, 4, 48, 96, FAKE, FAKE, None, None, 4, None, None) == -1        # f % 32
+    assert s(FAKE, 4, 32, 48, FAKE, FAKE, None, None, 4, None, None) == -1        # ldx < 2f
+    assert s(None, 4, 32, 64, FAKE, FAKE, None, None, 4, None, None) == -1        # null x
+    assert s(FAKE, 4, 32, 64, FAKE, FAKE, FAKE, None, 4, None, None) == -1        # half a column copy
+    assert s(FAKE, 4, 32, 64, FAKE, FAKE, FAKE, FAKE, 6, None, None) == -1        # column format
+    assert s(FAKE + 2, 4, 32, 64, FAKE, FAKE, None, None, 4, None, None) == -2    # misaligned x
+    assert s(FAKE, 4, 32, 68, FAKE, FAKE, None, None, 4, None, None) == -2        # ldx % 8
+    assert s(FAKE, 4, 32, 64, FAKE, FAKE, None, None, 4, FAKE + 8, None) == -2    # misaligned y_out
+    assert s(FAKE, 0, 32, 64, None, None, None, None, 4, None, None) == 0         # empty
+    r = L.mxfp4_rmsnorm_cast
+    ok = (FAKE, None, FAKE, 1e-5, 4, 64, FAKE, FAKE, None, None, 4, None, FAKE, None, None)
+
+    def call(**kw):
+        names = ["x", "res", "gamma", "eps", "rows", "d", "qr", "sr", "qc", "sc", "fmt", "res_out", "rstd", "y", "st"]
+        args = dict(zip(names, ok))
+        args.update(kw)
+        return r(*[args[n] for n in names])
+    assert call(d=48) == -1
+    assert call(eps=-1.0) == -1
+    assert call(eps=float("nan")) == -1
+    assert call(gamma=None) == -1
+    assert call(rstd=None) == -1
+    assert call(res=FAKE) == -1                      # a residual needs residual_out
+    assert call(res=FAKE, res_out=FAKE + 4) == -2
+    assert call(rstd=FAKE + 4) == -2
+    assert call(gamma=FAKE + 2) == -2
+    assert call(qc=FAKE, sc=FAKE, fmt=5) == -1
+    assert call(rows=0) == 0
