@@ -60,6 +60,9 @@ def parse():
                    help="the Hadamard gradient recipe: column copies of A and W and both copies of dOut transformed")
     p.add_argument("--fp8-wgrad", action="store_true",
                    help="dB as an MXFP8 GEMM (column copies of A and dOut in MXFP8), as in the FP8 dB variant")
+    p.add_argument("--fused-producers", action="store_true",
+                   help="A operands made by the fused producers: RMSNorm + cast for gate/up (of the block input), "
+                        "SiLU-and-mul + cast for down (of the gate/up output) instead of plain casts")
     p.add_argument("--no-kernel-events", action="store_true",
                    help="time only the whole step (no per-kernel events)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -138,7 +141,9 @@ def step_ops(P, L, sp, N, cached_weights=False, hadamard=False, fp8_wgrad=False)
 
     M, Nn, K, name = P["M"], P["N"], P["K"], P["name"]
     ops = []
-    casts = [("cast_dual(A)", P["a"], P["a_row"], P["a_col"])]
+    casts = [] if P.get("producer") else [("cast_dual(A)", P["a"], P["a_row"], P["a_col"])]
+    if P.get("producer"):
+        ops.append(producer_op(P, L, sp))
     if not cached_weights:
         casts.append(("cast_dual(W)", P["w"], P["w_row"], P["w_col"]))
     for label, x, row, col in casts:
@@ -158,6 +163,31 @@ def step_ops(P, L, sp, N, cached_weights=False, hadamard=False, fp8_wgrad=False)
     else:
         ops.append(("gemm", name + ".dB", gemm(L.mxfp4_gemm_nt, P["g_col"], P["a_col"], P["dw"]), fl, t))
     return ops
+
+
+def producer_op(P, L, sp):
+    """The A operand made by a fused producer + cast instead of a plain cast: RMSNorm of the
+    block input (gate/up) or SiLU-and-mul of the gate/up output (down).  Work: the producer's
+    inputs read once plus the copies written (minimum bytes); an unfused producer would also
+    write its bf16 output and the cast read it back (4 B more per element)."""
+    kind = P["producer"][0]
+    M, K = P["M"], P["K"]
+    row, col = P["a_row"], P["a_col"]
+    copies = 0.5 + (1.0 if col.fmt == 8 else 0.5) + 2.0 / 32
+    if kind == "rms":
+        _, x, gamma, rstd, eps = P["producer"]
+        launch = lambda: L.mxfp4_rmsnorm_cast(x.data_ptr(), None, gamma.data_ptr(), eps, M, K, row.q.data_ptr(),
+                                              row.s.data_ptr(), col.q.data_ptr(), col.s.data_ptr(), col.fmt, None,
+                                              rstd.data_ptr(), None, sp)
+        nb = (2.0 + copies) * M * K
+        label = "rmsnorm_cast(A)"
+    else:
+        _, src = P["producer"]
+        launch = lambda: L.mxfp4_silu_mul_cast(src.data_ptr(), M, K, src.stride(0), row.q.data_ptr(),
+                                               row.s.data_ptr(), col.q.data_ptr(), col.s.data_ptr(), col.fmt, None, sp)
+        nb = (4.0 + copies) * M * K
+        label = "silu_mul_cast(A)"
+    return ("cast", P["name"] + "." + label, launch, nb, nb / (HBM_PEAK_GBPS * 1e9))
 
 
 def alloc_projection(name, M, Nn, K, a, w, g, mx, torch, dev, fp8_wgrad=False):
@@ -366,6 +396,18 @@ def main():
     torch.cuda.synchronize()
     setup_s = time.time() - t0
 
+    if args.fused_producers:
+        if args.workload != "llama8b_mlp" and args.workload != "llama70b":
+            sys.stderr.write("--fused-producers needs an MLP workload (gate/up then down)\n")
+            sys.exit(2)
+        byname = {P["name"]: P for P in projs}
+        gu, dn = byname["gate_up"], byname["down"]
+        g = torch.from_numpy(W.bf16_bits((1 + 0.1 * np.random.default_rng(5).standard_normal(gu["K"]))
+                                         .astype(np.float32)).view(np.int16)).view(torch.bfloat16).to(dev)
+        gu["producer"] = ("rms", gu["a"], g, torch.empty(gu["M"], dtype=torch.float64, device=dev),
+                          float(np.float32(1e-5)))
+        # down's A is SiLU-and-mul of the gate/up output [M, 2 * K_down]
+        dn["producer"] = ("silu", gu["out"])
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
     ops = []
@@ -435,7 +477,9 @@ def main():
         "config": {"workload": WORKLOADS[args.workload] + (
                        "; weights quantized once (cached), no W cast in the step" if args.cached_weights else "") + (
                        "; Hadamard gradient recipe" if args.hadamard_grad else "") + (
-                       "; dB as an MXFP8 GEMM (FP8 wgrad)" if args.fp8_wgrad else ""),
+                       "; dB as an MXFP8 GEMM (FP8 wgrad)" if args.fp8_wgrad else "") + (
+                       "; A operands from fused RMSNorm + cast (gate/up) and SiLU-and-mul + cast (down)"
+                       if args.fused_producers else ""),
                    "projections": [[P["name"], P["M"], P["N"], P["K"]] for P in projs],
                    "step_tflop": round(step_flops / 1e12, 4)},
         "frac_of_fp4_peak": round(value / FP4_PEAK_TFLOPS, 4),

@@ -103,37 +103,97 @@ __device__ __forceinline__ unsigned bf16_from_f64(double v) {
     return sign | ((unsigned)((ue + 127) << 7) + (unsigned)n - 128u);
 }
 
-// bf16(silu(g) * u), rounded once.  The binary32 evaluation is within 2^-21 |y|
-// of the exact value (a few roundings and expf's error); unless that interval
-// may hold a bf16 rounding midpoint (the low half of the binary32 pattern near
-// 0x8000), the result is not finite, or e^-g overflows (g < -80), it rounds
-// like the exact value; otherwise the double evaluation decides.
-__device__ __forceinline__ unsigned silu_mul_bf16(float g, float u) {
-    const float y = g / (1.0f + expf(-g)) * u;
-    const unsigned low = __builtin_bit_cast(unsigned, y) & 0xFFFFu;
-    if ((low - 0x7FF0u) > 0x20u && g > -80.0f && __builtin_isfinite(y)) return f32_to_bf16_rne(y);
+// A binary32 result y known to within a few units of its last place rounds to
+// the same bf16 as the exact value unless the low half of its pattern is near
+// 0x8000 (a bf16 rounding midpoint within 16 units).  The error bounds below
+// hold for normal values far from overflow: 2^-100 <= |y| < 2^101 (exponent
+// field 27 .. 227).
+__device__ __forceinline__ bool decides(float y) {
+    const unsigned b = __builtin_bit_cast(unsigned, y);
+    const unsigned ef = (b >> 23) & 0xFFu;
+    return ((b & 0xFFFFu) - 0x7FF0u) > 0x20u && (ef - 27u) <= 200u;
+}
+
+// bf16(silu(g) * u) in double, rounded once: the rare fallback (out of line,
+// so the call sites of a tile do not each carry a copy).
+__device__ __attribute__((noinline)) unsigned silu_mul_f64(float g, float u) {
     const double gd = g;
     return bf16_from_f64(gd / (1.0 + exp(-gd)) * (double)u);
 }
 
-// 8 gate / 8 up bf16 values -> 8 bf16 outputs.
-__device__ __forceinline__ u32x4 silu_mul8(u32x4 g, u32x4 u) {
-    u32x4 r;
-#define MX_SM(F) r.F = silu_mul_bf16(bf16_lo(g.F), bf16_lo(u.F)) | (silu_mul_bf16(bf16_hi(g.F), bf16_hi(u.F)) << 16);
-    MX_SM(x) MX_SM(y) MX_SM(z) MX_SM(w)
-#undef MX_SM
-    return r;
+// Replace half e & 1 of word r[e >> 1] by the bf16 bits b.
+__device__ __forceinline__ void put_half(unsigned (&r)[4], int e, unsigned b) {
+    r[e >> 1] = (e & 1) ? ((r[e >> 1] & 0xFFFFu) | (b << 16)) : ((r[e >> 1] & 0xFFFF0000u) | b);
 }
 
-// 8 bf16 h -> bf16(h * rstd * gamma) in double, rounded once.
-__device__ __forceinline__ u32x4 rms8(u32x4 h, double rs, u32x4 gm) {
-    u32x4 r;
-#define MX_RMS(F)                                                                                  \
-    r.F = bf16_from_f64((double)bf16_lo(h.F) * rs * (double)bf16_lo(gm.F)) |                       \
-          (bf16_from_f64((double)bf16_hi(h.F) * rs * (double)bf16_hi(gm.F)) << 16);
-    MX_RMS(x) MX_RMS(y) MX_RMS(z) MX_RMS(w)
-#undef MX_RMS
-    return r;
+// bf16(silu(g) * u), rounded once, for 8 gate / 8 up bf16 values, as
+// (g * u) / (1 + e^-g).  The product of two bf16 values is exact in binary32
+// (and, when the result is normal, not below it).  e^-g = 2^t with t = -g
+// log2(e) carried as hi + lo (an fma recovers the product's rounding error),
+// e^-g = exp2(hi) (1 + lo ln 2): v_exp_f32 is within an ulp and the
+// correction's own error is far below one; v_rcp is within an ulp; with the
+// remaining roundings the binary32 result is within 5 units of the exact one.
+// It decides unless it is near a midpoint, out of range or g <= -80 (e^-g near
+// overflow), and is exact when g * u = 0.  The rest is redone in double.  One
+// branch per 8 values keeps the common case straight-line.
+__device__ __forceinline__ u32x4 silu_mul8(u32x4 gv, u32x4 uv) {
+    const unsigned gw[4] = {gv.x, gv.y, gv.z, gv.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w};
+    float g[8], u[8], y[8];
+    bool ok[8];
+    bool all_ok = true;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        g[e] = (e & 1) ? bf16_hi(gw[e >> 1]) : bf16_lo(gw[e >> 1]);
+        u[e] = (e & 1) ? bf16_hi(uw[e >> 1]) : bf16_lo(uw[e >> 1]);
+        const float p = g[e] * u[e];
+        const float hi = -g[e] * 1.44269502f;  // log2(e) rounded to binary32, and the rest below
+        const float lo = __builtin_fmaf(-g[e], 1.92596303e-8f, __builtin_fmaf(-g[e], 1.44269502f, -hi));
+        const float e0 = __builtin_amdgcn_exp2f(hi);
+        y[e] = p * __builtin_amdgcn_rcpf(1.0f + __builtin_fmaf(e0, lo * 0.693147182f, e0));
+        if (p == 0.0f) y[e] = p;  // exact signed zero (the factor may be NaN when e^-g overflows)
+        ok[e] = (decides(y[e]) && g[e] > -80.0f) || p == 0.0f;
+        all_ok = all_ok && ok[e];
+    }
+    unsigned r[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r[k] = f32x2_to_bf16x2_rne(y[2 * k], y[2 * k + 1]);
+    if (!all_ok) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (!ok[e]) put_half(r, e, silu_mul_f64(g[e], u[e]));
+    }
+    return u32x4{r[0], r[1], r[2], r[3]};
+}
+
+// bf16(h * rstd * gamma), rounded once, for 8 values of a row, as
+// (h * gamma) * rstd32: the bf16 product is exact, rstd rounded to binary32
+// and one more rounding leave the result within 2 units; it decides unless
+// near a midpoint or out of range, and is exact when h * gamma = 0.  The rest
+// is redone in double with the double rstd.
+__device__ __forceinline__ u32x4 rms8(u32x4 hv, double rs, u32x4 gmv) {
+    const float rs32 = (float)rs;
+    const unsigned hw[4] = {hv.x, hv.y, hv.z, hv.w}, gw[4] = {gmv.x, gmv.y, gmv.z, gmv.w};
+    float h[8], gm[8], y[8];
+    bool ok[8];
+    bool all_ok = true;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        h[e] = (e & 1) ? bf16_hi(hw[e >> 1]) : bf16_lo(hw[e >> 1]);
+        gm[e] = (e & 1) ? bf16_hi(gw[e >> 1]) : bf16_lo(gw[e >> 1]);
+        const float p = h[e] * gm[e];
+        y[e] = p * rs32;
+        ok[e] = decides(y[e]) || p == 0.0f;
+        all_ok = all_ok && ok[e];
+    }
+    unsigned r[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r[k] = f32x2_to_bf16x2_rne(y[2 * k], y[2 * k + 1]);
+    if (!all_ok) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (!ok[e]) put_half(r, e, bf16_from_f64((double)h[e] * rs * (double)gm[e]));
+    }
+    return u32x4{r[0], r[1], r[2], r[3]};
 }
 
 // Half-width H butterflies inside an array of N values (N a multiple of 2H).
@@ -186,26 +246,38 @@ __global__ __launch_bounds__(256, 4) void cast_kernel(const uint16_t* __restrict
     const int64_t col = c0 + cl * 8;
     const bool col_ok = col < C;
 
+    // every load is issued before any producer arithmetic or store (the optional
+    // y_out stores may alias the inputs as far as the compiler knows)
     u32x4 v[NI];
+    u32x4 aux[PROD == PROD_SILU_MUL ? NI : 1];  // SiLU-and-mul: the up values
+    double rsd[PROD == PROD_RMS ? NI : 1];      // RMS: the rows' rstd
     u32x4 gm = {0u, 0u, 0u, 0u};
     if constexpr (PROD == PROD_RMS)
         if (col_ok) gm = *reinterpret_cast<const u32x4*>(P.gamma + col);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const int64_t row = r0 + i * 8 + (t >> 5);
-        if (col_ok && row < R) {
-            const u32x4 a = *reinterpret_cast<const u32x4*>(x + row * ldx + col);
-            if constexpr (PROD == PROD_SILU_MUL) {
-                v[i] = silu_mul8(a, *reinterpret_cast<const u32x4*>(x + row * ldx + P.up_offset + col));
-            } else if constexpr (PROD == PROD_RMS) {
-                v[i] = rms8(a, P.rstd[row], gm);
-            } else {
-                v[i] = a;
+        const bool ok = col_ok && row < R;
+        v[i] = ok ? *reinterpret_cast<const u32x4*>(x + row * ldx + col) : u32x4{0u, 0u, 0u, 0u};
+        if constexpr (PROD == PROD_SILU_MUL)
+            aux[i] = ok ? *reinterpret_cast<const u32x4*>(x + row * ldx + P.up_offset + col) : u32x4{0u, 0u, 0u, 0u};
+        if constexpr (PROD == PROD_RMS) rsd[i] = ok ? P.rstd[row] : 0.0;
+    }
+    if constexpr (PROD != PROD_LOAD) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int64_t row = r0 + i * 8 + (t >> 5);
+            if constexpr (PROD == PROD_SILU_MUL) v[i] = silu_mul8(v[i], aux[i]);
+            else v[i] = rms8(v[i], rsd[i], gm);
+            // padding rows and columns stay +0 (0 * rstd * gamma could be -0)
+            if (!(col_ok && row < R)) v[i] = u32x4{0u, 0u, 0u, 0u};
+        }
+        if (P.y_out) {
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const int64_t row = r0 + i * 8 + (t >> 5);
+                if (col_ok && row < R) *reinterpret_cast<u32x4*>(P.y_out + row * C + col) = v[i];
             }
-            if constexpr (PROD != PROD_LOAD)
-                if (P.y_out) *reinterpret_cast<u32x4*>(P.y_out + row * C + col) = v[i];
-        } else {
-            v[i] = u32x4{0u, 0u, 0u, 0u};
         }
     }
 
@@ -504,6 +576,8 @@ __global__ __launch_bounds__(256) void rms_stats_kernel(const uint16_t* __restri
     if (row >= R) return;
     const uint16_t* xr = x + row * D;
     double ss = 0.0;
+    // unrolled so that several 16-byte loads of the row are in flight at once
+#pragma unroll 8
     for (int64_t c = lane * 8; c < D; c += 512) {
         u32x4 h = *reinterpret_cast<const u32x4*>(xr + c);
         if (res) {

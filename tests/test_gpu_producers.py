@@ -122,3 +122,66 @@ def test_rmsnorm_cast_edge_rows():
         assert np.array_equal(bits_of(y), y_ref)
         assert np.allclose(rstd.cpu().numpy(), rstd_ref, rtol=1e-14, atol=0)
         check_copies(t, y_ref, 4, "rmsnorm edge eps=%g" % eps)
+
+
+def test_silu_mul_every_gate_value():
+    # every finite bf16 gate value (the binary32 fast path depends on the gate alone up to the
+    # last multiplication), each against several up values
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    gates = pats[((pats >> 7) & 0xFF) != 0xFF]
+    F = 512
+    n = -(-gates.size // F) * F
+    g = np.resize(gates, n).reshape(-1, F)
+    for seed in range(3):
+        up = W.bf16_bits(np.random.default_rng(seed).standard_normal(g.shape).astype(np.float32))
+        x = np.concatenate([g, up], axis=1)
+        say("silu_mul every gate value, seed %d" % seed)
+        t, y = mx.silu_mul_cast(to_device(x), return_y=True)
+        torch.cuda.synchronize()
+        y_ref = oracle.silu_mul(x)
+        yb = bits_of(y)
+        bad = np.argwhere(yb != y_ref)
+        assert bad.size == 0, "y differs at %s: gate %s got %s want %s" % (
+            bad[:5].tolist(), [hex(x[tuple(i)]) for i in bad[:5]], [hex(yb[tuple(i)]) for i in bad[:5]],
+            [hex(y_ref[tuple(i)]) for i in bad[:5]])
+        check_copies(t, y_ref, 4, "silu_mul every gate")
+
+
+def near_midpoint_pairs(n_gates, seed, max_units=48):
+    """(gate, up) bf16 pairs whose exact silu(gate) * up lies within max_units binary32 units of a
+    bf16 rounding midpoint -- where a binary32 evaluation is closest to rounding the wrong way."""
+    rng = np.random.default_rng(seed)
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    fin = pats[((pats >> 7) & 0xFF) != 0xFF]
+    fv = fin.view(np.int16).astype(np.int32) << 16
+    vals = fv.astype(np.int32).view(np.float32).astype(np.float64)
+    gsel = fin[(np.abs(vals) < 80)]
+    gates = rng.choice(gsel, n_gates, replace=False)
+    gvals = (gates.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    out_g, out_u = [], []
+    for gb, g in zip(gates, gvals):
+        y = g / (1.0 + np.exp(-g)) * vals
+        m, e = np.frexp(np.abs(y))                    # |y| = m 2^e, m in [0.5, 1)
+        units = np.ldexp(np.abs(y), 24 - e)           # the significand in binary32 units (2^23 .. 2^24)
+        frac = np.mod(units, 2 ** 16)                 # position within a bf16 step (2^16 units)
+        near = (np.abs(frac - 2 ** 15) <= max_units) & (np.abs(y) > 2.0 ** -120) & (np.abs(y) < 2.0 ** 120)
+        k = np.nonzero(near)[0][:64]
+        out_g.append(np.full(k.size, gb, np.uint16))
+        out_u.append(fin[k])
+    return np.concatenate(out_g), np.concatenate(out_u)
+
+
+def test_silu_mul_near_midpoints():
+    g, u = near_midpoint_pairs(600, 21)
+    F = 256
+    n = g.size // F * F
+    assert n >= 4 * F
+    x = np.concatenate([g[:n].reshape(-1, F), u[:n].reshape(-1, F)], axis=1)
+    say("silu_mul near bf16 midpoints: %d pairs" % n)
+    t, y = mx.silu_mul_cast(to_device(x), return_y=True)
+    torch.cuda.synchronize()
+    y_ref = oracle.silu_mul(x)
+    yb = bits_of(y)
+    bad = np.argwhere(yb != y_ref)
+    assert bad.size == 0, "y differs at %s" % bad[:5].tolist()
+    check_copies(t, y_ref, 4, "silu_mul near midpoints")
