@@ -298,8 +298,10 @@ static hipError_t launch_skinny(const uint8_t* aq, const uint8_t* as, const uint
 //   wait for the DMA of tile kt+1 and for this wave's LDS reads, barrier
 //     (after it no wave reads stage kt%4 any more)
 //   MFMAs of K step 1 of tile kt, with the LDS reads of tile kt+1 (set 1-p)
-//     and the 9 DMA instructions of tile kt+4 into stage kt%4 spread
-//     between them
+//     and the DMA instructions of tile kt+4 into stage kt%4 spread
+//     between them (8 for the codes, plus the scale tile for the first K
+//     tile of each 256-wide scale tile; the other K tiles take the scale
+//     dwords of the previous one from registers -- one dword holds them all)
 // Memory instructions are spread one or two per MFMA: a wave that issues a
 // burst of them stalls on the address unit's queue and lets the MFMA pipe
 // drain.  With the register double buffer, 4 stages give a tile's DMA about
@@ -320,7 +322,15 @@ constexpr int ST_SA = ST_B + PBN * PROWB;         // 32768: A scale tiles
 constexpr int ST_SB = ST_SA + (PBM / 32) * 256;   // 34816: B scale tiles
 constexpr int STAGE = ST_SB + (PBN / 32) * 256;   // 36864 bytes
 constexpr unsigned kRsrcWord3 = 0x00020000u;      // gfx9 raw buffer: dword format, no swizzle
-constexpr int kDmaPerTile = 9;                    // DMA instructions per wave per tile
+// DMA instructions per wave per K tile: 8 for the codes, plus 1 for the scale
+// tile when the K tile is the first one its scale tile covers (a scale tile
+// spans 256 elements: 2 FP4 K tiles or 4 FP8 ones, and one scale dword holds
+// the scales of all of them, so the other K tiles reuse the dwords already in
+// registers).  t4 = K tile index mod 4 (the stage).
+template <int FMT>
+constexpr bool tile_loads_scales(int t4) { return FMT == 8 ? t4 == 0 : (t4 & 1) == 0; }
+template <int FMT>
+constexpr int dma_count(int t4) { return tile_loads_scales<FMT>(t4) ? 9 : 8; }
 
 // Chunk swizzle of a 64-byte tile row (depends on the row's low 4 bits only).
 __device__ __forceinline__ int swz64(int r) { return ((r >> 1) & 3) ^ (3 * ((r >> 3) & 1)); }
@@ -444,6 +454,7 @@ __device__ __forceinline__ void dma_one(const DmaPlan& P, const TileSrc& S, int 
     }
 }
 
+// All DMA instructions of K tile kt (kt % 4 == ST) into stage ST.
 template <int ST, int FMT = 4>
 __device__ __forceinline__ void dma_tile_all(const DmaPlan& P, const TileSrc& S, int kt, bool valid) {
     dma_one<ST, 0, FMT>(P, S, kt, valid);
@@ -454,8 +465,12 @@ __device__ __forceinline__ void dma_tile_all(const DmaPlan& P, const TileSrc& S,
     dma_one<ST, 5, FMT>(P, S, kt, valid);
     dma_one<ST, 6, FMT>(P, S, kt, valid);
     dma_one<ST, 7, FMT>(P, S, kt, valid);
-    dma_one<ST, 8, FMT>(P, S, kt, valid);
+    if constexpr (tile_loads_scales<FMT>(ST)) dma_one<ST, 8, FMT>(P, S, kt, valid);
 }
+
+// DMA instructions of K tiles 1, 2, 3: in flight while the prologue waits for K tile 0.
+template <int FMT>
+constexpr int prologue_wait() { return dma_count<FMT>(1) + dma_count<FMT>(2) + dma_count<FMT>(3); }
 
 // Operand descriptors of the output tile at (m0, n0), rebased at the tile and
 // bounded by the operand sizes (tiles past M / N read zero).
@@ -607,7 +622,20 @@ __device__ __forceinline__ void pipe_iter(f32x16 (&acc)[4][4], TileRegs& cur, Ti
                                           const TileSrc& Scur, const TileSrc& Snext, bool next_ok,
                                           const ReadPlan& R, lds_cptr lds, int kt, int nkt) {
     constexpr int DST = U;
-    constexpr int WAIT = 2 * kDmaPerTile + ((POST && U < 3) ? kEpiStores : 0);
+    // the DMA of K tiles kt+2 and kt+3 may still be in flight
+    constexpr int WAIT = dma_count<FMT>((U + 2) & 3) + dma_count<FMT>((U + 3) & 3) + ((POST && U < 3) ? kEpiStores : 0);
+    // K tile kt+1 reads its scale dwords from LDS, or takes tile kt's (same scale tile)
+    constexpr bool NXT_SCALES = tile_loads_scales<FMT>((U + 1) & 3);
+    // the K tile DMA'd here (kt+4, or K tile U of the next output tile) is congruent to U
+    constexpr bool DMA_SCALES = tile_loads_scales<FMT>(U);
+    constexpr int R0 = NXT_SCALES ? 0 : 8;  // first LDS read slot (0..7 are the scales)
+    if constexpr (!NXT_SCALES) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            nxt.sa[i] = cur.sa[i];
+            nxt.sb[i] = cur.sb[i];
+        }
+    }
     const TileSrc& S = LAST ? Snext : Scur;
     const int dkt = LAST ? U : kt + NST;
     const bool valid = LAST ? (next_ok && U < nkt) : (kt + NST < nkt);
@@ -628,8 +656,9 @@ __device__ __forceinline__ void pipe_iter(f32x16 (&acc)[4][4], TileRegs& cur, Ti
             // the step-0 data of tile kt+1 (reads 0..15) goes first: it is needed first
             const int r0 = (q * 3) / 2, r1 = ((q + 1) * 3) / 2;
 #pragma unroll
-            for (int r = r0; r < r1; ++r) read_one<FMT>(nxt, R, next, r);
-            // DMA instructions 0..7 before the odd MFMAs, 8 (scales) before MFMA 14
+            for (int r = r0; r < r1; ++r)
+                if (r >= R0) read_one<FMT>(nxt, R, next, r);
+            // DMA instructions 0..7 before the odd MFMAs, 8 (scales, even K tiles) before MFMA 14
             if (q == 1) dma_one<DST, 0, FMT>(P, S, dkt, valid);
             if (q == 3) dma_one<DST, 1, FMT>(P, S, dkt, valid);
             if (q == 5) dma_one<DST, 2, FMT>(P, S, dkt, valid);
@@ -637,7 +666,8 @@ __device__ __forceinline__ void pipe_iter(f32x16 (&acc)[4][4], TileRegs& cur, Ti
             if (q == 9) dma_one<DST, 4, FMT>(P, S, dkt, valid);
             if (q == 11) dma_one<DST, 5, FMT>(P, S, dkt, valid);
             if (q == 13) dma_one<DST, 6, FMT>(P, S, dkt, valid);
-            if (q == 14) dma_one<DST, 8, FMT>(P, S, dkt, valid);
+            if constexpr (DMA_SCALES)
+                if (q == 14) dma_one<DST, 8, FMT>(P, S, dkt, valid);
             if (q == 15) dma_one<DST, 7, FMT>(P, S, dkt, valid);
             mfma_one<OP + 1>(acc, cur.a1, cur.b1, cur.sa, cur.sb, q);
             order_point();
@@ -657,7 +687,8 @@ __device__ __forceinline__ void pipe_iter(f32x16 (&acc)[4][4], TileRegs& cur, Ti
         for (int q = 8; q < 16; ++q) {
             // all 24 reads of tile kt+1 (every MFMA of the next tile needs both halves)
 #pragma unroll
-            for (int r = (q - 8) * 3; r < (q - 7) * 3; ++r) read_one<FMT>(nxt, R, next, r);
+            for (int r = (q - 8) * 3; r < (q - 7) * 3; ++r)
+                if (r >= R0) read_one<FMT>(nxt, R, next, r);
             if (q == 8) dma_one<DST, 0, FMT>(P, S, dkt, valid);
             if (q == 9) dma_one<DST, 1, FMT>(P, S, dkt, valid);
             if (q == 10) dma_one<DST, 2, FMT>(P, S, dkt, valid);
@@ -667,7 +698,7 @@ __device__ __forceinline__ void pipe_iter(f32x16 (&acc)[4][4], TileRegs& cur, Ti
             if (q == 14) dma_one<DST, 6, FMT>(P, S, dkt, valid);
             if (q == 15) {
                 dma_one<DST, 7, FMT>(P, S, dkt, valid);
-                dma_one<DST, 8, FMT>(P, S, dkt, valid);
+                if constexpr (DMA_SCALES) dma_one<DST, 8, FMT>(P, S, dkt, valid);
             }
             mfma8_one<OP>(acc, cur, q);
             order_point();
@@ -729,7 +760,7 @@ __global__ __launch_bounds__(256, 1) void gemm_pipe_kernel(const uint8_t* __rest
     dma_tile_all<1, FMT>(P, S, 1, 1 < nkt);
     dma_tile_all<2, FMT>(P, S, 2, 2 < nkt);
     dma_tile_all<3, FMT>(P, S, 3, 3 < nkt);
-    wait_vmcnt<(NST - 1) * kDmaPerTile, true>();
+    wait_vmcnt<prologue_wait<FMT>(), true>();
     __syncthreads();
     TileRegs r0, r1;
 #pragma unroll
@@ -907,7 +938,7 @@ __global__ __launch_bounds__(256, 1) void gemm_persist_kernel(const uint8_t* __r
     dma_tile_all<1, FMT>(P, S, 1, 1 < nkt);
     dma_tile_all<2, FMT>(P, S, 2, 2 < nkt);
     dma_tile_all<3, FMT>(P, S, 3, 3 < nkt);
-    wait_vmcnt<(NST - 1) * kDmaPerTile, true>();
+    wait_vmcnt<prologue_wait<FMT>(), true>();
     __syncthreads();
     TileRegs r0, r1;
 #pragma unroll
