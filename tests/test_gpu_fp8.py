@@ -126,9 +126,10 @@ def test_tiled_shapes(M, N, K):
     assert_gemm_close(gpu_nt8(a, b, "tiled"), ref, absref, "fp8 tiled %dx%dx%d" % (M, N, K), trunc)
 
 
-# skinny kernel: split contraction, NB = 1 and 2 (FP8 stops at 2), the smaller side as A
+# skinny kernel: split contraction, NB = 1 and 2 (FP8 stops at 2), the smaller side as A (also in
+# two 32-row groups)
 @pytest.mark.parametrize("M,N,K", [(1, 4096, 14336), (4096, 32, 8192), (32, 65536, 1024), (65536, 100, 544),
-                                   (17, 300, 2080), (1000, 2000, 1024)])
+                                   (17, 300, 2080), (1000, 2000, 1024), (48, 3000, 544), (5000, 64, 2080)])
 def test_skinny_shapes(M, N, K):
     a = W.ragged_values((M, K), 7 * M + K)
     b = W.ragged_values((N, K), 11 * N + K)

@@ -65,9 +65,12 @@ def test_tiled_shapes(M, N, K):
 
 # Skinny kernel (one side below 128 or few tiles): split of the contraction over the waves of a
 # workgroup, 32 x 32*NB blocks with NB = 1, 2, 4, the smaller side taken as A (output written
-# transposed when that is the GEMM's B), K chunks past the padded code tiles.
+# transposed when that is the GEMM's B; small sides of 33..128 rows in several 32-row groups), K
+# chunks past the padded code tiles.
 @pytest.mark.parametrize("M,N,K", [(1, 4096, 14336), (4096, 32, 8192), (32, 65536, 1024), (128, 65536, 512),
-                                   (65536, 100, 544), (17, 300, 2080), (1, 128256, 32), (1000, 2000, 1024)])
+                                   (65536, 100, 544), (17, 300, 2080), (1, 128256, 32), (1000, 2000, 1024),
+                                   (48, 3000, 544), (5000, 64, 2080), (4096, 128, 14336), (97, 20000, 1024),
+                                   (16384, 128, 4096)])
 def test_skinny_shapes(M, N, K):
     a = W.ragged_values((M, K), 3 * M + K)
     b = W.ragged_values((N, K), 5 * N + K)
