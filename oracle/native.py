@@ -48,7 +48,8 @@ def lib():
         L.mxo_bf16_round.argtypes = [p, p, i64]
         L.mxo_silu_mul.argtypes = [p, i64, i64, i64, p, i32]
         L.mxo_rmsnorm.argtypes = [p, p, p, ctypes.c_double, i64, i64, p, p, p, i32]
-        for f in (L.mxo_bf16_round, L.mxo_silu_mul, L.mxo_rmsnorm,L.mxo_cast_rows, L.mxo_cast_cols, L.mxo_dequant, L.mxo_gemm, L.mxo_gemm_pairs,
+        for f in (L.mxo_bf16_round, L.mxo_silu_mul, L.mxo_rmsnorm,
+                  L.mxo_cast_rows, L.mxo_cast_cols, L.mxo_dequant, L.mxo_gemm, L.mxo_gemm_pairs,
                   L.mxo_cast_rows_hadamard, L.mxo_cast_cols_hadamard, L.mxo_fwht32, L.mxo_cast_rows_fp8,
                   L.mxo_cast_cols_fp8, L.mxo_dequant_fp8, L.mxo_gemm_fp8):
             f.restype = i32
