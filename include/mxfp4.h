@@ -222,7 +222,9 @@ int mxfp8_gemm_nt(const void* a_q, const void* a_s, const void* b_q, const void*
  * mxfp4_rmsnorm_cast: x bf16 [rows, d] contiguous, d % 32 == 0; gamma bf16
  *   [d]; 0 <= eps (finite).  Without a residual h = x; with residual (bf16
  *   [rows, d] contiguous) h = bf16(x + residual), written to residual_out
- *   (required then).  rstd: double [rows], 8-byte aligned, required: gets
+ *   (required then; it may be the residual or x buffer itself, updated in
+ *   place).  With eps = 0 an all-zero row gives rstd = inf and y = NaN, as
+ *   the formula does.  rstd: double [rows], 8-byte aligned, required: gets
  *   1 / sqrt(mean(h^2) + eps) (the norm's saved statistic; the cast pass
  *   reads it).  Output y = bf16(h * rstd * gamma) [rows, d].  Two kernels:
  *   the row statistics (and residual sum), then the producing cast.

@@ -185,3 +185,25 @@ def test_silu_mul_near_midpoints():
     bad = np.argwhere(yb != y_ref)
     assert bad.size == 0, "y differs at %s" % bad[:5].tolist()
     check_copies(t, y_ref, 4, "silu_mul near midpoints")
+
+
+def test_add_rmsnorm_in_place_residual():
+    # residual_out may be the residual buffer itself (the usual in-place residual update)
+    R, D = 96, 512
+    x, gamma = rms_inputs(R, D, 5)
+    res = W.normal_bf16((R, D), 3.0, 6)
+    eps = float(np.float32(1e-6))
+    y_ref, h_ref, _ = oracle.rmsnorm(x, gamma, eps, residual_bits=res)
+    L = mx._native.lib()
+    xd, rd, gd = to_device(x), to_device(res), to_device(gamma[None, :])[0]
+    row, col = mx.api._produced_copies(R, D, xd.device, True, 4)
+    rstd = torch.empty(R, dtype=torch.float64, device=xd.device)
+    say("add_rmsnorm in place")
+    st = L.mxfp4_rmsnorm_cast(xd.data_ptr(), rd.data_ptr(), gd.data_ptr(), eps, R, D, row.q.data_ptr(),
+                              row.s.data_ptr(), col.q.data_ptr(), col.s.data_ptr(), 4, rd.data_ptr(),
+                              rstd.data_ptr(), None, torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(rd), h_ref)
+    check(row, oracle.cast_rows(y_ref), "in-place row")
+    check(col, oracle.cast_cols(y_ref), "in-place col")
