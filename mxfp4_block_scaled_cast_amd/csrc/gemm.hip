@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256) void gemm_direct_kernel(const uint8_t* __restr
 // are not loaded (zero).
 // ---------------------------------------------------------------------------
 
-// NB = 1 runs up to 16 waves per workgroup (92 VGPRs), NB = 2, 4 up to 8.
+// NB = 1 runs up to 16 waves per workgroup (at most 128 VGPRs), NB = 2, 4 up to 8.
 template <int NB>
 constexpr int skinny_max_waves() { return NB == 1 ? 16 : 8; }
 
@@ -653,7 +653,8 @@ __device__ __forceinline__ void pipe_iter(f32x16 (&acc)[4][4], TileRegs& cur, Ti
         __syncthreads();
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-            // the step-0 data of tile kt+1 (reads 0..15) goes first: it is needed first
+            // the scales and step-0 data of tile kt+1 (reads 0..15; the scales only for
+            // the first K tile of a scale tile) go first: they are needed first
             const int r0 = (q * 3) / 2, r1 = ((q + 1) * 3) / 2;
 #pragma unroll
             for (int r = r0; r < r1; ++r)
@@ -685,7 +686,8 @@ __device__ __forceinline__ void pipe_iter(f32x16 (&acc)[4][4], TileRegs& cur, Ti
         __syncthreads();
 #pragma unroll
         for (int q = 8; q < 16; ++q) {
-            // all 24 reads of tile kt+1 (every MFMA of the next tile needs both halves)
+            // the reads of tile kt+1 (24, or 16 without the scales; every MFMA of the next
+            // tile needs both halves)
 #pragma unroll
             for (int r = (q - 8) * 3; r < (q - 7) * 3; ++r)
                 if (r >= R0) read_one<FMT>(nxt, R, next, r);
