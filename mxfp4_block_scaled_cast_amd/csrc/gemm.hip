@@ -113,40 +113,46 @@ __global__ __launch_bounds__(256) void gemm_direct_kernel(const uint8_t* __restr
 //
 // C[i, j] = sum_k A[i, k] B[j, k], written to out[i * ld_i + j * ld_j]; the
 // launcher passes the smaller operand as A (and swaps the output strides when
-// that is the GEMM's B).  A wave owns 32 rows of A x 32*NB rows of B (NB
-// scaled MFMAs per 64-wide K step, sharing the A fragment) over one slice of
-// the contraction; the W waves of a workgroup take consecutive slices of the
-// same output block and add their partial sums through LDS.  Operands come
-// straight from global memory in 256-wide K chunks: per lane four 16-byte
-// code loads per row group (one per K step; 32 rows x 256 K = four whole 1 KB
-// code tiles per row group) and one scale dword, whose four bytes are the
-// lane's scales for the four steps (the MFMA picks one with opsel).  All of a
-// chunk's loads are issued before its MFMAs; the other waves of the CU cover
-// the latency.  Rows past the operands and K steps past the padded code tiles
-// are not loaded (zero).
+// that is the GEMM's B).  A wave owns 32*MA rows of A x 32*NB rows of B (MA x
+// NB scaled MFMAs per 64-wide K step; each A fragment serves NB of them, each
+// B fragment MA) over one slice of the contraction; the W waves of a
+// workgroup take consecutive slices of the same output block and add their
+// partial sums through LDS.  Operands come straight from global memory in
+// 256-wide K chunks: per lane four 16-byte code loads per 32-row group (one
+// per K step; 32 rows x 256 K = four whole 1 KB code tiles) and one scale
+// dword, whose four bytes are the lane's scales for the four steps (the MFMA
+// picks one with opsel).  All of a chunk's loads are issued before its MFMAs;
+// the other waves of the CU cover the latency.  Rows past the operands and K
+// steps past the padded code tiles are not loaded (zero).
 // ---------------------------------------------------------------------------
 
-// NB = 1 runs up to 16 waves per workgroup (at most 128 VGPRs), NB = 2, 4 up to 8.
-template <int NB>
-constexpr int skinny_max_waves() { return NB == 1 ? 16 : 8; }
+// A single 32 x 32 block per wave runs up to 16 waves per workgroup (at most
+// 128 VGPRs), wider blocks up to 8.
+template <int MA, int NB>
+constexpr int skinny_max_waves() { return MA * NB == 1 ? 16 : 8; }
 
-template <int NB, int FMT>
-__global__ __launch_bounds__(64 * skinny_max_waves<NB>()) void gemm_skinny_kernel(
+template <int MA, int NB, int FMT>
+__global__ __launch_bounds__((64 * skinny_max_waves<MA, NB>())) void gemm_skinny_kernel(
     const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as, const uint8_t* __restrict__ bq,
     const uint8_t* __restrict__ bs, int Ma, int Nb, int K, uint16_t* __restrict__ out, int64_t ld_i, int64_t ld_j,
     int tiles_b) {
-    extern __shared__ float red[];  // [W][NB][16][64] partial sums (W > 1)
+    extern __shared__ float red[];  // [W][MA][NB][16][64] partial sums (W > 1)
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     const int W = blockDim.x >> 6;
     const int half = lane >> 5;
-    const int i0 = (blockIdx.x / tiles_b) * 32;
+    const int i0 = (blockIdx.x / tiles_b) * (32 * MA);
     const int j0 = (blockIdx.x % tiles_b) * (32 * NB);
     const int64_t kt128 = (K + 127) >> 7, kt64 = (K + 63) >> 6, kt256 = (K + 255) >> 8;
     const int64_t k_pad = FMT == 8 ? kt64 * 64 : kt128 * 128;  // K padded to whole code tiles
 
-    const int ia = i0 + (lane & 31);
-    const bool a_ok = ia < Ma;
+    int ia[MA];
+    bool a_ok[MA];
+#pragma unroll
+    for (int ma = 0; ma < MA; ++ma) {
+        ia[ma] = i0 + ma * 32 + (lane & 31);
+        a_ok[ma] = ia[ma] < Ma;
+    }
     int jb[NB];
     bool b_ok[NB];
 #pragma unroll
@@ -159,9 +165,11 @@ __global__ __launch_bounds__(64 * skinny_max_waves<NB>()) void gemm_skinny_kerne
     const int chunks = (int)kt256;
     const int c_begin = (int)((int64_t)chunks * w / W), c_end = (int)((int64_t)chunks * (w + 1) / W);
 
-    f32x16 acc[NB];
+    f32x16 acc[MA][NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16{};
+    for (int ma = 0; ma < MA; ++ma)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[ma][nb] = f32x16{};
 
     // lane fragment of (row, 64-wide step at k0): FP4, the 16 bytes of K k0+32h .. +31; FP8,
     // K k0+16h .. +15 and k0+32+16h .. +15 (16 bytes each)
@@ -177,53 +185,63 @@ __global__ __launch_bounds__(64 * skinny_max_waves<NB>()) void gemm_skinny_kerne
     constexpr int CODE = FMT == 8 ? 0 : 4;
 
     for (int c = c_begin; c < c_end; ++c) {
-        v8i av[4], bv[NB][4];
-        unsigned sa = 0u, sb[NB];
+        v8i av[MA][4], bv[NB][4];
+        unsigned sa[MA], sb[NB];
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
             const int64_t k0 = (int64_t)c * 256 + st * 64;
             const bool k_ok = k0 < k_pad;
-            av[st] = load(aq, ia, k0, a_ok && k_ok);
+#pragma unroll
+            for (int ma = 0; ma < MA; ++ma) av[ma][st] = load(aq, ia[ma], k0, a_ok[ma] && k_ok);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) bv[nb][st] = load(bq, jb[nb], k0, b_ok[nb] && k_ok);
         }
         // scale dword of (row, half): blocks c*8 + half + 2*st, st = 0..3
-        if (a_ok) sa = *reinterpret_cast<const unsigned*>(as + scale_offset(ia, (int64_t)c * 8 + half, kt256));
+#pragma unroll
+        for (int ma = 0; ma < MA; ++ma)
+            sa[ma] = a_ok[ma] ? *reinterpret_cast<const unsigned*>(as + scale_offset(ia[ma], (int64_t)c * 8 + half, kt256))
+                              : 0u;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
             sb[nb] = b_ok[nb] ? *reinterpret_cast<const unsigned*>(bs + scale_offset(jb[nb], (int64_t)c * 8 + half, kt256))
                               : 0u;
-#define MX_SKINNY_STEP(ST)                                                                                         \
-    _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) acc[nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4( \
-        av[ST], bv[nb][ST], acc[nb], CODE, CODE, ST, (int)sa, ST, (int)sb[nb]);
+#define MX_SKINNY_STEP(ST)                                                                                          \
+    _Pragma("unroll") for (int ma = 0; ma < MA; ++ma) _Pragma("unroll") for (int nb = 0; nb < NB; ++nb)            \
+        acc[ma][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[ma][ST], bv[nb][ST], acc[ma][nb], CODE, \
+                                                                      CODE, ST, (int)sa[ma], ST, (int)sb[nb]);
         MX_SKINNY_STEP(0) MX_SKINNY_STEP(1) MX_SKINNY_STEP(2) MX_SKINNY_STEP(3)
 #undef MX_SKINNY_STEP
     }
 
-    // acc[nb][r] is C[i0 + (r/4)*8 + half*4 + r%4, j0 + nb*32 + lane%32]
+    // acc[ma][nb][r] is C[i0 + ma*32 + (r/4)*8 + half*4 + r%4, j0 + nb*32 + lane%32]
     if (W == 1) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            if (!b_ok[nb]) continue;
+        for (int ma = 0; ma < MA; ++ma)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int i = i0 + (r >> 2) * 8 + half * 4 + (r & 3);
-                if (i < Ma) out[(int64_t)i * ld_i + (int64_t)jb[nb] * ld_j] = f32_to_bf16_rne(acc[nb][r]);
+            for (int nb = 0; nb < NB; ++nb) {
+                if (!b_ok[nb]) continue;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int i = i0 + ma * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+                    if (i < Ma) out[(int64_t)i * ld_i + (int64_t)jb[nb] * ld_j] = f32_to_bf16_rne(acc[ma][nb][r]);
+                }
             }
-        }
         return;
     }
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+    for (int ma = 0; ma < MA; ++ma)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) red[((w * NB + nb) * 16 + r) * 64 + lane] = acc[nb][r];
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) red[(((w * MA + ma) * NB + nb) * 16 + r) * 64 + lane] = acc[ma][nb][r];
     __syncthreads();
-    constexpr int ELEMS = NB * 16 * 64;
+    constexpr int ELEMS = MA * NB * 16 * 64;
     for (int e = threadIdx.x; e < ELEMS; e += blockDim.x) {
         float v = 0.f;
         for (int ww = 0; ww < W; ++ww) v += red[ww * ELEMS + e];
-        const int l = e & 63, r = (e >> 6) & 15, nb = e >> 10;
-        const int i = i0 + (r >> 2) * 8 + (l >> 5) * 4 + (r & 3);
+        const int l = e & 63, r = (e >> 6) & 15, blk = e >> 10;
+        const int ma = blk / NB, nb = blk % NB;
+        const int i = i0 + ma * 32 + (r >> 2) * 8 + (l >> 5) * 4 + (r & 3);
         const int j = j0 + nb * 32 + (l & 31);
         if (i < Ma && j < Nb) out[(int64_t)i * ld_i + (int64_t)j * ld_j] = f32_to_bf16_rne(v);
     }
@@ -233,37 +251,50 @@ __global__ __launch_bounds__(64 * skinny_max_waves<NB>()) void gemm_skinny_kerne
 template <int FMT>
 static hipError_t launch_skinny(const uint8_t* aq, const uint8_t* as, const uint8_t* bq, const uint8_t* bs, int64_t M,
                                 int64_t N, int64_t K, uint16_t* out, int64_t ldo, hipStream_t stream) {
-    // the smaller side is A (32-row groups), the larger one B (32*NB-row groups)
+    // the smaller side is A (32*MA-row groups), the larger one B (32*NB-row groups)
     const bool swap = M > N;
     const int64_t Ma = swap ? N : M, Nb = swap ? M : N;
     const int64_t ld_i = swap ? 1 : ldo, ld_j = swap ? ldo : 1;
-    // split the contraction over W waves (LDS: W * NB * 4 KB <= 64 KB) until ~16 waves per CU; take the
-    // widest B block (most reuse of the A fragment) that still reaches that, else NB = 1 (most waves)
+    // Wave block MA x NB MFMA tiles: fragments loaded per MFMA fall from 1 + 1/NB (MA = 1) to
+    // 1 (2 x 2).  The contraction is split over W waves (LDS: W * MA * NB * 4 KB <= 64 KB), W
+    // doubling until the launch has 16 waves per CU (or a limit); the first candidate whose launch
+    // then has at least `qualify` waves is taken, else the last one (a single 32 x 32 block: the
+    // most waves).  The 2 x 2 block (179 VGPRs, 2 waves per SIMD) pays from 6 waves per CU, 1 x 2
+    // from 8; 1 x 4 needs 16.  FP8 fragments are twice as wide: only 1 x 1 and 1 x 2.
     const int64_t chunks = (K + 255) / 256;
-    const int64_t target = (int64_t)mx::num_cus() * 16;
-    const int64_t tiles_a = (Ma + 31) / 32;
-    int nb = 1, W = 1;
-    int64_t tiles_b = 0;
-    // (FP8 fragments are twice as wide: NB = 4 would not fit the registers)
-    for (int cand = FMT == 8 ? 2 : 4; cand >= 1; cand /= 2) {
-        if (cand > 1 && Nb < 32 * cand) continue;
-        const int wmax = cand == 1 ? 16 : 8;
+    const int64_t cus = mx::num_cus();
+    const int64_t grow = cus * 16;
+    struct Cand { int ma, nb; int64_t qualify; };
+    const Cand cands4[] = {{2, 2, cus * 6}, {1, 4, cus * 16}, {1, 2, cus * 8}, {1, 1, 0}};
+    const Cand cands8[] = {{1, 2, cus * 16}, {1, 1, 0}};
+    const Cand* cands = FMT == 8 ? cands8 : cands4;
+    const int ncand = FMT == 8 ? 2 : 4;
+    int ma = 1, nb = 1, W = 1;
+    int64_t tiles_a = 0, tiles_b = 0;
+    for (int ci = 0; ci < ncand; ++ci) {
+        const Cand& cd = cands[ci];
+        if ((cd.ma > 1 && Ma < 32 * cd.ma) || (cd.nb > 1 && Nb < 32 * cd.nb)) continue;
+        const int wmax = cd.ma * cd.nb == 1 ? 16 : 8;
+        const int64_t ta = (Ma + 32 * cd.ma - 1) / (32 * cd.ma), tb = (Nb + 32 * cd.nb - 1) / (32 * cd.nb);
         int w = 1;
-        const int64_t tb = (Nb + 32 * cand - 1) / (32 * cand);
-        while (w * 2 <= wmax && w * 2 * cand <= 16 && w * 2 <= chunks && tiles_a * tb * w < target) w *= 2;
-        nb = cand;
+        while (w * 2 <= wmax && w * 2 * cd.ma * cd.nb <= 16 && w * 2 <= chunks && ta * tb * w < grow) w *= 2;
+        ma = cd.ma;
+        nb = cd.nb;
         W = w;
+        tiles_a = ta;
         tiles_b = tb;
-        if (tiles_a * tb * w >= target) break;
+        if (ta * tb * w >= cd.qualify) break;
     }
     const int64_t tiles = tiles_a * tiles_b;
     if (tiles > 0x7FFFFFFF || Ma > 0x7FFFFFFF || Nb > 0x7FFFFFFF) return hipErrorInvalidValue;
-    const size_t lds = W > 1 ? (size_t)W * nb * 16 * 64 * sizeof(float) : 0;
+    const size_t lds = W > 1 ? (size_t)W * ma * nb * 16 * 64 * sizeof(float) : 0;
     const dim3 grid((unsigned)tiles), block((unsigned)(64 * W));
     const uint8_t *pa = swap ? bq : aq, *psa = swap ? bs : as, *pb = swap ? aq : bq, *psb = swap ? as : bs;
-    auto kern = nb == 2 ? mx::gemm_skinny_kernel<2, FMT> : mx::gemm_skinny_kernel<1, FMT>;
-    if constexpr (FMT == 4)
-        if (nb == 4) kern = mx::gemm_skinny_kernel<4, FMT>;
+    auto kern = nb == 2 ? mx::gemm_skinny_kernel<1, 2, FMT> : mx::gemm_skinny_kernel<1, 1, FMT>;
+    if constexpr (FMT == 4) {
+        if (nb == 4) kern = mx::gemm_skinny_kernel<1, 4, FMT>;
+        if (ma == 2) kern = mx::gemm_skinny_kernel<2, 2, FMT>;
+    }
     hipLaunchKernelGGL(kern, grid, block, lds, stream, pa, psa, pb, psb, (int)Ma, (int)Nb, (int)K, out, ld_i, ld_j,
                        (int)tiles_b);
     return hipGetLastError();

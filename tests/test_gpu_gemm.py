@@ -64,13 +64,15 @@ def test_tiled_shapes(M, N, K):
 
 
 # Skinny kernel (one side below 128 or few tiles): split of the contraction over the waves of a
-# workgroup, 32 x 32*NB blocks with NB = 1, 2, 4, the smaller side taken as A (output written
-# transposed when that is the GEMM's B; small sides of 33..128 rows in several 32-row groups), K
-# chunks past the padded code tiles.
+# workgroup, 32*MA x 32*NB blocks with (MA, NB) = (1, 1), (1, 2), (1, 4), (2, 2), the smaller side
+# taken as A (output written transposed when that is the GEMM's B; small sides of 33..128 rows in
+# several 32-row groups), K chunks past the padded code tiles.  2 x 2 blocks: (1000, 2000, 1024),
+# (97, 20000, 1024) and (16384, 128, 4096) with 4 waves per workgroup, (1536, 2816, 544) with 2,
+# (2100, 3000, 256) with one (no LDS reduction); ragged 64-row groups.
 @pytest.mark.parametrize("M,N,K", [(1, 4096, 14336), (4096, 32, 8192), (32, 65536, 1024), (128, 65536, 512),
                                    (65536, 100, 544), (17, 300, 2080), (1, 128256, 32), (1000, 2000, 1024),
                                    (48, 3000, 544), (5000, 64, 2080), (4096, 128, 14336), (97, 20000, 1024),
-                                   (16384, 128, 4096)])
+                                   (16384, 128, 4096), (1536, 2816, 544), (2100, 3000, 256)])
 def test_skinny_shapes(M, N, K):
     a = W.ragged_values((M, K), 3 * M + K)
     b = W.ragged_values((N, K), 5 * N + K)
