@@ -503,8 +503,10 @@ def main():
                               "unit": "TFLOP/s", "frac": round(gemm_tflops / FP4_PEAK_TFLOPS, 4),
                               "avg_launch_ms": round(avg_gemm_ms, 4),
                               "flop_per_launch": gemm_work / gemm_launches,
-                              # counters were taken over the default step's six MXFP4 launches
-                              "traffic": None if gemm8_ms > 0 else measured_traffic()}
+                              # counters were taken over the 8B MLP step's six MXFP4 launches: the
+                              # figure belongs to that workload's GEMM set only
+                              "traffic": measured_traffic()
+                              if args.workload == "llama8b_mlp" and gemm8_ms == 0 else None}
         # sustained clock and power over ~0.5 s of further steps (not part of the timed region)
         with ClockSampler() as cs:
             t_end = time.time() + 0.5
