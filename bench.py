@@ -359,7 +359,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        sys.stderr.write("bench.py measures one GPU only: this build has no multi-GPU path "
+        sys.stderr.write("bench.py measures one GPU only: the library has no multi-GPU path "
                          "(--gpus %d, WORLD_SIZE %d requested)\n" % (args.gpus, world))
         sys.exit(2)
 
