@@ -1056,7 +1056,11 @@ static hipError_t launch_gemm(const uint8_t* a8, const uint8_t* as8, const uint8
     const bool persist = (reinterpret_cast<uintptr_t>(o16) & 15u) == 0 && (ldo & 7) == 0 && (N & 7) == 0 &&
                          (int64_t)PBM * ldo * 2 < 0x7FFFFFF0ll && getenv_persist() != 0;
     if (persist) {
-        const int64_t grid = std::min<int64_t>(tiles_m * tiles_n, num_cus());
+        // as many rounds as the tiles need on all CUs, spread evenly: every workgroup
+        // gets the same number of tiles (896 tiles run as 224 x 4, not 256 x 3.5)
+        const int64_t tiles_all = tiles_m * tiles_n;
+        const int64_t rounds = (tiles_all + num_cus() - 1) / num_cus();
+        const int64_t grid = (tiles_all + rounds - 1) / rounds;
         auto kern = nkt <= NST ? gemm_persist_kernel<true, FMT> : gemm_persist_kernel<false, FMT>;
         hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, stream, a8, as8, b8, bs8, (int)M, (int)N, (int)K,
                            o16, ldo, (int)tiles_m, (int)tiles_n, group_m);
