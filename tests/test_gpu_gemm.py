@@ -53,8 +53,10 @@ def test_ragged_small(M, N, K):
 # Shapes with at least 128 output tiles of 256 x 256 (the launcher gives fewer to the skinny kernel):
 # persistent kernel with one trip per tile (K <= 512, K = 32 included), with several trips and K not a
 # multiple of 512, the pipelined kernel for N % 8 != 0; ragged M / N edges and K tails.
+# (250, 65784, K): 257 tiles, two rounds on 129 workgroups, the last of which has one tile.
 @pytest.mark.parametrize("M,N,K", [(4096, 2048, 32), (2048, 4096, 256), (2100, 4000, 288), (4096, 2056, 800),
-                                   (2048, 4100, 1024), (2304, 3840, 1024), (3000, 2568, 1536)])
+                                   (2048, 4100, 1024), (2304, 3840, 1024), (3000, 2568, 1536),
+                                   (250, 65784, 288), (250, 65784, 1056)])
 def test_tiled_shapes(M, N, K):
     a = W.normal_bf16((M, K), 1.0, M + 7 * K)
     b = W.normal_bf16((N, K), 0.5, N + 11 * K)
