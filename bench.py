@@ -15,6 +15,11 @@ from K steps after W warm-up steps with nothing between the launches.
 launch over its average launch time, timed with events on the launch stream
 over a second pass of K steps that records an event after every launch.
 `cpu_baseline` times the CPU oracle on a bounded slab of the same workload.
+
+Other modes: `--workload llama70b | llama8b_attn` (the same step at other
+projection shapes), `--workload ragged` (the edge sweep), `--ceilings` (the
+sustained MFMA and HBM rates of the library's probes), `--copy-calibration`
+(a plain device copy for scaling HBM counters).
 """
 import argparse
 import json
@@ -65,6 +70,9 @@ def parse():
                         "SiLU-and-mul + cast for down (of the gate/up output) instead of plain casts")
     p.add_argument("--no-kernel-events", action="store_true",
                    help="time only the whole step (no per-kernel events)")
+    p.add_argument("--ceilings", action="store_true",
+                   help="only measure the chip's sustained FP4 MFMA rate (random and constant operands) and HBM "
+                        "stream rates (read, copy, the dual cast's read/write mix) with the library's probes")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device copy of COPY_BYTES (for scaling HBM counters), then exit")
     a = p.parse_args()
@@ -352,10 +360,68 @@ def ragged_sweep(args, torch, mx, N, W, L, dev):
             "per_combo": combos}
 
 
+def ceilings():
+    """What the chip sustains on the path's two bounds, measured with the library's probes
+    (include/mxfp4.h, mxfp4_probe_*): the GEMM's inner loop of FP4 32x32x64 scaled MFMAs over
+    register-resident operands, on random codes and on constant codes (the power limit shows
+    in the difference), and 16-byte HBM streams: read only, copy, and the dual cast's 2 : 1.0625
+    mix of read and written bytes.  Prints one JSON line."""
+    import torch
+    from mxfp4_block_scaled_cast_amd import _native as N
+    L = N.lib()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+
+    def timed(launch, reps):
+        N.check(launch(), "probe")
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            N.check(launch(), "probe")
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    result = {"metric": "sustained rates (probes)", "cus": cus}
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    words = cus * 256 * 32  # 128 bytes per lane
+    ops = {"mfma_random": torch.randint(-2 ** 31, 2 ** 31 - 1, (words,), dtype=torch.int32, device=dev, generator=g),
+           "mfma_constant": torch.full((words,), 0x24242424, dtype=torch.int32, device=dev)}  # E2M1 1.0 and 2.0
+    out_f = torch.empty(cus * 256, dtype=torch.float32, device=dev)
+    iters = 40000
+    flop = cus * 4 * iters * 16 * 2.0 * 32 * 32 * 64
+    for name, buf in ops.items():
+        t = timed(lambda: L.mxfp4_probe_mfma(buf.data_ptr(), iters, cus, out_f.data_ptr(), sp), 10)
+        tf = flop / t / 1e12
+        # each SIMD issues one 32-cycle MFMA after another: the clock implied if none is lost
+        result[name] = {"tflops": round(tf, 1), "frac_of_peak": round(tf / FP4_PEAK_TFLOPS, 4),
+                        "implied_clock_mhz": round(2400.0 * tf / FP4_PEAK_TFLOPS)}
+    nbytes = 4 << 30
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).random_(generator=g)
+    out_u = torch.empty(cus * 8 * 256, dtype=torch.int32, device=dev)
+    for name, w in (("hbm_read", 0), ("hbm_copy", 32), ("hbm_cast_mix", 17)):
+        dst_bytes = -(-nbytes // 512) * w * 16
+        dst = torch.empty(max(dst_bytes // 4, 4), dtype=torch.int32, device=dev) if w else None
+        t = timed(lambda: L.mxfp4_probe_stream(src.data_ptr(), nbytes, dst.data_ptr() if w else None, w, cus * 8,
+                                                     out_u.data_ptr(), sp), 10)
+        moved = nbytes + dst_bytes
+        result[name] = {"gbps": round(moved / t / 1e9, 1), "frac_of_hbm": round(moved / t / 1e9 / HBM_PEAK_GBPS, 4),
+                        "read_bytes": nbytes, "write_bytes": dst_bytes}
+        del dst
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.ceilings:
+        ceilings()
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

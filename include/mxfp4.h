@@ -345,6 +345,36 @@ int gemm_fp4_bf16_fwd_ex(const void* a, const void* w, const void* w_row_q, cons
 int gemm_fp4_bf16_bwd_ex(const void* dout, const void* w_col_q, const void* w_col_s, int64_t M, int64_t N, int64_t K,
                          void* ws, size_t ws_bytes, void* da, void* dw, unsigned flags, hipStream_t stream);
 
+/*
+ * Measurement probes.  Not steps of the MXFP4 path: they measure what the chip
+ * sustains on the two resources the path is bound by, with the instruction and
+ * access shapes the kernels use, so the kernels' rates can be read against
+ * them as well as against the published peaks.  All pointers are device
+ * memory owned by the caller; work goes on `stream`.
+ *
+ * mxfp4_probe_mfma: `workgroups` (1..65536) workgroups of 4 waves; every wave
+ *   runs `iters` (0..2^40) passes of 16 FP4 32x32x64 scaled MFMAs (a 4 x 4
+ *   block of accumulators, every scale 1) over operands held in registers.
+ *   operands: at least workgroups * 32768 bytes, 16-byte aligned, read once
+ *   (lane t of workgroup g reads the 128 bytes at (g * 256 + t) * 128);
+ *   out: float[workgroups * 256], each lane's sum of its accumulators.
+ *   FLOPs executed: workgroups * 4 * iters * 16 * 2 * 32 * 32 * 64.
+ * mxfp4_probe_stream: reads src_bytes (a multiple of 16) of src once, 16 bytes
+ *   per lane access, grid-stride over `workgroups` (1..65536) workgroups of
+ *   256 lanes; of every 32 consecutive 16-byte chunks the first writes_per_32
+ *   (0..32) are written to dst, packed: dst must hold
+ *   ceil(src_bytes / 512) * writes_per_32 * 16 bytes (NULL allowed when
+ *   writes_per_32 == 0).  0 reads only, 32 copies, 17 gives the dual cast's
+ *   2 : 1.0625 mix of read and written bytes.  out: unsigned[workgroups * 256].
+ * Errors: MXFP4_EINVAL (null pointer, size or count out of range),
+ * MXFP4_EALIGN (operands, src, dst not 16-byte aligned, out not 4-byte
+ * aligned), MXFP4_EDEVICE, MXFP4_ELAUNCH.
+ */
+int mxfp4_probe_mfma(const void* operands, int64_t iters, int64_t workgroups, float* out, hipStream_t stream);
+
+int mxfp4_probe_stream(const void* src, int64_t src_bytes, void* dst, int writes_per_32, int64_t workgroups,
+                       unsigned* out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -43,6 +43,8 @@ SIGNATURES = [
     ("gemm_fp4_bf16_workspace_bytes_ex", _sz, [_i64, _i64, _i64, ctypes.c_uint]),
     ("mxfp4_silu_mul_cast", _i32, [_p, _i64, _i64, _i64, _p, _p, _p, _p, _i32, _p, _p]),
     ("mxfp4_rmsnorm_cast", _i32, [_p, _p, _p, ctypes.c_float, _i64, _i64, _p, _p, _p, _p, _i32, _p, _p, _p, _p]),
+    ("mxfp4_probe_mfma", _i32, [_p, _i64, _i64, _p, _p]),
+    ("mxfp4_probe_stream", _i32, [_p, _i64, _p, _i32, _i64, _p, _p]),
 ]
 
 STEP_TRAINING, STEP_HADAMARD_GRAD, STEP_QUANTIZED_W, STEP_FP8_WGRAD = 1, 2, 4, 8

@@ -39,6 +39,10 @@ extern "C" hipError_t mx_launch_rmsnorm_cast(const void* x, const void* residual
                                              hipStream_t stream);
 extern "C" hipError_t mx_launch_gemm_f(const void* aq, const void* as, const void* bq, const void* bs, int64_t M,
                                        int64_t N, int64_t K, void* out, int64_t ldo, int fmt, hipStream_t stream);
+extern "C" hipError_t mx_launch_probe_mfma(const void* ops, int64_t iters, int64_t workgroups, float* out,
+                                           hipStream_t stream);
+extern "C" hipError_t mx_launch_probe_stream(const void* src, int64_t src_bytes, void* dst, int writes_per_32,
+                                             int64_t workgroups, unsigned* out, hipStream_t stream);
 
 namespace {
 
@@ -497,3 +501,24 @@ int gemm_fp4_bf16_bwd_ex(const void* dout, const void* w_col_q, const void* w_co
 }
 
 }  // extern "C"
+
+int mxfp4_probe_mfma(const void* operands, int64_t iters, int64_t workgroups, float* out, hipStream_t stream) {
+    if (!operands || !out || iters < 0 || iters > ((int64_t)1 << 40) || workgroups < 1 || workgroups > 65536)
+        return MXFP4_EINVAL;
+    if (!aligned16(operands) || (reinterpret_cast<uintptr_t>(out) & 3u) != 0) return MXFP4_EALIGN;
+    int st = check_device();
+    if (st != MXFP4_OK) return st;
+    return status_of(mx_launch_probe_mfma(operands, iters, workgroups, out, stream));
+}
+
+int mxfp4_probe_stream(const void* src, int64_t src_bytes, void* dst, int writes_per_32, int64_t workgroups,
+                       unsigned* out, hipStream_t stream) {
+    if (!src || !out || src_bytes < 0 || src_bytes % 16 != 0 || writes_per_32 < 0 || writes_per_32 > 32 ||
+        workgroups < 1 || workgroups > 65536 || (writes_per_32 > 0 && !dst))
+        return MXFP4_EINVAL;
+    if (!aligned16(src) || (dst && !aligned16(dst)) || (reinterpret_cast<uintptr_t>(out) & 3u) != 0)
+        return MXFP4_EALIGN;
+    int st = check_device();
+    if (st != MXFP4_OK) return st;
+    return status_of(mx_launch_probe_stream(src, src_bytes, dst, writes_per_32, workgroups, out, stream));
+}

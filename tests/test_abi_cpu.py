@@ -292,3 +292,20 @@ def test_fused_producer_cast_argument_validation():
     assert call(gamma=FAKE + 2) == -2
     assert call(qc=FAKE, sc=FAKE, fmt=5) == -1
     assert call(rows=0) == 0
+
+
+def test_probe_argument_validation():
+    L = N.lib()
+    assert L.mxfp4_probe_mfma(None, 1, 1, FAKE, None) == -1                 # null operands
+    assert L.mxfp4_probe_mfma(FAKE, -1, 1, FAKE, None) == -1                # negative iters
+    assert L.mxfp4_probe_mfma(FAKE, 1, 0, FAKE, None) == -1                 # no workgroups
+    assert L.mxfp4_probe_mfma(FAKE, 1, 65537, FAKE, None) == -1
+    assert L.mxfp4_probe_mfma(FAKE + 8, 1, 1, FAKE, None) == -2             # misaligned operands
+    assert L.mxfp4_probe_mfma(FAKE, 1, 1, FAKE + 2, None) == -2             # misaligned out
+    assert L.mxfp4_probe_stream(FAKE, 24, None, 0, 1, FAKE, None) == -1     # bytes % 16
+    assert L.mxfp4_probe_stream(FAKE, 32, None, 17, 1, FAKE, None) == -1    # writes without dst
+    assert L.mxfp4_probe_stream(FAKE, 32, FAKE, 33, 1, FAKE, None) == -1    # writes_per_32 > 32
+    assert L.mxfp4_probe_stream(FAKE, 32, FAKE + 4, 17, 1, FAKE, None) == -2
+    # valid arguments: the host has no gfx950, so the call fails on the device check, launching nothing
+    assert L.mxfp4_probe_mfma(FAKE, 1, 1, FAKE, None) == -3
+    assert L.mxfp4_probe_stream(FAKE, 32, None, 0, 1, FAKE, None) == -3
