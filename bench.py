@@ -3,7 +3,7 @@
 
 A step is the whole hot path for each MLP projection (gate/up 8192x28672x4096
 and down 8192x4096x14336, M = 8192 tokens, one GPU's share):
-    forward : dual cast A, dual cast W, out = A . W^T           (FP4 GEMM)
+    forward : dual casts of A and W (one launch), out = A . W^T (FP4 GEMM)
     backward: dual cast dOut, dA = dOut . W (NN), dW = dOut^T . A (NT wgrad)
 every kernel launched through the C ABI on torch's current stream, inputs
 resident in HBM before timing starts.
@@ -154,9 +154,22 @@ def step_ops(P, L, sp, N, cached_weights=False, hadamard=False, fp8_wgrad=False)
         ops.append(producer_op(P, L, sp))
     if not cached_weights:
         casts.append(("cast_dual(W)", P["w"], P["w_row"], P["w_col"]))
-    for label, x, row, col in casts:
+    def cast_bytes(x, col):
         # bytes per element: bf16 read, FP4 row codes, column codes (FP4 or FP8), two scale bytes per 32
-        nb = (2.5 + (1.0 if col.fmt == 8 else 0.5) + 2.0 / 32) * x.shape[0] * x.shape[1]
+        return (2.5 + (1.0 if col.fmt == 8 else 0.5) + 2.0 / 32) * x.shape[0] * x.shape[1]
+
+    if len(casts) == 2 and not hadamard and all(c[3].fmt == 4 for c in casts):
+        # the forward's two dual casts in one launch, as the training step's forward does them
+        (_, xa, ra, ca), (_, xw, rw, cw) = casts
+        nb = cast_bytes(xa, ca) + cast_bytes(xw, cw)
+        launch = lambda: L.mxfp4_cast_dual_pair(
+            xa.data_ptr(), xa.shape[0], xa.shape[1], xa.shape[1], ra.q.data_ptr(), ra.s.data_ptr(), ca.q.data_ptr(),
+            ca.s.data_ptr(), xw.data_ptr(), xw.shape[0], xw.shape[1], xw.shape[1], rw.q.data_ptr(), rw.s.data_ptr(),
+            cw.q.data_ptr(), cw.s.data_ptr(), sp)
+        ops.append(("cast", name + ".cast_dual(A,W)", launch, nb, nb / (HBM_PEAK_GBPS * 1e9)))
+        casts = []
+    for label, x, row, col in casts:
+        nb = cast_bytes(x, col)
         ops.append(("cast", name + "." + label, cast_dual(x, row, col, False, True, 0), nb, nb / (HBM_PEAK_GBPS * 1e9)))
     fl, _, _, t = gemm_roofline(M, Nn, K)
     ops.append(("gemm", name + ".fwd", gemm(L.mxfp4_gemm_nt, P["a_row"], P["w_row"], P["out"]), fl, t))

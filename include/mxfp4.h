@@ -122,6 +122,17 @@ int mxfp4_cast_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx, void
                     void* s_col, hipStream_t stream);
 
 /*
+ * A2 for two tensors in one launch -- e.g. a product's A and W before the
+ * forward GEMM (the training step's forward casts both).  Results are those
+ * of mxfp4_cast_dual on (x0, ...) and on (x1, ...); each tensor's arguments
+ * have the requirements of mxfp4_cast_dual, and a tensor with rows == 0 or
+ * cols == 0 is skipped.  The two tensors' buffers must not overlap.
+ */
+int mxfp4_cast_dual_pair(const void* x0, int64_t rows0, int64_t cols0, int64_t ldx0, void* q_row0, void* s_row0,
+                         void* q_col0, void* s_col0, const void* x1, int64_t rows1, int64_t cols1, int64_t ldx1,
+                         void* q_row1, void* s_row1, void* q_col1, void* s_col1, hipStream_t stream);
+
+/*
  * F2 -- Hadamard-transformed cast (jax-aiter README, "Quick start": in the
  * training recipe grad_out is cast with a Hadamard transform).  As
  * mxfp4_cast_dual when q_col / s_col are given, as mxfp4_cast when both are

@@ -24,6 +24,7 @@ SIGNATURES = [
     ("mxfp4_status_string", ctypes.c_char_p, [_i32]),
     ("mxfp4_cast", _i32, [_p, _i64, _i64, _i64, _p, _p, _p]),
     ("mxfp4_cast_dual", _i32, [_p, _i64, _i64, _i64, _p, _p, _p, _p, _p]),
+    ("mxfp4_cast_dual_pair", _i32, [_p, _i64, _i64, _i64, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p]),
     ("mxfp4_gemm_nt", _i32, [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _p]),
     ("mxfp4_gemm_nn", _i32, [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _p]),
     ("gemm_fp4_bf16_workspace_bytes", _sz, [_i64, _i64, _i64, _i32]),

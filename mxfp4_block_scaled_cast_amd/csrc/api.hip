@@ -39,6 +39,10 @@ extern "C" hipError_t mx_launch_rmsnorm_cast(const void* x, const void* residual
                                              hipStream_t stream);
 extern "C" hipError_t mx_launch_gemm_f(const void* aq, const void* as, const void* bq, const void* bs, int64_t M,
                                        int64_t N, int64_t K, void* out, int64_t ldo, int fmt, hipStream_t stream);
+extern "C" hipError_t mx_launch_cast_dual_pair(const void* x0, int64_t R0, int64_t C0, int64_t ldx0, void* q_row0,
+                                               void* s_row0, void* q_col0, void* s_col0, const void* x1, int64_t R1,
+                                               int64_t C1, int64_t ldx1, void* q_row1, void* s_row1, void* q_col1,
+                                               void* s_col1, hipStream_t stream);
 extern "C" hipError_t mx_launch_probe_mfma(const void* ops, int64_t iters, int64_t workgroups, float* out,
                                            hipStream_t stream);
 extern "C" hipError_t mx_launch_probe_stream(const void* src, int64_t src_bytes, void* dst, int writes_per_32,
@@ -97,6 +101,17 @@ int validate_cast(const void* x, int64_t rows, int64_t cols, int64_t ldx, const 
 }
 
 int status_of(hipError_t e) { return e == hipSuccess ? MXFP4_OK : MXFP4_ELAUNCH; }
+
+// The checks of mxfp4_cast_dual for one tensor; `empty` tells whether it has no elements.
+int validate_cast_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx, const void* q_row, const void* s_row,
+                       const void* q_col, const void* s_col, bool& empty) {
+    int st = validate_cast(x, rows, cols, ldx, q_row, s_row);
+    empty = rows == 0 || cols == 0;
+    if (st != MXFP4_OK || empty) return st;
+    if (!q_col || !s_col) return MXFP4_EINVAL;
+    if (!aligned16(q_col) || !aligned16(s_col)) return MXFP4_EALIGN;
+    return MXFP4_OK;
+}
 
 int validate_gemm(const void* aq, const void* as, const void* bq, const void* bs, int64_t M, int64_t N, int64_t K,
                   const void* out, int64_t ldo) {
@@ -219,6 +234,22 @@ int mxfp4_cast_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx, void
     if (!aligned16(q_col) || !aligned16(s_col)) return MXFP4_EALIGN;
     if ((st = check_device()) != MXFP4_OK) return st;
     return status_of(mx_launch_cast(x, rows, cols, ldx, q_row, s_row, q_col, s_col, true, stream));
+}
+
+int mxfp4_cast_dual_pair(const void* x0, int64_t rows0, int64_t cols0, int64_t ldx0, void* q_row0, void* s_row0,
+                         void* q_col0, void* s_col0, const void* x1, int64_t rows1, int64_t cols1, int64_t ldx1,
+                         void* q_row1, void* s_row1, void* q_col1, void* s_col1, hipStream_t stream) {
+    bool empty0 = true, empty1 = true;
+    int st = validate_cast_dual(x0, rows0, cols0, ldx0, q_row0, s_row0, q_col0, s_col0, empty0);
+    if (st != MXFP4_OK) return st;
+    if ((st = validate_cast_dual(x1, rows1, cols1, ldx1, q_row1, s_row1, q_col1, s_col1, empty1)) != MXFP4_OK)
+        return st;
+    if (empty0 && empty1) return MXFP4_OK;
+    if ((st = check_device()) != MXFP4_OK) return st;
+    // an empty tensor contributes no workgroups (its grid is 0 x 0 tiles)
+    return status_of(mx_launch_cast_dual_pair(x0, empty0 ? 0 : rows0, empty0 ? 0 : cols0, ldx0, q_row0, s_row0,
+                                              q_col0, s_col0, x1, empty1 ? 0 : rows1, empty1 ? 0 : cols1, ldx1,
+                                              q_row1, s_row1, q_col1, s_col1, stream));
 }
 
 int mxfp4_cast_hadamard(const void* x, int64_t rows, int64_t cols, int64_t ldx, void* q_row, void* s_row,
@@ -402,12 +433,20 @@ int step_fwd(const void* a, bool own_w, const void* w, const void* w_row_q, cons
     if (K > 0) {
         // with the Hadamard recipe the column copies (dB's and dA's B operands) carry the transform
         // with the FP8 wgrad A's column copy (dB's B operand) is MXFP8
-        e = mx_launch_cast_f(a, M, K, K, base + L.a_row_q, base + L.a_row_s, train ? base + L.a_col_q : nullptr,
-                             train ? base + L.a_col_s : nullptr, train, 4, fp8_wgrad ? 8 : 4, false, hadamard, 0,
-                             stream);
-        if (e == hipSuccess && own_w)
-            e = mx_launch_cast_h(w, N, K, K, base + L.w_row_q, base + L.w_row_s, train ? base + L.w_col_q : nullptr,
-                                 train ? base + L.w_col_s : nullptr, train, false, hadamard, 0, stream);
+        if (train && own_w && !hadamard && !fp8_wgrad) {
+            // both dual casts in one launch
+            e = mx_launch_cast_dual_pair(a, M, K, K, base + L.a_row_q, base + L.a_row_s, base + L.a_col_q,
+                                         base + L.a_col_s, w, N, K, K, base + L.w_row_q, base + L.w_row_s,
+                                         base + L.w_col_q, base + L.w_col_s, stream);
+        } else {
+            e = mx_launch_cast_f(a, M, K, K, base + L.a_row_q, base + L.a_row_s, train ? base + L.a_col_q : nullptr,
+                                 train ? base + L.a_col_s : nullptr, train, 4, fp8_wgrad ? 8 : 4, false, hadamard, 0,
+                                 stream);
+            if (e == hipSuccess && own_w)
+                e = mx_launch_cast_h(w, N, K, K, base + L.w_row_q, base + L.w_row_s,
+                                     train ? base + L.w_col_q : nullptr, train ? base + L.w_col_s : nullptr, train,
+                                     false, hadamard, 0, stream);
+        }
     }
     if (e == hipSuccess) e = mx_launch_gemm(base + L.a_row_q, base + L.a_row_s, wq, wsc, M, N, K, out, N, stream);
     return status_of(e);

@@ -79,6 +79,18 @@ struct ProdArgs {
     uint16_t* y_out;        // optional: the produced bf16 values [R, C], row stride C
 };
 
+// A second tensor converted by the same launch: workgroups from `split` on
+// (a multiple of 8, so that workgroup b and its index within its tensor sit on
+// the same XCD) take its tiles; the first tensor's grid is padded up to
+// `split` with workgroups that return at once.  split = INT_MAX: one tensor.
+struct CastSeg {
+    const uint16_t* x;
+    int64_t R, C, ldx;
+    uint8_t *q_row, *s_row, *q_col, *s_col;
+    int n_rtiles, n_ctiles, split;
+};
+constexpr CastSeg kOneTensor = {nullptr, 0, 0, 0, nullptr, nullptr, nullptr, nullptr, 0, 0, 0x7FFFFFFF};
+
 // bf16 bits (nearest even) of a double, rounded once: the significand is cut at
 // the bf16 grid of the value's binade (2^(e-7), or 2^-133 below 2^-126); past
 // the largest finite bf16 the result is infinity; NaN gives the quiet NaN 0x7FC0.
@@ -226,12 +238,29 @@ template <int TILE_R, bool DUAL, bool HROW, bool HCOL, int ROWF, int COLF, int P
 __global__ __launch_bounds__(256, 4) void cast_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C, int64_t ldx,
                                                    uint8_t* __restrict__ q_row, uint8_t* __restrict__ s_row,
                                                    uint8_t* __restrict__ q_col, uint8_t* __restrict__ s_col,
-                                                   int n_rtiles, int n_ctiles, int hshift, ProdArgs P) {
+                                                   int n_rtiles, int n_ctiles, int hshift, ProdArgs P,
+                                                   CastSeg second) {
     static_assert((ROWF == 4 || ROWF == 8) && (COLF == 4 || COLF == 8), "MXFP4 or MXFP8");
     static_assert(!(HROW && ROWF == 8) && !(HCOL && COLF == 8), "the transform goes with MXFP4 copies");
     constexpr int NI = TILE_R / 8;  // 16-byte loads per thread
     const int t = threadIdx.x;
-    const int tile = xcd_remap(blockIdx.x, n_rtiles * n_ctiles);
+    int bid = blockIdx.x;
+    if (bid >= second.split) {  // the second tensor (uniform per workgroup)
+        bid -= second.split;
+        x = second.x;
+        R = second.R;
+        C = second.C;
+        ldx = second.ldx;
+        q_row = second.q_row;
+        s_row = second.s_row;
+        q_col = second.q_col;
+        s_col = second.s_col;
+        n_rtiles = second.n_rtiles;
+        n_ctiles = second.n_ctiles;
+    } else if (bid >= n_rtiles * n_ctiles) {
+        return;  // padding between the two tensors' grids
+    }
+    const int tile = xcd_remap(bid, n_rtiles * n_ctiles);
     const int rt = tile % n_rtiles;
     const int ct = tile / n_rtiles;
     const int64_t r0 = (int64_t)rt * TILE_R;
@@ -524,7 +553,7 @@ extern "C" hipError_t mx_launch_cast_f(const void* x, int64_t R, int64_t C, int6
     const mx::ProdArgs P{};
 #define MX_CAST(D, HR, HC, RF, CF)                                                                         \
     hipLaunchKernelGGL((mx::cast_kernel<TILE_R, D, HR, HC, RF, CF>), grid, block, 0, stream, xb, R, C, ldx, qr, \
-                       sr, D ? qc : nullptr, D ? scl : nullptr, nr, nc, hshift, P)
+                       sr, D ? qc : nullptr, D ? scl : nullptr, nr, nc, hshift, P, mx::kOneTensor)
     if (row_fmt == 8 || col_fmt == 8) {
         if (transform_row || transform_col) return hipErrorInvalidValue;
         if (!dual) {
@@ -628,13 +657,13 @@ static hipError_t launch_produced_cast(const uint16_t* x, int64_t R, int64_t C, 
     uint8_t *qc = static_cast<uint8_t*>(q_col), *scl = static_cast<uint8_t*>(s_col);
     if (!dual)
         hipLaunchKernelGGL((cast_kernel<64, false, false, false, 4, 4, PROD>), grid, block, 0, stream, x, R, C, ldx,
-                           qr, sr, nullptr, nullptr, nr, nc, 0, P);
+                           qr, sr, nullptr, nullptr, nr, nc, 0, P, kOneTensor);
     else if (col_fmt == 8)
         hipLaunchKernelGGL((cast_kernel<64, true, false, false, 4, 8, PROD>), grid, block, 0, stream, x, R, C, ldx, qr,
-                           sr, qc, scl, nr, nc, 0, P);
+                           sr, qc, scl, nr, nc, 0, P, kOneTensor);
     else
         hipLaunchKernelGGL((cast_kernel<64, true, false, false, 4, 4, PROD>), grid, block, 0, stream, x, R, C, ldx, qr,
-                           sr, qc, scl, nr, nc, 0, P);
+                           sr, qc, scl, nr, nc, 0, P, kOneTensor);
     return hipGetLastError();
 }
 
@@ -677,4 +706,26 @@ extern "C" hipError_t mx_launch_rmsnorm_cast(const void* x, const void* residual
     P.y_out = static_cast<uint16_t*>(y_out);
     return mx::launch_produced_cast<mx::PROD_RMS>(rb ? hb : xb, R, D, D, q_row, s_row, q_col, s_col, dual, col_fmt, P,
                                                   stream);
+}
+
+// Dual casts (MXFP4 row + column copies) of two tensors in one launch: the
+// first tensor's workgroups, padded to a multiple of 8, then the second's.
+extern "C" hipError_t mx_launch_cast_dual_pair(const void* x0, int64_t R0, int64_t C0, int64_t ldx0, void* q_row0,
+                                               void* s_row0, void* q_col0, void* s_col0, const void* x1, int64_t R1,
+                                               int64_t C1, int64_t ldx1, void* q_row1, void* s_row1, void* q_col1,
+                                               void* s_col1, hipStream_t stream) {
+    int nr0 = 0, nc0 = 0, nr1 = 0, nc1 = 0;
+    if (!mx::cast_grid(R0, C0, true, nr0, nc0) || !mx::cast_grid(R1, C1, true, nr1, nc1)) return hipErrorInvalidValue;
+    const int64_t t0 = (int64_t)nr0 * nc0, t1 = (int64_t)nr1 * nc1;
+    const int64_t split = (t0 + 7) & ~(int64_t)7;
+    if (split + t1 > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (t0 + t1 == 0) return hipSuccess;
+    const mx::CastSeg second = {static_cast<const uint16_t*>(x1), R1, C1, ldx1,
+                                static_cast<uint8_t*>(q_row1), static_cast<uint8_t*>(s_row1),
+                                static_cast<uint8_t*>(q_col1), static_cast<uint8_t*>(s_col1), nr1, nc1, (int)split};
+    hipLaunchKernelGGL((mx::cast_kernel<64, true, false, false, 4, 4>), dim3((unsigned)(split + t1)), dim3(256), 0,
+                       stream, static_cast<const uint16_t*>(x0), R0, C0, ldx0, static_cast<uint8_t*>(q_row0),
+                       static_cast<uint8_t*>(s_row0), static_cast<uint8_t*>(q_col0), static_cast<uint8_t*>(s_col0),
+                       nr0, nc0, 0, mx::ProdArgs{}, second);
+    return hipGetLastError();
 }

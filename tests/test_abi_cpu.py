@@ -87,6 +87,13 @@ def test_cast_argument_validation():
     assert L.mxfp4_cast(FAKE, 1 << 31, 32, 32, FAKE, FAKE, None) == -5    # range
     assert L.mxfp4_cast_dual(FAKE, 4, 32, 32, FAKE, FAKE, None, FAKE, None) == -1
     assert L.mxfp4_cast_dual(FAKE, 4, 32, 32, FAKE, FAKE, FAKE + 4, FAKE, None) == -2
+    pair_ok = [FAKE, 4, 32, 32, FAKE, FAKE, FAKE, FAKE]
+    assert L.mxfp4_cast_dual_pair(*pair_ok, FAKE, 4, 33, 40, FAKE, FAKE, FAKE, FAKE, None) == -1  # second: cols % 32
+    assert L.mxfp4_cast_dual_pair(FAKE, 4, 32, 32, FAKE, FAKE, None, FAKE, *pair_ok, None) == -1   # first: no q_col
+    assert L.mxfp4_cast_dual_pair(*pair_ok, FAKE, 4, 32, 32, FAKE, FAKE, FAKE + 4, FAKE, None) == -2
+    assert L.mxfp4_cast_dual_pair(FAKE, 0, 32, 32, None, None, None, None, FAKE, 4, 0, 0, None, None, None, None,
+                                  None) == 0                                                          # both empty
+    assert L.mxfp4_cast_dual_pair(*pair_ok, *pair_ok, None) == -3                                     # no gfx950 here
 
 
 def test_gemm_argument_validation():

@@ -111,3 +111,34 @@ def test_side_stream_ordering():
     side.synchronize()
     check_row(x_bits, t.row, "side stream row")
     check_col(x_bits, t.col, "side stream col")
+
+
+@pytest.mark.parametrize("shape0,shape1", [((65, 544), (257, 2080)), ((8, 256), (300, 256)), ((0, 64), (17, 96)),
+                                           ((31, 288), (0, 0)), ((1, 4096), (1, 32))])
+def test_dual_pair_equals_two_dual_casts(shape0, shape1):
+    # one launch for two tensors: both results bit-equal to the oracle (and to separate launches);
+    # the first tensor's grid (padded to a multiple of 8 workgroups) and an empty tensor on either side
+    from mxfp4_block_scaled_cast_amd import _native as N
+    dev = torch.device("cuda:0")
+    xs, rows, cols = [], [], []
+    for i, (R, C) in enumerate((shape0, shape1)):
+        bits = W.ragged_values((R, C), 11 * R + C + i) if R * C else np.zeros((R, C), dtype=np.uint16)
+        xs.append(bits)
+    say("cast_dual_pair %s %s" % (shape0, shape1))
+    ops = []
+    for bits in xs:
+        R, C = bits.shape
+        x = to_device(bits) if R * C else torch.empty((max(R, 1), max(C, 32)), dtype=torch.bfloat16, device=dev)
+        ops.append((x, R, C, mx.empty_operand(R, C, dev), mx.empty_operand(C, -(-R // 32) * 32, dev)))
+    args = []
+    for x, R, C, row, col in ops:
+        args += [x.data_ptr(), R, C, x.stride(0), row.q.data_ptr(), row.s.data_ptr(), col.q.data_ptr(),
+                 col.s.data_ptr()]
+    sp = torch.cuda.current_stream(dev).cuda_stream
+    N.check(N.lib().mxfp4_cast_dual_pair(*args, sp), "mxfp4_cast_dual_pair")
+    torch.cuda.synchronize()
+    for bits, (x, R, C, row, col) in zip(xs, ops):
+        if R * C == 0:
+            continue
+        check_row(bits, row, "pair row %dx%d" % (R, C))
+        check_col(bits, col, "pair col %dx%d" % (R, C))
