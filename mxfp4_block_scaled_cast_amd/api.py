@@ -94,6 +94,23 @@ def cast_dual(x, row: Optional[MxOperand] = None, col: Optional[MxOperand] = Non
     return Mxfp4Tensor(row, col, (R, C))
 
 
+def cast_dual_pair(x0, x1):
+    """Row and column copies of two bf16 matrices in one launch (as the training forward casts its
+    A and W); the same results as cast_dual(x0), cast_dual(x1)."""
+    outs, args = [], []
+    for i, x in enumerate((x0, x1)):
+        _check_bf16_matrix(x, "x%d" % i)
+        if x.device != x0.device:
+            raise ValueError("x0 and x1 must be on the same device")
+        R, C = x.shape
+        row, col = empty_operand(R, C, x.device), empty_operand(C, -(-R // 32) * 32, x.device)
+        outs.append(Mxfp4Tensor(row, col, (R, C)))
+        args += [x.data_ptr(), R, C, x.stride(0), row.q.data_ptr(), row.s.data_ptr(), col.q.data_ptr(),
+                 col.s.data_ptr()]
+    N.check(N.lib().mxfp4_cast_dual_pair(*args, _stream(x0.device)), "mxfp4_cast_dual_pair")
+    return outs[0], outs[1]
+
+
 def cast_hadamard(x, transform_row=True, transform_col=True, shift=0, columnwise=True) -> Mxfp4Tensor:
     """Row (and, if columnwise, column) copy of bf16 x [R, C] with each 32-block of the chosen
     copies Walsh-Hadamard transformed and divided by 2^shift before quantization (the gradient

@@ -142,3 +142,15 @@ def test_dual_pair_equals_two_dual_casts(shape0, shape1):
             continue
         check_row(bits, row, "pair row %dx%d" % (R, C))
         check_col(bits, col, "pair col %dx%d" % (R, C))
+
+
+def test_python_cast_dual_pair():
+    a = W.ragged_values((300, 544), 21)
+    b = W.ragged_values((65, 96), 22)
+    say("cast_dual_pair (python) %s %s" % (a.shape, b.shape))
+    ta, tb = mx.cast_dual_pair(to_device(a), to_device(b))
+    torch.cuda.synchronize()
+    check_row(a, ta.row, "pair A row")
+    check_col(a, ta.col, "pair A col")
+    check_row(b, tb.row, "pair B row")
+    check_col(b, tb.col, "pair B col")
