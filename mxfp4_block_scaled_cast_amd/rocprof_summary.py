@@ -78,7 +78,7 @@ def kernel_stats(csv_path, out_md, command, include=None, trace=None, windows=()
 
 def sweep_table(json_path, out_md, command):
     d = json.load(open(json_path))
-    kinds = ["cast_dual(A)", "cast_dual(W)", "fwd", "cast_dual(dOut)", "dA", "dB"]
+    kinds = list(d["per_combo"][0]["kernels"])  # launch order of the step
     lines = ["# Edge / ragged sweep: one training step per (M, N, K)", "", "Command:", "", "```", command, "```", "",
              "Each cell: kernel time in us, its rate (TFLOP/s for GEMMs, GB/s for casts) and, in brackets, the "
              "fraction of the roofline that bounds it (ideal time at 10.1 PFLOP/s or 8 TB/s, whichever is "
