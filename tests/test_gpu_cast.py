@@ -154,3 +154,29 @@ def test_python_cast_dual_pair():
     check_col(a, ta.col, "pair A col")
     check_row(b, tb.row, "pair B row")
     check_col(b, tb.col, "pair B col")
+
+
+def test_dual_pair_strided_inputs():
+    # row strides larger than the row (views into wider matrices), different for the two tensors
+    from mxfp4_block_scaled_cast_amd import _native as N
+    dev = torch.device("cuda:0")
+    a = W.ragged_values((70, 256), 31)
+    b = W.ragged_values((129, 96), 32)
+    wide_a = np.zeros((70, 264), dtype=np.uint16)
+    wide_a[:, :256] = a
+    wide_b = np.zeros((129, 1000), dtype=np.uint16)
+    wide_b[:, 8:104] = b
+    xa = to_device(wide_a)[:, :256]
+    xb = to_device(wide_b)[:, 8:104]
+    say("cast_dual_pair strided %s %s" % (a.shape, b.shape))
+    outs, args = [], []
+    for x, (R, C) in ((xa, a.shape), (xb, b.shape)):
+        row, col = mx.empty_operand(R, C, dev), mx.empty_operand(C, -(-R // 32) * 32, dev)
+        outs.append((row, col))
+        args += [x.data_ptr(), R, C, x.stride(0), row.q.data_ptr(), row.s.data_ptr(), col.q.data_ptr(),
+                 col.s.data_ptr()]
+    N.check(N.lib().mxfp4_cast_dual_pair(*args, torch.cuda.current_stream(dev).cuda_stream), "pair")
+    torch.cuda.synchronize()
+    for bits, (row, col) in zip((a, b), outs):
+        check_row(bits, row, "strided pair row")
+        check_col(bits, col, "strided pair col")
