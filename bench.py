@@ -18,7 +18,7 @@ over a second pass of K steps that records an event after every launch.
 
 Other modes: `--workload llama70b | llama8b_attn` (the same step at other
 projection shapes), `--workload ragged` (the edge sweep), `--ceilings` (the
-sustained MFMA and HBM rates of the library's probes), `--copy-calibration`
+sustained MFMA and HBM rates of the bench's probes), `--copy-calibration`
 (a plain device copy for scaling HBM counters).
 """
 import argparse
@@ -72,7 +72,7 @@ def parse():
                    help="time only the whole step (no per-kernel events)")
     p.add_argument("--ceilings", action="store_true",
                    help="only measure the chip's sustained FP4 MFMA rate (random and constant operands) and HBM "
-                        "stream rates (read, copy, the dual cast's read/write mix) with the library's probes")
+                        "stream rates (read, copy, the dual cast's read/write mix) with the bench's probes")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device copy of COPY_BYTES (for scaling HBM counters), then exit")
     a = p.parse_args()
@@ -105,7 +105,7 @@ def measured_traffic():
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
-        from mxfp4_block_scaled_cast_amd import rocprof_summary as rs
+        import bench_rocprof as rs
         if t.get("source_hash") != rs.source_hash(rs.GEMM_SOURCES):
             return None
         return round(t["traffic_bytes_per_launch"])
@@ -374,13 +374,13 @@ def ragged_sweep(args, torch, mx, N, W, L, dev):
 
 
 def ceilings():
-    """What the chip sustains on the path's two bounds, measured with the library's probes
-    (include/mxfp4.h, mxfp4_probe_*): the GEMM's inner loop of FP4 32x32x64 scaled MFMAs over
+    """What the chip sustains on the path's two bounds, measured with the bench's probes
+    (bench_probes.hip, a library of their own): the GEMM's inner loop of FP4 32x32x64 scaled MFMAs over
     register-resident operands, on random codes and on constant codes (the power limit shows
     in the difference), and 16-byte HBM streams: read only, copy, and the dual cast's 2 : 1.0625
     mix of read and written bytes.  Prints one JSON line."""
     import torch
-    from mxfp4_block_scaled_cast_amd import _native as N
+    import bench_probes as N
     L = N.lib()
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
@@ -408,7 +408,7 @@ def ceilings():
     iters = 40000
     flop = cus * 4 * iters * 16 * 2.0 * 32 * 32 * 64
     for name, buf in ops.items():
-        t = timed(lambda: L.mxfp4_probe_mfma(buf.data_ptr(), iters, cus, out_f.data_ptr(), sp), 10)
+        t = timed(lambda: L.probe_mfma(buf.data_ptr(), iters, cus, out_f.data_ptr(), sp), 10)
         tf = flop / t / 1e12
         # each SIMD issues one 32-cycle MFMA after another: the clock implied if none is lost
         result[name] = {"tflops": round(tf, 1), "frac_of_peak": round(tf / FP4_PEAK_TFLOPS, 4),
@@ -419,7 +419,7 @@ def ceilings():
     for name, w in (("hbm_read", 0), ("hbm_copy", 32), ("hbm_cast_mix", 17)):
         dst_bytes = -(-nbytes // 512) * w * 16
         dst = torch.empty(max(dst_bytes // 4, 4), dtype=torch.int32, device=dev) if w else None
-        t = timed(lambda: L.mxfp4_probe_stream(src.data_ptr(), nbytes, dst.data_ptr() if w else None, w, cus * 8,
+        t = timed(lambda: L.probe_stream(src.data_ptr(), nbytes, dst.data_ptr() if w else None, w, cus * 8,
                                                      out_u.data_ptr(), sp), 10)
         moved = nbytes + dst_bytes
         result[name] = {"gbps": round(moved / t / 1e9, 1), "frac_of_hbm": round(moved / t / 1e9 / HBM_PEAK_GBPS, 4),

@@ -1,5 +1,7 @@
-// Measurement probes: what the chip sustains on the two resources the hot path
-// is bound by, measured with the same instruction and access shapes.
+// Measurement probes for bench.py --ceilings (not part of the MXFP4 library):
+// what the chip sustains on the two resources the cast and the GEMM are bound
+// by, measured with the same instruction and access shapes as the kernels.
+// Built into a library of their own (bench_probes.py), loaded by the bench.
 //
 // * mfma: the GEMM's inner loop with nothing else -- one workgroup of four
 //   waves per CU, each wave a 4 x 4 block of 32x32x64 FP4 scaled MFMAs over
@@ -8,7 +10,9 @@
 //   limit allows on random data from the one on quiet data.
 // * stream: grid-stride 16-byte accesses -- read only, read + write of the
 //   same size, or the dual cast's 2 : 1.0625 mix of reads and writes.
-#include "mx_device.h"
+#include <string.h>
+
+#include "mxfp4_block_scaled_cast_amd/csrc/mx_device.h"
 
 namespace mx {
 
@@ -74,17 +78,51 @@ __global__ __launch_bounds__(256) void probe_stream_kernel(const u32x4* __restri
 
 }  // namespace mx
 
-extern "C" hipError_t mx_launch_probe_mfma(const void* ops, int64_t iters, int64_t workgroups, float* out,
-                                           hipStream_t stream) {
-    hipLaunchKernelGGL(mx::probe_mfma_kernel, dim3((unsigned)workgroups), dim3(256), 0, stream,
-                       static_cast<const mx::u32x4*>(ops), iters, out);
-    return hipGetLastError();
+// C entry points.  Return 0, -1 for an argument out of range (null pointer,
+// size, count), -2 for a misaligned pointer, -3 when the current device is not
+// a gfx950, -4 when the launch failed.  All pointers are device memory.
+
+static int probe_device_ok() {
+    int dev = -1;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
+    return strncmp(prop.gcnArchName, "gfx950", 6) == 0;
 }
 
-extern "C" hipError_t mx_launch_probe_stream(const void* src, int64_t src_bytes, void* dst, int writes_per_32,
-                                             int64_t workgroups, unsigned* out, hipStream_t stream) {
+static bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// At most 2^24 passes per wave (a few seconds at the MFMA rate of the chip).
+constexpr int64_t kMaxProbeIters = (int64_t)1 << 24;
+
+// `workgroups` (1..65536) workgroups of 4 waves; every wave runs `iters`
+// (0..2^24) passes of 16 FP4 32x32x64 scaled MFMAs (a 4 x 4 block of
+// accumulators, every scale 1) over operands held in registers.  operands: at
+// least workgroups * 32768 bytes, 16-byte aligned (lane t of workgroup g reads
+// the 128 bytes at (g * 256 + t) * 128); out: float[workgroups * 256], each
+// lane's sum of its accumulators.  FLOPs: workgroups * 4 * iters * 16 * 2 * 32 * 32 * 64.
+extern "C" int probe_mfma(const void* operands, int64_t iters, int64_t workgroups, float* out, hipStream_t stream) {
+    if (!operands || !out || iters < 0 || iters > kMaxProbeIters || workgroups < 1 || workgroups > 65536) return -1;
+    if (!aligned(operands, 16) || !aligned(out, 4)) return -2;
+    if (!probe_device_ok()) return -3;
+    hipLaunchKernelGGL(mx::probe_mfma_kernel, dim3((unsigned)workgroups), dim3(256), 0, stream,
+                       static_cast<const mx::u32x4*>(operands), iters, out);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+// Reads src_bytes (a multiple of 16) of src once, 16 bytes per lane access,
+// grid-stride over `workgroups` (1..65536) workgroups of 256 lanes; of every
+// 32 consecutive 16-byte chunks the first writes_per_32 (0..32) are written to
+// dst, packed: dst holds ceil(src_bytes / 512) * writes_per_32 * 16 bytes (NULL
+// allowed when writes_per_32 == 0).  out: unsigned[workgroups * 256].
+extern "C" int probe_stream(const void* src, int64_t src_bytes, void* dst, int writes_per_32, int64_t workgroups,
+                            unsigned* out, hipStream_t stream) {
+    if (!src || !out || src_bytes < 0 || src_bytes % 16 != 0 || writes_per_32 < 0 || writes_per_32 > 32 ||
+        workgroups < 1 || workgroups > 65536 || (writes_per_32 > 0 && !dst))
+        return -1;
+    if (!aligned(src, 16) || (dst && !aligned(dst, 16)) || !aligned(out, 4)) return -2;
+    if (!probe_device_ok()) return -3;
     hipLaunchKernelGGL(mx::probe_stream_kernel, dim3((unsigned)workgroups), dim3(256), 0, stream,
                        static_cast<const mx::u32x4*>(src), src_bytes / 16, static_cast<mx::u32x4*>(dst), writes_per_32,
                        out);
-    return hipGetLastError();
+    return hipGetLastError() == hipSuccess ? 0 : -4;
 }

@@ -1,4 +1,4 @@
-"""Summaries of rocprofv3 output for the committed profiles.
+"""Summaries of rocprofv3 output for the committed profiles (bench-side tool, not part of the library).
 
 Two uses:
 
@@ -16,9 +16,9 @@ Two uses:
   is unchanged.
 
 Usage:
-  python -m mxfp4_block_scaled_cast_amd.rocprof_summary kernel-stats STATS_CSV OUT_MD --command "..." [--include REGEX]
-  python -m mxfp4_block_scaled_cast_amd.rocprof_summary sweep-table BENCH_JSON OUT_MD --command "..."
-  python -m mxfp4_block_scaled_cast_amd.rocprof_summary traffic --kernel REGEX --fetch CSV --write CSV \
+  python bench_rocprof.py kernel-stats STATS_CSV OUT_MD --command "..." [--include REGEX]
+  python bench_rocprof.py sweep-table BENCH_JSON OUT_MD --command "..."
+  python bench_rocprof.py traffic --kernel REGEX --fetch CSV --write CSV \
       --copy-fetch CSV --copy-write CSV --copy-bytes N --out OUT_JSON --command "..."
 """
 import argparse
@@ -29,7 +29,7 @@ import os
 import re
 import statistics
 
-PKG = os.path.dirname(os.path.abspath(__file__))
+PKG = os.path.join(os.path.dirname(os.path.abspath(__file__)), "mxfp4_block_scaled_cast_amd")
 GEMM_SOURCES = [os.path.join(PKG, "csrc", f) for f in ("gemm.hip", "mx_device.h", "mx_host.h")]
 CAST_SOURCES = [os.path.join(PKG, "csrc", f) for f in ("cast.hip", "mx_device.h", "mx_host.h")]
 

@@ -97,6 +97,20 @@ typedef struct {
  * Returns MXFP4_EINVAL for a null `out`, negative sizes or k % 32 != 0. */
 int mxfp4_operand_layout_of(int64_t rows, int64_t k, mxfp4_operand_layout* out);
 
+/* Sizes of both copies of a cast bf16 matrix x [rows, cols] (jax-aiter README,
+ * "Quick start": quantize(w) returns an Mxfp4Tensor of row + column copies and
+ * their scales).  Host only; touches no device. */
+typedef struct {
+    int64_t rows, cols;          /* x [rows, cols] */
+    int64_t padded_rows;         /* ceil(rows/32) * 32: the column copy's contraction length */
+    mxfp4_operand_layout row;    /* the row copy: operand (rows, K = cols) */
+    mxfp4_operand_layout col;    /* the column copy: operand (cols, K = padded_rows) */
+} mxfp4_layout_t;
+
+/* Fill *out for x [rows, cols].  MXFP4_EINVAL for a null `out`, negative sizes
+ * or cols % 32 != 0; MXFP4_ERANGE for rows or cols >= 2^31. */
+int mxfp4_layout(int64_t rows, int64_t cols, mxfp4_layout_t* out);
+
 /* Static description of a status code (never NULL). */
 const char* mxfp4_status_string(int status);
 
@@ -159,10 +173,12 @@ int mxfp4_cast_hadamard(const void* x, int64_t rows, int64_t cols, int64_t ldx, 
  * (low-level)", gemm_fp4(a, b, a_scale, b_scale), and the A[M,K] @ B[N,K]^T
  * convention of its GEMM rows):
  *   out[m, n] = bf16_rne( sum_k dq(a)[m, k] * dq(b)[n, k] ),  fp32 accumulation
- * a_q, a_s : MX operand (M rows, K);   b_q, b_s : MX operand (N rows, K)
+ * a_q, a_s : MX operand (M rows, K);   b_q, b_s : MX operand (N rows, K);
+ *            all four 16-byte aligned (MXFP4_EALIGN otherwise)
  * out      : bf16 [M, N], row stride ldo >= N elements (2-byte aligned).
  * K % 32 == 0.  M or N == 0: no-op.  K == 0: out is filled with +0.
- * Limits: M, N < 2^31, K < 2^31.
+ * Limits: M, N < 2^31; K <= 2^23 = 8388608 (the tiled kernels address a
+ * wave's operand loads with 32-bit offsets); MXFP4_ERANGE beyond.
  */
 int mxfp4_gemm_nt(const void* a_q, const void* a_s, const void* b_q, const void* b_s, int64_t M, int64_t N, int64_t K,
                   void* out, int64_t ldo, hipStream_t stream);
@@ -262,7 +278,9 @@ size_t gemm_fp4_bf16_workspace_bytes(int64_t M, int64_t N, int64_t K, int traini
  *   out[M, N] = bf16( cast(a)[M, K] . cast(w)[N, K]^T )
  * a : bf16 [M, K] contiguous;  w : bf16 [N, K] contiguous;  out : bf16 [M, N]
  * contiguous.  K % 32 == 0; with training != 0 also N % 32 == 0 (the backward
- * pass contracts over N).  ws : device workspace of ws_bytes >=
+ * pass contracts over N).  Each product's contraction is at most 2^23 (K; in
+ * training also N and ceil(M/32)*32), MXFP4_ERANGE beyond.  ws : device
+ * workspace of ws_bytes >=
  * gemm_fp4_bf16_workspace_bytes(M, N, K, training) bytes, 256-byte aligned.
  * training != 0: a and w are dual-cast and their column copies stay in ws for
  * gemm_fp4_bf16_bwd; otherwise they are row-cast only.
@@ -355,36 +373,6 @@ int gemm_fp4_bf16_fwd_ex(const void* a, const void* w, const void* w_row_q, cons
 
 int gemm_fp4_bf16_bwd_ex(const void* dout, const void* w_col_q, const void* w_col_s, int64_t M, int64_t N, int64_t K,
                          void* ws, size_t ws_bytes, void* da, void* dw, unsigned flags, hipStream_t stream);
-
-/*
- * Measurement probes.  Not steps of the MXFP4 path: they measure what the chip
- * sustains on the two resources the path is bound by, with the instruction and
- * access shapes the kernels use, so the kernels' rates can be read against
- * them as well as against the published peaks.  All pointers are device
- * memory owned by the caller; work goes on `stream`.
- *
- * mxfp4_probe_mfma: `workgroups` (1..65536) workgroups of 4 waves; every wave
- *   runs `iters` (0..2^40) passes of 16 FP4 32x32x64 scaled MFMAs (a 4 x 4
- *   block of accumulators, every scale 1) over operands held in registers.
- *   operands: at least workgroups * 32768 bytes, 16-byte aligned, read once
- *   (lane t of workgroup g reads the 128 bytes at (g * 256 + t) * 128);
- *   out: float[workgroups * 256], each lane's sum of its accumulators.
- *   FLOPs executed: workgroups * 4 * iters * 16 * 2 * 32 * 32 * 64.
- * mxfp4_probe_stream: reads src_bytes (a multiple of 16) of src once, 16 bytes
- *   per lane access, grid-stride over `workgroups` (1..65536) workgroups of
- *   256 lanes; of every 32 consecutive 16-byte chunks the first writes_per_32
- *   (0..32) are written to dst, packed: dst must hold
- *   ceil(src_bytes / 512) * writes_per_32 * 16 bytes (NULL allowed when
- *   writes_per_32 == 0).  0 reads only, 32 copies, 17 gives the dual cast's
- *   2 : 1.0625 mix of read and written bytes.  out: unsigned[workgroups * 256].
- * Errors: MXFP4_EINVAL (null pointer, size or count out of range),
- * MXFP4_EALIGN (operands, src, dst not 16-byte aligned, out not 4-byte
- * aligned), MXFP4_EDEVICE, MXFP4_ELAUNCH.
- */
-int mxfp4_probe_mfma(const void* operands, int64_t iters, int64_t workgroups, float* out, hipStream_t stream);
-
-int mxfp4_probe_stream(const void* src, int64_t src_bytes, void* dst, int writes_per_32, int64_t workgroups,
-                       unsigned* out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

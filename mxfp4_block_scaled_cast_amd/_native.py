@@ -19,8 +19,13 @@ class OperandLayout(ctypes.Structure):
                 ("scale_k_tiles", _i64)]
 
 
+class Layout(ctypes.Structure):
+    _fields_ = [("rows", _i64), ("cols", _i64), ("padded_rows", _i64), ("row", OperandLayout), ("col", OperandLayout)]
+
+
 SIGNATURES = [
     ("mxfp4_operand_layout_of", _i32, [_i64, _i64, ctypes.POINTER(OperandLayout)]),
+    ("mxfp4_layout", _i32, [_i64, _i64, ctypes.POINTER(Layout)]),
     ("mxfp4_status_string", ctypes.c_char_p, [_i32]),
     ("mxfp4_cast", _i32, [_p, _i64, _i64, _i64, _p, _p, _p]),
     ("mxfp4_cast_dual", _i32, [_p, _i64, _i64, _i64, _p, _p, _p, _p, _p]),
@@ -44,8 +49,6 @@ SIGNATURES = [
     ("gemm_fp4_bf16_workspace_bytes_ex", _sz, [_i64, _i64, _i64, ctypes.c_uint]),
     ("mxfp4_silu_mul_cast", _i32, [_p, _i64, _i64, _i64, _p, _p, _p, _p, _i32, _p, _p]),
     ("mxfp4_rmsnorm_cast", _i32, [_p, _p, _p, ctypes.c_float, _i64, _i64, _p, _p, _p, _p, _i32, _p, _p, _p, _p]),
-    ("mxfp4_probe_mfma", _i32, [_p, _i64, _i64, _p, _p]),
-    ("mxfp4_probe_stream", _i32, [_p, _i64, _p, _i32, _i64, _p, _p]),
 ]
 
 STEP_TRAINING, STEP_HADAMARD_GRAD, STEP_QUANTIZED_W, STEP_FP8_WGRAD = 1, 2, 4, 8
@@ -86,6 +89,13 @@ def status_string(status):
 def check(status, where):
     if status != 0:
         raise Mxfp4Error(status, where)
+
+
+def layout(rows, cols):
+    """Sizes of both copies (row copy, column copy) of a cast bf16 matrix [rows, cols]."""
+    out = Layout()
+    check(lib().mxfp4_layout(int(rows), int(cols), ctypes.byref(out)), "mxfp4_layout")
+    return out
 
 
 def operand_layout(rows, k, fmt=4):

@@ -43,10 +43,6 @@ extern "C" hipError_t mx_launch_cast_dual_pair(const void* x0, int64_t R0, int64
                                                void* s_row0, void* q_col0, void* s_col0, const void* x1, int64_t R1,
                                                int64_t C1, int64_t ldx1, void* q_row1, void* s_row1, void* q_col1,
                                                void* s_col1, hipStream_t stream);
-extern "C" hipError_t mx_launch_probe_mfma(const void* ops, int64_t iters, int64_t workgroups, float* out,
-                                           hipStream_t stream);
-extern "C" hipError_t mx_launch_probe_stream(const void* src, int64_t src_bytes, void* dst, int writes_per_32,
-                                             int64_t workgroups, unsigned* out, hipStream_t stream);
 
 namespace {
 
@@ -73,6 +69,11 @@ int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 // Largest element count / byte count the kernels index with 64-bit offsets
 // but 32-bit tile counts and row indices.
 constexpr int64_t kMaxDim = 0x7FFFFFFF;
+
+// Longest contraction of a GEMM: the tiled kernels address a wave's operand
+// loads with 32-bit lane offsets of up to 15 code-tile rows of K/2 bytes
+// (MXFP4) or K bytes (MXFP8) each, which stay below 2^31 for K <= 2^23.
+constexpr int64_t kMaxK = (int64_t)1 << 23;
 
 struct OperandSizes {
     int64_t q, s;
@@ -116,13 +117,13 @@ int validate_cast_dual(const void* x, int64_t rows, int64_t cols, int64_t ldx, c
 int validate_gemm(const void* aq, const void* as, const void* bq, const void* bs, int64_t M, int64_t N, int64_t K,
                   const void* out, int64_t ldo) {
     if (M < 0 || N < 0 || K < 0 || K % 32 != 0) return MXFP4_EINVAL;
-    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return MXFP4_ERANGE;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxK) return MXFP4_ERANGE;
     if (M == 0 || N == 0) return MXFP4_OK;
     if (!out || ldo < N) return MXFP4_EINVAL;
     if ((reinterpret_cast<uintptr_t>(out) & 1u) != 0) return MXFP4_EALIGN;
     if (K == 0) return MXFP4_OK;
     if (!aq || !as || !bq || !bs) return MXFP4_EINVAL;
-    if (!aligned16(aq) || !aligned16(bq)) return MXFP4_EALIGN;
+    if (!aligned16(aq) || !aligned16(bq) || !aligned16(as) || !aligned16(bs)) return MXFP4_EALIGN;
     return MXFP4_OK;
 }
 
@@ -181,10 +182,13 @@ bool step_flags_ok(unsigned flags) {
     return !((flags & MXFP4_STEP_HADAMARD_GRAD) && (flags & MXFP4_STEP_FP8_WGRAD));
 }
 
+// The forward contracts over K; in training dA contracts over N and dB over
+// ceil(M/32)*32, so those are bounded by the GEMM's contraction limit too.
 int validate_step_sizes(int64_t M, int64_t N, int64_t K, bool training) {
     if (M < 0 || N < 0 || K < 0 || K % 32 != 0) return MXFP4_EINVAL;
     if (training && N % 32 != 0) return MXFP4_EINVAL;
-    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return MXFP4_ERANGE;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxK) return MXFP4_ERANGE;
+    if (training && (N > kMaxK || round_up(M, 32) > kMaxK)) return MXFP4_ERANGE;
     return MXFP4_OK;
 }
 
@@ -217,6 +221,17 @@ int mxfp4_operand_layout_of(int64_t rows, int64_t k, mxfp4_operand_layout* out) 
     out->scale_row_tiles = (rows + 127) / 128;
     out->scale_k_tiles = (k + 255) / 256;
     return MXFP4_OK;
+}
+
+int mxfp4_layout(int64_t rows, int64_t cols, mxfp4_layout_t* out) {
+    if (!out || rows < 0 || cols < 0 || cols % 32 != 0) return MXFP4_EINVAL;
+    if (rows > kMaxDim || cols > kMaxDim) return MXFP4_ERANGE;
+    out->rows = rows;
+    out->cols = cols;
+    out->padded_rows = round_up(rows, 32);
+    int st = mxfp4_operand_layout_of(rows, cols, &out->row);
+    if (st == MXFP4_OK) st = mxfp4_operand_layout_of(cols, out->padded_rows, &out->col);
+    return st;
 }
 
 int mxfp4_cast(const void* x, int64_t rows, int64_t cols, int64_t ldx, void* q, void* s, hipStream_t stream) {
@@ -540,24 +555,3 @@ int gemm_fp4_bf16_bwd_ex(const void* dout, const void* w_col_q, const void* w_co
 }
 
 }  // extern "C"
-
-int mxfp4_probe_mfma(const void* operands, int64_t iters, int64_t workgroups, float* out, hipStream_t stream) {
-    if (!operands || !out || iters < 0 || iters > ((int64_t)1 << 40) || workgroups < 1 || workgroups > 65536)
-        return MXFP4_EINVAL;
-    if (!aligned16(operands) || (reinterpret_cast<uintptr_t>(out) & 3u) != 0) return MXFP4_EALIGN;
-    int st = check_device();
-    if (st != MXFP4_OK) return st;
-    return status_of(mx_launch_probe_mfma(operands, iters, workgroups, out, stream));
-}
-
-int mxfp4_probe_stream(const void* src, int64_t src_bytes, void* dst, int writes_per_32, int64_t workgroups,
-                       unsigned* out, hipStream_t stream) {
-    if (!src || !out || src_bytes < 0 || src_bytes % 16 != 0 || writes_per_32 < 0 || writes_per_32 > 32 ||
-        workgroups < 1 || workgroups > 65536 || (writes_per_32 > 0 && !dst))
-        return MXFP4_EINVAL;
-    if (!aligned16(src) || (dst && !aligned16(dst)) || (reinterpret_cast<uintptr_t>(out) & 3u) != 0)
-        return MXFP4_EALIGN;
-    int st = check_device();
-    if (st != MXFP4_OK) return st;
-    return status_of(mx_launch_probe_stream(src, src_bytes, dst, writes_per_32, workgroups, out, stream));
-}

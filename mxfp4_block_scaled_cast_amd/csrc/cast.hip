@@ -599,35 +599,53 @@ namespace mx {
 // lies too close to the larger one for a bf16 midpoint to fall in between, so
 // its nearest-even bf16 is the exactly rounded sum; h is stored (the residual
 // output, and the input of the cast pass).  The squares of h (exact in double,
-// tiny values included) are accumulated in double; rstd = 1 / sqrt(ss / D +
-// eps) in double.
-__global__ __launch_bounds__(256) void rms_stats_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ res,
-                                                        uint16_t* __restrict__ h_out, int64_t R, int64_t D, float eps,
+// tiny values included) are accumulated in double, chunk by chunk in column
+// order; rstd = 1 / sqrt(ss / D + eps) in double.
+//
+// h_out may be x or res itself (an in-place residual update), so x, res and
+// h_out are not declared __restrict__.  The row is processed in groups of
+// kStatChunks 16-byte chunks per lane: all loads of a group are issued before
+// any of its stores (several loads in flight per wave), and a store only
+// overwrites a chunk that this lane has already read from both inputs.
+constexpr int kStatChunks = 8;
+
+__global__ __launch_bounds__(256) void rms_stats_kernel(const uint16_t* x, const uint16_t* res, uint16_t* h_out,
+                                                        int64_t R, int64_t D, float eps,
                                                         double* __restrict__ rstd) {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= R) return;
     const uint16_t* xr = x + row * D;
+    const uint16_t* rr = res ? res + row * D : nullptr;
+    uint16_t* hr = res ? h_out + row * D : nullptr;
     double ss = 0.0;
-    // unrolled so that several 16-byte loads of the row are in flight at once
-#pragma unroll 8
-    for (int64_t c = lane * 8; c < D; c += 512) {
-        u32x4 h = *reinterpret_cast<const u32x4*>(xr + c);
-        if (res) {
-            const u32x4 r = *reinterpret_cast<const u32x4*>(res + row * D + c);
-#define MX_ADD(F) h.F = f32x2_to_bf16x2_rne(bf16_lo(h.F) + bf16_lo(r.F), bf16_hi(h.F) + bf16_hi(r.F));
-            MX_ADD(x) MX_ADD(y) MX_ADD(z) MX_ADD(w)
-#undef MX_ADD
-            *reinterpret_cast<u32x4*>(h_out + row * D + c) = h;
+    for (int64_t c0 = lane * 8; c0 < D; c0 += 512 * kStatChunks) {
+        u32x4 h[kStatChunks], r[kStatChunks];
+#pragma unroll
+        for (int g = 0; g < kStatChunks; ++g) {
+            const int64_t c = c0 + g * 512;
+            h[g] = c < D ? *reinterpret_cast<const u32x4*>(xr + c) : u32x4{0u, 0u, 0u, 0u};
+            r[g] = (rr && c < D) ? *reinterpret_cast<const u32x4*>(rr + c) : u32x4{0u, 0u, 0u, 0u};
         }
+#pragma unroll
+        for (int g = 0; g < kStatChunks; ++g) {
+            const int64_t c = c0 + g * 512;
+            if (c >= D) break;
+            if (rr) {
+#define MX_ADD(F) h[g].F = f32x2_to_bf16x2_rne(bf16_lo(h[g].F) + bf16_lo(r[g].F), bf16_hi(h[g].F) + bf16_hi(r[g].F));
+                MX_ADD(x) MX_ADD(y) MX_ADD(z) MX_ADD(w)
+#undef MX_ADD
+                *reinterpret_cast<u32x4*>(hr + c) = h[g];
+            }
 #define MX_SQ(F)                                                  \
     {                                                             \
-        const double lo = bf16_lo(h.F), hi = bf16_hi(h.F);        \
+        const double lo = bf16_lo(h[g].F), hi = bf16_hi(h[g].F);  \
         ss = __builtin_fma(lo, lo, ss);                           \
         ss = __builtin_fma(hi, hi, ss);                           \
     }
-        MX_SQ(x) MX_SQ(y) MX_SQ(z) MX_SQ(w)
+            MX_SQ(x) MX_SQ(y) MX_SQ(z) MX_SQ(w)
 #undef MX_SQ
+        }
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);

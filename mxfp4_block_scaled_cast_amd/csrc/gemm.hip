@@ -20,91 +20,13 @@
 // swizzle are shared; lane half h supplies K elements 16h .. 16h+15 and
 // 32+16h .. 47+16h of the step (two 16-byte pieces), while the scale of K
 // block b still comes from lane half b % 2.
-#include <stdlib.h>
-
 #include <algorithm>
 #include <type_traits>
 
 #include "mx_device.h"
 #include "mx_host.h"
 
-// MXFP4_GEMM_PERSIST=0 disables the persistent kernel (comparison aid).
-static int getenv_persist() {
-    static const int v = [] {
-        const char* e = getenv("MXFP4_GEMM_PERSIST");
-        return e && e[0] == '0' ? 0 : 1;
-    }();
-    return v;
-}
-
-// MXFP4_GEMM_DIRECT=1 forces the untiled kernel (testing aid).
-static int getenv_direct() {
-    static const int v = [] {
-        const char* e = getenv("MXFP4_GEMM_DIRECT");
-        return e && e[0] == '1' ? 1 : 0;
-    }();
-    return v;
-}
-
 namespace mx {
-
-// Reference-shaped kernel: each wave computes a 32x32 output tile reading its
-// operands straight from global memory (no LDS), one 64-wide K step at a
-// time.  Only used when MXFP4_GEMM_DIRECT=1 (a cross-check of the others).
-template <int FMT>
-__global__ __launch_bounds__(256) void gemm_direct_kernel(const uint8_t* __restrict__ aq,
-                                                          const uint8_t* __restrict__ as,
-                                                          const uint8_t* __restrict__ bq,
-                                                          const uint8_t* __restrict__ bs, int M, int N, int K,
-                                                          uint16_t* __restrict__ out, int64_t ldo) {
-    const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
-    const int m0 = blockIdx.y * 64 + (w >> 1) * 32;
-    const int n0 = blockIdx.x * 64 + (w & 1) * 32;
-    const int ra = m0 + (lane & 31);
-    const int rb = n0 + (lane & 31);
-    const int half = lane >> 5;
-    const int64_t kt128 = (K + 127) >> 7, kt64 = (K + 63) >> 6, kt256 = (K + 255) >> 8;
-    constexpr int CODE = FMT == 8 ? 0 : 4;  // MFMA format code: E4M3 or E2M1
-
-    f32x16 acc = {};
-    for (int k0 = 0; k0 < K; k0 += 64) {
-        const int kk = k0 + half * 32;
-        v8i a = {}, b = {};
-        int sa = 0, sb = 0;
-        if (kk < K) {
-            // FP8 lane operand: K k0+16h .. +15 and k0+32+16h .. +15 (the layout pads to 64)
-            if (ra < M) {
-                if constexpr (FMT == 8) {
-                    const uint8_t* p = aq + code8_offset(ra, k0 + half * 16, kt64);
-                    a = as_operand8(*reinterpret_cast<const u32x4*>(p), *reinterpret_cast<const u32x4*>(p + 32));
-                } else {
-                    a = as_operand(*reinterpret_cast<const u32x4*>(aq + code_offset(ra, kk, kt128)));
-                }
-                sa = as[scale_offset(ra, kk >> 5, kt256)];
-            }
-            if (rb < N) {
-                if constexpr (FMT == 8) {
-                    const uint8_t* p = bq + code8_offset(rb, k0 + half * 16, kt64);
-                    b = as_operand8(*reinterpret_cast<const u32x4*>(p), *reinterpret_cast<const u32x4*>(p + 32));
-                } else {
-                    b = as_operand(*reinterpret_cast<const u32x4*>(bq + code_offset(rb, kk, kt128)));
-                }
-                sb = bs[scale_offset(rb, kk >> 5, kt256)];
-            }
-        }
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, CODE, CODE, 0, sa, 0, sb);
-    }
-    const int n = n0 + (lane & 31);
-    if (n < N) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int m = m0 + (i >> 2) * 8 + half * 4 + (i & 3);
-            if (m < M) out[(int64_t)m * ldo + n] = f32_to_bf16_rne(acc[i]);
-        }
-    }
-}
-
 
 // ---------------------------------------------------------------------------
 // Skinny kernel, for outputs too small to fill the chip with 256 x 256 tiles
@@ -1037,13 +959,6 @@ namespace mx {
 template <int FMT>
 static hipError_t launch_gemm(const uint8_t* a8, const uint8_t* as8, const uint8_t* b8, const uint8_t* bs8, int64_t M,
                               int64_t N, int64_t K, uint16_t* o16, int64_t ldo, hipStream_t stream) {
-    if (getenv_direct() != 0) {
-        if ((M + 63) / 64 > 65535 || (N + 63) / 64 > 0x7FFFFFFF) return hipErrorInvalidValue;
-        const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64)), block(256);
-        hipLaunchKernelGGL(gemm_direct_kernel<FMT>, grid, block, 0, stream, a8, as8, b8, bs8, (int)M, (int)N, (int)K,
-                           o16, ldo);
-        return hipGetLastError();
-    }
     const int64_t tiles_m = (M + PBM - 1) / PBM, tiles_n = (N + PBN - 1) / PBN;
     // 256 x 256 tiles need both sides >= 128 and enough tiles to fill half the CUs
     const bool tiled = K > 0 && M >= 128 && N >= 128 && tiles_m * tiles_n * 2 >= num_cus();
@@ -1057,7 +972,7 @@ static hipError_t launch_gemm(const uint8_t* a8, const uint8_t* as8, const uint8
     // persistent kernel: needs 16-byte aligned output rows, N % 8 == 0, and a tile's output
     // bytes (256 rows) addressable by a 31-bit buffer offset
     const bool persist = (reinterpret_cast<uintptr_t>(o16) & 15u) == 0 && (ldo & 7) == 0 && (N & 7) == 0 &&
-                         (int64_t)PBM * ldo * 2 < 0x7FFFFFF0ll && getenv_persist() != 0;
+                         (int64_t)PBM * ldo * 2 < 0x7FFFFFF0ll;
     if (persist) {
         // as many rounds as the tiles need on all CUs, spread evenly: every workgroup
         // gets the same number of tiles (896 tiles run as 224 x 4, not 256 x 3.5)

@@ -18,6 +18,7 @@ With ``columnwise=False`` only the row copy is made (inference).  With
 backward contractions carry the block Walsh-Hadamard transform
 (``cast_hadamard``).
 """
+import weakref
 from dataclasses import dataclass
 from typing import Dict, Optional, Tuple
 
@@ -71,13 +72,20 @@ def _key(w: torch.Tensor, q: MXFP4Quantizer) -> Tuple:
 class WeightWorkspace:
     """Quantized weights by name, re-quantized only when the weight changed.
 
-    A cached entry is reused while the tensor has the same storage, shape,
-    strides and in-place version (``Tensor._version`` counts in-place updates
-    such as an optimizer step) and the quantizer is the same.
+    A cached entry is reused only for the same tensor object (held by a weak
+    reference, so a new tensor that the allocator places at a freed weight's
+    address never matches) with the same storage, shape, strides and in-place
+    version (``Tensor._version`` counts in-place updates such as an optimizer
+    step), and the same quantizer.
+
+    Updates that bypass the version counter are not seen: writing through
+    ``w.data`` (``w.data.copy_(...)``, ``w.data.add_(...)``) or through another
+    tensor that aliases w's memory.  After such an update call
+    ``invalidate(cache_name)``.
     """
 
     def __init__(self):
-        self._cache: Dict[str, Tuple[Tuple, Mxfp4Tensor]] = {}
+        self._cache: Dict[str, Tuple[Tuple, "weakref.ref", Mxfp4Tensor]] = {}
         self.hits = 0
         self.misses = 0
 
@@ -86,12 +94,12 @@ class WeightWorkspace:
         name = cache_name if cache_name is not None else "@%x" % w.data_ptr()
         key = _key(w, quantizer)
         hit = self._cache.get(name)
-        if hit is not None and hit[0] == key:
+        if hit is not None and hit[0] == key and hit[1]() is w:
             self.hits += 1
-            return hit[1]
+            return hit[2]
         self.misses += 1
         q = quantizer.quantize(w)
-        self._cache[name] = (key, q)
+        self._cache[name] = (key, weakref.ref(w), q)
         return q
 
     def invalidate(self, cache_name: Optional[str] = None):

@@ -102,3 +102,49 @@ def fp8_truncation_bound(qa, sa, qb, sb, chunk_rows=64):
         emax = (ea[m0:m1, None] + eb[None]).amax(-1)                  # [m, N, G] int16
         out[m0:m1] = torch.ldexp(torch.ones((), dtype=torch.float64), (emax - 10).to(torch.float64)).sum(-1).numpy()
     return out
+
+
+# ---- whole-buffer images of the device layout -------------------------------------------
+# The tiled MX layout is a pure tiling of the row-major arrays, so the bytes a device copy must
+# hold (padding included) come from the oracle's row-major output by padding and one transpose:
+# codes (r//16, k//128, r%16, byte of the 64-byte tile row), scales (r//128, b//8, (r//32)%4,
+# r%32, b%2, (b%8)//2).  tests/test_layout_images.py pins these against the index maps.
+
+def codes_image(q_rm, rows, k):
+    """Device bytes of an MXFP4 code buffer from row-major q [rows, k/2] (zeros at padding)."""
+    kt, r16 = -(-k // 128), -(-rows // 16)
+    buf = np.zeros((r16 * 16, kt * 64), np.uint8)
+    buf[:rows, :k // 2] = q_rm
+    return buf.reshape(r16, 16, kt, 64).transpose(0, 2, 1, 3).ravel()
+
+
+def codes8_image(q_rm, rows, k):
+    """Device bytes of an MXFP8 code buffer from row-major q [rows, k]."""
+    kt, r16 = -(-k // 64), -(-rows // 16)
+    buf = np.zeros((r16 * 16, kt * 64), np.uint8)
+    buf[:rows, :k] = q_rm
+    return buf.reshape(r16, 16, kt, 64).transpose(0, 2, 1, 3).ravel()
+
+
+def scales_image(s_rm, rows, k):
+    """Device bytes of a scale buffer from row-major s [rows, k/32]."""
+    kt2, r128 = -(-k // 256), -(-rows // 128)
+    buf = np.zeros((r128 * 128, kt2 * 8), np.uint8)
+    buf[:rows, :k // 32] = s_rm
+    return buf.reshape(r128, 4, 32, kt2, 4, 2).transpose(0, 3, 1, 2, 5, 4).ravel()
+
+
+def assert_operand_equal(op, q_rm, s_rm, what):
+    """Every byte of a device MX operand (codes, scales, padding) equals the image of the
+    oracle's row-major (q, s)."""
+    img = codes8_image if getattr(op, "fmt", 4) == 8 else codes_image
+    for part, dev, expect in (("scales", op.s, scales_image(s_rm, op.rows, op.k)),
+                              ("codes", op.q, img(q_rm, op.rows, op.k))):
+        got = dev.cpu().numpy()
+        if got.size != expect.size:
+            raise AssertionError("%s %s: device buffer holds %d bytes, layout needs %d"
+                                 % (what, part, got.size, expect.size))
+        if not np.array_equal(got, expect):
+            bad = np.flatnonzero(got != expect)
+            raise AssertionError("%s %s: %d of %d bytes differ, first at byte %d (got %#x, expected %#x)"
+                                 % (what, part, bad.size, got.size, bad[0], got[bad[0]], expect[bad[0]]))

@@ -301,18 +301,77 @@ def test_fused_producer_cast_argument_validation():
     assert call(rows=0) == 0
 
 
-def test_probe_argument_validation():
+def test_bench_probe_argument_validation():
+    # the bench's probes are a library of their own (bench_probes.hip), not part of the MXFP4 ABI
+    import bench_probes
+    if not os.path.exists(bench_probes.LIB):
+        bench_probes.build()
+    L = bench_probes.lib()
+    assert L.probe_mfma(None, 1, 1, FAKE, None) == -1                 # null operands
+    assert L.probe_mfma(FAKE, -1, 1, FAKE, None) == -1                # negative iters
+    assert L.probe_mfma(FAKE, (1 << 24) + 1, 1, FAKE, None) == -1     # iteration cap
+    assert L.probe_mfma(FAKE, 1, 0, FAKE, None) == -1                 # no workgroups
+    assert L.probe_mfma(FAKE, 1, 65537, FAKE, None) == -1
+    assert L.probe_mfma(FAKE + 8, 1, 1, FAKE, None) == -2             # misaligned operands
+    assert L.probe_mfma(FAKE, 1, 1, FAKE + 2, None) == -2             # misaligned out
+    assert L.probe_stream(FAKE, 24, None, 0, 1, FAKE, None) == -1     # bytes % 16
+    assert L.probe_stream(FAKE, 32, None, 17, 1, FAKE, None) == -1    # writes without dst
+    assert L.probe_stream(FAKE, 32, FAKE, 33, 1, FAKE, None) == -1    # writes_per_32 > 32
+    assert L.probe_stream(FAKE, 32, FAKE + 4, 17, 1, FAKE, None) == -2
+    if _no_gpu():
+        # valid arguments: the host has no gfx950, so the call fails on the device check, launching nothing
+        assert L.probe_mfma(FAKE, 1, 1, FAKE, None) == -3
+        assert L.probe_stream(FAKE, 32, None, 0, 1, FAKE, None) == -3
+
+
+def test_library_exports_no_measurement_probes():
+    assert not any("probe" in n for n in declared_functions())
     L = N.lib()
-    assert L.mxfp4_probe_mfma(None, 1, 1, FAKE, None) == -1                 # null operands
-    assert L.mxfp4_probe_mfma(FAKE, -1, 1, FAKE, None) == -1                # negative iters
-    assert L.mxfp4_probe_mfma(FAKE, 1, 0, FAKE, None) == -1                 # no workgroups
-    assert L.mxfp4_probe_mfma(FAKE, 1, 65537, FAKE, None) == -1
-    assert L.mxfp4_probe_mfma(FAKE + 8, 1, 1, FAKE, None) == -2             # misaligned operands
-    assert L.mxfp4_probe_mfma(FAKE, 1, 1, FAKE + 2, None) == -2             # misaligned out
-    assert L.mxfp4_probe_stream(FAKE, 24, None, 0, 1, FAKE, None) == -1     # bytes % 16
-    assert L.mxfp4_probe_stream(FAKE, 32, None, 17, 1, FAKE, None) == -1    # writes without dst
-    assert L.mxfp4_probe_stream(FAKE, 32, FAKE, 33, 1, FAKE, None) == -1    # writes_per_32 > 32
-    assert L.mxfp4_probe_stream(FAKE, 32, FAKE + 4, 17, 1, FAKE, None) == -2
-    # valid arguments: the host has no gfx950, so the call fails on the device check, launching nothing
-    assert L.mxfp4_probe_mfma(FAKE, 1, 1, FAKE, None) == -3
-    assert L.mxfp4_probe_stream(FAKE, 32, None, 0, 1, FAKE, None) == -3
+    for name in ("mxfp4_probe_mfma", "mxfp4_probe_stream", "probe_mfma", "probe_stream"):
+        assert not hasattr(L, name), name
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 32), (17, 96), (8192, 4096), (128256, 14336), (0, 64), (5, 0)])
+def test_both_copies_layout(rows, cols):
+    L = N.layout(rows, cols)
+    rp = -(-rows // 32) * 32
+    assert (L.rows, L.cols, L.padded_rows) == (rows, cols, rp)
+    assert (L.row.rows, L.row.k) == (rows, cols) and (L.col.rows, L.col.k) == (cols, rp)
+    assert L.row.q_bytes == layout.code_bytes(rows, cols) and L.row.s_bytes == layout.scale_bytes(rows, cols)
+    assert L.col.q_bytes == layout.code_bytes(cols, rp) and L.col.s_bytes == layout.scale_bytes(cols, rp)
+
+
+def test_both_copies_layout_rejects():
+    out = N.Layout()
+    f = N.lib().mxfp4_layout
+    assert f(4, 33, ctypes.byref(out)) == -1
+    assert f(-1, 32, ctypes.byref(out)) == -1
+    assert f(4, 32, None) == -1
+    assert f(1 << 31, 32, ctypes.byref(out)) == -5
+
+
+def test_contraction_limit_of_the_tiled_kernels():
+    # lane offsets of the tiled kernels' operand loads are 32-bit: K <= 2^23
+    L = N.lib()
+    kmax = 1 << 23
+    for g in (L.mxfp4_gemm_nt, L.mxfp4_gemm_nn, L.mxfp8_gemm_nt):
+        assert g(FAKE, FAKE, FAKE, FAKE, 4, 4, kmax + 32, FAKE, 4, None) == -5
+        assert g(FAKE, FAKE, FAKE, FAKE, 0, 4, kmax + 32, None, 4, None) == -5   # checked before the no-op
+    if _no_gpu():
+        assert L.mxfp4_gemm_nt(FAKE, FAKE, FAKE, FAKE, 4, 4, kmax, FAKE, 4, None) == -3  # in range
+    # the step: the forward contracts over K, dA over N, dB over ceil(M/32)*32
+    assert L.gemm_fp4_bf16_workspace_bytes(64, 64, kmax + 32, 0) == 0
+    assert L.gemm_fp4_bf16_workspace_bytes(64, kmax + 32, 64, 1) == 0
+    assert L.gemm_fp4_bf16_workspace_bytes(kmax + 1, 64, 64, 1) == 0
+    assert L.gemm_fp4_bf16_workspace_bytes(kmax, 64, 64, 1) > 0
+    assert L.gemm_fp4_bf16_workspace_bytes(kmax + 1, 64, 64, 0) > 0          # inference: M is not contracted
+    assert L.gemm_fp4_bf16_fwd(FAKE, FAKE, 64, 64, kmax + 32, FAKE, FAKE, 1 << 40, 0, None) == -5
+    assert L.gemm_fp4_bf16_bwd(FAKE, kmax + 1, 64, 64, FAKE, 1 << 40, FAKE, FAKE, None) == -5
+
+
+def test_gemm_scale_pointers_must_be_aligned():
+    # the tiled kernels move scale tiles with 16-byte loads
+    L = N.lib()
+    for g in (L.mxfp4_gemm_nt, L.mxfp8_gemm_nt):
+        assert g(FAKE, FAKE + 4, FAKE, FAKE, 4, 4, 32, FAKE, 4, None) == -2
+        assert g(FAKE, FAKE, FAKE, FAKE + 8, 4, 4, 32, FAKE, 4, None) == -2

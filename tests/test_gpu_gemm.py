@@ -180,3 +180,39 @@ def test_output_leading_dimension():
     got = bf16_to_f64(big)
     assert_gemm_close(got[:, 10:10 + N], ref, absref, "ldo")
     assert np.all(got[:, :10] == -1.0) and np.all(got[:, 10 + N:] == -1.0)
+
+
+def test_persistent_multi_round_whole_output():
+    # 2048 x 20480: 8 x 80 = 640 tiles of 256 x 256, three rounds of the balanced persistent grid
+    # (214 workgroups, 3 tiles each but the last ones), tile rows grouped by 4 (tiles_m = 8 >
+    # group_m), K = 1024 (two trips per tile); every output checked
+    M, N, K = 2048, 20480, 1024
+    a = W.normal_bf16((M, K), 1.0, 71)
+    b = W.normal_bf16((N, K), 0.3, 72)
+    got = gpu_nt(a, b, "persistent 3 rounds")
+    ref, absref = oracle_nt(a, b)
+    assert_gemm_close(got, ref, absref, "persistent %dx%dx%d" % (M, N, K))
+
+
+# Tiled launches (128 tiles of 256 x 256) writing into a wider output buffer: ldo % 8 == 0 and a
+# 16-byte aligned start (persistent kernel), ldo % 8 == 4 (pipelined kernel, 8-byte stores), and a
+# start 2 bytes past 8-byte alignment (pipelined kernel, 2-byte stores); the columns around the
+# window must stay untouched.
+@pytest.mark.parametrize("extra,offset,K", [(64, 0, 512), (64, 8, 1536), (4, 0, 512), (64, 1, 512), (4, 1, 1024)],
+                         ids=["persist-ldo", "persist-ldo-offset", "pipe-vec-ldo", "pipe-unaligned",
+                              "pipe-unaligned-ldo4"])
+def test_tiled_output_leading_dimension(extra, offset, K):
+    M, N = 2048, 4096
+    a = W.normal_bf16((M, K), 1.0, 81 + extra + offset)
+    b = W.normal_bf16((N, K), 1.0, 82 + extra + offset)
+    ldo = N + extra
+    big = torch.full((M, ldo + offset), -1.0, dtype=torch.bfloat16, device="cuda:0")
+    view = big.view(-1)[offset:offset + M * ldo].view(M, ldo)[:, :N]
+    say("gemm ldo=%d offset=%d K=%d" % (ldo, offset, K))
+    mx.gemm_nt(mx.cast(to_device(a)), mx.cast(to_device(b)), out=view)
+    torch.cuda.synchronize()
+    ref, absref = oracle_nt(a, b)
+    flat = bf16_to_f64(big).reshape(-1)
+    win = flat[offset:offset + M * ldo].reshape(M, ldo)
+    assert_gemm_close(win[:, :N], ref, absref, "ldo %d offset %d" % (ldo, offset))
+    assert np.all(win[:, N:] == -1.0) and np.all(flat[:offset] == -1.0) and np.all(flat[offset + M * ldo:] == -1.0)

@@ -1,10 +1,11 @@
-"""The measurement probes do what their timings assume: the stream probe reads
-every chunk and writes the selected ones where stated; the MFMA probe runs."""
+"""The bench's measurement probes (bench_probes.hip, a library of their own) do what their
+timings assume: the stream probe reads every chunk and writes the selected ones where stated;
+the MFMA probe runs."""
 import numpy as np
 import pytest
 import torch
 
-from mxfp4_block_scaled_cast_amd import _native as N
+import bench_probes as N
 from gpu_util import say
 
 pytestmark = pytest.mark.gpu
@@ -20,7 +21,7 @@ def test_stream_probe_writes_the_selected_chunks(w):
     dst = torch.full((dst_chunks * 4,), -1, dtype=torch.int32, device=dev)
     out = torch.empty(3 * 256, dtype=torch.int32, device=dev)
     sp = torch.cuda.current_stream(dev).cuda_stream
-    N.check(N.lib().mxfp4_probe_stream(src.data_ptr(), chunks * 16, dst.data_ptr(), w, 3, out.data_ptr(), sp), "probe")
+    N.check(N.lib().probe_stream(src.data_ptr(), chunks * 16, dst.data_ptr(), w, 3, out.data_ptr(), sp), "probe")
     torch.cuda.synchronize()
     s = src.view(-1, 4).cpu().numpy()
     d = dst.view(-1, 4).cpu().numpy()
@@ -41,7 +42,7 @@ def test_mfma_probe_accumulates():
     ops = torch.full((wg * 256 * 32,), 0x22222222, dtype=torch.int32, device=dev)
     out = torch.empty(wg * 256, dtype=torch.float32, device=dev)
     sp = torch.cuda.current_stream(dev).cuda_stream
-    N.check(N.lib().mxfp4_probe_mfma(ops.data_ptr(), 3, wg, out.data_ptr(), sp), "probe")
+    N.check(N.lib().probe_mfma(ops.data_ptr(), 3, wg, out.data_ptr(), sp), "probe")
     torch.cuda.synchronize()
     # a lane holds 16 accumulators of each of its 16 blocks: 256 values of 3 * 64
     assert torch.all(out == 256 * 3 * 64.0)

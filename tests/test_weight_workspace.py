@@ -45,6 +45,42 @@ def test_other_tensor_or_view_requantizes():
     assert CountingQuantizer.calls == 3
 
 
+def test_other_tensor_object_requantizes():
+    # a view with the same storage, shape, strides and version counter is another tensor
+    # object: it may not reuse the entry (the allocator can also hand a new tensor a freed
+    # weight's address with the same version)
+    q, ws = fresh()
+    w = torch.zeros(64, 32, dtype=torch.bfloat16)
+    ws.get_or_quantize(w, q, cache_name="w")
+    alias = w.view(64, 32)
+    assert alias.data_ptr() == w.data_ptr() and alias._version == w._version
+    ws.get_or_quantize(alias, q, cache_name="w")
+    assert CountingQuantizer.calls == 2
+
+
+def test_dead_weight_entry_never_matches():
+    q, ws = fresh()
+    w = torch.zeros(64, 32, dtype=torch.bfloat16)
+    ws.get_or_quantize(w, q, cache_name="w")
+    del w
+    w2 = torch.zeros(64, 32, dtype=torch.bfloat16)
+    ws.get_or_quantize(w2, q, cache_name="w")
+    assert CountingQuantizer.calls == 2
+
+
+def test_data_updates_need_invalidate():
+    # w.data has its own version counter: the documented case for invalidate()
+    q, ws = fresh()
+    w = torch.zeros(64, 32, dtype=torch.bfloat16)
+    ws.get_or_quantize(w, q, cache_name="w")
+    w.data.add_(1)
+    ws.get_or_quantize(w, q, cache_name="w")
+    assert CountingQuantizer.calls == 1
+    ws.invalidate("w")
+    ws.get_or_quantize(w, q, cache_name="w")
+    assert CountingQuantizer.calls == 2
+
+
 def test_names_and_roles_are_separate_entries():
     q, ws = fresh()
     w = torch.zeros(64, 32, dtype=torch.bfloat16)
