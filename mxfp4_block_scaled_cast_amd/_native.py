@@ -49,9 +49,12 @@ SIGNATURES = [
     ("gemm_fp4_bf16_workspace_bytes_ex", _sz, [_i64, _i64, _i64, ctypes.c_uint]),
     ("mxfp4_silu_mul_cast", _i32, [_p, _i64, _i64, _i64, _p, _p, _p, _p, _i32, _p, _p]),
     ("mxfp4_rmsnorm_cast", _i32, [_p, _p, _p, ctypes.c_float, _i64, _i64, _p, _p, _p, _p, _i32, _p, _p, _p, _p]),
+    ("gemm_fp4_bf16_fwd_qw_noalloc", _i32, [_p, _p, _p, _i64, _i64, _i64, _p, _p]),
 ]
 
 STEP_TRAINING, STEP_HADAMARD_GRAD, STEP_QUANTIZED_W, STEP_FP8_WGRAD = 1, 2, 4, 8
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MXFP4_NOALLOC_SCRATCH_BYTES
 
 STATUS = {0: "MXFP4_OK", -1: "MXFP4_EINVAL", -2: "MXFP4_EALIGN", -3: "MXFP4_EDEVICE",
           -4: "MXFP4_ELAUNCH", -5: "MXFP4_ERANGE", -6: "MXFP4_ESPACE"}

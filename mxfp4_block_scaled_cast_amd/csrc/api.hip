@@ -18,6 +18,8 @@
 #include <mutex>
 #include <string.h>
 
+#include <hip/hip_runtime.h>
+
 #include "../../include/mxfp4.h"
 
 extern "C" hipError_t mx_launch_cast(const void* x, int64_t R, int64_t C, int64_t ldx, void* q_row, void* s_row,
@@ -555,3 +557,54 @@ int gemm_fp4_bf16_bwd_ex(const void* dout, const void* w_col_q, const void* w_co
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free inference forward with a pre-quantized weight, for callers
+// that cannot allocate device memory (code under HIP graph capture, tight
+// serving loops, harnesses that forbid hipMalloc).  It is
+// gemm_fp4_bf16_fwd_qw(training = 0) with the workspace -- A's row copy, the
+// only scratch that forward needs -- taken from a library-owned device array
+// instead of a caller buffer.
+//
+// `scratch` is a file-scope device array; each GPU holds its own copy until
+// the process ends.  Host code never uses its name as an address: the device
+// address comes from hipGetSymbolAddress, once per device with that device
+// current, and is kept in g_scratch_ptr.  Every call on a device shares the
+// array (calls that overlap on one device race).  Nothing in it must start at
+// zero: the cast writes every byte of the row copy it uses, padding included.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = MXFP4_NOALLOC_SCRATCH_BYTES;
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of this device's scratch array, or nullptr if the runtime could not provide it.
+void* scratch_ptr(int dev) {
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) p = nullptr;
+        g_scratch_ptr[dev] = p;
+    });
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" int gemm_fp4_bf16_fwd_qw_noalloc(const void* a, const void* w_row_q, const void* w_row_s, int64_t M,
+                                            int64_t N, int64_t K, void* out, hipStream_t stream) {
+    int st = validate_step_sizes(M, N, K, false);
+    if (st != MXFP4_OK) return st;
+    if (M == 0 || N == 0) return MXFP4_OK;
+    // A's row copy must fit the scratch array
+    if (workspace_layout(M, N, K, false, false).total > (int64_t)kScratchBytes) return MXFP4_ERANGE;
+    if ((st = check_device()) != MXFP4_OK) return st;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MXFP4_EDEVICE;
+    void* ws = scratch_ptr(dev);
+    if (!ws) return MXFP4_ELAUNCH;
+    return step_fwd(a, false, nullptr, w_row_q, w_row_s, M, N, K, out, ws, kScratchBytes, false, false, false, stream);
+}

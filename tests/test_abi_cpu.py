@@ -375,3 +375,14 @@ def test_gemm_scale_pointers_must_be_aligned():
     for g in (L.mxfp4_gemm_nt, L.mxfp8_gemm_nt):
         assert g(FAKE, FAKE + 4, FAKE, FAKE, 4, 4, 32, FAKE, 4, None) == -2
         assert g(FAKE, FAKE, FAKE, FAKE + 8, 4, 4, 32, FAKE, 4, None) == -2
+
+
+def test_noalloc_forward_rejects_before_any_device_work():
+    L = N.lib()
+    M, K = 16384, 8192  # A's row copy (71 MB) exceeds the 64 MiB scratch array
+    assert L.gemm_fp4_bf16_workspace_bytes_qw(M, 64, K, 0) > N.NOALLOC_SCRATCH_BYTES
+    assert L.gemm_fp4_bf16_fwd_qw_noalloc(FAKE, FAKE, FAKE, M, 64, K, FAKE, None) == -5
+    assert L.gemm_fp4_bf16_fwd_qw_noalloc(FAKE, FAKE, FAKE, 64, 64, 48, FAKE, None) == -1   # K % 32
+    assert L.gemm_fp4_bf16_fwd_qw_noalloc(None, FAKE, FAKE, 0, 64, 64, None, None) == 0    # empty
+    if _no_gpu():
+        assert L.gemm_fp4_bf16_fwd_qw_noalloc(FAKE, FAKE, FAKE, 64, 64, 64, FAKE, None) == -3
