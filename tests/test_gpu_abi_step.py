@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import mxfp4_block_scaled_cast_amd as mx
-from mxfp4_block_scaled_cast_amd import _native as N
+from mxfp4_block_scaled_cast_amd import _native as native
 from mxfp4_block_scaled_cast_amd import workloads as W
 from gpu_util import say, to_device, bf16_to_f64, assert_gemm_close
 
@@ -55,16 +55,16 @@ def stream():
 @pytest.mark.parametrize("M,N,K", SHAPES)
 def test_plain_entry_points_training(M, N, K):
     a, w, g = inputs(M, N, K)
-    L = N.lib()
+    L = native.lib()
     nbytes = L.gemm_fp4_bf16_workspace_bytes(M, N, K, 1)
     assert nbytes > 0
     ws = torch.empty((nbytes,), dtype=torch.uint8, device="cuda:0")
     ad, wd, gd = to_device(a), to_device(w), to_device(g)
     out, da, dw = empty_bf16(M, N), empty_bf16(M, K), empty_bf16(N, K)
     say("gemm_fp4_bf16_fwd/_bwd (C ABI) M=%d N=%d K=%d" % (M, N, K))
-    N.check(L.gemm_fp4_bf16_fwd(ad.data_ptr(), wd.data_ptr(), M, N, K, out.data_ptr(), ws.data_ptr(), nbytes,
+    native.check(L.gemm_fp4_bf16_fwd(ad.data_ptr(), wd.data_ptr(), M, N, K, out.data_ptr(), ws.data_ptr(), nbytes,
                                 1, stream()), "gemm_fp4_bf16_fwd")
-    N.check(L.gemm_fp4_bf16_bwd(gd.data_ptr(), M, N, K, ws.data_ptr(), nbytes, da.data_ptr(), dw.data_ptr(),
+    native.check(L.gemm_fp4_bf16_bwd(gd.data_ptr(), M, N, K, ws.data_ptr(), nbytes, da.data_ptr(), dw.data_ptr(),
                                 stream()), "gemm_fp4_bf16_bwd")
     torch.cuda.synchronize()
     (f, fa), (d, dab), (e, eab) = oracle_step(a, w, g)
@@ -74,9 +74,9 @@ def test_plain_entry_points_training(M, N, K):
     # either gradient alone (the other pointer NULL) gives the same bits
     da2, dw2 = empty_bf16(M, K), empty_bf16(N, K)
     say("gemm_fp4_bf16_bwd dA only, dB only")
-    N.check(L.gemm_fp4_bf16_bwd(gd.data_ptr(), M, N, K, ws.data_ptr(), nbytes, da2.data_ptr(), None, stream()),
+    native.check(L.gemm_fp4_bf16_bwd(gd.data_ptr(), M, N, K, ws.data_ptr(), nbytes, da2.data_ptr(), None, stream()),
             "gemm_fp4_bf16_bwd")
-    N.check(L.gemm_fp4_bf16_bwd(gd.data_ptr(), M, N, K, ws.data_ptr(), nbytes, None, dw2.data_ptr(), stream()),
+    native.check(L.gemm_fp4_bf16_bwd(gd.data_ptr(), M, N, K, ws.data_ptr(), nbytes, None, dw2.data_ptr(), stream()),
             "gemm_fp4_bf16_bwd")
     torch.cuda.synchronize()
     assert torch.equal(da2.view(torch.int16), da.view(torch.int16))
@@ -86,14 +86,14 @@ def test_plain_entry_points_training(M, N, K):
 @pytest.mark.parametrize("M,N,K", [(1, 96, 64), (17, 130, 544), (2048, 4096, 512)])
 def test_plain_forward_inference(M, N, K):
     a, w, _ = inputs(M, N, K)
-    L = N.lib()
+    L = native.lib()
     nbytes = L.gemm_fp4_bf16_workspace_bytes(M, N, K, 0)
     assert nbytes > 0
     ws = torch.empty((nbytes,), dtype=torch.uint8, device="cuda:0")
     out = empty_bf16(M, N)
     ad, wd = to_device(a), to_device(w)
     say("gemm_fp4_bf16_fwd inference (C ABI) M=%d N=%d K=%d" % (M, N, K))
-    N.check(L.gemm_fp4_bf16_fwd(ad.data_ptr(), wd.data_ptr(), M, N, K, out.data_ptr(), ws.data_ptr(), nbytes, 0,
+    native.check(L.gemm_fp4_bf16_fwd(ad.data_ptr(), wd.data_ptr(), M, N, K, out.data_ptr(), ws.data_ptr(), nbytes, 0,
                                 stream()), "gemm_fp4_bf16_fwd")
     torch.cuda.synchronize()
     (f, fa), _, _ = oracle_step(a, w, None)
@@ -103,7 +103,7 @@ def test_plain_forward_inference(M, N, K):
 @pytest.mark.parametrize("M,N,K", SHAPES)
 def test_quantized_weight_entry_points(M, N, K):
     a, w, g = inputs(M, N, K)
-    L = N.lib()
+    L = native.lib()
     Wt = mx.cast_dual(to_device(w))  # W's row + column copies, made once (mxfp4_cast_dual)
     nbytes = L.gemm_fp4_bf16_workspace_bytes_qw(M, N, K, 1)
     assert 0 < nbytes < L.gemm_fp4_bf16_workspace_bytes(M, N, K, 1)
@@ -111,9 +111,9 @@ def test_quantized_weight_entry_points(M, N, K):
     ad, gd = to_device(a), to_device(g)
     out, da, dw = empty_bf16(M, N), empty_bf16(M, K), empty_bf16(N, K)
     say("gemm_fp4_bf16_fwd_qw/_bwd_qw (C ABI) M=%d N=%d K=%d" % (M, N, K))
-    N.check(L.gemm_fp4_bf16_fwd_qw(ad.data_ptr(), Wt.row.q.data_ptr(), Wt.row.s.data_ptr(), M, N, K,
+    native.check(L.gemm_fp4_bf16_fwd_qw(ad.data_ptr(), Wt.row.q.data_ptr(), Wt.row.s.data_ptr(), M, N, K,
                                    out.data_ptr(), ws.data_ptr(), nbytes, 1, stream()), "gemm_fp4_bf16_fwd_qw")
-    N.check(L.gemm_fp4_bf16_bwd_qw(gd.data_ptr(), Wt.col.q.data_ptr(), Wt.col.s.data_ptr(), M, N, K, ws.data_ptr(),
+    native.check(L.gemm_fp4_bf16_bwd_qw(gd.data_ptr(), Wt.col.q.data_ptr(), Wt.col.s.data_ptr(), M, N, K, ws.data_ptr(),
                                    nbytes, da.data_ptr(), dw.data_ptr(), stream()), "gemm_fp4_bf16_bwd_qw")
     torch.cuda.synchronize()
     (f, fa), (d, dab), (e, eab) = oracle_step(a, w, g)
