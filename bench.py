@@ -68,6 +68,8 @@ def parse():
     p.add_argument("--fused-producers", action="store_true",
                    help="A operands made by the fused producers: RMSNorm + cast for gate/up (of the block input), "
                         "SiLU-and-mul + cast for down (of the gate/up output) instead of plain casts")
+    p.add_argument("--headline-only", action="store_true",
+                   help="the default 8B MLP line without the secondary 70B and 8B-attention configs")
     p.add_argument("--no-kernel-events", action="store_true",
                    help="time only the whole step (no per-kernel events)")
     p.add_argument("--ceilings", action="store_true",
@@ -143,9 +145,15 @@ def step_ops(P, L, sp, N, cached_weights=False, hadamard=False, fp8_wgrad=False)
                                          col.q.data_ptr(), col.s.data_ptr(), sp)
 
     def gemm(fn, a, b, out):
+        # MXFP4 products go through the workspace form (a long contraction behind a small output
+        # is split over several workgroups); the same kernels as mxfp4_gemm_nt / _nn otherwise
         M, Nn = a.rows, b.rows
-        return lambda: fn(a.q.data_ptr(), a.s.data_ptr(), b.q.data_ptr(), b.s.data_ptr(), M, Nn, a.k,
-                          out.data_ptr(), Nn, sp)
+        ws = P["gemm_ws"]
+        if a.fmt == 8:
+            return lambda: fn(a.q.data_ptr(), a.s.data_ptr(), b.q.data_ptr(), b.s.data_ptr(), M, Nn, a.k,
+                              out.data_ptr(), Nn, sp)
+        return lambda: L.mxfp4_gemm_nt_ws(a.q.data_ptr(), a.s.data_ptr(), b.q.data_ptr(), b.s.data_ptr(), M, Nn, a.k,
+                                          out.data_ptr(), Nn, ws.data_ptr(), ws.numel(), sp)
 
     M, Nn, K, name = P["M"], P["N"], P["K"], P["name"]
     ops = []
@@ -223,6 +231,8 @@ def alloc_projection(name, M, Nn, K, a, w, g, mx, torch, dev, fp8_wgrad=False):
     P["out"] = torch.empty((M, Nn), dtype=torch.bfloat16, device=dev)
     P["da"] = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
     P["dw"] = torch.empty((Nn, K), dtype=torch.bfloat16, device=dev)
+    # split-contraction scratch shared by the step's three products (run in order on one stream)
+    P["gemm_ws"] = mx.gemm_workspace([(M, Nn, K), (M, K, Nn), (Nn, K, Mp)], dev)
     return P
 
 
@@ -442,7 +452,6 @@ def main():
                          "(--gpus %d, WORLD_SIZE %d requested)\n" % (args.gpus, world))
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import mxfp4_block_scaled_cast_amd as mx
@@ -456,17 +465,41 @@ def main():
     if args.workload == "ragged":
         print(json.dumps(ragged_sweep(args, torch, mx, N, W, L, dev)), flush=True)
         return
-    projections = {"llama8b_mlp": W.LLAMA8B_MLP, "llama8b_attn": W.LLAMA8B_ATTN, "llama70b": W.LLAMA70B}[args.workload]
+    result = measure_workload(args.workload, args, args.steps, args.warmup, args.cpu_seconds, torch, mx, N, W, L,
+                              dev)
+    plain = not (args.cached_weights or args.hadamard_grad or args.fp8_wgrad or args.fused_producers)
+    if args.workload == "llama8b_mlp" and plain and not args.headline_only:
+        # the other per-GPU projection configs, as secondary fields of the same line (fewer steps)
+        for wl in SECONDARY:
+            r = measure_workload(wl, args, min(args.steps, SECONDARY_STEPS), min(args.warmup, SECONDARY_WARMUP),
+                                 min(args.cpu_seconds, SECONDARY_CPU_S), torch, mx, N, W, L, dev)
+            result[wl] = {k: r[k] for k in SECONDARY_KEYS if k in r}
+    print(json.dumps(result), flush=True)
+
+
+SECONDARY = ("llama70b", "llama8b_attn")
+SECONDARY_STEPS, SECONDARY_WARMUP, SECONDARY_CPU_S = 30, 20, 8.0
+SECONDARY_KEYS = ("config", "steps", "warmup", "ms_per_step", "value", "frac_of_fp4_peak", "gemm_tflops",
+                  "gemm_frac_of_fp4_peak", "cast_gbps", "cast_frac_of_hbm", "per_kernel", "roofline", "clock",
+                  "cpu_baseline")
+
+
+def measure_workload(workload, args, steps, warmup, cpu_seconds, torch, mx, N, W, L, dev):
+    """The training step of one projection config: inputs made and resident, `warmup` untimed
+    steps, `steps` timed steps bracketed by two events (the step time), the same steps again
+    with an event after every launch (per-kernel times), the clock over 0.5 s more, and the
+    CPU oracle on a bounded sample.  Returns the result dict; frees the config's buffers."""
+    import numpy as np
+    projections = {"llama8b_mlp": W.LLAMA8B_MLP, "llama8b_attn": W.LLAMA8B_ATTN, "llama70b": W.LLAMA70B}[workload]
 
     def to_dev(bits):
         return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
-
     # ---- inputs and preallocated operands (resident before timing)
     t0 = time.time()
     projs = []
     host_inputs = {}
     for idx, (name, M, Nn, K) in enumerate(projections):
-        a, w, g = W.projection_inputs(args.workload, idx, M, Nn, K)
+        a, w, g = W.projection_inputs(workload, idx, M, Nn, K)
         if idx == 0:
             host_inputs = {"a": a, "w": w, "M": M, "N": Nn, "K": K, "name": name}
         projs.append(alloc_projection(name, M, Nn, K, to_dev(a), to_dev(w), to_dev(g), mx, torch, dev,
@@ -476,7 +509,7 @@ def main():
     setup_s = time.time() - t0
 
     if args.fused_producers:
-        if args.workload != "llama8b_mlp" and args.workload != "llama70b":
+        if workload != "llama8b_mlp" and workload != "llama70b":
             sys.stderr.write("--fused-producers needs an MLP workload (gate/up then down)\n")
             sys.exit(2)
         byname = {P["name"]: P for P in projs}
@@ -507,13 +540,13 @@ def main():
         sys.exit(2)
     use_events = not args.no_kernel_events
     # the timed region: K steps bracketed by two events, nothing between the launches
-    ms_per_step, _ = time_ops(ops, args.steps, args.warmup, stream, torch, N, per_kernel=False)
+    ms_per_step, _ = time_ops(ops, steps, warmup, stream, torch, N, per_kernel=False)
     per = None
     if use_events:
         # per-kernel durations: the same K steps again with an event after every launch
         # (each event adds a few microseconds between launches, so the step time above
         # comes from the uninstrumented pass)
-        _, per = time_ops(ops, args.steps, 0, stream, torch, N, per_kernel=True)
+        _, per = time_ops(ops, steps, 0, stream, torch, N, per_kernel=True)
 
     per_op = {}
     gemm_ms = cast_ms = 0.0
@@ -545,15 +578,15 @@ def main():
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "mxfp4+mxfp8" if args.fp8_wgrad else "mxfp4",
         "data": "synthetic",
-        "config": {"workload": WORKLOADS[args.workload] + (
+        "config": {"workload": WORKLOADS[workload] + (
                        "; weights quantized once (cached), no W cast in the step" if args.cached_weights else "") + (
                        "; Hadamard gradient recipe" if args.hadamard_grad else "") + (
                        "; dB as an MXFP8 GEMM (FP8 wgrad)" if args.fp8_wgrad else "") + (
@@ -585,7 +618,7 @@ def main():
                               # counters were taken over the 8B MLP step's six MXFP4 launches: the
                               # figure belongs to that workload's GEMM set only
                               "traffic": measured_traffic()
-                              if args.workload == "llama8b_mlp" and gemm8_ms == 0 else None}
+                              if workload == "llama8b_mlp" and gemm8_ms == 0 else None}
         # sustained clock and power over ~0.5 s of further steps (not part of the timed region)
         with ClockSampler() as cs:
             t_end = time.time() + 0.5
@@ -598,10 +631,17 @@ def main():
             result["roofline"]["peak_at_clock"] = round(peak_clk, 1)
             result["roofline"]["frac_at_clock"] = round(gemm_tflops / peak_clk, 4)
 
-    if args.cpu_seconds > 0:
-        result["cpu_baseline"] = cpu_baseline(host_inputs, args.cpu_seconds)
+    # free the config's device buffers before the CPU sample (and the next config)
+    del ops, projs
+    P = gu = dn = None  # noqa: F841 (the loop variables held the last projection's buffers)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(host_inputs, cpu_seconds)
     result["setup_s"] = round(setup_s, 1)
-    print(json.dumps(result), flush=True)
+    return result
+
+
 
 
 def cpu_baseline(inp, target_s):

@@ -195,6 +195,27 @@ int mxfp4_gemm_nn(const void* a_q, const void* a_s, const void* bcol_q, const vo
                   int64_t K, void* out, int64_t ldo, hipStream_t stream);
 
 /*
+ * A3 with a workspace -- the same product as mxfp4_gemm_nt (and, on a column
+ * copy, mxfp4_gemm_nn), for outputs too small to fill the chip behind a long
+ * contraction (A8: e.g. the dA of an LM head, 1..17 x 4096 or 4096 x 32
+ * outputs over a contraction of 128256): several workgroups then share each
+ * output block, write fp32 partial sums to ws, and a second kernel adds them
+ * in a fixed order and rounds to bf16.
+ * mxfp4_gemm_workspace_bytes: the bytes that split needs for these sizes (0
+ *   when the launch does not split, or for invalid sizes).  Host only.
+ * mxfp4_gemm_nt_ws: arguments and errors as mxfp4_gemm_nt; ws is device
+ *   memory of ws_bytes, 16-byte aligned (MXFP4_EALIGN otherwise), or NULL.
+ *   With fewer bytes than mxfp4_gemm_workspace_bytes (or NULL) the
+ *   contraction is split only as far as ws holds the partials.  The
+ *   workspace needs no initialization; calls sharing one ws must be ordered
+ *   (e.g. on one stream).
+ */
+size_t mxfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+int mxfp4_gemm_nt_ws(const void* a_q, const void* a_s, const void* b_q, const void* b_s, int64_t M, int64_t N,
+                     int64_t K, void* out, int64_t ldo, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * F3 -- MXFP8 (E4M3) operands for the FP8 dB of the jax-aiter README,
  * "MXFP4 training architecture" (its backward runs dB as an FP8 dot while
  * the forward pass and dA stay FP4).  Argument rules, alignment and errors
@@ -268,7 +289,10 @@ int mxfp4_rmsnorm_cast(const void* x, const void* residual, const void* gamma, f
  * weights [N, K].  training != 0 sizes for fwd + bwd: it holds the row copies
  * of A and W, the saved column copies of A and W that the backward pass reads,
  * and the row and column copies of dOut.  training == 0 sizes for an
- * inference forward (row copies only).  Returns 0 for invalid sizes.
+ * inference forward (row copies only).  Both also hold the partial sums of
+ * the step's GEMMs where they split their contraction (the largest
+ * mxfp4_gemm_workspace_bytes of the step's products).  Returns 0 for invalid
+ * sizes.
  */
 size_t gemm_fp4_bf16_workspace_bytes(int64_t M, int64_t N, int64_t K, int training);
 

@@ -224,7 +224,7 @@ def rmsnorm_cast(x, gamma, eps=1e-5, residual=None, columnwise=True, col_fmt=4, 
     return Mxfp4Tensor(row, col, (R, D)), h, rstd, y
 
 
-def _gemm(fn, name, a: MxOperand, b: MxOperand, out):
+def _gemm(fn, name, a: MxOperand, b: MxOperand, out, ws=None):
     if a.k != b.k:
         raise ValueError("contraction lengths differ: %d vs %d" % (a.k, b.k))
     M, Nn, K = a.rows, b.rows, a.k
@@ -232,10 +232,27 @@ def _gemm(fn, name, a: MxOperand, b: MxOperand, out):
         out = torch.empty((M, Nn), dtype=torch.bfloat16, device=a.q.device)
     elif out.dtype != torch.bfloat16 or out.shape != (M, Nn) or out.stride(1) != 1:
         raise ValueError("out must be a bfloat16 [%d, %d] tensor with unit column stride" % (M, Nn))
-    st = fn(a.q.data_ptr(), a.s.data_ptr(), b.q.data_ptr(), b.s.data_ptr(), M, Nn, K, out.data_ptr(),
-            out.stride(0), _stream(out.device))
+    args = (a.q.data_ptr(), a.s.data_ptr(), b.q.data_ptr(), b.s.data_ptr(), M, Nn, K, out.data_ptr(), out.stride(0))
+    if ws is not None:
+        if ws.dtype != torch.uint8 or not ws.is_contiguous() or ws.device != out.device:
+            raise ValueError("ws must be a contiguous uint8 tensor on the output's device")
+        st = N.lib().mxfp4_gemm_nt_ws(*args, ws.data_ptr(), ws.numel(), _stream(out.device))
+        name = "mxfp4_gemm_nt_ws"
+    else:
+        st = fn(*args, _stream(out.device))
     N.check(st, name)
     return out
+
+
+def gemm_workspace_bytes(M, Nn, K):
+    """Bytes of scratch the split contraction of out[M, N] (contraction K) uses; 0 if it does not split."""
+    return int(N.lib().mxfp4_gemm_workspace_bytes(int(M), int(Nn), int(K)))
+
+
+def gemm_workspace(shapes, device):
+    """One scratch tensor for GEMMs run in order on one stream: the largest need among (M, N, K) shapes."""
+    nbytes = max([gemm_workspace_bytes(*s) for s in shapes] + [0])
+    return torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=device)
 
 
 def _check_formats(a, b, fmt):
@@ -243,16 +260,19 @@ def _check_formats(a, b, fmt):
         raise ValueError("operands are MXFP%d / MXFP%d, this product takes MXFP%d" % (a.fmt, b.fmt, fmt))
 
 
-def gemm_nt(a: MxOperand, b: MxOperand, out=None):
-    """out[M, N] = dq(a)[M, K] . dq(b)[N, K]^T in bf16 (two MXFP4 operands)."""
+def gemm_nt(a: MxOperand, b: MxOperand, out=None, ws=None):
+    """out[M, N] = dq(a)[M, K] . dq(b)[N, K]^T in bf16 (two MXFP4 operands).  With ws (a uint8
+    scratch tensor, see gemm_workspace) a long contraction behind a small output is split over
+    several workgroups (mxfp4_gemm_nt_ws)."""
     _check_formats(a, b, 4)
-    return _gemm(N.lib().mxfp4_gemm_nt, "mxfp4_gemm_nt", a, b, out)
+    return _gemm(N.lib().mxfp4_gemm_nt, "mxfp4_gemm_nt", a, b, out, ws)
 
 
-def gemm_nn(a: MxOperand, bcol: MxOperand, out=None):
-    """out[M, N] = dq(a)[M, K] . B[K, N], B given by its column copy (N rows, contraction K)."""
+def gemm_nn(a: MxOperand, bcol: MxOperand, out=None, ws=None):
+    """out[M, N] = dq(a)[M, K] . B[K, N], B given by its column copy (N rows, contraction K);
+    ws as for gemm_nt (the same kernel on the column copy)."""
     _check_formats(a, bcol, 4)
-    return _gemm(N.lib().mxfp4_gemm_nn, "mxfp4_gemm_nn", a, bcol, out)
+    return _gemm(N.lib().mxfp4_gemm_nn, "mxfp4_gemm_nn", a, bcol, out, ws)
 
 
 def gemm_fp8_nt(a: MxOperand, b: MxOperand, out=None):

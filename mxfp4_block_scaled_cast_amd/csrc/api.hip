@@ -15,6 +15,7 @@
 // With the FP8 wgrad option (the dB of the "MXFP4 training architecture"
 // section runs as an FP8 product) the column copies of A and dOut are MXFP8
 // and dB is the MXFP8 GEMM; the forward pass and dA stay MXFP4.
+#include <algorithm>
 #include <mutex>
 #include <string.h>
 
@@ -41,6 +42,10 @@ extern "C" hipError_t mx_launch_rmsnorm_cast(const void* x, const void* residual
                                              hipStream_t stream);
 extern "C" hipError_t mx_launch_gemm_f(const void* aq, const void* as, const void* bq, const void* bs, int64_t M,
                                        int64_t N, int64_t K, void* out, int64_t ldo, int fmt, hipStream_t stream);
+extern "C" hipError_t mx_launch_gemm_ws(const void* aq, const void* as, const void* bq, const void* bs, int64_t M,
+                                        int64_t N, int64_t K, void* out, int64_t ldo, int fmt, void* ws,
+                                        int64_t ws_bytes, hipStream_t stream);
+extern "C" int64_t mx_gemm_split_bytes(int64_t M, int64_t N, int64_t K, int fmt);
 extern "C" hipError_t mx_launch_cast_dual_pair(const void* x0, int64_t R0, int64_t C0, int64_t ldx0, void* q_row0,
                                                void* s_row0, void* q_col0, void* s_col0, const void* x1, int64_t R1,
                                                int64_t C1, int64_t ldx1, void* q_row1, void* s_row1, void* q_col1,
@@ -134,6 +139,7 @@ struct Workspace {
     int64_t a_row_q, a_row_s, w_row_q, w_row_s;  // forward operands
     int64_t a_col_q, a_col_s, w_col_q, w_col_s;  // saved for the backward pass
     int64_t g_row_q, g_row_s, g_col_q, g_col_s;  // backward operands
+    int64_t split, split_bytes;                  // partial sums of a split contraction (shared by the GEMMs)
     int64_t total;
 };
 
@@ -168,6 +174,15 @@ Workspace workspace_layout(int64_t M, int64_t N, int64_t K, bool training, bool 
         w.g_col_q = take(g_col.q);
         w.g_col_s = take(g_col.s);
     }
+    // the step's GEMMs run one after another on one stream, so they share one region
+    int64_t split = mx_gemm_split_bytes(M, N, K, 4);
+    if (training) {
+        const int64_t Mp = round_up(M, 32);
+        split = std::max(split, mx_gemm_split_bytes(M, K, N, 4));
+        split = std::max(split, mx_gemm_split_bytes(N, K, Mp, fp8_wgrad ? 8 : 4));
+    }
+    w.split_bytes = split;
+    w.split = take(split);
     w.total = off;
     return w;
 }
@@ -299,6 +314,21 @@ int mxfp4_gemm_nn(const void* a_q, const void* a_s, const void* bcol_q, const vo
     // B[K, N] enters through its column copy, which is the MX operand (N rows, K):
     // the NN product is the NT kernel on that operand.
     return mxfp4_gemm_nt(a_q, a_s, bcol_q, bcol_s, M, N, K, out, ldo, stream);
+}
+
+size_t mxfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K < 0 || K % 32 != 0 || M > kMaxDim || N > kMaxDim || K > kMaxK) return 0;
+    return (size_t)mx_gemm_split_bytes(M, N, K, 4);
+}
+
+int mxfp4_gemm_nt_ws(const void* a_q, const void* a_s, const void* b_q, const void* b_s, int64_t M, int64_t N,
+                     int64_t K, void* out, int64_t ldo, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int st = validate_gemm(a_q, a_s, b_q, b_s, M, N, K, out, ldo);
+    if (st != MXFP4_OK || M == 0 || N == 0) return st;
+    if (ws && !aligned16(ws)) return MXFP4_EALIGN;
+    if ((st = check_device()) != MXFP4_OK) return st;
+    const int64_t bytes = ws ? (int64_t)std::min(ws_bytes, (size_t)INT64_MAX) : 0;
+    return status_of(mx_launch_gemm_ws(a_q, a_s, b_q, b_s, M, N, K, out, ldo, 4, ws, bytes, stream));
 }
 
 int mxfp8_operand_layout_of(int64_t rows, int64_t k, mxfp4_operand_layout* out) {
@@ -465,7 +495,9 @@ int step_fwd(const void* a, bool own_w, const void* w, const void* w_row_q, cons
                                      false, hadamard, 0, stream);
         }
     }
-    if (e == hipSuccess) e = mx_launch_gemm(base + L.a_row_q, base + L.a_row_s, wq, wsc, M, N, K, out, N, stream);
+    if (e == hipSuccess)
+        e = mx_launch_gemm_ws(base + L.a_row_q, base + L.a_row_s, wq, wsc, M, N, K, out, N, 4, base + L.split,
+                              L.split_bytes, stream);
     return status_of(e);
 }
 
@@ -507,10 +539,12 @@ int step_bwd(const void* dout, bool own_w, const void* w_col_q, const void* w_co
     hipError_t e = mx_launch_cast_f(dout, M, N, N, base + L.g_row_q, base + L.g_row_s, base + L.g_col_q,
                                     base + L.g_col_s, true, 4, wfmt, hadamard, hadamard,
                                     hadamard ? kHadamardShift : 0, stream);
-    if (e == hipSuccess && da) e = mx_launch_gemm(base + L.g_row_q, base + L.g_row_s, wq, wsc, M, K, N, da, K, stream);
+    if (e == hipSuccess && da)
+        e = mx_launch_gemm_ws(base + L.g_row_q, base + L.g_row_s, wq, wsc, M, K, N, da, K, 4, base + L.split,
+                              L.split_bytes, stream);
     if (e == hipSuccess && dw)
-        e = mx_launch_gemm_f(base + L.g_col_q, base + L.g_col_s, base + L.a_col_q, base + L.a_col_s, N, K, Mp, dw, K,
-                             wfmt, stream);
+        e = mx_launch_gemm_ws(base + L.g_col_q, base + L.g_col_s, base + L.a_col_q, base + L.a_col_s, N, K, Mp, dw, K,
+                              wfmt, base + L.split, L.split_bytes, stream);
     return status_of(e);
 }
 

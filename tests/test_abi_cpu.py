@@ -386,3 +386,38 @@ def test_noalloc_forward_rejects_before_any_device_work():
     assert L.gemm_fp4_bf16_fwd_qw_noalloc(None, FAKE, FAKE, 0, 64, 64, None, None) == 0    # empty
     if _no_gpu():
         assert L.gemm_fp4_bf16_fwd_qw_noalloc(FAKE, FAKE, FAKE, 64, 64, 64, FAKE, None) == -3
+
+
+def test_split_workspace_query_and_validation():
+    L = N.lib()
+    # long contractions behind small outputs split; tiled products and short contractions do not
+    assert L.mxfp4_gemm_workspace_bytes(1, 32, 128256) > 0
+    assert L.mxfp4_gemm_workspace_bytes(4096, 32, 128256) > 0
+    assert L.mxfp4_gemm_workspace_bytes(8192, 28672, 4096) == 0
+    assert L.mxfp4_gemm_workspace_bytes(17, 4096, 4096) == 0
+    assert L.mxfp4_gemm_workspace_bytes(4, 4, 48) == 0                      # K % 32: invalid
+    assert L.mxfp4_gemm_workspace_bytes(4, 4, (1 << 23) + 32) == 0          # past the contraction limit
+    f = L.mxfp4_gemm_nt_ws
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 4, 48, FAKE, 4, FAKE, 64, None) == -1
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 4, 32, FAKE, 4, FAKE + 4, 64, None) == -2   # misaligned workspace
+    assert f(FAKE, FAKE + 4, FAKE, FAKE, 4, 4, 32, FAKE, 4, None, 0, None) == -2   # misaligned scales
+    assert f(FAKE, FAKE, FAKE, FAKE, 0, 4, 32, None, 4, None, 0, None) == 0        # empty
+    if _no_gpu():
+        assert f(FAKE, FAKE, FAKE, FAKE, 4, 4, 32, FAKE, 4, None, 0, None) == -3
+
+
+def test_step_workspace_holds_the_split_partials():
+    # the step's workspace adds one region for the largest split of its three products
+    def op(rows, k):
+        return layout.code_bytes(rows, k) + layout.scale_bytes(rows, k)
+
+    def r256(x):
+        return -(-x // 256) * 256
+    L = N.lib()
+    M, Nn, K = 17, 128256, 32          # dA contracts over 128256 behind 17 x 32 outputs
+    Mp = 32
+    copies = [op(M, K), op(Nn, K), op(K, Mp), op(K, Nn), op(M, Nn), op(Nn, Mp)]
+    split = max(L.mxfp4_gemm_workspace_bytes(M, Nn, K), L.mxfp4_gemm_workspace_bytes(M, K, Nn),
+                L.mxfp4_gemm_workspace_bytes(Nn, K, Mp))
+    assert split == L.mxfp4_gemm_workspace_bytes(M, K, Nn) > 0
+    assert L.gemm_fp4_bf16_workspace_bytes(M, Nn, K, 1) == sum(r256(c) for c in copies) + r256(split)

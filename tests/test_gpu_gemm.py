@@ -216,3 +216,31 @@ def test_tiled_output_leading_dimension(extra, offset, K):
     win = flat[offset:offset + M * ldo].reshape(M, ldo)
     assert_gemm_close(win[:, :N], ref, absref, "ldo %d offset %d" % (ldo, offset))
     assert np.all(win[:, N:] == -1.0) and np.all(flat[:offset] == -1.0) and np.all(flat[offset + M * ldo:] == -1.0)
+
+
+# Split contraction (mxfp4_gemm_nt_ws): long contractions behind small outputs -- the dA of an LM head
+# (1 or 17 x 32 outputs over 128256, 31 splits; 4096 x 32 and 32 x 4096, 2 splits), ragged blocks of a
+# row vector and of 33 x 100 and 64 x 96 outputs -- with the full workspace, with half of it (fewer
+# splits), and with a workspace full of garbage (the partials need no initialization); against the
+# oracle, and the same bits as a second call.
+@pytest.mark.parametrize("M,N,K", [(1, 32, 128256), (17, 32, 128256), (4096, 32, 128256), (32, 4096, 128256),
+                                   (1, 1000, 100000), (33, 100, 20000), (64, 96, 65536)])
+def test_split_contraction(M, N, K):
+    a = W.ragged_values((M, K), 7 * M + K)
+    b = W.ragged_values((N, K), 9 * N + K)
+    need = mx.gemm_workspace_bytes(M, N, K)
+    assert need > 0, "the shape should split its contraction"
+    ad, bd = mx.cast(to_device(a)), mx.cast(to_device(b))
+    ref, absref = oracle_nt(a, b)
+    outs = []
+    for what, nbytes in (("full", need), ("half", need // 2), ("garbage", need)):
+        ws = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device="cuda:0")
+        if what == "garbage":
+            ws.fill_(0x7F)  # every partial float starts as a huge value
+        say("gemm_nt_ws %s M=%d N=%d K=%d ws=%d" % (what, M, N, K, nbytes))
+        out = mx.gemm_nt(ad, bd, ws=ws)
+        torch.cuda.synchronize()
+        got = bf16_to_f64(out)
+        assert_gemm_close(got, ref, absref, "split %s %dx%dx%d" % (what, M, N, K))
+        outs.append(out.view(torch.int16).clone())
+    assert torch.equal(outs[0], outs[2])  # same split, same order: same bits
