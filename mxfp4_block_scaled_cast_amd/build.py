@@ -8,7 +8,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIB_DIR, "libmxfp4.so")
-SOURCES = ["cast.hip", "gemm.hip", "api.hip"]
+SOURCES = ["cast.hip", "gemm.hip", "gemm_skinny.hip", "api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
