@@ -247,6 +247,183 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restr
     if (i < Ma && j < Nb) out[(int64_t)i * ld_i + (int64_t)j * ld_j] = f32_to_bf16_rne(v);
 }
 
+// ---------------------------------------------------------------------------
+// Panel kernel, for skinny-regime outputs whose smaller side has 128 rows or
+// more (e.g. 16384 x 128 outputs over a contraction of 14336, or 2048 x 2048):
+// a workgroup owns a 128 x 128 output block and its 4 waves (2 x 2, each 64 x
+// 64 = 2 x 2 MFMA tiles) share the block's operand panels through LDS, so an
+// operand byte crosses L2 -> CU once per workgroup rather than once per wave
+// as in the skinny kernel.  Per 256-wide chunk of the contraction the
+// workgroup moves 34 KB: 16 code tiles of A and 16 of B (one 1 KB tile per
+// wave load instruction, lane l taking its bytes 16l .. 16l+15) and the A and
+// B scale tiles that cover the chunk.  Chunks are staged in registers two
+// ahead (the loads of chunk c+2 are in flight while chunk c's MFMAs run) and
+// double-buffered in LDS, one barrier per chunk.  An LDS row holds a row's
+// 256 codes (128 bytes) as eight 16-byte pieces, piece p at slot p ^ f(r)
+// with f(r) = 4 (r % 2) + (r / 2) % 4: the fragment reads (8 consecutive
+// rows at one piece per lane group) and the tile stores (2 rows x 4 pieces)
+// each hit 8 distinct slots.  With a workspace, S workgroups split each
+// block's contraction as in the skinny kernel; each wave writes its 64 x 64
+// partial block in the 2 x 2 skinny layout (virtual block (2 ta + wa) of
+// vt_a x (2 tb + wb) of vt_b) and skinny_reduce_kernel<2, 2> adds them.
+// ---------------------------------------------------------------------------
+constexpr unsigned kRsrcFlags = 0x00020000u;             // gfx9 raw buffer: dword format, no swizzle
+constexpr int kPanelRows = 128;                            // rows of A and of B per block
+constexpr int kPanelCodes = kPanelRows * 128;              // 16 KB of codes per operand and chunk
+constexpr int kPanelStage = 2 * kPanelCodes + 2 * 1024;    // + the two scale tiles: 34 KB
+
+__device__ __forceinline__ int panel_slot(int row) { return ((row & 1) << 2) | ((row >> 1) & 3); }
+
+__global__ __launch_bounds__(256, 2) void gemm_panel_kernel(
+    const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as, const uint8_t* __restrict__ bq,
+    const uint8_t* __restrict__ bs, int Ma, int Nb, int K, uint16_t* __restrict__ out, int64_t ld_i, int64_t ld_j,
+    int tiles_b, int tiles, float* __restrict__ part, int vt_a, int vt_b) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kPanelStage];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (descriptors in SGPRs)
+    const int half = lane >> 5;
+    const int wa = w >> 1, wb = w & 1;
+    // workgroup = split * tiles + block; S = 1 without a workspace (part == nullptr)
+    const int tile = (int)(blockIdx.x % (unsigned)tiles);
+    const int split = (int)(blockIdx.x / (unsigned)tiles);
+    const int S = (int)(gridDim.x / (unsigned)tiles);
+    const int ta = tile / tiles_b, tb = tile % tiles_b;
+    const int64_t kt128 = (K + 127) >> 7, kt256 = (K + 255) >> 8;
+    const int chunks = (int)kt256;
+    const int c_begin = (int)((int64_t)chunks * split / S), c_end = (int)((int64_t)chunks * (split + 1) / S);
+
+    // load u (0..7) of wave w moves code tile 8w + u of the chunk: operand w / 2 (A, B), 16-row
+    // group 4 (w % 2) + u / 2 of the block, K tile u % 2 of the chunk; load 8 moves half w % 2 of
+    // the operand's scale tile (rows of the block x the chunk's 256 elements; lanes 0-31).  Raw
+    // buffer loads through descriptors that span the wave's four 16-row groups and the block's scale
+    // row: groups past the operand, K tiles past the codes and chunks past the split read as zero,
+    // and every load is issued unconditionally (static wait counts).
+    const int op = w >> 1;
+    const int64_t groups = op == 0 ? ((int64_t)Ma + 15) >> 4 : ((int64_t)Nb + 15) >> 4;
+    const int64_t g0 = (int64_t)(op == 0 ? ta : tb) * 8 + 4 * (w & 1);
+    const int64_t left = groups - g0 < 0 ? 0 : (groups - g0 < 4 ? groups - g0 : 4);
+    const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>((op == 0 ? aq : bq) + (left > 0 ? g0 * kt128 * 1024 : 0)), (short)0,
+        (int)(left * kt128 * 1024), (int)kRsrcFlags);
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>((op == 0 ? as : bs) + (int64_t)(op == 0 ? ta : tb) * kt256 * 1024), (short)0,
+        (int)(kt256 * 1024), (int)kRsrcFlags);
+    typedef u32x4 Stage[9];
+    auto load_chunk = [&](int c, Stage& R, bool valid) {
+#pragma unroll
+        // offsets are pushed past the descriptor by setting bit 31 (arithmetic, not a select: a
+        // select on the uniform flag becomes branches around the loads, and the wait counts
+        // then no longer see which loads are in flight)
+        for (int u = 0; u < 8; ++u) {
+            const int kt = c * 2 + (u & 1);
+            const unsigned out_bit = (unsigned)(!(valid && kt < kt128)) << 31;
+            const unsigned off = (unsigned)(((u >> 1) * (int)kt128 + kt) * 1024 + lane * 16) | out_bit;
+            R[u] = __builtin_amdgcn_raw_buffer_load_b128(crs, (int)off, 0, 0);
+        }
+        const unsigned s_out = ((unsigned)!valid | (unsigned)(lane >> 5)) << 31;
+        R[8] = __builtin_amdgcn_raw_buffer_load_b128(srs, (int)((unsigned)(c * 1024 + (w & 1) * 512 + lane * 16) | s_out),
+                                                     0, 0);
+    };
+    // LDS place of load u: row 16 (4 (w % 2) + u / 2) + lane / 4 of operand w / 2, piece 4 (u % 2) + lane % 4
+    const int lrow = lane >> 2;
+    auto store_chunk = [&](const Stage& R, int buf) {
+        uint8_t* L = lds + buf * kPanelStage;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int row = 16 * (4 * (w & 1) + (u >> 1)) + lrow;
+            const int piece = 4 * (u & 1) + (lane & 3);
+            *reinterpret_cast<u32x4*>(L + op * kPanelCodes + row * 128 + ((piece ^ panel_slot(row)) << 4)) = R[u];
+        }
+        if (lane < 32) *reinterpret_cast<u32x4*>(L + 2 * kPanelCodes + op * 1024 + (w & 1) * 512 + lane * 16) = R[8];
+    };
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int ma = 0; ma < 2; ++ma)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) acc[ma][nb] = f32x16{};
+
+    // the MFMAs of one chunk from LDS buffer buf: the lane's fragments of rows lane % 32 of each
+    // 32-row group at piece 2 st + half (K step st), its scale dwords (the skinny layout's
+    // (row, half) dword; byte st scales step st)
+    const int frow = lane & 31;
+    const int fslot = panel_slot(frow);
+    auto mfma_chunk = [&](int buf) {
+        const uint8_t* L = lds + buf * kPanelStage;
+        int sa[2], sb[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            sa[m] = *reinterpret_cast<const int*>(L + 2 * kPanelCodes + (wa * 2 + m) * 256 + frow * 8 + half * 4);
+            sb[m] = *reinterpret_cast<const int*>(L + 2 * kPanelCodes + 1024 + (wb * 2 + m) * 256 + frow * 8 +
+                                                  half * 4);
+        }
+#define MX_PANEL_STEP(ST)                                                                                            \
+    {                                                                                                                \
+        u32x4 af[2], bf[2];                                                                                          \
+        _Pragma("unroll") for (int m = 0; m < 2; ++m) {                                                              \
+            af[m] = *reinterpret_cast<const u32x4*>(L + (wa * 64 + m * 32 + frow) * 128 +                            \
+                                                    (((2 * ST + half) ^ fslot) << 4));                               \
+            bf[m] = *reinterpret_cast<const u32x4*>(L + kPanelCodes + (wb * 64 + m * 32 + frow) * 128 +              \
+                                                    (((2 * ST + half) ^ fslot) << 4));                               \
+        }                                                                                                            \
+        _Pragma("unroll") for (int ma = 0; ma < 2; ++ma) _Pragma("unroll") for (int nb = 0; nb < 2; ++nb)           \
+            acc[ma][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(as_operand(af[ma]), as_operand(bf[nb]),    \
+                                                                          acc[ma][nb], 4, 4, ST, sa[ma], ST, sb[nb]); \
+    }
+        MX_PANEL_STEP(0) MX_PANEL_STEP(1) MX_PANEL_STEP(2) MX_PANEL_STEP(3)
+#undef MX_PANEL_STEP
+    };
+
+    // chunk c in LDS buffer (c - c_begin) % 2; registers X and Y alternate as the staging of the
+    // chunk two ahead.  Every thread's reads of a buffer are done before the barrier that precedes
+    // the next store into it.  Past the split's last chunk the loads read zeros and the odd
+    // chunk's MFMAs are skipped (a uniform branch; no exit from the middle of the body, so the
+    // accumulators keep their registers).
+    Stage X, Y;
+    load_chunk(c_begin, X, c_begin < c_end);
+    load_chunk(c_begin + 1, Y, c_begin + 1 < c_end);
+    store_chunk(X, 0);
+    __syncthreads();
+    for (int c = c_begin; c < c_end; c += 2) {
+        load_chunk(c + 2, X, c + 2 < c_end);
+        mfma_chunk(0);
+        store_chunk(Y, 1);
+        __syncthreads();
+        load_chunk(c + 3, Y, c + 3 < c_end);
+        if (c + 1 < c_end) mfma_chunk(1);
+        store_chunk(X, 0);
+        __syncthreads();
+    }
+
+    // acc[ma][nb][r] is C[i0 + ma*32 + (r/4)*8 + half*4 + r%4, j0 + nb*32 + lane%32] of the wave's
+    // 64 x 64 block (i0, j0)
+    const int va = 2 * ta + wa, vb = 2 * tb + wb;
+    if (part) {
+        if (va >= vt_a || vb >= vt_b) return;
+        float* pblk = part + ((int64_t)split * vt_a * vt_b + (int64_t)va * vt_b + vb) * 4096;
+#pragma unroll
+        for (int ma = 0; ma < 2; ++ma)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) pblk[((ma * 2 + nb) * 16 + r) * 64 + lane] = acc[ma][nb][r];
+        return;
+    }
+    const int i0 = va * 64, j0 = vb * 64;
+#pragma unroll
+    for (int ma = 0; ma < 2; ++ma)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            const int j = j0 + nb * 32 + frow;
+            if (j >= Nb) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = i0 + ma * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+                if (i < Ma) out[(int64_t)i * ld_i + (int64_t)j * ld_j] = f32_to_bf16_rne(acc[ma][nb][r]);
+            }
+        }
+}
+
 // Launch plan of the skinny kernel for out[M, N] = a . b^T: the smaller side is A
 // (32*MA-row groups), the larger one B (32*NB-row groups).
 //
@@ -266,14 +443,17 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restr
 struct SkinnyPlan {
     bool swap;
     int64_t Ma, Nb;
+    bool panel;          // the panel kernel (128 x 128 blocks, operands shared through LDS)
     int ma, nb, W;
     int64_t tiles_a, tiles_b, chunks;
+    int64_t vt_a, vt_b;  // panel kernel: 64 x 64 partial blocks along A and B
     int64_t S;
     int64_t part_bytes;  // workspace the S partial blocks take (0 for S = 1)
 };
 
 constexpr int64_t kMaxSplits = 64;
 constexpr int64_t kSplitMinChunks = 4;
+constexpr int64_t kPanelMinChunks = 4;  // 256-wide chunks per split of the panel kernel, at least
 
 template <int FMT>
 static SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int64_t cus, int64_t ws_bytes) {
@@ -282,6 +462,40 @@ static SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int64_t cus, int6
     P.Ma = P.swap ? N : M;
     P.Nb = P.swap ? M : N;
     P.chunks = (K + 255) / 256;
+    if (FMT == 4 && P.Ma >= kPanelRows) {
+        // both sides hold at least one 128-row panel: the panel kernel when its blocks, split over
+        // the contraction, give at least half the CUs a workgroup.  Splits: up to one workgroup per
+        // CU (two per CU measured no faster), at least kPanelMinChunks chunks each, and the fp32
+        // partials (S copies of the output, written and read back) within half the operand bytes
+        // (measured: 1000 x 2000 x 1024 took 13.1 us unsplit, 19.3 with 2 splits; 16384 x 128 x
+        // 14336 took 64.2 us on 128 blocks, 49.2 on 2 x 128).  Otherwise the skinny kernel below,
+        // whose waves split the contraction inside the workgroup at no traffic (128 x 4096 x 4096:
+        // 12.8 us, against 16.0 at best here).
+        const int64_t ta = (P.Ma + kPanelRows - 1) / kPanelRows, tb = (P.Nb + kPanelRows - 1) / kPanelRows;
+        const int64_t vt_a = (P.Ma + 63) / 64, vt_b = (P.Nb + 63) / 64;
+        const int64_t tiles = ta * tb;
+        const int64_t part1 = vt_a * vt_b * 4096 * (int64_t)sizeof(float);  // one split's partials
+        const int64_t op_bytes = (P.Ma + P.Nb) * (K / 2 + K / 32);
+        int64_t S = 1;
+        if (tiles < cus && P.chunks >= 2 * kPanelMinChunks) {
+            S = std::min(std::min(cus / tiles, P.chunks / kPanelMinChunks), kMaxSplits);
+            S = std::min(S, op_bytes / (2 * part1));
+            S = std::min(S, ws_bytes / part1);
+            if (S < 2) S = 1;
+        }
+        if (tiles * S * 2 >= cus) {
+            P.panel = true;
+            P.ma = P.nb = 2;
+            P.W = 4;
+            P.tiles_a = ta;
+            P.tiles_b = tb;
+            P.vt_a = vt_a;
+            P.vt_b = vt_b;
+            P.S = S;
+            P.part_bytes = S > 1 ? S * part1 : 0;
+            return P;
+        }
+    }
     const int64_t grow = cus * 16;
     struct Cand { int ma, nb; int64_t qualify; };
     const Cand cands4[] = {{2, 2, cus * 6}, {1, 4, cus * 16}, {1, 2, cus * 8}, {1, 1, 0}};
@@ -328,6 +542,19 @@ static hipError_t launch_skinny(const uint8_t* aq, const uint8_t* as, const uint
     const dim3 grid((unsigned)(tiles * P.S)), block((unsigned)(64 * P.W));
     const uint8_t *pa = P.swap ? bq : aq, *psa = P.swap ? bs : as, *pb = P.swap ? aq : bq, *psb = P.swap ? as : bs;
     float* part = P.S > 1 ? static_cast<float*>(ws) : nullptr;
+    if (P.panel) {
+        const int64_t vtiles = P.vt_a * P.vt_b;
+        if (vtiles * 4096 > 0x7FFFFFFF) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(mx::gemm_panel_kernel, dim3((unsigned)(tiles * P.S)), dim3(256), 0, stream, pa, psa, pb,
+                           psb, (int)P.Ma, (int)P.Nb, (int)K, out, ld_i, ld_j, (int)P.tiles_b, (int)tiles, part,
+                           (int)P.vt_a, (int)P.vt_b);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || P.S == 1) return e;
+        auto red22 = mx::skinny_reduce_kernel<2, 2>;
+        hipLaunchKernelGGL(red22, dim3((unsigned)((vtiles * 4096 + 255) / 256)), dim3(256), 0,
+                           stream, part, (int)vtiles, (int)P.S, (int)P.vt_b, (int)P.Ma, (int)P.Nb, out, ld_i, ld_j);
+        return hipGetLastError();
+    }
     auto kern = P.nb == 2 ? mx::gemm_skinny_kernel<1, 2, FMT> : mx::gemm_skinny_kernel<1, 1, FMT>;
     auto red = P.nb == 2 ? mx::skinny_reduce_kernel<1, 2> : mx::skinny_reduce_kernel<1, 1>;
     if constexpr (FMT == 4) {
