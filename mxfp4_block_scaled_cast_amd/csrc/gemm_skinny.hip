@@ -463,27 +463,32 @@ static SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, int64_t cus, int6
     P.Nb = P.swap ? M : N;
     P.chunks = (K + 255) / 256;
     if (FMT == 4 && P.Ma >= kPanelRows) {
-        // both sides hold at least one 128-row panel: the panel kernel when its blocks, split over
-        // the contraction, give at least half the CUs a workgroup.  Splits: up to one workgroup per
-        // CU (two per CU measured no faster), at least kPanelMinChunks chunks each, and the fp32
-        // partials (S copies of the output, written and read back) within half the operand bytes
-        // (measured: 1000 x 2000 x 1024 took 13.1 us unsplit, 19.3 with 2 splits; 16384 x 128 x
-        // 14336 took 64.2 us on 128 blocks, 49.2 on 2 x 128).  Otherwise the skinny kernel below,
-        // whose waves split the contraction inside the workgroup at no traffic (128 x 4096 x 4096:
-        // 12.8 us, against 16.0 at best here).
+        // Both sides hold at least one 128-row panel.  The panel kernel is taken where it measured
+        // faster than the skinny kernel in the step's order (the GEMM right after the casts that
+        // wrote its operands, which then sit in the MALL):
+        //  (a) a smaller side of 512 rows or more with blocks for half the CUs, unsplit -- there
+        //      the skinny kernel re-reads both operands once per 64-row group of the other side
+        //      (2048 x 2048 x 4096: 38.7 -> 24.1 us; 1000 x 2000 x 1024: 14.2 -> 12.6 us);
+        //  (b) at least 2^20 outputs over a contraction of 8192 or more, split up to one workgroup
+        //      per CU (16384 x 128 x 14336: 56.5 -> 46.0 us; 128 x 14336 x 16384: 60.6 -> 44.2;
+        //      1024 x 1024 x 14336: 33.0 -> 28.3), when the split launch covers 3/4 of the CUs.
+        // Elsewhere the skinny kernel stays faster: its waves split the contraction inside the
+        // workgroup at no traffic, while the panel split writes and reads back S fp32 copies of
+        // the output and adds a launch (4096 x 128 x 14336: 20.5 us against 24.0 at best;
+        // 16384 x 128 x 4096: 26.4 against 27.5; 16384 x 128 x 32: 10.0 against 14.4).
         const int64_t ta = (P.Ma + kPanelRows - 1) / kPanelRows, tb = (P.Nb + kPanelRows - 1) / kPanelRows;
         const int64_t vt_a = (P.Ma + 63) / 64, vt_b = (P.Nb + 63) / 64;
         const int64_t tiles = ta * tb;
         const int64_t part1 = vt_a * vt_b * 4096 * (int64_t)sizeof(float);  // one split's partials
-        const int64_t op_bytes = (P.Ma + P.Nb) * (K / 2 + K / 32);
+        const bool wide = P.Ma >= 512 && tiles * 2 >= cus;
+        const bool deep = P.Ma * P.Nb >= ((int64_t)1 << 20) && K >= 8192;
         int64_t S = 1;
-        if (tiles < cus && P.chunks >= 2 * kPanelMinChunks) {
+        if (deep && tiles < cus) {
             S = std::min(std::min(cus / tiles, P.chunks / kPanelMinChunks), kMaxSplits);
-            S = std::min(S, op_bytes / (2 * part1));
             S = std::min(S, ws_bytes / part1);
             if (S < 2) S = 1;
         }
-        if (tiles * S * 2 >= cus) {
+        if (wide || (deep && tiles * S * 4 >= cus * 3)) {
             P.panel = true;
             P.ma = P.nb = 2;
             P.W = 4;

@@ -65,14 +65,13 @@ def test_tiled_shapes(M, N, K):
     assert_gemm_close(got, ref, absref, "tiled %dx%dx%d" % (M, N, K))
 
 
-# Outputs too small for the tiled kernels.  Skinny kernel (smaller side below 128): split of the
-# contraction over the waves of a workgroup, 32*MA x 32*NB blocks with (MA, NB) = (1, 1), (1, 2),
-# (1, 4), (2, 2), the smaller side taken as A (output written transposed when that is the GEMM's B;
-# small sides of 33..127 rows in several 32-row groups), K chunks past the padded code tiles; 2 x 2
-# blocks in (97, 20000, 1024) and (65536, 100, 544).  With both sides of 128 rows or more, the panel
-# kernel takes (1000, 2000, 1024), (1536, 2816, 544), (2100, 3000, 256) and, without a workspace
-# (unsplit), (4096, 128, 14336) and (16384, 128, 4096); (128, 65536, 512) has enough 256 x 256 tiles
-# for the tiled kernels.
+# Outputs too small for the tiled kernels.  Skinny kernel: split of the contraction over the waves of
+# a workgroup, 32*MA x 32*NB blocks with (MA, NB) = (1, 1), (1, 2), (1, 4), (2, 2), the smaller side
+# taken as A (output written transposed when that is the GEMM's B; small sides of 33..128 rows in
+# several 32-row groups), K chunks past the padded code tiles; 2 x 2 blocks in (97, 20000, 1024),
+# (65536, 100, 544) and (16384, 128, 4096).  The panel kernel takes
+# (1000, 2000, 1024), (1536, 2816, 544) and (2100, 3000, 256); (128, 65536, 512) has enough
+# 256 x 256 tiles for the tiled kernels.
 @pytest.mark.parametrize("M,N,K", [(1, 4096, 14336), (4096, 32, 8192), (32, 65536, 1024), (128, 65536, 512),
                                    (65536, 100, 544), (17, 300, 2080), (1, 128256, 32), (1000, 2000, 1024),
                                    (48, 3000, 544), (5000, 64, 2080), (4096, 128, 14336), (97, 20000, 1024),
@@ -85,13 +84,15 @@ def test_skinny_shapes(M, N, K):
     assert_gemm_close(got, ref, absref, "skinny %dx%dx%d" % (M, N, K))
 
 
-# Panel kernel (both output sides of 128 rows or more, too few 256 x 256 tiles for the tiled kernels,
-# enough 128 x 128 blocks for half the CUs): blocks whose 4 waves share the operand panels through LDS.
-# Ragged rows on either side (the output written transposed when the GEMM's B is the smaller side:
-# 2100 x 1000, 16500 x 130), K with an odd number of 128-wide code tiles (the last chunk's second K
-# tile reads zero: K = 32, 288, 2080), a 130-row side (a 64-row partial block with 2 valid rows).
-@pytest.mark.parametrize("M,N,K", [(1000, 2100, 288), (2100, 1000, 416), (130, 16500, 160), (16500, 130, 2080),
-                                   (1100, 1900, 32), (1024, 2048, 1024)])
+# Panel kernel (both output sides of 128 rows or more, too few 256 x 256 tiles for the tiled kernels):
+# 128 x 128 blocks whose 4 waves share the operand panels through LDS.  Taken unsplit for a smaller
+# side of 512 rows or more with blocks for half the CUs (1000 x 2100, 2100 x 1000, 1100 x 1900,
+# 1024 x 2048), and for 2^20 outputs or more over contractions of 8192 or more (130 x 12500 over 8192,
+# 12500 x 130 over 8320: 196 blocks, a 130-row side, i.e. a 64-row partial block with 2 valid rows).
+# The output is written transposed when the GEMM's B is the smaller side; K with an odd number of
+# 128-wide code tiles (the last chunk's second K tile reads zero: K = 32, 288, 8320).
+@pytest.mark.parametrize("M,N,K", [(1000, 2100, 288), (2100, 1000, 416), (1100, 1900, 32), (1024, 2048, 1024),
+                                   (130, 12500, 8192), (12500, 130, 8320)])
 def test_panel_shapes(M, N, K):
     a = W.ragged_values((M, K), 13 * M + K)
     b = W.ragged_values((N, K), 19 * N + K)
@@ -101,12 +102,12 @@ def test_panel_shapes(M, N, K):
 
 
 # Panel kernel with a workspace: the contraction of each 128 x 128 block split over S workgroups, whose
-# fp32 partials of the waves' 64 x 64 blocks the reduction kernel adds in split order.  128 x 4096 over
-# 8192, 130 x 2000 and 2048 x 130 over 12160 (95 K tiles, ragged 64-row partial blocks): 32 blocks, 4
-# splits each with the full workspace (half of it gives fewer splits, and with them too few workgroups:
-# the skinny kernel takes over); full, half and garbage workspace as for the skinny split, and the same
+# fp32 partials of the waves' 64 x 64 blocks the reduction kernel adds in split order.  128 x 8192 over
+# 8192 (64 blocks, 4 splits), 130 x 8150 and 8150 x 130 over 8320 (128 blocks, 2 splits, 65 K tiles,
+# ragged 64-row partial blocks); full, half and garbage workspace as for the skinny split (half of it
+# gives fewer splits, and with them too few workgroups: the skinny kernel takes over), and the same
 # bits from the full and the garbage run.
-@pytest.mark.parametrize("M,N,K", [(128, 4096, 8192), (130, 2000, 12160), (2048, 130, 12160)])
+@pytest.mark.parametrize("M,N,K", [(128, 8192, 8192), (130, 8150, 8320), (8150, 130, 8320)])
 def test_panel_split(M, N, K):
     a = W.ragged_values((M, K), 23 * M + K)
     b = W.ragged_values((N, K), 29 * N + K)
