@@ -1,10 +1,13 @@
 """Helpers for the GPU parity tests: moving bf16 bit arrays to the device,
 reading MX operands back in the oracle's row-major form, and the GEMM bar."""
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
 
+import oracle
 from mxfp4_block_scaled_cast_amd import layout
 
 
@@ -148,3 +151,56 @@ def assert_operand_equal(op, q_rm, s_rm, what):
             bad = np.flatnonzero(got != expect)
             raise AssertionError("%s %s: %d of %d bytes differ, first at byte %d (got %#x, expected %#x)"
                                  % (what, part, bad.size, got.size, bad[0], got[bad[0]], expect[bad[0]]))
+
+
+def dequant_to_device(q, s, device, workers=None):
+    """The oracle's dequantized values (fp64, exact) of a canonical (q, s) pair, as a float64 tensor on
+    `device`; the oracle runs on row slices in parallel threads."""
+    R, K = q.shape[0], q.shape[1] * 2
+    out = torch.empty((R, K), dtype=torch.float64, device=device)
+    if R == 0:
+        return out
+    workers = workers or min(16, os.cpu_count() or 1)
+    step = max(1, -(-R // (4 * workers)))
+    spans = [(r0, min(R, r0 + step)) for r0 in range(0, R, step)]
+    with ThreadPoolExecutor(workers) as ex:
+        parts = ex.map(lambda sp: oracle.dequant(q[sp[0]:sp[1]], s[sp[0]:sp[1]]), spans)
+        for (r0, r1), part in zip(spans, parts):
+            out[r0:r1].copy_(torch.from_numpy(part))
+    return out
+
+
+def device_ref_blocks(a, b, device, block_rows=2048):
+    """Row blocks (r0, ref, absref) of the exact product of oracle-quantized operands a = (q, s) [M, K]
+    and b = (q, s) [N, K]: the oracle dequantizes them (exact in fp64); their products are summed by
+    torch.matmul in float64 on the device (a library DGEMM that shares nothing with the kernels under
+    test; its rounding, ~1e-16 relative, is far below the GEMM bar), and sum|a b| likewise from the
+    magnitudes.  Row blocks bound the device memory."""
+    A = dequant_to_device(a[0], a[1], device)
+    Bt = dequant_to_device(b[0], b[1], device).t().contiguous()
+    Bt_abs = Bt.abs()
+    for r0 in range(0, A.shape[0], block_rows):
+        blk = A[r0:r0 + block_rows]
+        yield r0, blk @ Bt, blk.abs() @ Bt_abs
+
+
+def assert_gemm_whole(got, a, b, what, block_rows=2048):
+    """Every output of got [M, N] (bf16 on the device) against device_ref_blocks(a, b), to the GEMM
+    bar 2^-7 |ref| + 1e-5 sum|ab| + 2^-126."""
+    M, Nn = a[0].shape[0], b[0].shape[0]
+    assert tuple(got.shape) == (M, Nn), "output shape %s, operands %d x %d" % (tuple(got.shape), M, Nn)
+    bad_total, examples = 0, []
+    for r0, ref, absref in device_ref_blocks(a, b, got.device, block_rows):
+        g = got[r0:r0 + ref.shape[0]].double()
+        bound = ref.abs() * 2.0 ** -7 + absref * 1e-5 + 2.0 ** -126
+        bad = ~((g - ref).abs() <= bound)
+        n = int(bad.sum().item())
+        if n and len(examples) < 5:
+            for i, j in bad.nonzero()[:5 - len(examples)].tolist():
+                examples.append("(%d, %d): got %r ref %r bound %r" % (r0 + i, j, g[i, j].item(), ref[i, j].item(),
+                                                                       bound[i, j].item()))
+        bad_total += n
+        del ref, absref, g, bound, bad
+    if bad_total:
+        raise AssertionError("%s: %d of %d outputs outside the bound; %s" % (what, bad_total, got.numel(),
+                                                                           "; ".join(examples)))

@@ -6,14 +6,16 @@ every (M, N, K) of the ragged sweep, run the whole training step on the GPU
 * casts, whole: every byte of the row and column copies of A, W and dOut
   (codes, scales and the zero padding of the tiled layout) against the
   oracle's cast of the whole bf16 input;
-* GEMMs, whole rows and whole columns: for each of fwd, dA and dB, one
-  complete output row in every 256-row tile row (a seeded position in it)
-  plus the first and last rows, and one complete output column in every
-  256-column tile column plus the first and last columns, against the oracle
-  GEMM of those operand rows (tolerance 2^-7 |ref| + 1e-5 sum|ab| + 2^-126).
-  Every 256 x 256 output tile of every launch, in every round of the
-  persistent kernel's tile walk, thus has checked outputs; outputs with
-  64 rows or columns or fewer are checked completely along that side.
+* GEMMs, every output: for each of fwd, dA and dB, the whole output against
+  the exact product of the oracle's copies (dequantized by the oracle, summed
+  in float64 by torch.matmul on the device, a library DGEMM independent of
+  the kernels under test), tolerance 2^-7 |ref| + 1e-5 sum|ab| + 2^-126;
+* GEMMs against the oracle's own GEMM: one complete output row in every
+  256-row tile row (a seeded position in it) plus the first and last rows,
+  and one complete output column in every 256-column tile column plus the
+  first and last columns, same tolerance.  This pins the device reference:
+  every 256 x 256 output tile of every launch has outputs checked against
+  both.
 The oracle casts the whole bf16 inputs; the GEMM references come from those
 oracle copies.
 """
@@ -24,7 +26,7 @@ import torch
 import oracle
 import mxfp4_block_scaled_cast_amd as mx
 from mxfp4_block_scaled_cast_amd import workloads as W
-from gpu_util import say, to_device, assert_gemm_close, assert_operand_equal
+from gpu_util import say, to_device, assert_gemm_close, assert_gemm_whole, assert_operand_equal
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -69,7 +71,8 @@ def check_casts(bits, T, name, what):
 
 
 def check_gemm(out, a, b, rng, what):
-    """Complete output rows and columns of out = a . b^T (a, b oracle (q, s) copies)."""
+    """Complete output rows and columns of out = a . b^T (a, b oracle (q, s) copies) against the
+    oracle's GEMM, then every output against the device reference of the same copies."""
     qa, sa = a
     qb, sb = b
     rows = tile_picks(qa.shape[0], rng)
@@ -81,6 +84,7 @@ def check_gemm(out, a, b, rng, what):
     ref, ab = oracle.gemm(qa, sa, qb[cols], sb[cols])
     got = out[:, torch.from_numpy(cols).to(dev)].float().cpu().numpy()
     assert_gemm_close(got, ref, ab, "%s columns %s" % (what, cols[:8].tolist()))
+    assert_gemm_whole(out, a, b, "%s whole output" % what)
 
 
 def check_step(a_bits, w_bits, g_bits, A, Wt, G, out, da, dw, rng, what):

@@ -12,7 +12,7 @@ import torch
 import oracle
 import mxfp4_block_scaled_cast_amd as mx
 from mxfp4_block_scaled_cast_amd import workloads as W
-from gpu_util import say, to_device, bf16_to_f64, assert_gemm_close, bf16_rne_of_exact
+from gpu_util import say, to_device, bf16_to_f64, assert_gemm_close, bf16_rne_of_exact, device_ref_blocks
 
 pytestmark = pytest.mark.gpu
 
@@ -30,6 +30,25 @@ def oracle_nt(a_bits, b_bits):
     qa, sa = oracle.cast_rows(a_bits)
     qb, sb = oracle.cast_rows(b_bits)
     return oracle.gemm(qa, sa, qb, sb)
+
+
+# The device reference of the full-size whole-output checks (oracle-dequantized operands, float64
+# torch.matmul on the device) against the oracle's own GEMM: ragged shape, several row blocks, one
+# operand with all-zero and subnormal-magnitude blocks.
+def test_device_reference_matches_oracle():
+    M, N, K = 700, 530, 2080
+    a = W.ragged_values((M, K), 41)
+    b = W.ragged_values((N, K), 43)
+    qa, sa = oracle.cast_rows(a)
+    qb, sb = oracle.cast_rows(b)
+    ref, absref = oracle.gemm(qa, sa, qb, sb)
+    say("device reference %dx%dx%d" % (M, N, K))
+    got_ref, got_abs = np.empty_like(ref), np.empty_like(absref)
+    for r0, r, ab in device_ref_blocks((qa, sa), (qb, sb), torch.device("cuda:0"), block_rows=256):
+        got_ref[r0:r0 + r.shape[0]] = r.cpu().numpy()
+        got_abs[r0:r0 + r.shape[0]] = ab.cpu().numpy()
+    assert np.all(np.abs(got_ref - ref) <= 1e-12 * absref + 1e-300)
+    assert np.all(np.abs(got_abs - absref) <= 1e-12 * absref + 1e-300)
 
 
 def test_tiny_config():
