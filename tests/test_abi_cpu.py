@@ -406,6 +406,23 @@ def test_split_workspace_query_and_validation():
         assert f(FAKE, FAKE, FAKE, FAKE, 4, 4, 32, FAKE, 4, None, 0, None) == -3
 
 
+def test_panel_split_workspace_sizes():
+    # 128 x 128 panel blocks split over the contraction only for 2^20 outputs or more over a contraction
+    # of 8192 or more, up to one workgroup per CU of 256; the partials are S copies of the 64 x 64 partial
+    # blocks (16 KB of fp32 each)
+    L = N.lib()
+    blk = 64 * 64 * 4
+    assert L.mxfp4_gemm_workspace_bytes(16384, 128, 14336) == 2 * (256 * 2) * blk   # 128 blocks, 2 splits
+    assert L.mxfp4_gemm_workspace_bytes(128, 14336, 16384) == 2 * (2 * 224) * blk   # 112 blocks, 2 splits
+    assert L.mxfp4_gemm_workspace_bytes(1024, 1024, 14336) == 4 * (16 * 16) * blk   # 64 blocks, 4 splits
+    assert L.mxfp4_gemm_workspace_bytes(130, 8150, 8320) == 2 * (3 * 128) * blk     # ragged: 64-row blocks
+    # unsplit panel launches (a side of 512 or more, blocks for half the CUs) and shapes that stay on
+    # the skinny kernel without a split (its own split needs fewer blocks than CUs)
+    assert L.mxfp4_gemm_workspace_bytes(2048, 2048, 4096) == 0
+    assert L.mxfp4_gemm_workspace_bytes(1000, 2000, 1024) == 0
+    assert L.mxfp4_gemm_workspace_bytes(16384, 128, 4096) == 0
+
+
 def test_step_workspace_holds_the_split_partials():
     # the step's workspace adds one region for the largest split of its three products
     def op(rows, k):
