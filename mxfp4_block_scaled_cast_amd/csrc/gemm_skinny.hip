@@ -1,6 +1,8 @@
-// Skinny MXFP4 / MXFP8 GEMM for gfx950: out[M, N] = bf16( A[M, K] . B[N, K]^T ) when the
-// output is too small to fill the chip with 256 x 256 tiles, including the split of a long
-// contraction over several workgroups.
+// MXFP4 / MXFP8 GEMMs for gfx950 whose output is too small to fill the chip with 256 x 256
+// tiles: out[M, N] = bf16( A[M, K] . B[N, K]^T ) by the skinny kernel (operands straight from
+// memory, the contraction split over the waves of a workgroup) or, for MXFP4 outputs with both
+// sides of 128 rows or more, the panel kernel (128 x 128 blocks sharing operand panels through
+// LDS); both split a long contraction over several workgroups when given a workspace.
 //
 // Operation: jax-aiter README, Supported ops, "FP4 GEMM (low-level)" in the A[M,K] @ B[N,K]^T
 // convention of its GEMM rows; the same products as the tiled kernels of gemm.hip, for the small
@@ -310,10 +312,10 @@ __global__ __launch_bounds__(256, 2) void gemm_panel_kernel(
         (int)(kt256 * 1024), (int)kRsrcFlags);
     typedef u32x4 Stage[9];
     auto load_chunk = [&](int c, Stage& R, bool valid) {
-#pragma unroll
         // offsets are pushed past the descriptor by setting bit 31 (arithmetic, not a select: a
         // select on the uniform flag becomes branches around the loads, and the wait counts
         // then no longer see which loads are in flight)
+#pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int kt = c * 2 + (u & 1);
             const unsigned out_bit = (unsigned)(!(valid && kt < kt128)) << 31;
