@@ -19,7 +19,7 @@ import oracle
 import mxfp4_block_scaled_cast_amd as mx
 from mxfp4_block_scaled_cast_amd import workloads as W
 from gpu_util import (say, to_device, operand_rowmajor, operand_padding, bf16_to_f64, assert_gemm_close,
-                      bf16_rne_of_exact, fp8_truncation_bound)
+                      bf16_rne_of_exact, fp8_truncation_bound, device_ref_blocks)
 
 pytestmark = pytest.mark.gpu
 
@@ -103,6 +103,29 @@ def oracle_nt8(a_bits, b_bits):
     qb, sb = oracle.cast_rows_fp8(b_bits)
     ref, absref = oracle.gemm_fp8(qa, sa, qb, sb)
     return ref, absref, fp8_truncation_bound(qa, sa, qb, sb)
+
+
+# The device reference of the full-size whole-output FP8 check against the oracle: the oracle-dequantized
+# MXFP8 operands' float64 product equals the oracle's MXFP8 GEMM (to 1e-12 of sum|ab|), and the
+# envelope allowance (one matrix product of per-group exponent maxima) is never below the per-group
+# truncation bound of fp8_truncation_bound.
+def test_device_reference_fp8_matches_oracle():
+    M, N, K = 300, 260, 1056
+    a = W.ragged_values((M, K), 61)
+    b = W.ragged_values((N, K), 67)
+    qa, sa = oracle.cast_rows_fp8(a)
+    qb, sb = oracle.cast_rows_fp8(b)
+    ref, absref = oracle.gemm_fp8(qa, sa, qb, sb)
+    tight = fp8_truncation_bound(qa, sa, qb, sb)
+    say("fp8 device reference %dx%dx%d" % (M, N, K))
+    got_ref, got_abs, got_extra = np.empty_like(ref), np.empty_like(absref), np.empty_like(ref)
+    for r0, r, ab, ex in device_ref_blocks((qa, sa), (qb, sb), torch.device("cuda:0"), block_rows=128, fmt=8):
+        got_ref[r0:r0 + r.shape[0]] = r.cpu().numpy()
+        got_abs[r0:r0 + r.shape[0]] = ab.cpu().numpy()
+        got_extra[r0:r0 + r.shape[0]] = ex.cpu().numpy()
+    assert np.all(np.abs(got_ref - ref) <= 1e-12 * absref + 1e-300)
+    assert np.all(np.abs(got_abs - absref) <= 1e-12 * absref + 1e-300)
+    assert np.all(got_extra >= tight)
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 32), (17, 128, 32), (33, 65, 96), (64, 64, 64), (100, 200, 288),

@@ -2,10 +2,12 @@
 them (--fp8-wgrad, --fused-producers), checked whole like test_gpu_fullsize:
 
 * FP8 wgrad: every byte of the MXFP4 row and MXFP8 column copies of A and dOut against the
-  oracle's casts of the whole inputs, and complete rows (one per 256-row tile row, plus the
+  oracle's casts of the whole inputs; complete rows (one per 256-row tile row, plus the
   edges) and complete columns (one per 256-column tile column) of dB from the MXFP8 GEMM
   against the oracle's MXFP8 GEMM (MXFP4 bar plus the FP8 MFMA's in-group truncation
-  allowance);
+  allowance); and every output of dB against the device reference of the oracle's copies
+  (dequantized by the oracle, float64 matmul on the device) with the envelope form of that
+  allowance (one matrix product; never below the per-group bound);
 * fused producers: SiLU-and-mul + cast of the 8192 x 28672 gate/up output and RMSNorm (+
   residual) + cast of the 8192 x 4096 block input -- every produced value, residual sum and
   statistic, and every byte of the row and column copies, against the oracle producers and
@@ -18,7 +20,7 @@ import torch
 import oracle
 import mxfp4_block_scaled_cast_amd as mx
 from mxfp4_block_scaled_cast_amd import workloads as W
-from gpu_util import say, to_device, assert_gemm_close, assert_operand_equal, fp8_truncation_bound
+from gpu_util import say, to_device, assert_gemm_close, assert_gemm_whole, assert_operand_equal, fp8_truncation_bound
 from test_gpu_fullsize import tile_picks
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -57,6 +59,7 @@ def test_fp8_wgrad_step_full_size(index):
     got = dw[:, torch.from_numpy(cols).cuda()].float().cpu().numpy()
     extra = fp8_truncation_bound(qg, sg, qa[cols], sa[cols])
     assert_gemm_close(got, ref, ab, "full-size FP8 dB columns " + name, extra)
+    assert_gemm_whole(dw, (qg, sg), (qa, sa), "full-size FP8 dB whole output " + name, fmt=8)
 
 
 def test_silu_mul_cast_full_size():

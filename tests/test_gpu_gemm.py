@@ -44,7 +44,7 @@ def test_device_reference_matches_oracle():
     ref, absref = oracle.gemm(qa, sa, qb, sb)
     say("device reference %dx%dx%d" % (M, N, K))
     got_ref, got_abs = np.empty_like(ref), np.empty_like(absref)
-    for r0, r, ab in device_ref_blocks((qa, sa), (qb, sb), torch.device("cuda:0"), block_rows=256):
+    for r0, r, ab, _ in device_ref_blocks((qa, sa), (qb, sb), torch.device("cuda:0"), block_rows=256):
         got_ref[r0:r0 + r.shape[0]] = r.cpu().numpy()
         got_abs[r0:r0 + r.shape[0]] = ab.cpu().numpy()
     assert np.all(np.abs(got_ref - ref) <= 1e-12 * absref + 1e-300)
