@@ -1,5 +1,5 @@
 """Parity of the step variants at the full 8B MLP per-GPU sizes, launched as bench.py launches
-them (--fp8-wgrad, --fused-producers), checked whole like test_gpu_fullsize:
+them (--fp8-wgrad, --hadamard-grad, --fused-producers), checked whole like test_gpu_fullsize:
 
 * FP8 wgrad: every byte of the MXFP4 row and MXFP8 column copies of A and dOut against the
   oracle's casts of the whole inputs; complete rows (one per 256-row tile row, plus the
@@ -8,6 +8,10 @@ them (--fp8-wgrad, --fused-producers), checked whole like test_gpu_fullsize:
   allowance); and every output of dB against the device reference of the oracle's copies
   (dequantized by the oracle, float64 matmul on the device) with the envelope form of that
   allowance (one matrix product; never below the per-group bound);
+* Hadamard gradient recipe: the casts as the bench's --hadamard-grad launches them (A and W:
+  column copies block-transformed; dOut: both copies transformed and divided by 32), every byte
+  of every copy against the oracle's (transformed) casts of the whole inputs, and every output
+  of fwd, dA and dB against the device reference of the oracle's copies;
 * fused producers: SiLU-and-mul + cast of the 8192 x 28672 gate/up output and RMSNorm (+
   residual) + cast of the 8192 x 4096 block input -- every produced value, residual sum and
   statistic, and every byte of the row and column copies, against the oracle producers and
@@ -60,6 +64,33 @@ def test_fp8_wgrad_step_full_size(index):
     extra = fp8_truncation_bound(qg, sg, qa[cols], sa[cols])
     assert_gemm_close(got, ref, ab, "full-size FP8 dB columns " + name, extra)
     assert_gemm_whole(dw, (qg, sg), (qa, sa), "full-size FP8 dB whole output " + name, fmt=8)
+
+
+@pytest.mark.parametrize("index", [0, 1], ids=["gate_up", "down"])
+def test_hadamard_grad_step_full_size(index):
+    name, M, Nn, K = W.LLAMA8B_MLP[index]
+    a, w, g = W.projection_inputs("llama8b_mlp", index, M, Nn, K)
+    dev = torch.device("cuda:0")
+    say("full-size Hadamard-grad step %s M=%d N=%d K=%d" % (name, M, Nn, K))
+    A = mx.cast_hadamard(to_device(a), False, True, 0)
+    Wt = mx.cast_hadamard(to_device(w), False, True, 0)
+    G = mx.cast_hadamard(to_device(g), True, True, 5)
+    ws = mx.gemm_workspace([(M, Nn, K), (M, K, Nn), (Nn, K, A.col.k)], dev)
+    out = mx.gemm_nt(A.row, Wt.row, ws=ws)
+    da = mx.gemm_nn(G.row, Wt.col, ws=ws)
+    dw = mx.gemm_nt(G.col, A.col, ws=ws)
+    torch.cuda.synchronize()
+    copies = {}
+    for what, T, x, t_row, shift in (("A", A, a, False, 0), ("W", Wt, w, False, 0), ("dOut", G, g, True, 5)):
+        row = oracle.cast_rows_hadamard(x, shift) if t_row else oracle.cast_rows(x)
+        assert_operand_equal(T.row, row[0], row[1], "Hadamard %s %s row copy" % (name, what))
+        col = oracle.cast_cols_hadamard(x, shift)
+        assert_operand_equal(T.col, col[0], col[1], "Hadamard %s %s column copy" % (name, what))
+        copies[what] = (row, col)
+    del a, w, g
+    assert_gemm_whole(out, copies["A"][0], copies["W"][0], "Hadamard %s fwd whole output" % name)
+    assert_gemm_whole(da, copies["dOut"][0], copies["W"][1], "Hadamard %s dA whole output" % name)
+    assert_gemm_whole(dw, copies["dOut"][1], copies["A"][1], "Hadamard %s dB whole output" % name)
 
 
 def test_silu_mul_cast_full_size():
