@@ -18,7 +18,8 @@ over a second pass of K steps that records an event after every launch.
 
 Other modes: `--workload llama70b | llama8b_attn` (the same step at other
 projection shapes), `--workload ragged` (the edge sweep), `--ceilings` (the
-sustained MFMA and HBM rates of the bench's probes), `--copy-calibration`
+sustained MFMA and HBM rates of the bench's probes), `--cast-scaling` (the dual
+cast's marginal rate and fixed cost per launch), `--copy-calibration`
 (a plain device copy for scaling HBM counters).
 """
 import argparse
@@ -75,6 +76,9 @@ def parse():
     p.add_argument("--ceilings", action="store_true",
                    help="only measure the chip's sustained FP4 MFMA rate (random and constant operands) and HBM "
                         "stream rates (read, copy, the dual cast's read/write mix) with the bench's probes")
+    p.add_argument("--cast-scaling", action="store_true",
+                   help="only time the dual cast at several sizes (1 GiB read before each launch) and report its "
+                        "marginal rate and fixed cost per launch")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device copy of COPY_BYTES (for scaling HBM counters), then exit")
     a = p.parse_args()
@@ -438,10 +442,54 @@ def ceilings():
     print(json.dumps(result), flush=True)
 
 
+def cast_scaling():
+    """Dual cast of x [R, C] (bf16 N(0,1)) for R = 4096 .. 32768 at C = 4096 and 14336, a 1 GiB read
+    before every launch (no operand served from the MALL), hip events around each launch: per size the
+    median time and rate, and per C the marginal rate between the two largest sizes (the stream's own
+    rate) and the fixed cost per launch it leaves (launch latency, ramp and tail).  Prints one JSON line."""
+    import numpy as np
+    import torch
+    import mxfp4_block_scaled_cast_amd as mx
+    dev = torch.device("cuda:0")
+    flush = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    result = {"metric": "dual cast time against size", "bytes_per_element": 3.0625, "sizes": [], "fits": []}
+    for C in (4096, 14336):
+        pts = []
+        for R in (4096, 8192, 16384, 32768):
+            x = torch.randn(R, C, device=dev, generator=g).to(torch.bfloat16)
+            t = mx.cast_dual(x)
+            ts = []
+            for rep in range(15):
+                flush.sum()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                mx.cast_dual(x, t.row, t.col)
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3)
+            us = float(np.median(ts[3:]))
+            nb = R * C * 3.0625
+            pts.append((nb, us))
+            result["sizes"].append({"R": R, "C": C, "us": round(us, 2), "gbps": round(nb / us * 1e-3, 1),
+                                    "frac_of_hbm": round(nb / us * 1e-3 / HBM_PEAK_GBPS, 4)})
+            del x, t
+        (b0, t0), (b1, t1) = pts[-2], pts[-1]
+        marginal = (b1 - b0) / (t1 - t0) * 1e-3
+        result["fits"].append({"C": C, "marginal_gbps": round(marginal, 1),
+                               "marginal_frac_of_hbm": round(marginal / HBM_PEAK_GBPS, 4),
+                               "fixed_us": round(t1 - b1 / marginal * 1e-3, 2)})
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.cast_scaling:
+        cast_scaling()
         return
     if args.ceilings:
         ceilings()
