@@ -147,6 +147,24 @@ def test_panel_split(M, N, K):
     assert torch.equal(outs[0], outs[2])
 
 
+# The largest contraction the boundary accepts, K = 2^23 (65536 code tiles and 32768 scale tiles per
+# row): 1 x 32 and 17 x 32 outputs on the skinny kernel, without a workspace (the waves of a workgroup
+# split the contraction) and with one (the split over workgroups at its largest chunk counts).
+@pytest.mark.parametrize("M,N", [(1, 32), (17, 32)])
+def test_max_contraction(M, N):
+    K = 1 << 23
+    a = W.normal_bf16((M, K), 1.0, 71 + M)
+    b = W.normal_bf16((N, K), 1.0, 73 + N)
+    ref, absref = oracle_nt(a, b)
+    ad, bd = mx.cast(to_device(a)), mx.cast(to_device(b))
+    assert mx.gemm_workspace_bytes(M, N, K) > 0
+    for ws in (None, mx.gemm_workspace([(M, N, K)], "cuda:0")):
+        say("gemm_nt at K = 2^23 M=%d N=%d workspace=%s" % (M, N, ws is not None))
+        out = mx.gemm_nt(ad, bd, ws=ws)
+        torch.cuda.synchronize()
+        assert_gemm_close(bf16_to_f64(out), ref, absref, "K = 2^23 %dx%d ws=%s" % (M, N, ws is not None))
+
+
 @pytest.mark.parametrize("M,N,K", [(384, 320, 768), (2048, 4096, 1024)])
 def test_same_scale_bit_exact(M, N, K):
     # skinny (few tiles) and persistent tiled kernels
