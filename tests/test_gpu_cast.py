@@ -6,7 +6,7 @@ import torch
 import oracle
 import mxfp4_block_scaled_cast_amd as mx
 from mxfp4_block_scaled_cast_amd import workloads as W
-from gpu_util import say, to_device, operand_rowmajor, operand_padding
+from gpu_util import say, to_device, operand_rowmajor, operand_padding, assert_operand_equal
 
 pytestmark = pytest.mark.gpu
 
@@ -180,3 +180,23 @@ def test_dual_pair_strided_inputs():
     for bits, (row, col) in zip((a, b), outs):
         check_row(bits, row, "strided pair row")
         check_col(bits, col, "strided pair col")
+
+
+# A tensor of more than 2^31 elements (16384 x 131104 = 2^31 + 524288, 4.3 GB of bf16): element, code
+# and scale offsets past 32 bits in both copies.  Every byte of the row and column copies (padding
+# included) against the oracle's casts of the whole input.
+@pytest.mark.slow
+def test_dual_cast_past_2_31_elements():
+    R, C = 16384, 131104
+    dev = torch.device("cuda:0")
+    x = W.ragged_values_torch((R, C), 8801, dev).view(torch.bfloat16)
+    say("cast_dual %d x %d (%d elements)" % (R, C, R * C))
+    t = mx.cast_dual(x)
+    torch.cuda.synchronize()
+    bits = x.view(torch.int16).cpu().numpy().view(np.uint16)
+    del x
+    q, s = oracle.cast_rows(bits)
+    assert_operand_equal(t.row, q, s, "2^31+ row copy")
+    del q, s
+    q, s = oracle.cast_cols(bits)
+    assert_operand_equal(t.col, q, s, "2^31+ column copy")
