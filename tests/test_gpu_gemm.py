@@ -225,13 +225,16 @@ def test_empty_and_zero_k():
     b = mx.empty_operand(16, 64, "cuda:0")
     out = mx.gemm_nt(a, b)
     assert out.shape == (0, 16)
-    say("gemm K=0")
-    a0 = mx.empty_operand(8, 0, "cuda:0")
-    b0 = mx.empty_operand(16, 0, "cuda:0")
-    out = torch.full((8, 16), 7.0, dtype=torch.bfloat16, device="cuda:0")
-    mx.gemm_nt(a0, b0, out=out)
-    torch.cuda.synchronize()
-    assert torch.all(out == 0)
+    # K = 0 writes zeros: a skinny output, and outputs the panel kernel takes (its descriptors then
+    # span no bytes, every load reads zero)
+    for M, N in ((8, 16), (1000, 2000), (4096, 4096)):
+        say("gemm K=0 M=%d N=%d" % (M, N))
+        a0 = mx.empty_operand(M, 0, "cuda:0")
+        b0 = mx.empty_operand(N, 0, "cuda:0")
+        out = torch.full((M, N), 7.0, dtype=torch.bfloat16, device="cuda:0")
+        mx.gemm_nt(a0, b0, out=out)
+        torch.cuda.synchronize()
+        assert torch.all(out == 0)
 
 
 def test_nn_form_with_column_copy():
