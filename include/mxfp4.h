@@ -198,9 +198,11 @@ int mxfp4_gemm_nn(const void* a_q, const void* a_s, const void* bcol_q, const vo
  * A3 with a workspace -- the same product as mxfp4_gemm_nt (and, on a column
  * copy, mxfp4_gemm_nn), for outputs too small to fill the chip behind a long
  * contraction (A8: e.g. the dA of an LM head, 1..17 x 4096 or 4096 x 32
- * outputs over a contraction of 128256): several workgroups then share each
- * output block, write fp32 partial sums to ws, and a second kernel adds them
- * in a fixed order and rounds to bf16.
+ * outputs over a contraction of 128256; 16384 x 128 outputs over 14336):
+ * several workgroups then share each output block, write fp32 partial sums
+ * to ws, and a second kernel adds them in a fixed order and rounds to bf16.
+ * The result does not depend on the workspace beyond the tolerance of the
+ * product (the split count changes only the fp32 summation order).
  * mxfp4_gemm_workspace_bytes: the bytes that split needs for these sizes (0
  *   when the launch does not split, or for invalid sizes).  Host only.
  * mxfp4_gemm_nt_ws: arguments and errors as mxfp4_gemm_nt; ws is device

@@ -262,8 +262,8 @@ def _check_formats(a, b, fmt):
 
 def gemm_nt(a: MxOperand, b: MxOperand, out=None, ws=None):
     """out[M, N] = dq(a)[M, K] . dq(b)[N, K]^T in bf16 (two MXFP4 operands).  With ws (a uint8
-    scratch tensor, see gemm_workspace) a long contraction behind a small output is split over
-    several workgroups (mxfp4_gemm_nt_ws)."""
+    scratch tensor, see gemm_workspace) the contraction of an output too small for the tiled
+    kernels may be split over several workgroups (mxfp4_gemm_nt_ws)."""
     _check_formats(a, b, 4)
     return _gemm(N.lib().mxfp4_gemm_nt, "mxfp4_gemm_nt", a, b, out, ws)
 
