@@ -404,13 +404,15 @@ int gemm_fp4_bf16_bwd_ex(const void* dout, const void* w_col_q, const void* w_co
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the
  * inference forward of gemm_fp4_bf16_fwd_qw (training = 0) with no workspace
- * argument.  A's row copy -- the forward's only scratch -- goes into a device
- * array of MXFP4_NOALLOC_SCRATCH_BYTES that the library itself holds on each
- * GPU it runs on until the process ends; nothing is allocated per call.
+ * argument.  The forward's scratch -- A's row copy, and the partial sums where
+ * the GEMM splits its contraction over workgroups -- goes into a device array
+ * of MXFP4_NOALLOC_SCRATCH_BYTES that the library itself holds on each GPU it
+ * runs on until the process ends; nothing is allocated per call.
  *   out[M, N] = bf16( cast(a)[M, K] . W_row^T )
  * Arguments, requirements and errors as gemm_fp4_bf16_fwd_qw, plus
- * MXFP4_ERANGE when A's row copy (gemm_fp4_bf16_workspace_bytes_qw(M, N, K, 0)
- * bytes, about 0.53 * M * K) exceeds MXFP4_NOALLOC_SCRATCH_BYTES, and
+ * MXFP4_ERANGE when that scratch (gemm_fp4_bf16_workspace_bytes_qw(M, N, K, 0)
+ * bytes, about 0.53 * M * K plus any split) exceeds
+ * MXFP4_NOALLOC_SCRATCH_BYTES, and
  * MXFP4_ELAUNCH if the runtime cannot give the array's device address.
  * Every call on one GPU uses the same array: calls that overlap on one GPU
  * (other streams, other threads) race and must be serialized by the caller.

@@ -1,8 +1,9 @@
 """The allocation-free inference forward (gemm_fp4_bf16_fwd_qw_noalloc) against the entry point
 it varies, gemm_fp4_bf16_fwd_qw with training = 0 and a caller workspace: two calls in a row,
 the second with a smaller input (the library's scratch array keeps the first call's contents),
-each bit-identical to the workspace form and within the GEMM bar of the oracle.  Also: sizes
-past the scratch array are rejected before anything runs."""
+each bit-identical to the workspace form and within the GEMM bar of the oracle; the same for
+two calls whose GEMMs split their contraction (partials in the scratch array as well).  Also:
+sizes past the scratch array are rejected before anything runs."""
 import numpy as np
 import pytest
 import torch
@@ -49,6 +50,15 @@ def test_two_calls_second_smaller():
     # ragged skinny shape whose row copy is a fraction of the first one left in the array
     run_pair(2048, 4096, 512, 501)
     run_pair(17, 160, 288, 503)
+
+
+def test_split_contractions_through_the_scratch():
+    # the split partials live in the scratch array too: first a 128 x 8192 output over 8192 on the
+    # panel kernel (4 splits, 16 MiB of partials after A's row copy), then a smaller 17 x 1024 output
+    # over 20480 on the skinny kernel (its partials where the first call's were)
+    assert mx.gemm_workspace_bytes(128, 8192, 8192) > 0 and mx.gemm_workspace_bytes(17, 1024, 20480) > 0
+    run_pair(128, 8192, 8192, 507)
+    run_pair(17, 1024, 20480, 509)
 
 
 def test_sizes_past_the_scratch_are_rejected():
