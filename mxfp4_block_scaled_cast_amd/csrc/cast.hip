@@ -7,7 +7,7 @@
 // nearest-even with saturation.
 //
 // Work decomposition.  A workgroup of 256 threads owns a tile of TILE_R rows
-// x 256 columns of x.  Loads are 16 bytes per lane with consecutive lanes on
+// (64, or 32 for small plain casts: see cast_tile_rows) x 256 columns of x.  Loads are 16 bytes per lane with consecutive lanes on
 // consecutive columns (a wave reads 2 rows x 512 contiguous bytes per
 // instruction).  Four consecutive lanes hold one 32-element row block; its
 // amax is a packed-u16 max in registers followed by two DPP quad exchanges,
@@ -242,6 +242,7 @@ __global__ __launch_bounds__(256, 4) void cast_kernel(const uint16_t* __restrict
                                                    CastSeg second) {
     static_assert((ROWF == 4 || ROWF == 8) && (COLF == 4 || COLF == 8), "MXFP4 or MXFP8");
     static_assert(!(HROW && ROWF == 8) && !(HCOL && COLF == 8), "the transform goes with MXFP4 copies");
+    static_assert(TILE_R == 32 || TILE_R == 64, "32- or 64-row tiles");
     constexpr int NI = TILE_R / 8;  // 16-byte loads per thread
     const int t = threadIdx.x;
     int bid = blockIdx.x;
@@ -394,10 +395,11 @@ __global__ __launch_bounds__(256, 4) void cast_kernel(const uint16_t* __restrict
         const int64_t kt256_col = (Rp + 255) >> 8;
         const int64_t col16 = (C + 15) & ~(int64_t)15;
         const int64_t col128 = (C + 127) & ~(int64_t)127;
-        constexpr int ITEMS = TILE_R / 64;          // 32x2 strips per thread
+        constexpr int ITEMS = TILE_R >= 64 ? TILE_R / 64 : 1;  // 32x2 strips per thread
 #pragma unroll
         for (int it = 0; it < ITEMS; ++it) {
             const int item = it * 256 + t;
+            if (TILE_R < 64 && item >= 128) continue;  // a 32-row tile has 128 strips
             const int cp = item & 127;              // column pair within the tile
             const int rb = item >> 7;               // 32-row block within the tile
             const int64_t c = c0 + cp * 2;
@@ -530,18 +532,40 @@ __global__ __launch_bounds__(256, 4) void cast_kernel(const uint16_t* __restrict
 
 }  // namespace mx
 
+namespace mx {
+
+// Rows covered by the grid: the row copy's padded scale rows (a multiple of
+// 128), and for the dual cast the column copy's padded contraction (a
+// multiple of 256).
+static int64_t cast_rows_cover(int64_t R, bool dual) {
+    return dual ? ((R + 255) & ~(int64_t)255) : ((R + 127) & ~(int64_t)127);
+}
+
+// Tile rows of a plain MXFP4 cast (no transform, no MXFP8 copy) covering
+// `tiles64` 64-row tiles in all: a workgroup's tile takes ~9 us of the chip's
+// steady stream, and the grid's tail (the last workgroups running with part
+// of the chip idle) costs about one tile's time, so casts of few tiles use
+// 32-row tiles.  Measured (dual casts, 1 GiB read before each, 64 vs 32 rows,
+// us): 2048 x 4096 12.4 -> 11.5, 4096 x 4096 18.2 -> 16.4, 8192 x 4096 28.4 ->
+// 27.3, 16384 x 4096 46.4 -> 45.8 (4096 tiles), 4096 x 14336 42.8 -> 42.5;
+// larger casts were 0.4-3.7% slower with 32 rows (8192 x 28672 140.9 ->
+// 146.1), their column copy then leaving in 16-byte pieces of more lines.
+constexpr int64_t kSmallCastTiles = 4096;
+static int cast_tile_rows(int64_t tiles64) { return tiles64 <= kSmallCastTiles ? 32 : 64; }
+
+}  // namespace mx
+
 // Launchers (internal, called by the C ABI layer after validation).
 // transform_row / transform_col: Walsh-Hadamard on the row / column copy, the
 // transformed copies divided by 2^hshift.
 extern "C" hipError_t mx_launch_cast_f(const void* x, int64_t R, int64_t C, int64_t ldx, void* q_row, void* s_row,
                                        void* q_col, void* s_col, bool dual, int row_fmt, int col_fmt, bool transform_row,
                                        bool transform_col, int hshift, hipStream_t stream) {
-    constexpr int TILE_R = 64;
-    // rows covered: the row copy's padded scale rows (a multiple of 128), and for
-    // the dual cast the column copy's padded contraction (a multiple of 256)
-    const int64_t rows_cover = dual ? ((R + 255) & ~(int64_t)255) : ((R + 127) & ~(int64_t)127);
-    const int64_t n_rtiles = (rows_cover + TILE_R - 1) / TILE_R;
+    const int64_t rows_cover = mx::cast_rows_cover(R, dual);
     const int64_t n_ctiles = (C + 255) / 256;
+    const bool plain = row_fmt == 4 && col_fmt == 4 && !transform_row && !transform_col;
+    const int tile_r = plain ? mx::cast_tile_rows((rows_cover + 63) / 64 * n_ctiles) : 64;
+    const int64_t n_rtiles = (rows_cover + tile_r - 1) / tile_r;
     const int64_t total = n_rtiles * n_ctiles;
     if (total == 0) return hipSuccess;
     if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
@@ -551,10 +575,14 @@ extern "C" hipError_t mx_launch_cast_f(const void* x, int64_t R, int64_t C, int6
     uint8_t *qc = static_cast<uint8_t*>(q_col), *scl = static_cast<uint8_t*>(s_col);
     const int nr = (int)n_rtiles, nc = (int)n_ctiles;
     const mx::ProdArgs P{};
-#define MX_CAST(D, HR, HC, RF, CF)                                                                         \
-    hipLaunchKernelGGL((mx::cast_kernel<TILE_R, D, HR, HC, RF, CF>), grid, block, 0, stream, xb, R, C, ldx, qr, \
-                       sr, D ? qc : nullptr, D ? scl : nullptr, nr, nc, hshift, P, mx::kOneTensor)
-    if (row_fmt == 8 || col_fmt == 8) {
+#define MX_CAST_T(T, D, HR, HC, RF, CF)                                                                      \
+    hipLaunchKernelGGL((mx::cast_kernel<T, D, HR, HC, RF, CF>), grid, block, 0, stream, xb, R, C, ldx, qr, sr,   \
+                       D ? qc : nullptr, D ? scl : nullptr, nr, nc, hshift, P, mx::kOneTensor)
+#define MX_CAST(D, HR, HC, RF, CF) MX_CAST_T(64, D, HR, HC, RF, CF)
+    if (plain && tile_r == 32) {
+        if (dual) MX_CAST_T(32, true, false, false, 4, 4);
+        else MX_CAST_T(32, false, false, false, 4, 4);
+    } else if (row_fmt == 8 || col_fmt == 8) {
         if (transform_row || transform_col) return hipErrorInvalidValue;
         if (!dual) {
             if (row_fmt != 8) return hipErrorInvalidValue;
@@ -576,6 +604,7 @@ extern "C" hipError_t mx_launch_cast_f(const void* x, int64_t R, int64_t C, int6
         else MX_CAST(true, false, false, 4, 4);
     }
 #undef MX_CAST
+#undef MX_CAST_T
     return hipGetLastError();
 }
 
@@ -652,11 +681,11 @@ __global__ __launch_bounds__(256) void rms_stats_kernel(const uint16_t* x, const
     if (lane == 0) rstd[row] = 1.0 / sqrt(ss / (double)D + (double)eps);
 }
 
-// Grid of the cast kernel over x [R, C] (TILE_R = 64 rows x 256 columns per
+// Grid of the cast kernel over x [R, C] (tile_r rows x 256 columns per
 // workgroup), covering the padded rows of the copies it writes.
-static bool cast_grid(int64_t R, int64_t C, bool dual, int& nr, int& nc) {
-    const int64_t rows_cover = dual ? ((R + 255) & ~(int64_t)255) : ((R + 127) & ~(int64_t)127);
-    const int64_t n_rtiles = (rows_cover + 63) / 64, n_ctiles = (C + 255) / 256;
+static bool cast_grid(int64_t R, int64_t C, bool dual, int tile_r, int& nr, int& nc) {
+    const int64_t rows_cover = cast_rows_cover(R, dual);
+    const int64_t n_rtiles = (rows_cover + tile_r - 1) / tile_r, n_ctiles = (C + 255) / 256;
     if (n_rtiles * n_ctiles > 0x7FFFFFFF) return false;
     nr = (int)n_rtiles;
     nc = (int)n_ctiles;
@@ -668,7 +697,7 @@ static hipError_t launch_produced_cast(const uint16_t* x, int64_t R, int64_t C, 
                                        void* s_row, void* q_col, void* s_col, bool dual, int col_fmt,
                                        const ProdArgs& P, hipStream_t stream) {
     int nr = 0, nc = 0;
-    if (!cast_grid(R, C, dual, nr, nc)) return hipErrorInvalidValue;
+    if (!cast_grid(R, C, dual, 64, nr, nc)) return hipErrorInvalidValue;
     if ((int64_t)nr * nc == 0) return hipSuccess;
     const dim3 grid((unsigned)((int64_t)nr * nc)), block(256);
     uint8_t *qr = static_cast<uint8_t*>(q_row), *sr = static_cast<uint8_t*>(s_row);
@@ -732,8 +761,13 @@ extern "C" hipError_t mx_launch_cast_dual_pair(const void* x0, int64_t R0, int64
                                                void* s_row0, void* q_col0, void* s_col0, const void* x1, int64_t R1,
                                                int64_t C1, int64_t ldx1, void* q_row1, void* s_row1, void* q_col1,
                                                void* s_col1, hipStream_t stream) {
+    // one tile size for both tensors, chosen by their 64-row tiles together
+    const int64_t tiles64 = (mx::cast_rows_cover(R0, true) + 63) / 64 * ((C0 + 255) / 256) +
+                            (mx::cast_rows_cover(R1, true) + 63) / 64 * ((C1 + 255) / 256);
+    const int tile_r = mx::cast_tile_rows(tiles64);
     int nr0 = 0, nc0 = 0, nr1 = 0, nc1 = 0;
-    if (!mx::cast_grid(R0, C0, true, nr0, nc0) || !mx::cast_grid(R1, C1, true, nr1, nc1)) return hipErrorInvalidValue;
+    if (!mx::cast_grid(R0, C0, true, tile_r, nr0, nc0) || !mx::cast_grid(R1, C1, true, tile_r, nr1, nc1))
+        return hipErrorInvalidValue;
     const int64_t t0 = (int64_t)nr0 * nc0, t1 = (int64_t)nr1 * nc1;
     const int64_t split = (t0 + 7) & ~(int64_t)7;
     if (split + t1 > 0x7FFFFFFF) return hipErrorInvalidValue;
@@ -741,9 +775,10 @@ extern "C" hipError_t mx_launch_cast_dual_pair(const void* x0, int64_t R0, int64
     const mx::CastSeg second = {static_cast<const uint16_t*>(x1), R1, C1, ldx1,
                                 static_cast<uint8_t*>(q_row1), static_cast<uint8_t*>(s_row1),
                                 static_cast<uint8_t*>(q_col1), static_cast<uint8_t*>(s_col1), nr1, nc1, (int)split};
-    hipLaunchKernelGGL((mx::cast_kernel<64, true, false, false, 4, 4>), dim3((unsigned)(split + t1)), dim3(256), 0,
-                       stream, static_cast<const uint16_t*>(x0), R0, C0, ldx0, static_cast<uint8_t*>(q_row0),
-                       static_cast<uint8_t*>(s_row0), static_cast<uint8_t*>(q_col0), static_cast<uint8_t*>(s_col0),
-                       nr0, nc0, 0, mx::ProdArgs{}, second);
+    auto kern = tile_r == 32 ? mx::cast_kernel<32, true, false, false, 4, 4> : mx::cast_kernel<64, true, false, false, 4, 4>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(split + t1)), dim3(256), 0, stream, static_cast<const uint16_t*>(x0), R0,
+                       C0, ldx0, static_cast<uint8_t*>(q_row0), static_cast<uint8_t*>(s_row0),
+                       static_cast<uint8_t*>(q_col0), static_cast<uint8_t*>(s_col0), nr0, nc0, 0, mx::ProdArgs{},
+                       second);
     return hipGetLastError();
 }
