@@ -4,7 +4,8 @@
 A step is the whole hot path for each MLP projection (gate/up 8192x28672x4096
 and down 8192x4096x14336, M = 8192 tokens, one GPU's share):
     forward : dual casts of A and W (one launch), out = A . W^T (FP4 GEMM)
-    backward: dual cast dOut, dA = dOut . W (NN), dW = dOut^T . A (NT wgrad)
+    backward: dual cast dOut, dA = dOut . W (NN) and dW = dOut^T . A (NT wgrad),
+              the two in one persistent launch where that is faster
 every kernel launched through the C ABI on torch's current stream, inputs
 resident in HBM before timing starts.
 
@@ -189,12 +190,20 @@ def step_ops(P, L, sp, N, cached_weights=False, hadamard=False, fp8_wgrad=False)
     ops.append(("cast", name + ".cast_dual(dOut)", cast_dual(P["g"], P["g_row"], P["g_col"], True, True, 5), nb,
                 nb / (HBM_PEAK_GBPS * 1e9)))
     fl, _, _, t = gemm_roofline(M, K, Nn)
-    ops.append(("gemm", name + ".dA", gemm(L.mxfp4_gemm_nn, P["g_row"], P["w_col"], P["da"]), fl, t))
-    fl, _, _, t = gemm_roofline(Nn, K, M, fmt=8 if fp8_wgrad else 4)
     if fp8_wgrad:
+        ops.append(("gemm", name + ".dA", gemm(L.mxfp4_gemm_nn, P["g_row"], P["w_col"], P["da"]), fl, t))
+        fl, _, _, t = gemm_roofline(Nn, K, M, fmt=8)
         ops.append(("gemm8", name + ".dB(fp8)", gemm(L.mxfp8_gemm_nt, P["g_col"], P["a_col"], P["dw"]), fl, t))
     else:
-        ops.append(("gemm", name + ".dB", gemm(L.mxfp4_gemm_nt, P["g_col"], P["a_col"], P["dw"]), fl, t))
+        # dA and dB in one call, as the training backward makes them: one persistent launch with
+        # the XCDs divided between the two where that is faster, else two launches
+        fl1, _, _, t1 = gemm_roofline(Nn, K, M)
+        gr, wc, gc, ac, ws = P["g_row"], P["w_col"], P["g_col"], P["a_col"], P["gemm_ws"]
+        pair = lambda: L.mxfp4_gemm_nt_pair_ws(
+            gr.q.data_ptr(), gr.s.data_ptr(), wc.q.data_ptr(), wc.s.data_ptr(), M, K, Nn, P["da"].data_ptr(), K,
+            gc.q.data_ptr(), gc.s.data_ptr(), ac.q.data_ptr(), ac.s.data_ptr(), Nn, K, gc.k, P["dw"].data_ptr(), K,
+            ws.data_ptr(), ws.numel(), sp)
+        ops.append(("gemm", name + ".dA+dB", pair, fl + fl1, t + t1))
     return ops
 
 
@@ -658,12 +667,12 @@ def measure_workload(workload, args, steps, warmup, cpu_seconds, torch, mx, N, W
             result["fp8_gemm"] = {"kernel": "mxfp8 block-scaled GEMM (dB launches)", "achieved": round(t8, 1),
                                   "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(t8 / FP8_PEAK_TFLOPS, 4)}
         result["roofline"] = {"kernel": "mxfp4 block-scaled GEMM (%s launches)" % (
-                                  "fwd, dA" if gemm8_ms > 0 else "fwd, dA, dB"),
+                                  "fwd, dA" if gemm8_ms > 0 else "fwd; dA + dB paired"),
                               "bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": FP4_PEAK_TFLOPS,
                               "unit": "TFLOP/s", "frac": round(gemm_tflops / FP4_PEAK_TFLOPS, 4),
                               "avg_launch_ms": round(avg_gemm_ms, 4),
                               "flop_per_launch": gemm_work / gemm_launches,
-                              # counters were taken over the 8B MLP step's six MXFP4 launches: the
+                              # counters were taken over the 8B MLP step's MXFP4 GEMM launches: the
                               # figure belongs to that workload's GEMM set only
                               "traffic": measured_traffic()
                               if workload == "llama8b_mlp" and gemm8_ms == 0 else None}

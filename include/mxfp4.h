@@ -218,6 +218,33 @@ int mxfp4_gemm_nt_ws(const void* a_q, const void* a_s, const void* b_q, const vo
                      int64_t K, void* out, int64_t ldo, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * A5 + A6 in one call -- two independent MXFP4 products, as the training
+ * backward's dA = dOut . W and dB = dOut^T . A, which read the copies of one
+ * dOut cast (jax-aiter README, "MXFP4 training architecture"):
+ *   out0[M0, N0] = A0 . B0^T over K0,   out1[M1, N1] = A1 . B1^T over K1.
+ * Each product's arguments, alignment, limits and errors as for
+ * mxfp4_gemm_nt_ws (products 0, then 1, validated before anything is
+ * enqueued); out0 and out1 must not overlap each other or any operand.
+ * When both outputs take the tiled kernel (16-byte aligned rows, N % 8 == 0)
+ * with the same trip structure and a cost model favours it, both run in one
+ * persistent launch with the chip's 8 XCDs divided between them: what a
+ * launch costs beyond its tile rounds (the pipeline's first fill, the last
+ * round's output written back) is paid once and the rounds of the two
+ * balance.  Otherwise the two products run as two mxfp4_gemm_nt_ws calls in
+ * order, sharing ws.  Either way each output is bit-identical to its own
+ * mxfp4_gemm_nt_ws call.
+ * mxfp4_gemm_pair_split: the XCDs (of 8) the paired launch gives product 0
+ * for these sizes (16-byte aligned outputs, ldo = N, a chip of 256 CUs); 0
+ * when the products run as two launches, and for invalid sizes.  Host only.
+ */
+int mxfp4_gemm_nt_pair_ws(const void* a0_q, const void* a0_s, const void* b0_q, const void* b0_s, int64_t M0,
+                          int64_t N0, int64_t K0, void* out0, int64_t ldo0, const void* a1_q, const void* a1_s,
+                          const void* b1_q, const void* b1_s, int64_t M1, int64_t N1, int64_t K1, void* out1,
+                          int64_t ldo1, void* ws, size_t ws_bytes, hipStream_t stream);
+
+int mxfp4_gemm_pair_split(int64_t M0, int64_t N0, int64_t K0, int64_t M1, int64_t N1, int64_t K1);
+
+/*
  * F3 -- MXFP8 (E4M3) operands for the FP8 dB of the jax-aiter README,
  * "MXFP4 training architecture" (its backward runs dB as an FP8 dot while
  * the forward pass and dA stay FP4).  Argument rules, alignment and errors

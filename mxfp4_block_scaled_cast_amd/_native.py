@@ -34,6 +34,8 @@ SIGNATURES = [
     ("mxfp4_gemm_nn", _i32, [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _p]),
     ("mxfp4_gemm_workspace_bytes", _sz, [_i64, _i64, _i64]),
     ("mxfp4_gemm_nt_ws", _i32, [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _p, _sz, _p]),
+    ("mxfp4_gemm_nt_pair_ws", _i32, [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i64] * 2 + [_p, _sz, _p]),
+    ("mxfp4_gemm_pair_split", _i32, [_i64] * 6),
     ("gemm_fp4_bf16_workspace_bytes", _sz, [_i64, _i64, _i64, _i32]),
     ("gemm_fp4_bf16_fwd", _i32, [_p, _p, _i64, _i64, _i64, _p, _p, _sz, _i32, _p]),
     ("gemm_fp4_bf16_bwd", _i32, [_p, _i64, _i64, _i64, _p, _sz, _p, _p, _p]),

@@ -244,6 +244,46 @@ def _gemm(fn, name, a: MxOperand, b: MxOperand, out, ws=None):
     return out
 
 
+def _out_for(a: MxOperand, b: MxOperand, out):
+    if a.k != b.k:
+        raise ValueError("contraction lengths differ: %d vs %d" % (a.k, b.k))
+    M, Nn = a.rows, b.rows
+    if out is None:
+        return torch.empty((M, Nn), dtype=torch.bfloat16, device=a.q.device)
+    if out.dtype != torch.bfloat16 or out.shape != (M, Nn) or out.stride(1) != 1:
+        raise ValueError("out must be a bfloat16 [%d, %d] tensor with unit column stride" % (M, Nn))
+    return out
+
+
+def gemm_nt_pair(a0: MxOperand, b0: MxOperand, a1: MxOperand, b1: MxOperand, out0=None, out1=None, ws=None):
+    """(out0, out1) = (dq(a0) . dq(b0)^T, dq(a1) . dq(b1)^T), two independent MXFP4 products in one
+    call (mxfp4_gemm_nt_pair_ws): one persistent launch with the chip's XCDs divided between them
+    where the cost model favours it (the training backward's dA and dB), else two launches in order
+    sharing ws.  Each output is bit-identical to gemm_nt with the same ws."""
+    for a, b in ((a0, b0), (a1, b1)):
+        _check_formats(a, b, 4)
+    out0, out1 = _out_for(a0, b0, out0), _out_for(a1, b1, out1)
+    if out0.device != out1.device:
+        raise ValueError("both outputs must be on one device")
+    wp, wn = 0, 0
+    if ws is not None:
+        if ws.dtype != torch.uint8 or not ws.is_contiguous() or ws.device != out0.device:
+            raise ValueError("ws must be a contiguous uint8 tensor on the outputs' device")
+        wp, wn = ws.data_ptr(), ws.numel()
+    st = N.lib().mxfp4_gemm_nt_pair_ws(
+        a0.q.data_ptr(), a0.s.data_ptr(), b0.q.data_ptr(), b0.s.data_ptr(), a0.rows, b0.rows, a0.k, out0.data_ptr(),
+        out0.stride(0), a1.q.data_ptr(), a1.s.data_ptr(), b1.q.data_ptr(), b1.s.data_ptr(), a1.rows, b1.rows, a1.k,
+        out1.data_ptr(), out1.stride(0), wp or None, wn, _stream(out0.device))
+    N.check(st, "mxfp4_gemm_nt_pair_ws")
+    return out0, out1
+
+
+def gemm_pair_split(M0, N0, K0, M1, N1, K1):
+    """XCDs (of 8) the paired launch of gemm_nt_pair gives its first product for these sizes
+    (aligned outputs, ldo = N); 0 when the two run as two launches."""
+    return int(N.lib().mxfp4_gemm_pair_split(int(M0), int(N0), int(K0), int(M1), int(N1), int(K1)))
+
+
 def gemm_workspace_bytes(M, Nn, K):
     """Bytes of scratch the split contraction of out[M, N] (contraction K) uses; 0 if it does not split."""
     return int(N.lib().mxfp4_gemm_workspace_bytes(int(M), int(Nn), int(K)))

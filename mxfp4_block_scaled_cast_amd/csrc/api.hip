@@ -46,6 +46,12 @@ extern "C" hipError_t mx_launch_gemm_ws(const void* aq, const void* as, const vo
                                         int64_t N, int64_t K, void* out, int64_t ldo, int fmt, void* ws,
                                         int64_t ws_bytes, hipStream_t stream);
 extern "C" int64_t mx_gemm_split_bytes(int64_t M, int64_t N, int64_t K, int fmt);
+extern "C" hipError_t mx_launch_gemm_pair_ws(const void* aq0, const void* as0, const void* bq0, const void* bs0,
+                                             int64_t M0, int64_t N0, int64_t K0, void* out0, int64_t ldo0,
+                                             const void* aq1, const void* as1, const void* bq1, const void* bs1,
+                                             int64_t M1, int64_t N1, int64_t K1, void* out1, int64_t ldo1, int fmt,
+                                             void* ws, int64_t ws_bytes, hipStream_t stream);
+extern "C" int mx_gemm_pair_split(int64_t M0, int64_t N0, int64_t K0, int64_t M1, int64_t N1, int64_t K1);
 extern "C" hipError_t mx_launch_cast_dual_pair(const void* x0, int64_t R0, int64_t C0, int64_t ldx0, void* q_row0,
                                                void* s_row0, void* q_col0, void* s_col0, const void* x1, int64_t R1,
                                                int64_t C1, int64_t ldx1, void* q_row1, void* s_row1, void* q_col1,
@@ -331,6 +337,28 @@ int mxfp4_gemm_nt_ws(const void* a_q, const void* a_s, const void* b_q, const vo
     return status_of(mx_launch_gemm_ws(a_q, a_s, b_q, b_s, M, N, K, out, ldo, 4, ws, bytes, stream));
 }
 
+int mxfp4_gemm_nt_pair_ws(const void* a0_q, const void* a0_s, const void* b0_q, const void* b0_s, int64_t M0,
+                          int64_t N0, int64_t K0, void* out0, int64_t ldo0, const void* a1_q, const void* a1_s,
+                          const void* b1_q, const void* b1_s, int64_t M1, int64_t N1, int64_t K1, void* out1,
+                          int64_t ldo1, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int st = validate_gemm(a0_q, a0_s, b0_q, b0_s, M0, N0, K0, out0, ldo0);
+    if (st != MXFP4_OK) return st;
+    if ((st = validate_gemm(a1_q, a1_s, b1_q, b1_s, M1, N1, K1, out1, ldo1)) != MXFP4_OK) return st;
+    if ((M0 == 0 || N0 == 0) && (M1 == 0 || N1 == 0)) return MXFP4_OK;
+    if (ws && !aligned16(ws)) return MXFP4_EALIGN;
+    if ((st = check_device()) != MXFP4_OK) return st;
+    const int64_t bytes = ws ? (int64_t)std::min(ws_bytes, (size_t)INT64_MAX) : 0;
+    return status_of(mx_launch_gemm_pair_ws(a0_q, a0_s, b0_q, b0_s, M0, N0, K0, out0, ldo0, a1_q, a1_s, b1_q, b1_s,
+                                            M1, N1, K1, out1, ldo1, 4, ws, bytes, stream));
+}
+
+int mxfp4_gemm_pair_split(int64_t M0, int64_t N0, int64_t K0, int64_t M1, int64_t N1, int64_t K1) {
+    if (M0 < 0 || N0 < 0 || K0 < 0 || M1 < 0 || N1 < 0 || K1 < 0 || K0 % 32 != 0 || K1 % 32 != 0 ||
+        M0 > kMaxDim || N0 > kMaxDim || M1 > kMaxDim || N1 > kMaxDim || K0 > kMaxK || K1 > kMaxK)
+        return 0;
+    return mx_gemm_pair_split(M0, N0, K0, M1, N1, K1);
+}
+
 int mxfp8_operand_layout_of(int64_t rows, int64_t k, mxfp4_operand_layout* out) {
     if (!out || rows < 0 || k < 0 || k % 32 != 0) return MXFP4_EINVAL;
     const OperandSizes sz = operand_sizes8(rows, k);
@@ -539,6 +567,13 @@ int step_bwd(const void* dout, bool own_w, const void* w_col_q, const void* w_co
     hipError_t e = mx_launch_cast_f(dout, M, N, N, base + L.g_row_q, base + L.g_row_s, base + L.g_col_q,
                                     base + L.g_col_s, true, 4, wfmt, hadamard, hadamard,
                                     hadamard ? kHadamardShift : 0, stream);
+    if (e == hipSuccess && da && dw && wfmt == 4) {
+        // both products read the dOut copies just made: one launch where it pays
+        e = mx_launch_gemm_pair_ws(base + L.g_row_q, base + L.g_row_s, wq, wsc, M, K, N, da, K, base + L.g_col_q,
+                                   base + L.g_col_s, base + L.a_col_q, base + L.a_col_s, N, K, Mp, dw, K, 4,
+                                   base + L.split, L.split_bytes, stream);
+        return status_of(e);
+    }
     if (e == hipSuccess && da)
         e = mx_launch_gemm_ws(base + L.g_row_q, base + L.g_row_s, wq, wsc, M, K, N, da, K, 4, base + L.split,
                               L.split_bytes, stream);

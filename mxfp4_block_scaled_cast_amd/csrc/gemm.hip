@@ -667,13 +667,33 @@ __device__ __forceinline__ void persist_epilogue(const f32x16 (&acc)[4][4], uint
     }
 }
 
-template <bool SINGLE, int FMT>
-__global__ __launch_bounds__(256, 1) void gemm_persist_kernel(const uint8_t* __restrict__ aq,
-                                                              const uint8_t* __restrict__ as,
-                                                              const uint8_t* __restrict__ bq,
-                                                              const uint8_t* __restrict__ bs, int M, int N, int K,
-                                                              uint16_t* __restrict__ out, int64_t ldo, int tiles_m,
-                                                              int tiles_n, int group_m) {
+// One product of a persistent launch: out[M, N] (row stride ldo) = A . B^T over
+// K, in tiles_m x tiles_n output tiles, run by G workgroups.
+struct PersistProblem {
+    const uint8_t* aq;
+    const uint8_t* as;
+    const uint8_t* bq;
+    const uint8_t* bs;
+    uint16_t* out;
+    int64_t ldo;
+    int M, N, K, tiles_m, tiles_n, G;
+};
+
+// XCD-aware slot of workgroup `bid` among G workgroups spread over nx XCDs
+// (bid % nx is the XCD): each XCD takes a contiguous range of slots per round.
+__device__ __forceinline__ int xcd_remap_n(int bid, int G, int nx) {
+    const int x = bid % nx, idx = bid / nx;
+    return x * (G / nx) + min(x, G % nx) + idx;
+}
+
+// PAIR: two independent products of the same K-tile parity (SINGLE) in one
+// grid of 8 x 32 workgroups: the workgroups of XCDs 0 .. split_xcds-1 run p0,
+// the others p1 (each XCD's L2 then holds the panels of one product); the
+// workgroups beyond a product's G leave at once.  Without PAIR, p0 runs on the
+// whole grid (G = gridDim.x).
+template <bool SINGLE, int FMT, bool PAIR>
+__global__ __launch_bounds__(256, 1) void gemm_persist_kernel(PersistProblem p0, PersistProblem p1, int split_xcds,
+                                                              int group_m) {
     __shared__ __attribute__((aligned(1024))) char lds_raw[NST * STAGE];
     lds_cptr lds = (lds_cptr)lds_raw;
 
@@ -681,9 +701,29 @@ __global__ __launch_bounds__(256, 1) void gemm_persist_kernel(const uint8_t* __r
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave >> 1, wn = wave & 1;
 
+    int slot, G;
+    PersistProblem Q = p0;
+    if constexpr (PAIR) {
+        const int xcd = blockIdx.x & 7;
+        const bool second = xcd >= split_xcds;
+        if (second) Q = p1;
+        const int nx = second ? 8 - split_xcds : split_xcds;
+        const int lb = (blockIdx.x >> 3) * nx + (xcd - (second ? split_xcds : 0));
+        G = Q.G;
+        if (lb >= G) return;
+        slot = xcd_remap_n(lb, G, nx);
+    } else {
+        G = gridDim.x;
+        slot = xcd_remap(blockIdx.x, G);  // each XCD takes a contiguous range of slots per round
+    }
+    const uint8_t* __restrict__ aq = Q.aq;
+    const uint8_t* __restrict__ as = Q.as;
+    const uint8_t* __restrict__ bq = Q.bq;
+    const uint8_t* __restrict__ bs = Q.bs;
+    uint16_t* __restrict__ out = Q.out;
+    const int64_t ldo = Q.ldo;
+    const int M = Q.M, N = Q.N, K = Q.K, tiles_m = Q.tiles_m, tiles_n = Q.tiles_n;
     const int total = tiles_m * tiles_n;
-    const int G = gridDim.x;
-    const int slot = xcd_remap(blockIdx.x, G);  // each XCD takes a contiguous range of slots per round
 
     const int nkt = k_tiles<FMT>(K);
     const int trips = (nkt + NST - 1) / NST;  // 1 with SINGLE, else >= 2; K tiles past nkt read as zero
@@ -770,10 +810,79 @@ __global__ __launch_bounds__(256, 1) void gemm_persist_kernel(const uint8_t* __r
 
 namespace mx {
 
+// Tiles are ordered in groups of 4 tile rows: an XCD's 32 concurrent tiles then span 4 A panels
+// and 8 B panels (0.3-2% faster per GEMM than groups of 8 rows, 0.8% on the MLP, 8B attention
+// and 70B steps; groups of 16 were slower).
+constexpr int kGroupM = 4;
+
+// Workgroups of a persistent launch of `tiles` tiles on `slots` CUs: as many rounds as the tiles
+// need, every workgroup the same number of tiles.
+static int64_t balanced_grid(int64_t tiles, int64_t slots) {
+    const int64_t rounds = (tiles + slots - 1) / slots;
+    return (tiles + rounds - 1) / rounds;
+}
+
 // 256 x 256 tiles need both sides >= 128 and enough tiles to fill half the CUs.
 static bool uses_tiles(int64_t M, int64_t N, int64_t K, int64_t cus) {
     const int64_t tiles_m = (M + PBM - 1) / PBM, tiles_n = (N + PBN - 1) / PBN;
     return K > 0 && M >= 128 && N >= 128 && tiles_m * tiles_n * 2 >= cus;
+}
+
+// The persistent kernel needs 16-byte aligned output rows, N % 8 == 0, and a tile's output
+// bytes (256 rows) addressable by a 31-bit buffer offset.
+static bool persist_ok(const uint16_t* o16, int64_t ldo, int64_t N) {
+    return (reinterpret_cast<uintptr_t>(o16) & 15u) == 0 && (ldo & 7) == 0 && (N & 7) == 0 &&
+           (int64_t)PBM * ldo * 2 < 0x7FFFFFF0ll;
+}
+
+// Two independent products in one persistent launch (XCDs split between them) or one after the
+// other, by a cost model in K tiles per workgroup: a tile costs its K tiles (a multiple of 4)
+// plus kEpiKTiles (its epilogue), and a second launch kLaunchKTiles more.  The pair is taken
+// only when it comes out at least 1% cheaper: what it gains is the tail of a partial last round
+// (8B QKV's dB, 384 tiles: -6.5% on dA + dB; the MLP down projection's dB, 896 tiles: -1.9%),
+// while two large products in one launch share the caches between them (70B down, 3584 + 3584
+// tiles in even rounds either way: +1.3% paired).
+constexpr int64_t kEpiKTiles = 1;
+constexpr int64_t kLaunchKTiles = 3;
+
+struct PairPlan {
+    bool pair;
+    int split_xcds;  // XCDs of the first product
+    int64_t g0, g1;  // workgroups of each
+};
+
+static PairPlan plan_pair(int64_t tiles0, int64_t kt0, int64_t tiles1, int64_t kt1, int64_t cus) {
+    PairPlan P{false, 0, 0, 0};
+    constexpr int64_t kXcds = 8, kPerXcd = 32;
+    if (cus != kXcds * kPerXcd) return P;
+    const int64_t c0 = kt0 + kEpiKTiles, c1 = kt1 + kEpiKTiles;
+    const auto rounds = [](int64_t t, int64_t g) { return (t + g - 1) / g; };
+    // one after the other: both launches' rounds and one more launch cost than the pair
+    const int64_t seq = rounds(tiles0, cus) * c0 + rounds(tiles1, cus) * c1 + kLaunchKTiles;
+    int64_t best = seq;
+    for (int s = 1; s < kXcds; ++s) {
+        const int64_t w0 = s * kPerXcd, w1 = (kXcds - s) * kPerXcd;
+        const int64_t t = std::max(rounds(tiles0, w0) * c0, rounds(tiles1, w1) * c1);
+        if (t < best && t * 100 <= seq * 99) {
+            best = t;
+            P = PairPlan{true, s, balanced_grid(tiles0, w0), balanced_grid(tiles1, w1)};
+        }
+    }
+    return P;
+}
+
+// The paired launch of two MXFP4 products (outputs assumed to meet persist_ok): both on the
+// tiled kernel, with the same trip structure (one trip per tile or several), and cheaper than
+// two launches by the model.
+static PairPlan plan_pair_for(int64_t M0, int64_t N0, int64_t K0, int64_t M1, int64_t N1, int64_t K1, int64_t cus) {
+    if (M0 <= 0 || N0 <= 0 || M1 <= 0 || N1 <= 0 || !uses_tiles(M0, N0, K0, cus) || !uses_tiles(M1, N1, K1, cus))
+        return PairPlan{false, 0, 0, 0};
+    const int64_t nkt0 = (K0 + PBK - 1) / PBK, nkt1 = (K1 + PBK - 1) / PBK;
+    const int64_t tiles0 = ((M0 + PBM - 1) / PBM) * ((N0 + PBN - 1) / PBN);
+    const int64_t tiles1 = ((M1 + PBM - 1) / PBM) * ((N1 + PBN - 1) / PBN);
+    if ((nkt0 <= NST) != (nkt1 <= NST) || tiles0 > 0x7FFFFFFF || tiles1 > 0x7FFFFFFF) return PairPlan{false, 0, 0, 0};
+    const auto kt4 = [](int64_t n) { return (n + NST - 1) / NST * NST; };  // K tiles a tile runs
+    return plan_pair(tiles0, kt4(nkt0), tiles1, kt4(nkt1), cus);
 }
 
 template <int FMT>
@@ -784,24 +893,17 @@ static hipError_t launch_gemm(const uint8_t* a8, const uint8_t* as8, const uint8
     if (!uses_tiles(M, N, K, num_cus())) return mx_launch_skinny(a8, as8, b8, bs8, M, N, K, o16, ldo, FMT, ws, ws_bytes,
                                                                  stream);
     if (tiles_m * tiles_n > 0x7FFFFFFF) return hipErrorInvalidValue;
-    // tiles are ordered in groups of 4 tile rows: an XCD's 32 concurrent tiles then span 4 A panels
-    // and 8 B panels (0.3-2% faster per GEMM than groups of 8 rows, 0.8% on the MLP, 8B attention
-    // and 70B steps; groups of 16 were slower)
-    const int group_m = 4;
+    const int group_m = kGroupM;
     const int64_t nkt = FMT == 8 ? (K + 63) / 64 : (K + 127) / 128;
-    // persistent kernel: needs 16-byte aligned output rows, N % 8 == 0, and a tile's output
-    // bytes (256 rows) addressable by a 31-bit buffer offset
-    const bool persist = (reinterpret_cast<uintptr_t>(o16) & 15u) == 0 && (ldo & 7) == 0 && (N & 7) == 0 &&
-                         (int64_t)PBM * ldo * 2 < 0x7FFFFFF0ll;
-    if (persist) {
+    if (persist_ok(o16, ldo, N)) {
         // as many rounds as the tiles need on all CUs, spread evenly: every workgroup
         // gets the same number of tiles (896 tiles run as 224 x 4, not 256 x 3.5)
         const int64_t tiles_all = tiles_m * tiles_n;
-        const int64_t rounds = (tiles_all + num_cus() - 1) / num_cus();
-        const int64_t grid = (tiles_all + rounds - 1) / rounds;
-        auto kern = nkt <= NST ? gemm_persist_kernel<true, FMT> : gemm_persist_kernel<false, FMT>;
-        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, stream, a8, as8, b8, bs8, (int)M, (int)N, (int)K,
-                           o16, ldo, (int)tiles_m, (int)tiles_n, group_m);
+        const int64_t grid = balanced_grid(tiles_all, num_cus());
+        const PersistProblem p{a8, as8, b8, bs8, o16, ldo, (int)M, (int)N, (int)K, (int)tiles_m, (int)tiles_n,
+                               (int)grid};
+        auto kern = nkt <= NST ? gemm_persist_kernel<true, FMT, false> : gemm_persist_kernel<false, FMT, false>;
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, stream, p, p, 8, kGroupM);
         return hipGetLastError();
     }
     // 8-byte output stores need an 8-byte aligned start for every row
@@ -836,6 +938,49 @@ extern "C" hipError_t mx_launch_gemm_f(const void* aq, const void* as, const voi
 extern "C" hipError_t mx_launch_gemm(const void* aq, const void* as, const void* bq, const void* bs, int64_t M,
                                      int64_t N, int64_t K, void* out, int64_t ldo, hipStream_t stream) {
     return mx_launch_gemm_f(aq, as, bq, bs, M, N, K, out, ldo, 4, stream);
+}
+
+// out0 = A0 . B0^T and out1 = A1 . B1^T (independent products, both MXFP4 or both MXFP8):
+// one persistent launch when both use the tiled kernel with the same trip structure and the
+// cost model favours it, else the two launches of mx_launch_gemm_ws in order (ws shared).
+extern "C" hipError_t mx_launch_gemm_pair_ws(const void* aq0, const void* as0, const void* bq0, const void* bs0,
+                                             int64_t M0, int64_t N0, int64_t K0, void* out0, int64_t ldo0,
+                                             const void* aq1, const void* as1, const void* bq1, const void* bs1,
+                                             int64_t M1, int64_t N1, int64_t K1, void* out1, int64_t ldo1, int fmt,
+                                             void* ws, int64_t ws_bytes, hipStream_t stream) {
+    using namespace mx;
+    uint16_t *o0 = static_cast<uint16_t*>(out0), *o1 = static_cast<uint16_t*>(out1);
+    const int64_t cus = num_cus();
+    if (fmt == 4 && persist_ok(o0, ldo0, N0) && persist_ok(o1, ldo1, N1)) {
+        const PairPlan P = plan_pair_for(M0, N0, K0, M1, N1, K1, cus);
+        if (P.pair) {
+            const PersistProblem p0{static_cast<const uint8_t*>(aq0), static_cast<const uint8_t*>(as0),
+                                    static_cast<const uint8_t*>(bq0), static_cast<const uint8_t*>(bs0),
+                                    o0, ldo0, (int)M0, (int)N0, (int)K0, (int)((M0 + PBM - 1) / PBM),
+                                    (int)((N0 + PBN - 1) / PBN), (int)P.g0};
+            const PersistProblem p1{static_cast<const uint8_t*>(aq1), static_cast<const uint8_t*>(as1),
+                                    static_cast<const uint8_t*>(bq1), static_cast<const uint8_t*>(bs1),
+                                    o1, ldo1, (int)M1, (int)N1, (int)K1, (int)((M1 + PBM - 1) / PBM),
+                                    (int)((N1 + PBN - 1) / PBN), (int)P.g1};
+            auto kern = (K0 + PBK - 1) / PBK <= NST ? gemm_persist_kernel<true, 4, true>
+                                                      : gemm_persist_kernel<false, 4, true>;
+            hipLaunchKernelGGL(kern, dim3((unsigned)cus), dim3(256), 0, stream, p0, p1, P.split_xcds, kGroupM);
+            return hipGetLastError();
+        }
+    }
+    hipError_t e = mx_launch_gemm_ws(aq0, as0, bq0, bs0, M0, N0, K0, out0, ldo0, fmt, ws, ws_bytes, stream);
+    if (e != hipSuccess) return e;
+    return mx_launch_gemm_ws(aq1, as1, bq1, bs1, M1, N1, K1, out1, ldo1, fmt, ws, ws_bytes, stream);
+}
+
+// XCDs the paired launch of two MXFP4 products gives the first (16-byte aligned outputs, ldo =
+// N), on a chip of 256 CUs (MI355X); 0 when they run as two launches.  Host only.
+extern "C" int mx_gemm_pair_split(int64_t M0, int64_t N0, int64_t K0, int64_t M1, int64_t N1, int64_t K1) {
+    if (N0 % 8 != 0 || N1 % 8 != 0 || (int64_t)mx::PBM * N0 * 2 >= 0x7FFFFFF0ll ||
+        (int64_t)mx::PBM * N1 * 2 >= 0x7FFFFFF0ll)
+        return 0;
+    const mx::PairPlan P = mx::plan_pair_for(M0, N0, K0, M1, N1, K1, 256);
+    return P.pair ? P.split_xcds : 0;
 }
 
 // Workspace the split contraction of out[M, N] (contraction K) can use, sized for a chip of

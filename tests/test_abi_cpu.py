@@ -438,3 +438,40 @@ def test_step_workspace_holds_the_split_partials():
                 L.mxfp4_gemm_workspace_bytes(Nn, K, Mp))
     assert split == L.mxfp4_gemm_workspace_bytes(M, K, Nn) > 0
     assert L.gemm_fp4_bf16_workspace_bytes(M, Nn, K, 1) == sum(r256(c) for c in copies) + r256(split)
+
+
+def test_pair_split_query():
+    # the training backward's dA [M, K] over N and dB [N, K] over M of the projection configs: one
+    # paired launch (4 XCDs each) where a partial last round of two launches goes away (8B QKV, O,
+    # MLP down), two launches where both already run in whole rounds (8B gate/up, 70B); uneven and
+    # ragged pairs take other splits; a product too small for the tiled kernels, differing trip
+    # structures, N % 8 != 0 and invalid sizes: two launches (0)
+    L = N.lib()
+    f = L.mxfp4_gemm_pair_split
+    for M, Nn, K in [(8192, 6144, 4096), (8192, 4096, 4096), (8192, 4096, 14336)]:
+        assert f(M, K, Nn, Nn, K, M) == 4, (M, Nn, K)
+    for M, Nn, K in [(8192, 28672, 4096), (8192, 10240, 8192), (8192, 57344, 8192), (8192, 8192, 28672)]:
+        assert f(M, K, Nn, Nn, K, M) == 0, (M, Nn, K)
+    assert f(2100, 4000, 1056, 4000, 2056, 2080) == 3
+    assert f(4096, 4096, 1024, 2048, 4096, 8192) == 2
+    assert f(17, 4096, 4096, 4096, 4096, 1024) == 0
+    assert f(2048, 4096, 512, 4096, 2048, 1024) == 0
+    assert f(2048, 4092, 1024, 2048, 4096, 1024) == 0
+    assert f(2048, 4096, 48, 2048, 4096, 1024) == 0
+    assert f(-1, 4096, 1024, 2048, 4096, 1024) == 0
+
+
+def test_pair_gemm_argument_validation():
+    # each product validated as mxfp4_gemm_nt_ws, product 0 first, before anything is enqueued
+    L = N.lib()
+    f = L.mxfp4_gemm_nt_pair_ws
+    good = (FAKE, FAKE, FAKE, FAKE, 4, 4, 32, FAKE, 4)
+    assert f(*good[:6], 48, *good[7:], *good, None, 0, None) == -1                 # K0 % 32
+    assert f(*good, *good[:6], 48, *good[7:], None, 0, None) == -1                 # K1 % 32
+    assert f(*good, *good[:5], 8, 32, FAKE, 4, None, 0, None) == -1                # ldo1 < N1
+    assert f(*good, FAKE, FAKE + 4, FAKE, FAKE, 4, 4, 32, FAKE, 4, None, 0, None) == -2   # misaligned scales
+    assert f(*good[:7], FAKE + 1, 4, *good, None, 0, None) == -2                     # odd output address
+    assert f(*good, *good, FAKE + 4, 64, None) == -2                                # misaligned workspace
+    assert f(*good[:4], 0, 4, 32, None, 4, *good[:4], 4, 0, 32, None, 4, None, 0, None) == 0   # both empty
+    if _no_gpu():
+        assert f(*good, *good, None, 0, None) == -3

@@ -2,7 +2,7 @@
 
 For each projection GEMM of the 8B attention, 8B MLP and 70B configs, and for
 every (M, N, K) of the ragged sweep, run the whole training step on the GPU
-(dual casts of A, W, dOut; fwd; dA; dB) and check:
+(dual casts of A, W, dOut; fwd; dA and dB in one paired call) and check:
 * casts, whole: every byte of the row and column copies of A, W and dOut
   (codes, scales and the zero padding of the tiled layout) against the
   oracle's cast of the whole bf16 input;
@@ -54,8 +54,8 @@ def run_step(a_d, w_d, g_d):
     Wt = mx.cast_dual(w_d)
     out = mx.gemm_nt(A.row, Wt.row, ws=ws)
     G = mx.cast_dual(g_d)
-    da = mx.gemm_nn(G.row, Wt.col, ws=ws)
-    dw = mx.gemm_nt(G.col, A.col, ws=ws)
+    # dA = dOut . W (the NT kernel on W's column copy) and dB in one call, as the step makes them
+    da, dw = mx.gemm_nt_pair(G.row, Wt.col, G.col, A.col, ws=ws)
     torch.cuda.synchronize()
     assert A.col.k == Mp and G.col.k == Mp
     return A, Wt, G, out, da, dw

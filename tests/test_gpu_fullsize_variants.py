@@ -77,8 +77,7 @@ def test_hadamard_grad_step_full_size(index):
     G = mx.cast_hadamard(to_device(g), True, True, 5)
     ws = mx.gemm_workspace([(M, Nn, K), (M, K, Nn), (Nn, K, A.col.k)], dev)
     out = mx.gemm_nt(A.row, Wt.row, ws=ws)
-    da = mx.gemm_nn(G.row, Wt.col, ws=ws)
-    dw = mx.gemm_nt(G.col, A.col, ws=ws)
+    da, dw = mx.gemm_nt_pair(G.row, Wt.col, G.col, A.col, ws=ws)
     torch.cuda.synchronize()
     copies = {}
     for what, T, x, t_row, shift in (("A", A, a, False, 0), ("W", Wt, w, False, 0), ("dOut", G, g, True, 5)):

@@ -12,7 +12,8 @@ import torch
 import oracle
 import mxfp4_block_scaled_cast_amd as mx
 from mxfp4_block_scaled_cast_amd import workloads as W
-from gpu_util import say, to_device, bf16_to_f64, assert_gemm_close, bf16_rne_of_exact, device_ref_blocks
+from gpu_util import (say, to_device, bf16_to_f64, assert_gemm_close, assert_gemm_whole, bf16_rne_of_exact,
+                      device_ref_blocks)
 
 pytestmark = pytest.mark.gpu
 
@@ -329,3 +330,64 @@ def test_split_contraction(M, N, K):
         assert_gemm_close(got, ref, absref, "split %s %dx%dx%d" % (what, M, N, K))
         outs.append(out.view(torch.int16).clone())
     assert torch.equal(outs[0], outs[2])  # same split, same order: same bits
+
+
+# Two products in one call (mxfp4_gemm_nt_pair_ws), as the training backward runs dA and dB.  Paired
+# launches (one persistent grid, XCDs 0..s-1 on the first product, the rest on the second): the dA /
+# dB shapes of a 2048 x 4096 x 2048 step (4 + 4 XCDs), one trip per tile (K = 512 and 256), a
+# ragged pair (9 x 16 tiles each, K = 1056 and 2080: 3 + 5 XCDs, so the slot mapping runs over 3
+# and 5 XCDs), an uneven pair (256 tiles over 1024 and 128 over 8192: 2 + 6 XCDs, part of the
+# second product's workgroups idle) and a partial last tile column (N = 4032).  Two launches: a
+# skinny product beside a tiled one (with its split contraction in ws), and tiled products whose
+# trip structures differ (one trip per tile against two).  Every output against the device reference
+# of the oracle's copies, and bit for bit against its own mxfp4_gemm_nt_ws call.
+PAIRS = [((2048, 4096, 4096), (4096, 4096, 2048), 4), ((2048, 4096, 512), (4096, 2048, 256), 4),
+         ((2100, 4000, 1056), (4000, 2056, 2080), 3), ((4096, 4096, 1024), (2048, 4096, 8192), 2),
+         ((2048, 4032, 1024), (2048, 4096, 1024), 4), ((17, 4096, 4096), (4096, 4096, 1024), 0),
+         ((2048, 4096, 512), (4096, 2048, 1024), 0)]
+
+
+@pytest.mark.parametrize("s0,s1,split", PAIRS, ids=["step", "one-trip", "ragged-3-5", "uneven-2-6", "partial-col",
+                                                    "skinny-tiled", "trips-differ"])
+def test_gemm_pair(s0, s1, split):
+    assert mx.gemm_pair_split(*s0, *s1) == split
+    ops, copies = [], []
+    for i, (M, N, K) in enumerate((s0, s1)):
+        a = W.ragged_values((M, K), 37 * M + K + i)
+        b = W.ragged_values((N, K), 41 * N + K + i)
+        ops.append((mx.cast(to_device(a)), mx.cast(to_device(b))))
+        copies.append((oracle.cast_rows(a), oracle.cast_rows(b)))
+    ws = mx.gemm_workspace([s0, s1], "cuda:0")
+    say("gemm_nt_pair %s + %s split %d" % (s0, s1, split))
+    out0, out1 = mx.gemm_nt_pair(ops[0][0], ops[0][1], ops[1][0], ops[1][1], ws=ws)
+    torch.cuda.synchronize()
+    for i, out in enumerate((out0, out1)):
+        alone = mx.gemm_nt(ops[i][0], ops[i][1], ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), alone.view(torch.int16)), "product %d differs from its own call" % i
+        assert_gemm_whole(out, copies[i][0], copies[i][1], "pair %s + %s, product %d" % (s0, s1, i))
+
+
+# Paired outputs inside wider buffers: ldo % 8 == 0 with 16-byte aligned starts (the paired launch),
+# and the second output at ldo % 8 == 4 (the pipelined kernel: two launches); columns around the
+# windows untouched.
+@pytest.mark.parametrize("extra1", [72, 4], ids=["paired", "second-ldo4"])
+def test_gemm_pair_output_leading_dimension(extra1):
+    shapes = ((2048, 4096, 1024), (4096, 2048, 1536))
+    ops, copies, bigs, views = [], [], [], []
+    for i, ((M, N, K), extra) in enumerate(zip(shapes, (64, extra1))):
+        a = W.normal_bf16((M, K), 1.0, 91 + i)
+        b = W.normal_bf16((N, K), 1.0, 93 + i)
+        ops.append((mx.cast(to_device(a)), mx.cast(to_device(b))))
+        copies.append((oracle.cast_rows(a), oracle.cast_rows(b)))
+        big = torch.full((M, N + extra + 8), -1.0, dtype=torch.bfloat16, device="cuda:0")
+        bigs.append(big)
+        views.append(big[:, 8:8 + N])
+    say("gemm_nt_pair ldo %d / %d" % (views[0].stride(0), views[1].stride(0)))
+    mx.gemm_nt_pair(ops[0][0], ops[0][1], ops[1][0], ops[1][1], out0=views[0], out1=views[1])
+    torch.cuda.synchronize()
+    for i, ((M, N, K), big, view) in enumerate(zip(shapes, bigs, views)):
+        assert_gemm_whole(view, copies[i][0], copies[i][1], "pair ldo, product %d" % i)
+        got = big.view(torch.int16)
+        minus1 = torch.tensor(-1.0, dtype=torch.bfloat16).view(torch.int16).item()
+        assert bool((got[:, :8] == minus1).all()) and bool((got[:, 8 + N:] == minus1).all())

@@ -36,9 +36,10 @@ def step_calls(a, w, g, out, ws, da, dw, flags):
                                    N.STEP_TRAINING | N.STEP_FP8_WGRAD], ids=["plain", "hadamard", "fp8wgrad"])
 # (17, 32768, 256): dA is 17 x 256 outputs over a contraction of 32768, split across workgroups
 # (partials in the workspace, then the reduction kernel) inside the captured graph;
-# (128, 8192, 8192): fwd and dA are 128 x 8192 outputs over 8192 on the panel kernel, split likewise
+# (128, 8192, 8192): fwd and dA are 128 x 8192 outputs over 8192 on the panel kernel, split likewise;
+# (2048, 2048, 4096): dA and dB in one paired persistent launch
 @pytest.mark.parametrize("M,Nn,K", [(256, 512, 1024), (17, 4096, 4096), (2048, 4096, 1024), (17, 32768, 256),
-                                    (128, 8192, 8192)])
+                                    (128, 8192, 8192), (2048, 2048, 4096)])
 def test_captured_step_replays_like_eager(M, Nn, K, flags):
     a = to_device(W.normal_bf16((M, K), 1.0, 1))
     w = to_device(W.normal_bf16((Nn, K), 0.05, 2))
@@ -49,6 +50,8 @@ def test_captured_step_replays_like_eager(M, Nn, K, flags):
     if (M, Nn, K) == (128, 8192, 8192):
         assert mx.gemm_workspace_bytes(M, Nn, K) > 0 and mx.gemm_workspace_bytes(M, K, Nn) > 0, \
             "fwd and dA should split their contraction"
+    if (M, Nn, K) == (2048, 2048, 4096):
+        assert mx.gemm_pair_split(M, K, Nn, Nn, K, M) > 0, "dA and dB should share one launch"
     out = torch.empty((M, Nn), dtype=torch.bfloat16, device="cuda:0")
     da = torch.empty((M, K), dtype=torch.bfloat16, device="cuda:0")
     dw = torch.empty((Nn, K), dtype=torch.bfloat16, device="cuda:0")

@@ -46,6 +46,16 @@ def test_step_matches_oracle(M, N, K):
     assert_gemm_close(bf16_to_f64(wt.grad), g, ga, "dB")
 
 
+# Steps whose dA and dB run as one paired launch (the XCDs divided between them): 2048 x 2048 x 4096
+# (128 tiles each, 4 + 4 XCDs) and a ragged 2100 x 2080 x 4000 (144 tiles each, 3 + 5 XCDs, M padded
+# to 2112 in the column copies).
+@pytest.mark.parametrize("M,N,K", [(2048, 2048, 4096), (2100, 2080, 4000)])
+def test_step_paired_backward_matches_oracle(M, N, K):
+    Mp = -(-M // 32) * 32
+    assert mx.gemm_pair_split(M, K, N, N, K, Mp) > 0, "dA and dB should share one launch"
+    test_step_matches_oracle(M, N, K)
+
+
 def test_inference_forward_uses_row_copies_only():
     M, N, K = 64, 96, 128
     a = W.normal_bf16((M, K), 1.0, 51)
