@@ -207,6 +207,15 @@ def step_ops(P, L, sp, N, cached_weights=False, hadamard=False, fp8_wgrad=False)
     return ops
 
 
+def gemm_kernel_launches(label, projs, L):
+    """GEMM kernel launches behind one GEMM op of step_ops: the paired dA + dB call is one launch
+    when it pairs and two otherwise; every other GEMM op one."""
+    if not label.endswith(".dA+dB"):
+        return 1
+    P = {p["name"]: p for p in projs}[label[:-len(".dA+dB")]]
+    return 1 if L.mxfp4_gemm_pair_split(P["M"], P["K"], P["N"], P["N"], P["K"], P["Mp"]) > 0 else 2
+
+
 def producer_op(P, L, sp):
     """The A operand made by a fused producer + cast instead of a plain cast: RMSNorm of the
     block input (gate/up) or SiLU-and-mul of the gate/up output (down).  Work: the producer's
@@ -623,7 +632,7 @@ def measure_workload(workload, args, steps, warmup, cpu_seconds, torch, mx, N, W
                 gemm8_work += work
             elif kind == "gemm":
                 gemm_ms += avg
-                gemm_launches += 1
+                gemm_launches += gemm_kernel_launches(label, projs, L)
                 gemm_work += work
             else:
                 cast_ms += avg
@@ -670,6 +679,7 @@ def measure_workload(workload, args, steps, warmup, cpu_seconds, torch, mx, N, W
                                   "fwd, dA" if gemm8_ms > 0 else "fwd; dA + dB paired"),
                               "bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": FP4_PEAK_TFLOPS,
                               "unit": "TFLOP/s", "frac": round(gemm_tflops / FP4_PEAK_TFLOPS, 4),
+                              "launches_per_step": gemm_launches,
                               "avg_launch_ms": round(avg_gemm_ms, 4),
                               "flop_per_launch": gemm_work / gemm_launches,
                               # counters were taken over the 8B MLP step's MXFP4 GEMM launches: the
