@@ -391,3 +391,33 @@ def test_gemm_pair_output_leading_dimension(extra1):
         got = big.view(torch.int16)
         minus1 = torch.tensor(-1.0, dtype=torch.bfloat16).view(torch.int16).item()
         assert bool((got[:, :8] == minus1).all()) and bool((got[:, 8 + N:] == minus1).all())
+
+
+# Non-finite inputs: a 32-block holding Inf or NaN gets the scale byte 0xFF (the E8M0 NaN) and zero
+# codes, and every output whose dot product touches such a block is NaN; the other outputs are
+# unaffected.  One Inf in a row of A and one NaN in a row of B, in K blocks that a skinny, a panel, a
+# persistent and a pipelined launch each reach (N % 8 != 0 for the last).
+@pytest.mark.parametrize("M,N,K", [(17, 300, 2080), (1000, 2100, 288), (2048, 4096, 1024), (2048, 4100, 1024)],
+                         ids=["skinny", "panel", "persistent", "pipelined"])
+def test_non_finite_blocks_give_nan_outputs(M, N, K):
+    a = W.normal_bf16((M, K), 1.0, 101 + M)
+    b = W.normal_bf16((N, K), 1.0, 103 + N)
+    ia, ka = M // 3, K - 40          # +Inf in A's last-but-one block of row ia
+    ib, kb = (2 * N) // 3, 70        # NaN in B's third block of row ib
+    a[ia, ka] = 0x7F80
+    b[ib, kb] = 0x7FC1
+    qa, sa = oracle.cast_rows(a)
+    qb, sb = oracle.cast_rows(b)
+    assert sa[ia, ka // 32] == 0xFF and sb[ib, kb // 32] == 0xFF
+    got = gpu_nt(a, b, "non-finite")
+    nan_mask = np.zeros((M, N), bool)
+    nan_mask[ia, :] = True
+    nan_mask[:, ib] = True
+    assert np.all(np.isnan(got[nan_mask])), "outputs touching a non-finite block must be NaN"
+    assert np.all(np.isfinite(got[~nan_mask]))
+    a2, b2 = a.copy(), b.copy()
+    a2[ia, :] = 0
+    b2[ib, :] = 0
+    ref, absref = oracle_nt(a2, b2)  # the finite outputs do not depend on the non-finite rows
+    keep = ~nan_mask
+    assert_gemm_close(np.where(keep, got, 0.0), np.where(keep, ref, 0.0), absref, "non-finite %dx%dx%d" % (M, N, K))
