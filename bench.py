@@ -20,7 +20,8 @@ over a second pass of K steps that records an event after every launch.
 Other modes: `--workload llama70b | llama8b_attn` (the same step at other
 projection shapes), `--workload ragged` (the edge sweep), `--ceilings` (the
 sustained MFMA and HBM rates of the bench's probes), `--cast-scaling` (the dual
-cast's marginal rate and fixed cost per launch), `--copy-calibration`
+cast's marginal rate and fixed cost per launch), `--gemm-data` (the MLP GEMM
+products on random against constant operands), `--copy-calibration`
 (a plain device copy for scaling HBM counters).
 """
 import argparse
@@ -80,6 +81,9 @@ def parse():
     p.add_argument("--cast-scaling", action="store_true",
                    help="only time the dual cast at several sizes (1 GiB read before each launch) and report its "
                         "marginal rate and fixed cost per launch")
+    p.add_argument("--gemm-data", action="store_true",
+                   help="only time the 8B MLP step's six GEMM products back to back on random and on constant "
+                        "operands (the same kernel, launches and bytes; less switching power), with the clock")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device copy of COPY_BYTES (for scaling HBM counters), then exit")
     a = p.parse_args()
@@ -501,8 +505,70 @@ def cast_scaling():
     print(json.dumps(result), flush=True)
 
 
+def gemm_data():
+    """The 8B MLP step's six GEMM products (fwd, dA, dB of gate/up and down), each launched back to back
+    (20 untimed, then 60 timed between two events) on random operands (bf16 N(0, 1) cast to MXFP4) and
+    on constant ones (every element 1.0: one code, one scale), alternating, with the shader clock
+    sampled over each timed run.  Same kernel, launch sequence and bytes moved; only the operands'
+    switching activity differs.  Prints one JSON line."""
+    import numpy as np
+    import torch
+    import mxfp4_block_scaled_cast_amd as mx
+    from mxfp4_block_scaled_cast_amd import workloads as W
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(17)
+    out = {"metric": "MXFP4 GEMM TFLOP/s by operand data (8B MLP products)", "products": []}
+    tot = {"random": [0.0, 0.0], "constant": [0.0, 0.0]}
+    for name, M, Nn, K in W.LLAMA8B_MLP:
+        for what, (m, n, k) in (("fwd", (M, Nn, K)), ("dA", (M, K, Nn)), ("dB", (Nn, K, M))):
+            ops = {}
+            for kind in ("random", "constant"):
+                if kind == "random":
+                    xa = torch.randn(m, k, device=dev, generator=g).to(torch.bfloat16)
+                    xb = torch.randn(n, k, device=dev, generator=g).to(torch.bfloat16)
+                else:
+                    xa = torch.ones(m, k, device=dev, dtype=torch.bfloat16)
+                    xb = torch.ones(n, k, device=dev, dtype=torch.bfloat16)
+                ops[kind] = (mx.cast(xa), mx.cast(xb))
+                del xa, xb
+            o = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+            row = {"product": "%s.%s" % (name, what), "M": m, "N": n, "K": k}
+            for kind in ("random", "constant", "random", "constant"):
+                a, b = ops[kind]
+                for _ in range(20):
+                    mx.gemm_nt(a, b, out=o)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                with ClockSampler() as cs:
+                    e0.record()
+                    for _ in range(60):
+                        mx.gemm_nt(a, b, out=o)
+                    e1.record()
+                    torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / 60
+                clk = cs.summary()
+                tf = 2.0 * m * n * k / us * 1e-6
+                row.setdefault(kind, []).append({"us": round(us, 1), "tflops": round(tf, 1),
+                                                 "sclk_mhz": clk["sclk_mhz"]["p50"] if clk and "sclk_mhz" in clk
+                                                 else None})
+            for kind in ("random", "constant"):
+                best = min(row[kind], key=lambda r: r["us"])
+                tot[kind][0] += 2.0 * m * n * k
+                tot[kind][1] += best["us"]
+            out["products"].append(row)
+            del ops, o
+            torch.cuda.empty_cache()
+    for kind, (fl, us) in tot.items():
+        tf = fl / us * 1e-6
+        out[kind] = {"tflops": round(tf, 1), "frac_of_fp4_peak": round(tf / FP4_PEAK_TFLOPS, 4)}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
+    if args.gemm_data:
+        gemm_data()
+        return
     if args.copy_calibration:
         copy_calibration()
         return
