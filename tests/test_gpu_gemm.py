@@ -421,3 +421,20 @@ def test_non_finite_blocks_give_nan_outputs(M, N, K):
     ref, absref = oracle_nt(a2, b2)  # the finite outputs do not depend on the non-finite rows
     keep = ~nan_mask
     assert_gemm_close(np.where(keep, got, 0.0), np.where(keep, ref, 0.0), absref, "non-finite %dx%dx%d" % (M, N, K))
+
+
+# Outputs past 2^31 elements (the row offset m * ldo past 32 bits): 32768 x 66560 on the persistent kernel
+# (N % 8 == 0; 33280 tiles of 256 x 256 in 130 rounds) and 32768 x 66564 on the pipelined one (N % 8 == 4,
+# 8-byte stores), K = 32 (one block per output: the launch is output-bound); every output against the
+# device reference of the oracle's copies.
+@pytest.mark.slow
+@pytest.mark.parametrize("N", [66560, 66564], ids=["persistent", "pipelined"])
+def test_gemm_output_past_2_31_elements(N):
+    M, K = 32768, 32
+    assert M * N > 2 ** 31
+    a = W.ragged_values((M, K), 111)
+    b = W.ragged_values((N, K), 113 + N)
+    say("gemm_nt output past 2^31 elements M=%d N=%d K=%d" % (M, N, K))
+    out = mx.gemm_nt(mx.cast(to_device(a)), mx.cast(to_device(b)))
+    torch.cuda.synchronize()
+    assert_gemm_whole(out, oracle.cast_rows(a), oracle.cast_rows(b), "output past 2^31 %dx%d" % (M, N))
