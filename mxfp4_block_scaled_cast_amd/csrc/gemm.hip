@@ -14,6 +14,10 @@
 // lane needs over a 256-wide K range into one dword.  Accumulation is fp32;
 // the epilogue rounds to bf16 (nearest even).
 //
+// The training backward's two products (dA on dOut's row copy and W's column
+// copy, dB on the column copies of dOut and A) can share one persistent launch,
+// the chip's XCDs divided between them (mx_launch_gemm_pair_ws).
+//
 // The same kernels also run the MXFP8 product of the FP8 dB variant (format
 // code 0, E4M3 on both sides): an FP8 code tile has the FP4 tile's geometry
 // in bytes (64 bytes per row = one 64-wide K step), so loads, LDS stages and
