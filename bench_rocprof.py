@@ -34,11 +34,19 @@ GEMM_SOURCES = [os.path.join(PKG, "csrc", f) for f in ("gemm.hip", "mx_device.h"
 CAST_SOURCES = [os.path.join(PKG, "csrc", f) for f in ("cast.hip", "mx_device.h", "mx_host.h")]
 
 
+def _code_only(text):
+    """The source without its comments and blank lines (a comment edit leaves the kernels, and so
+    the counters taken on them, unchanged).  String literals holding // or /* are not expected."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def source_hash(paths):
     h = hashlib.sha256()
     for p in paths:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
