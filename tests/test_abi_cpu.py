@@ -475,3 +475,19 @@ def test_pair_gemm_argument_validation():
     assert f(*good[:4], 0, 4, 32, None, 4, *good[:4], 4, 0, 32, None, 4, None, 0, None) == 0   # both empty
     if _no_gpu():
         assert f(*good, *good, None, 0, None) == -3
+
+
+def test_counter_summary_hash_follows_code_not_comments(tmp_path):
+    # the committed HBM counter figure is reported only while the GEMM sources' code is the code it
+    # was measured on: comments and blank lines do not count, a changed statement does
+    import sys
+    sys.path.insert(0, ROOT)
+    import bench_rocprof as rs
+    src = "int f(int x) {\n    return x + 1;  // one more\n}\n"
+    p = tmp_path / "k.hip"
+    p.write_text(src)
+    h0 = rs.source_hash([str(p)])
+    p.write_text("/* a kernel */\n" + src.replace("// one more", "// one more than x") + "\n\n")
+    assert rs.source_hash([str(p)]) == h0
+    p.write_text(src.replace("x + 1", "x + 2"))
+    assert rs.source_hash([str(p)]) != h0
