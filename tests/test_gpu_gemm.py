@@ -344,11 +344,15 @@ def test_split_contraction(M, N, K):
 PAIRS = [((2048, 4096, 4096), (4096, 4096, 2048), 4), ((2048, 4096, 512), (4096, 2048, 256), 4),
          ((2100, 4000, 1056), (4000, 2056, 2080), 3), ((4096, 4096, 1024), (2048, 4096, 8192), 2),
          ((2048, 4032, 1024), (2048, 4096, 1024), 4), ((17, 4096, 4096), (4096, 4096, 1024), 0),
-         ((2048, 4096, 512), (4096, 2048, 1024), 0)]
+         ((2048, 4096, 512), (4096, 2048, 1024), 0),
+         ((2048, 4096, 1024), (2048, 4096, 8192), 1), ((8192, 8192, 1024), (2048, 4096, 4096), 5),
+         ((4096, 8192, 1024), (2048, 4096, 1024), 6), ((8192, 8192, 1024), (2048, 4096, 1024), 7)]
 
 
+# (the last four take the remaining splits: 1 + 7, 5 + 3, 6 + 2 and 7 + 1 XCDs)
 @pytest.mark.parametrize("s0,s1,split", PAIRS, ids=["step", "one-trip", "ragged-3-5", "uneven-2-6", "partial-col",
-                                                    "skinny-tiled", "trips-differ"])
+                                                    "skinny-tiled", "trips-differ", "xcds-1-7", "xcds-5-3",
+                                                    "xcds-6-2", "xcds-7-1"])
 def test_gemm_pair(s0, s1, split):
     assert mx.gemm_pair_split(*s0, *s1) == split
     ops, copies = [], []
