@@ -442,3 +442,25 @@ def test_gemm_output_past_2_31_elements(N):
     out = mx.gemm_nt(mx.cast(to_device(a)), mx.cast(to_device(b)))
     torch.cuda.synchronize()
     assert_gemm_whole(out, oracle.cast_rows(a), oracle.cast_rows(b), "output past 2^31 %dx%d" % (M, N))
+
+
+# A seeded draw of shapes across the launch-selection boundaries (numpy default_rng(2024): a small side
+# below 128, both sides 128..1500, both 1500..5000, and odd N; K a multiple of 32 up to 2528; half of
+# them transposed), each through mxfp4_gemm_nt_ws with the workspace its split needs; every output
+# against the device reference of the oracle's copies.
+RANDOM_SHAPES = [(4055, 31, 256), (422, 1374, 2048), (1997, 1774, 2208), (5655, 1236, 928), (3532, 59, 2048),
+                 (797, 974, 1440), (2209, 3127, 192), (4063, 3926, 1536), (1238, 17, 1952), (1117, 735, 2240),
+                 (2459, 2787, 2048), (2259, 3421, 704), (100, 2803, 2464), (490, 973, 736), (2772, 3205, 1248),
+                 (2965, 2404, 2272), (41, 1471, 1632), (1242, 381, 1408), (1749, 4418, 224), (2495, 2046, 608),
+                 (4177, 24, 1376), (1486, 590, 704), (3495, 3499, 2336), (2001, 4429, 512)]
+
+
+@pytest.mark.parametrize("M,N,K", RANDOM_SHAPES)
+def test_random_shapes_whole_output(M, N, K):
+    a = W.ragged_values((M, K), 7 * M + 3 * K)
+    b = W.ragged_values((N, K), 11 * N + 5 * K)
+    ws = mx.gemm_workspace([(M, N, K)], "cuda:0")
+    say("gemm_nt_ws random shape M=%d N=%d K=%d" % (M, N, K))
+    out = mx.gemm_nt(mx.cast(to_device(a)), mx.cast(to_device(b)), ws=ws)
+    torch.cuda.synchronize()
+    assert_gemm_whole(out, oracle.cast_rows(a), oracle.cast_rows(b), "random %dx%dx%d" % (M, N, K))
