@@ -200,3 +200,32 @@ def test_dual_cast_past_2_31_elements():
     del q, s
     q, s = oracle.cast_cols(bits)
     assert_operand_equal(t.col, q, s, "2^31+ column copy")
+
+
+# Seeded random shapes (numpy default_rng(77), plus two just under the switch) on both sides of the
+# launcher's tile switch: casts of up to 4096 tiles of 64 rows take 32-row tiles, larger ones 64-row
+# tiles (9224 x 8160: 4640 tiles; 9224 x 7168: 4060; 16138 x 4000: 4048), rows and columns not
+# multiples of the tile; row cast and dual cast, every byte of every copy against the oracle.
+RANDOM_CAST_SHAPES = [(180, 5024), (1904, 3520), (2386, 1568), (2595, 2144), (2905, 2048), (1073, 2496),
+                      (9224, 8160), (5452, 14528), (7367, 10080), (16138, 4480), (9224, 7168), (16138, 4000)]
+
+
+@pytest.mark.parametrize("R,C", RANDOM_CAST_SHAPES)
+def test_random_shapes(R, C):
+    run_both(W.ragged_values((R, C), 13 * R + C), "random")
+
+
+# Pairs in one launch, the switch decided on both tensors' tiles together (1815, 4025 and 926 tiles:
+# 32-row tiles for all three).
+@pytest.mark.parametrize("shape0,shape1", [((8768, 1056), (7175, 2464)), ((6396, 5600), (4617, 6240)),
+                                           ((2636, 4576), (2138, 1216))])
+def test_random_shape_pairs(shape0, shape1):
+    a = W.ragged_values(shape0, 17 * shape0[0] + shape0[1])
+    b = W.ragged_values(shape1, 19 * shape1[0] + shape1[1])
+    say("cast_dual_pair random %s %s" % (shape0, shape1))
+    ta, tb = mx.cast_dual_pair(to_device(a), to_device(b))
+    torch.cuda.synchronize()
+    check_row(a, ta.row, "random pair A row")
+    check_col(a, ta.col, "random pair A col")
+    check_row(b, tb.row, "random pair B row")
+    check_col(b, tb.col, "random pair B col")
