@@ -11,7 +11,7 @@ import torch
 import oracle
 import mxfp4_block_scaled_cast_amd as mx
 from mxfp4_block_scaled_cast_amd import workloads as W
-from gpu_util import say, to_device, bf16_to_f64, assert_gemm_close
+from gpu_util import say, to_device, bf16_to_f64, assert_gemm_close, assert_gemm_whole
 
 pytestmark = pytest.mark.gpu
 
@@ -136,3 +136,28 @@ def test_cached_weight_inference_and_role_checks():
     assert q1 is not q2 and ws.misses == 2
     # doubling W moves every nonzero block's scale up by one (codes unchanged)
     assert torch.equal(q1.row.q, q2.row.q)
+
+
+# Seeded random steps (numpy default_rng(99): M in 1..6000, N and K multiples of 32 up to 5088) through
+# the autograd wrapper: fwd, dA and dB (the backward's pair call, one launch for 5749 x 2592 x 3872, two
+# for the others), every output against the device reference of the oracle's copies.
+RANDOM_STEPS = [(5749, 2592, 3872), (3390, 928, 2624), (5651, 4960, 4928), (3689, 1600, 2912),
+                (3899, 1472, 4896), (3327, 1792, 2400), (639, 3104, 1760), (5582, 1536, 1280),
+                (3615, 1600, 1760), (2347, 3520, 1376)]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("M,N,K", RANDOM_STEPS)
+def test_random_steps_whole_output(M, N, K):
+    a = W.ragged_values((M, K), 3 * M + 5 * K)
+    w = W.ragged_values((N, K), 7 * N + 11 * K)
+    dout = W.ragged_values((M, N), 13 * M + 17 * N)
+    say("gemm_fp4_bf16 random step M=%d N=%d K=%d" % (M, N, K))
+    at = to_device(a).requires_grad_(True)
+    wt = to_device(w).requires_grad_(True)
+    out = mx.gemm_fp4_bf16(at, wt)
+    out.backward(to_device(dout))
+    torch.cuda.synchronize()
+    assert_gemm_whole(out.detach(), oracle.cast_rows(a), oracle.cast_rows(w), "random step fwd")
+    assert_gemm_whole(at.grad, oracle.cast_rows(dout), oracle.cast_cols(w), "random step dA")
+    assert_gemm_whole(wt.grad, oracle.cast_cols(dout), oracle.cast_cols(a), "random step dB")
