@@ -161,3 +161,31 @@ def test_random_steps_whole_output(M, N, K):
     assert_gemm_whole(out.detach(), oracle.cast_rows(a), oracle.cast_rows(w), "random step fwd")
     assert_gemm_whole(at.grad, oracle.cast_rows(dout), oracle.cast_cols(w), "random step dA")
     assert_gemm_whole(wt.grad, oracle.cast_cols(dout), oracle.cast_cols(a), "random step dB")
+
+
+# The same kind of seeded random steps with the Hadamard gradient recipe (dA, dB on transformed copies:
+# dOut's divided by 32) and with the FP8 wgrad (dB an MXFP8 product, its bar widened by the MFMA's
+# in-group truncation envelope); every output against the device reference of the oracle's copies.
+@pytest.mark.slow
+@pytest.mark.parametrize("M,N,K", RANDOM_STEPS[:5])
+@pytest.mark.parametrize("variant", ["hadamard", "fp8wgrad"])
+def test_random_variant_steps_whole_output(M, N, K, variant):
+    a = W.ragged_values((M, K), 3 * M + 5 * K + 1)
+    w = W.ragged_values((N, K), 7 * N + 11 * K + 1)
+    dout = W.ragged_values((M, N), 13 * M + 17 * N + 1)
+    say("gemm_fp4_bf16 random %s step M=%d N=%d K=%d" % (variant, M, N, K))
+    at = to_device(a).requires_grad_(True)
+    wt = to_device(w).requires_grad_(True)
+    out = mx.gemm_fp4_bf16(at, wt, hadamard_grad=variant == "hadamard", fp8_wgrad=variant == "fp8wgrad")
+    out.backward(to_device(dout))
+    torch.cuda.synchronize()
+    assert_gemm_whole(out.detach(), oracle.cast_rows(a), oracle.cast_rows(w), "random %s fwd" % variant)
+    if variant == "hadamard":
+        assert_gemm_whole(at.grad, oracle.cast_rows_hadamard(dout, 5), oracle.cast_cols_hadamard(w, 0),
+                          "random hadamard dA")
+        assert_gemm_whole(wt.grad, oracle.cast_cols_hadamard(dout, 5), oracle.cast_cols_hadamard(a, 0),
+                          "random hadamard dB")
+    else:
+        assert_gemm_whole(at.grad, oracle.cast_rows(dout), oracle.cast_cols(w), "random fp8wgrad dA")
+        assert_gemm_whole(wt.grad, oracle.cast_cols_fp8(dout), oracle.cast_cols_fp8(a), "random fp8wgrad dB",
+                          fmt=8)
