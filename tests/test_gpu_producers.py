@@ -47,7 +47,9 @@ def silu_inputs(R, F, seed):
 
 
 @pytest.mark.parametrize("col_fmt", [4, 8])
-@pytest.mark.parametrize("R,F", [(1, 32), (17, 96), (64, 256), (100, 800), (257, 2080), (1024, 14336)])
+# the last two drawn at random (rows not a multiple of any tile, F a multiple of 32)
+@pytest.mark.parametrize("R,F", [(1, 32), (17, 96), (64, 256), (100, 800), (257, 2080), (1024, 14336), (2777, 1376),
+                                 (513, 5056)])
 def test_silu_mul_cast(R, F, col_fmt):
     x = silu_inputs(R, F, 7 * R + F)
     say("silu_mul_cast R=%d F=%d col_fmt=%d" % (R, F, col_fmt))
@@ -83,7 +85,8 @@ def rms_inputs(R, D, seed):
 
 @pytest.mark.parametrize("col_fmt", [4, 8])
 @pytest.mark.parametrize("with_residual", [False, True])
-@pytest.mark.parametrize("R,D", [(1, 32), (17, 96), (64, 4096), (300, 800), (1000, 4096)])
+@pytest.mark.parametrize("R,D", [(1, 32), (17, 96), (64, 4096), (300, 800), (1000, 4096), (3001, 2912),
+                                 (129, 7168)])
 def test_rmsnorm_cast(R, D, with_residual, col_fmt):
     x, gamma = rms_inputs(R, D, 11 * R + D)
     res = W.ragged_values((R, D), R + 5 * D, lo=-20, hi=20) if with_residual else None
