@@ -19,7 +19,7 @@
  *   each element is x / 2^X rounded to the nearest E2M1 value (ties to the
  *   even code, saturating at +-6), sign bit copied from x (so -0 and small
  *   negatives give code 0x8).  A block holding Inf/NaN gets scale 0xFF and
- *   codes 0.
+ *   codes 0; every GEMM output whose dot product takes in such a block is NaN.
  *
  * Conventions for every entry point:
  *   - All data pointers are DEVICE memory owned by the caller; the library
