@@ -25,6 +25,7 @@
 // 32+16h .. 47+16h of the step (two 16-byte pieces), while the scale of K
 // block b still comes from lane half b % 2.
 #include <algorithm>
+#include <cmath>
 #include <type_traits>
 
 #include "mx_device.h"
@@ -841,13 +842,20 @@ static bool persist_ok(const uint16_t* o16, int64_t ldo, int64_t N) {
 
 // Two independent products in one persistent launch (XCDs split between them) or one after the
 // other, by a cost model in K tiles per workgroup: a tile costs its K tiles (a multiple of 4)
-// plus kEpiKTiles (its epilogue), and a second launch kLaunchKTiles more.  The pair is taken
-// only when it comes out at least 1% cheaper: what it gains is the tail of a partial last round
-// (8B QKV's dB, 384 tiles: -6.5% on dA + dB; the MLP down projection's dB, 896 tiles: -1.9%),
-// while two large products in one launch share the caches between them (70B down, 3584 + 3584
-// tiles in even rounds either way: +1.3% paired).
+// plus kEpiKTiles (its epilogue), and a second launch kLaunchKTiles more.  A launch whose
+// balanced grid leaves CUs idle runs each round faster (the others clock higher under the power
+// limit): measured 0.904x per round on 224 of 256 CUs and 0.816x on 192, i.e. about
+// (grid / CUs)^0.7, which the model applies to each of the two launches, no lower than the
+// 0.8x measured (the clock has a ceiling; smaller grids were not measured).  The pair is taken only
+// when it comes out at least 1% cheaper: what it gains is the tail of a partial last round (8B
+// QKV's dB, 384 tiles: -6.5% on dA + dB; the MLP down projection's dB, 896 tiles: -1.9%), while
+// two large products in one launch share the caches between them (70B down, 3584 + 3584 tiles in
+// even rounds either way: +1.3% paired; 4096 x 14336 over 128256 beside 128256 x 14336 over 4096:
+// +7% paired).
 constexpr int64_t kEpiKTiles = 1;
 constexpr int64_t kLaunchKTiles = 3;
+constexpr double kIdleCuExponent = 0.7;
+constexpr double kIdleCuFloor = 0.8;
 
 struct PairPlan {
     bool pair;
@@ -861,13 +869,18 @@ static PairPlan plan_pair(int64_t tiles0, int64_t kt0, int64_t tiles1, int64_t k
     if (cus != kXcds * kPerXcd) return P;
     const int64_t c0 = kt0 + kEpiKTiles, c1 = kt1 + kEpiKTiles;
     const auto rounds = [](int64_t t, int64_t g) { return (t + g - 1) / g; };
-    // one after the other: both launches' rounds and one more launch cost than the pair
-    const int64_t seq = rounds(tiles0, cus) * c0 + rounds(tiles1, cus) * c1 + kLaunchKTiles;
-    int64_t best = seq;
+    // one launch alone: its rounds, each shortened when its balanced grid leaves CUs idle
+    const auto alone = [&](int64_t t, int64_t c) {
+        const double busy = (double)balanced_grid(t, cus) / (double)cus;
+        return (double)(rounds(t, cus) * c) * std::max(std::pow(busy, kIdleCuExponent), kIdleCuFloor);
+    };
+    // one after the other: both launches and one more launch cost than the pair
+    const double seq = alone(tiles0, c0) + alone(tiles1, c1) + (double)kLaunchKTiles;
+    double best = seq;
     for (int s = 1; s < kXcds; ++s) {
         const int64_t w0 = s * kPerXcd, w1 = (kXcds - s) * kPerXcd;
-        const int64_t t = std::max(rounds(tiles0, w0) * c0, rounds(tiles1, w1) * c1);
-        if (t < best && t * 100 <= seq * 99) {
+        const double t = (double)std::max(rounds(tiles0, w0) * c0, rounds(tiles1, w1) * c1);
+        if (t < best && t <= 0.99 * seq) {
             best = t;
             P = PairPlan{true, s, balanced_grid(tiles0, w0), balanced_grid(tiles1, w1)};
         }

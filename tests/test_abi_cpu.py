@@ -453,7 +453,11 @@ def test_pair_split_query():
     for M, Nn, K in [(8192, 28672, 4096), (8192, 10240, 8192), (8192, 57344, 8192), (8192, 8192, 28672)]:
         assert f(M, K, Nn, Nn, K, M) == 0, (M, Nn, K)
     assert f(2100, 4000, 1056, 4000, 2056, 2080) == 3
-    assert f(4096, 4096, 1024, 2048, 4096, 8192) == 2
+    assert f(2048, 4000, 640, 2100, 6144, 640) == 2
+    assert f(8192, 8192, 640, 2048, 4000, 640) == 7
+    # a partial round alone runs faster on its idle CUs' power: kept as two launches
+    assert f(4096, 14336, 128256, 128256, 14336, 4096) == 0
+    assert f(4096, 4096, 1024, 2048, 4096, 8192) == 0
     assert f(17, 4096, 4096, 4096, 4096, 1024) == 0
     assert f(2048, 4096, 512, 4096, 2048, 1024) == 0
     assert f(2048, 4092, 1024, 2048, 4096, 1024) == 0

@@ -336,23 +336,24 @@ def test_split_contraction(M, N, K):
 # launches (one persistent grid, XCDs 0..s-1 on the first product, the rest on the second): the dA /
 # dB shapes of a 2048 x 4096 x 2048 step (4 + 4 XCDs), one trip per tile (K = 512 and 256), a
 # ragged pair (9 x 16 tiles each, K = 1056 and 2080: 3 + 5 XCDs, so the slot mapping runs over 3
-# and 5 XCDs), an uneven pair (256 tiles over 1024 and 128 over 8192: 2 + 6 XCDs, part of the
-# second product's workgroups idle) and a partial last tile column (N = 4032).  Two launches: a
-# skinny product beside a tiled one (with its split contraction in ws), and tiled products whose
-# trip structures differ (one trip per tile against two).  Every output against the device reference
-# of the oracle's copies, and bit for bit against its own mxfp4_gemm_nt_ws call.
+# and 5 XCDs), a partial last tile column (N = 4032), and the remaining splits 1 + 7, 2 + 6, 5 + 3,
+# 6 + 2 and 7 + 1 at K = 640 (two trips per tile, the second half past K; the smaller product's
+# grid leaves part of its XCDs' workgroups idle).  Two launches: a skinny product beside a tiled
+# one (with its split contraction in ws), tiled products whose trip structures differ (one trip per
+# tile against two), and an uneven pair the cost model keeps apart.  Every output against the device
+# reference of the oracle's copies, and bit for bit against its own mxfp4_gemm_nt_ws call.
 PAIRS = [((2048, 4096, 4096), (4096, 4096, 2048), 4), ((2048, 4096, 512), (4096, 2048, 256), 4),
-         ((2100, 4000, 1056), (4000, 2056, 2080), 3), ((4096, 4096, 1024), (2048, 4096, 8192), 2),
-         ((2048, 4032, 1024), (2048, 4096, 1024), 4), ((17, 4096, 4096), (4096, 4096, 1024), 0),
-         ((2048, 4096, 512), (4096, 2048, 1024), 0),
-         ((2048, 4096, 1024), (2048, 4096, 8192), 1), ((8192, 8192, 1024), (2048, 4096, 4096), 5),
-         ((4096, 8192, 1024), (2048, 4096, 1024), 6), ((8192, 8192, 1024), (2048, 4096, 1024), 7)]
+         ((2100, 4000, 1056), (4000, 2056, 2080), 3), ((2048, 4032, 1024), (2048, 4096, 1024), 4),
+         ((2048, 4000, 640), (6144, 8192, 640), 1), ((2048, 4000, 640), (2100, 6144, 640), 2),
+         ((2100, 8192, 640), (2048, 4000, 640), 5), ((6144, 4000, 640), (2048, 4000, 640), 6),
+         ((8192, 8192, 640), (2048, 4000, 640), 7),
+         ((17, 4096, 4096), (4096, 4096, 1024), 0), ((2048, 4096, 512), (4096, 2048, 1024), 0),
+         ((4096, 4096, 1024), (2048, 4096, 8192), 0)]
 
 
-# (the last four take the remaining splits: 1 + 7, 5 + 3, 6 + 2 and 7 + 1 XCDs)
-@pytest.mark.parametrize("s0,s1,split", PAIRS, ids=["step", "one-trip", "ragged-3-5", "uneven-2-6", "partial-col",
-                                                    "skinny-tiled", "trips-differ", "xcds-1-7", "xcds-5-3",
-                                                    "xcds-6-2", "xcds-7-1"])
+@pytest.mark.parametrize("s0,s1,split", PAIRS, ids=["step", "one-trip", "ragged-3-5", "partial-col", "xcds-1-7",
+                                                    "xcds-2-6", "xcds-5-3", "xcds-6-2", "xcds-7-1", "skinny-tiled",
+                                                    "trips-differ", "uneven-apart"])
 def test_gemm_pair(s0, s1, split):
     assert mx.gemm_pair_split(*s0, *s1) == split
     ops, copies = [], []

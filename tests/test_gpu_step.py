@@ -47,13 +47,30 @@ def test_step_matches_oracle(M, N, K):
 
 
 # Steps whose dA and dB run as one paired launch (the XCDs divided between them): 2048 x 2048 x 4096
-# (128 tiles each, 4 + 4 XCDs) and a ragged 2100 x 2080 x 4000 (144 tiles each, 3 + 5 XCDs, M padded
-# to 2112 in the column copies).
-@pytest.mark.parametrize("M,N,K", [(2048, 2048, 4096), (2100, 2080, 4000)])
-def test_step_paired_backward_matches_oracle(M, N, K):
-    Mp = -(-M // 32) * 32
-    assert mx.gemm_pair_split(M, K, N, N, K, Mp) > 0, "dA and dB should share one launch"
+# (128 tiles each, 4 + 4 XCDs) against the oracle's GEMM, and a ragged 5000 x 3072 x 3104 (dA 240
+# tiles over 3072, dB 156 tiles over 5024, M padded to 5024 in the column copies: 3 + 5 XCDs)
+# against the device reference of the oracle's copies.
+def test_step_paired_backward_matches_oracle():
+    M, N, K = 2048, 2048, 4096
+    assert mx.gemm_pair_split(M, K, N, N, K, M) == 4, "dA and dB should share one launch"
     test_step_matches_oracle(M, N, K)
+
+
+def test_ragged_step_paired_backward_whole_output():
+    M, N, K = 5000, 3072, 3104
+    assert mx.gemm_pair_split(M, K, N, N, K, 5024) == 3, "dA and dB should share one launch"
+    a = W.ragged_values((M, K), 31)
+    w = W.ragged_values((N, K), 37)
+    dout = W.ragged_values((M, N), 41)
+    say("gemm_fp4_bf16 ragged paired step M=%d N=%d K=%d" % (M, N, K))
+    at = to_device(a).requires_grad_(True)
+    wt = to_device(w).requires_grad_(True)
+    out = mx.gemm_fp4_bf16(at, wt)
+    out.backward(to_device(dout))
+    torch.cuda.synchronize()
+    assert_gemm_whole(out.detach(), oracle.cast_rows(a), oracle.cast_rows(w), "ragged paired step fwd")
+    assert_gemm_whole(at.grad, oracle.cast_rows(dout), oracle.cast_cols(w), "ragged paired step dA")
+    assert_gemm_whole(wt.grad, oracle.cast_cols(dout), oracle.cast_cols(a), "ragged paired step dB")
 
 
 def test_inference_forward_uses_row_copies_only():
@@ -139,8 +156,8 @@ def test_cached_weight_inference_and_role_checks():
 
 
 # Seeded random steps (numpy default_rng(99): M in 1..6000, N and K multiples of 32 up to 5088) through
-# the autograd wrapper: fwd, dA and dB (the backward's pair call, one launch for 5749 x 2592 x 3872, two
-# for the others), every output against the device reference of the oracle's copies.
+# the autograd wrapper: fwd, dA and dB (the backward's pair call, which runs these as two launches),
+# every output against the device reference of the oracle's copies.
 RANDOM_STEPS = [(5749, 2592, 3872), (3390, 928, 2624), (5651, 4960, 4928), (3689, 1600, 2912),
                 (3899, 1472, 4896), (3327, 1792, 2400), (639, 3104, 1760), (5582, 1536, 1280),
                 (3615, 1600, 1760), (2347, 3520, 1376)]
