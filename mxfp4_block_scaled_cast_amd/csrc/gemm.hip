@@ -388,8 +388,11 @@ constexpr int kEpiStores = 32;  // 16-byte output stores per wave per tile (pers
 // final trip of a tile) for K tile U of the next output tile; both land in
 // stage U.  With POST (first trip after an epilogue) the waits of the first
 // three iterations also let the epilogue's stores, issued after the DMA of K
-// tile 3, be outstanding.
-template <int U, bool POST = false, bool LAST = false, int FMT = 4>
+// tile 3, be outstanding.  MFMA_LIVE: K tile kt holds contraction data (off
+// for the K tiles that one-trip launches run wholly past K: their MFMAs would
+// add zeros); READ_LIVE: the K tile read into registers here (kt+1, or the next
+// output tile's K tile 0) does.  The DMA and the waits are the same either way.
+template <int U, bool POST = false, bool LAST = false, int FMT = 4, bool MFMA_LIVE = true, bool READ_LIVE = true>
 __device__ __forceinline__ void pipe_iter(f32x16 (&acc)[4][4], TileRegs& cur, TileRegs& nxt, const DmaPlan& P,
                                           const TileSrc& Scur, const TileSrc& Snext, bool next_ok,
                                           const ReadPlan& R, lds_cptr lds, int kt, int nkt) {
@@ -414,10 +417,12 @@ __device__ __forceinline__ void pipe_iter(f32x16 (&acc)[4][4], TileRegs& cur, Ti
     lds_cptr next = lds + ((U + 1) % NST) * STAGE;
     if constexpr (FMT == 4) {
         constexpr int OP = (U & 1) * 2;  // tile kt uses bytes 2*(kt%2) and 2*(kt%2)+1 of its scale dwords
+        if constexpr (MFMA_LIVE) {
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            mfma_one<OP>(acc, cur.a0, cur.b0, cur.sa, cur.sb, q);
-            order_point();
+            for (int q = 0; q < 16; ++q) {
+                mfma_one<OP>(acc, cur.a0, cur.b0, cur.sa, cur.sb, q);
+                order_point();
+            }
         }
         // tile kt+1 has landed (tiles kt+2 and kt+3 may be in flight), this wave's
         // LDS reads are done, and after the barrier nobody reads stage U any more
@@ -428,9 +433,11 @@ __device__ __forceinline__ void pipe_iter(f32x16 (&acc)[4][4], TileRegs& cur, Ti
             // the scales and step-0 data of tile kt+1 (reads 0..15; the scales only for
             // the first K tile of a scale tile) go first: they are needed first
             const int r0 = (q * 3) / 2, r1 = ((q + 1) * 3) / 2;
+            if constexpr (READ_LIVE) {
 #pragma unroll
-            for (int r = r0; r < r1; ++r)
-                if (r >= R0) read_one<FMT>(nxt, R, next, r);
+                for (int r = r0; r < r1; ++r)
+                    if (r >= R0) read_one<FMT>(nxt, R, next, r);
+            }
             // DMA instructions 0..7 before the odd MFMAs, 8 (scales, even K tiles) before MFMA 14
             if (q == 1) dma_one<DST, 0, FMT>(P, S, dkt, valid);
             if (q == 3) dma_one<DST, 1, FMT>(P, S, dkt, valid);
@@ -442,17 +449,19 @@ __device__ __forceinline__ void pipe_iter(f32x16 (&acc)[4][4], TileRegs& cur, Ti
             if constexpr (DMA_SCALES)
                 if (q == 14) dma_one<DST, 8, FMT>(P, S, dkt, valid);
             if (q == 15) dma_one<DST, 7, FMT>(P, S, dkt, valid);
-            mfma_one<OP + 1>(acc, cur.a1, cur.b1, cur.sa, cur.sb, q);
+            if constexpr (MFMA_LIVE) mfma_one<OP + 1>(acc, cur.a1, cur.b1, cur.sa, cur.sb, q);
             order_point();
         }
     } else {
         // FP8: one 64-wide K step per tile, each MFMA twice as long; a0/a1 (b0/b1) are registers
         // 0-3 / 4-7 of a lane's 32-byte operand; tile kt uses byte kt%4 of its scale dwords
         constexpr int OP = U;
+        if constexpr (MFMA_LIVE) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            mfma8_one<OP>(acc, cur, q);
-            order_point();
+            for (int q = 0; q < 8; ++q) {
+                mfma8_one<OP>(acc, cur, q);
+                order_point();
+            }
         }
         wait_vmcnt<WAIT, true>();
         __syncthreads();
@@ -460,9 +469,11 @@ __device__ __forceinline__ void pipe_iter(f32x16 (&acc)[4][4], TileRegs& cur, Ti
         for (int q = 8; q < 16; ++q) {
             // the reads of tile kt+1 (24, or 16 without the scales; every MFMA of the next
             // tile needs both halves)
+            if constexpr (READ_LIVE) {
 #pragma unroll
-            for (int r = (q - 8) * 3; r < (q - 7) * 3; ++r)
-                if (r >= R0) read_one<FMT>(nxt, R, next, r);
+                for (int r = (q - 8) * 3; r < (q - 7) * 3; ++r)
+                    if (r >= R0) read_one<FMT>(nxt, R, next, r);
+            }
             if (q == 8) dma_one<DST, 0, FMT>(P, S, dkt, valid);
             if (q == 9) dma_one<DST, 1, FMT>(P, S, dkt, valid);
             if (q == 10) dma_one<DST, 2, FMT>(P, S, dkt, valid);
@@ -474,21 +485,25 @@ __device__ __forceinline__ void pipe_iter(f32x16 (&acc)[4][4], TileRegs& cur, Ti
                 dma_one<DST, 7, FMT>(P, S, dkt, valid);
                 if constexpr (DMA_SCALES) dma_one<DST, 8, FMT>(P, S, dkt, valid);
             }
-            mfma8_one<OP>(acc, cur, q);
+            if constexpr (MFMA_LIVE) mfma8_one<OP>(acc, cur, q);
             order_point();
         }
     }
 }
 
-// Four iterations kt0 .. kt0+3 (kt0 a multiple of 4).
-template <bool POST, bool LAST, int FMT = 4>
+// Four iterations kt0 .. kt0+3 (kt0 a multiple of 4).  LIVE < 4 only for the one
+// trip of a tile whose contraction has LIVE K tiles (K tiles LIVE..3 past K): their
+// MFMAs and register reads are left out, the last iteration's read (the next output
+// tile's K tile 0) stays.
+template <bool POST, bool LAST, int FMT = 4, int LIVE = NST>
 __device__ __forceinline__ void pipe_trip(f32x16 (&acc)[4][4], TileRegs& r0, TileRegs& r1, const DmaPlan& P,
                                           const TileSrc& Scur, const TileSrc& Snext, bool next_ok,
                                           const ReadPlan& R, lds_cptr lds, int kt0, int nkt) {
-    pipe_iter<0, POST, LAST, FMT>(acc, r0, r1, P, Scur, Snext, next_ok, R, lds, kt0 + 0, nkt);
-    pipe_iter<1, POST, LAST, FMT>(acc, r1, r0, P, Scur, Snext, next_ok, R, lds, kt0 + 1, nkt);
-    pipe_iter<2, POST, LAST, FMT>(acc, r0, r1, P, Scur, Snext, next_ok, R, lds, kt0 + 2, nkt);
-    pipe_iter<3, POST, LAST, FMT>(acc, r1, r0, P, Scur, Snext, next_ok, R, lds, kt0 + 3, nkt);
+    static_assert(LIVE >= 1 && LIVE <= NST && (LIVE == NST || LAST), "dead K tiles only in a tile's one trip");
+    pipe_iter<0, POST, LAST, FMT, (0 < LIVE), (1 < LIVE)>(acc, r0, r1, P, Scur, Snext, next_ok, R, lds, kt0 + 0, nkt);
+    pipe_iter<1, POST, LAST, FMT, (1 < LIVE), (2 < LIVE)>(acc, r1, r0, P, Scur, Snext, next_ok, R, lds, kt0 + 1, nkt);
+    pipe_iter<2, POST, LAST, FMT, (2 < LIVE), (3 < LIVE)>(acc, r0, r1, P, Scur, Snext, next_ok, R, lds, kt0 + 2, nkt);
+    pipe_iter<3, POST, LAST, FMT, (3 < LIVE), true>(acc, r1, r0, P, Scur, Snext, next_ok, R, lds, kt0 + 3, nkt);
 }
 
 template <bool VEC_STORE, int FMT>
@@ -696,9 +711,12 @@ __device__ __forceinline__ int xcd_remap_n(int bid, int G, int nx) {
 // the others p1 (each XCD's L2 then holds the panels of one product); the
 // workgroups beyond a product's G leave at once.  Without PAIR, p0 runs on the
 // whole grid (G = gridDim.x).
-template <bool SINGLE, int FMT, bool PAIR>
+// LIVE (one trip per tile only): the K tiles that hold contraction data, the
+// larger of the two products' counts when PAIR.
+template <bool SINGLE, int FMT, bool PAIR, int LIVE = NST>
 __global__ __launch_bounds__(256, 1) void gemm_persist_kernel(PersistProblem p0, PersistProblem p1, int split_xcds,
                                                               int group_m) {
+    static_assert(SINGLE || LIVE == NST, "dead K tiles only with one trip per tile");
     __shared__ __attribute__((aligned(1024))) char lds_raw[NST * STAGE];
     lds_cptr lds = (lds_cptr)lds_raw;
 
@@ -772,7 +790,7 @@ __global__ __launch_bounds__(256, 1) void gemm_persist_kernel(PersistProblem p0,
         m0 = (int64_t)tm * PBM;
         n0 = (int64_t)tn * PBN;
         const TileSrc Sn = tile_src(aq, as, bq, bs, M, N, nkt, kt2, m0, n0, wave);
-        pipe_trip<POST, true, FMT>(acc, r0, r1, P, S, Sn, more, R, lds, kt0, nkt);
+        pipe_trip<POST, true, FMT, LIVE>(acc, r0, r1, P, S, Sn, more, R, lds, kt0, nkt);
         S = Sn;
 
         // stage 0 (the next tile's K tile 0, now in r0) is free until the next
@@ -902,6 +920,20 @@ static PairPlan plan_pair_for(int64_t M0, int64_t N0, int64_t K0, int64_t M1, in
     return plan_pair(tiles0, kt4(nkt0), tiles1, kt4(nkt1), cus);
 }
 
+// The persistent kernel for nkt K tiles per tile (the larger count of a pair): one trip per
+// tile up to NST K tiles, with the MFMAs of the K tiles past K left out.
+using PersistKernel = void (*)(PersistProblem, PersistProblem, int, int);
+template <int FMT, bool PAIR>
+static PersistKernel persist_kernel(int64_t nkt) {
+    switch (nkt) {
+    case 1: return gemm_persist_kernel<true, FMT, PAIR, 1>;
+    case 2: return gemm_persist_kernel<true, FMT, PAIR, 2>;
+    case 3: return gemm_persist_kernel<true, FMT, PAIR, 3>;
+    case NST: return gemm_persist_kernel<true, FMT, PAIR, NST>;
+    default: return gemm_persist_kernel<false, FMT, PAIR>;
+    }
+}
+
 template <int FMT>
 static hipError_t launch_gemm(const uint8_t* a8, const uint8_t* as8, const uint8_t* b8, const uint8_t* bs8, int64_t M,
                               int64_t N, int64_t K, uint16_t* o16, int64_t ldo, void* ws, int64_t ws_bytes,
@@ -919,7 +951,7 @@ static hipError_t launch_gemm(const uint8_t* a8, const uint8_t* as8, const uint8
         const int64_t grid = balanced_grid(tiles_all, num_cus());
         const PersistProblem p{a8, as8, b8, bs8, o16, ldo, (int)M, (int)N, (int)K, (int)tiles_m, (int)tiles_n,
                                (int)grid};
-        auto kern = nkt <= NST ? gemm_persist_kernel<true, FMT, false> : gemm_persist_kernel<false, FMT, false>;
+        auto kern = persist_kernel<FMT, false>(nkt);
         hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, stream, p, p, 8, kGroupM);
         return hipGetLastError();
     }
@@ -979,8 +1011,8 @@ extern "C" hipError_t mx_launch_gemm_pair_ws(const void* aq0, const void* as0, c
                                     static_cast<const uint8_t*>(bq1), static_cast<const uint8_t*>(bs1),
                                     o1, ldo1, (int)M1, (int)N1, (int)K1, (int)((M1 + PBM - 1) / PBM),
                                     (int)((N1 + PBN - 1) / PBN), (int)P.g1};
-            auto kern = (K0 + PBK - 1) / PBK <= NST ? gemm_persist_kernel<true, 4, true>
-                                                      : gemm_persist_kernel<false, 4, true>;
+            // both products have the same trip structure; one trip per tile runs the larger K-tile count
+            auto kern = persist_kernel<4, true>(std::max((K0 + PBK - 1) / PBK, (K1 + PBK - 1) / PBK));
             hipLaunchKernelGGL(kern, dim3((unsigned)cus), dim3(256), 0, stream, p0, p1, P.split_xcds, kGroupM);
             return hipGetLastError();
         }
