@@ -138,10 +138,11 @@ def test_ragged_small(M, N, K):
 
 
 # at least 128 output tiles of 256 x 256: persistent kernel with one trip per tile (K <= 256: four
-# 64-wide K tiles), several trips with a K tail (K not a multiple of 256), the pipelined kernel
-# (N % 8 != 0), ragged M / N edges
-@pytest.mark.parametrize("M,N,K", [(4096, 2048, 32), (2048, 4096, 256), (2100, 4000, 288), (4096, 2056, 800),
-                                   (2048, 4100, 1024), (2304, 3840, 1024), (3000, 2568, 1568)])
+# 64-wide K tiles, of which K = 32, 128, 192 and 256 fill 1, 2, 3 and 4), several trips with a K tail
+# (K not a multiple of 256), the pipelined kernel (N % 8 != 0), ragged M / N edges
+@pytest.mark.parametrize("M,N,K", [(4096, 2048, 32), (2048, 4096, 128), (2048, 4096, 192), (2048, 4096, 256),
+                                   (2100, 4000, 288), (4096, 2056, 800), (2048, 4100, 1024), (2304, 3840, 1024),
+                                   (3000, 2568, 1568)])
 def test_tiled_shapes(M, N, K):
     a = W.normal_bf16((M, K), 1.0, M + 5 * K)
     b = W.normal_bf16((N, K), 0.5, N + 13 * K)

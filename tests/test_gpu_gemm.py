@@ -465,3 +465,28 @@ def test_random_shapes_whole_output(M, N, K):
     out = mx.gemm_nt(mx.cast(to_device(a)), mx.cast(to_device(b)), ws=ws)
     torch.cuda.synchronize()
     assert_gemm_whole(out, oracle.cast_rows(a), oracle.cast_rows(b), "random %dx%dx%d" % (M, N, K))
+
+
+# One trip per tile with every count of K tiles that hold data (the kernel leaves out the MFMAs and
+# register reads of the K tiles wholly past K): K = 32 and 128 (1 of 4), 160 and 256 (2), 288 and 384
+# (3), 416 and 512 (4), on 2048 x 4096 outputs (128 tiles) and, paired, beside a product with fewer
+# live K tiles (the pair runs the larger count; the other product's extra K tiles add zeros).
+@pytest.mark.parametrize("K", [32, 128, 160, 256, 288, 384, 416, 512])
+def test_one_trip_live_k_tiles(K):
+    M, N = 2048, 4096
+    a = W.ragged_values((M, K), 51 + K)
+    b = W.ragged_values((N, K), 53 + K)
+    got = gpu_nt(a, b, "one trip, K = %d" % K)
+    ref, absref = oracle_nt(a, b)
+    assert_gemm_close(got, ref, absref, "one trip %dx%dx%d" % (M, N, K))
+    # paired with a 32-deep product: K tiles beyond the shorter product's own count add zeros
+    a2 = W.ragged_values((M, 32), 55 + K)
+    b2 = W.ragged_values((N, 32), 57 + K)
+    ops = [(mx.cast(to_device(a)), mx.cast(to_device(b))), (mx.cast(to_device(a2)), mx.cast(to_device(b2)))]
+    assert mx.gemm_pair_split(M, N, K, M, N, 32) in (0, 4)
+    say("gemm_nt_pair one trip K = %d and 32" % K)
+    o0, o1 = mx.gemm_nt_pair(ops[0][0], ops[0][1], ops[1][0], ops[1][1])
+    torch.cuda.synchronize()
+    assert_gemm_close(bf16_to_f64(o0), ref, absref, "paired one trip K = %d" % K)
+    ref2, absref2 = oracle_nt(a2, b2)
+    assert_gemm_close(bf16_to_f64(o1), ref2, absref2, "paired one trip K = 32 beside K = %d" % K)
